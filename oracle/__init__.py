@@ -1,0 +1,6 @@
+"""Float64 CPU oracle (test infrastructure; see mxfp4_oracle's header)."""
+from .mxfp4_oracle import (  # noqa: F401
+    E2M1_VALUES, E2M1_TABLE, SCALE_BIAS, split_nibbles, group_codes, scale_factor,
+    decode_rows, decode_expert, bucket_pairs, expert_linear, expert_linear_rows,
+    expert_linear_scalar,
+)

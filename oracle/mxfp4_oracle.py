@@ -1,0 +1,264 @@
+"""Float64 CPU oracle for the MXFP4 routed-expert linear.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module. The GPU library never imports it, and this
+module imports nothing from the library: the two share no code.
+
+What is computed. Page "MXFP4 Routed Expert Linear" (Kimi K3), section
+"Route, weight, and add the shared path", defines for every token t
+
+    y_t = y_t^shared + sum over selected experts e of p_{t,e} * W_e x_t
+
+where W_e (O rows by I = 32G columns) is held as packed bytes (E, O, G, 16)
+and scale bytes (E, O, G) (page "MXFP4 Experts", shape paragraph; page
+"MXFP4 Dequant", "How it works": the scale array has the packed array's
+shape without its last axis). The method has no approximation step: the
+decoded weights are exact, so this float64 oracle is the defining formula
+written out, and its only rounding is float64 accumulation.
+
+Decoding follows the pages:
+
+* one group is 16 bytes = 32 four-bit E2M1 codes plus one E8M0 scale byte
+  (page "MXFP4 Routed Expert Linear", "What is stored in one group");
+* every byte gives its low nibble first, then its high nibble, i.e.
+  n_lo = b mod 16, n_hi = floor(b / 16) (same section; page "MXFP4 Dequant",
+  "How it works");
+* a code indexes the 16-entry E2M1 table printed in the starter code;
+* each decoded value of a group is multiplied by 2^(s - 127) for the group's
+  scale byte s ("Apply the shared group scale"); the scale belongs to one
+  expert, one output row and one group;
+* group g fills input columns 32g .. 32g+31, and output coordinate o is the
+  dot product of the token with row o ("Reconstruct the matrix in the right
+  orientation").
+
+The steps of ``expert_linear`` follow the page's "Implementation order":
+start from a copy of the shared output, decode each selected expert once,
+multiply each token by its selected experts, weight and accumulate the
+contributions, then add them to the shared output.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+* every scale byte 0..255 follows 2^(s-127); 255 is not treated as NaN;
+* a token that lists the same expert twice gets both contributions
+  (the page speaks of a list of selected experts);
+* the mixture weights are used as given, never renormalised;
+* an expert index outside [0, E) violates a stated precondition; the oracle
+  raises ValueError.
+
+Parity status: every function here is pinned by tests against values the
+pages print, closed forms, invariants and a brute-force scalar version.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# The 16-entry E2M1 value table of the starter code (page "MXFP4 Routed
+# Expert Linear", "Starter Code"; the same table is printed in page
+# "MXFP4 Dequant", "How it works"). Index 8 is negative zero.
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+               -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0)
+E2M1_TABLE = np.array(E2M1_VALUES, dtype=np.float64)
+
+SCALE_BIAS = 127  # "Apply the shared group scale": factor 2^(s - 127)
+GROUP_BYTES = 16  # "What is stored in one group": sixteen bytes
+GROUP_VALUES = 32  # ... holding 32 four-bit codes
+
+
+# ---------------------------------------------------------------- decoding
+
+def split_nibbles(packed: np.ndarray):
+    """Low and high nibble of every byte: (b & 0xF, b >> 4).
+
+    Page "MXFP4 Routed Expert Linear", hints: a bit mask for the low nibble,
+    a right shift then the same mask for the high one.
+    """
+    b = np.asarray(packed, dtype=np.uint8)
+    return b & 0x0F, (b >> 4) & 0x0F
+
+
+def group_codes(packed: np.ndarray) -> np.ndarray:
+    """Codes of each 16-byte group in decode order: (..., 16) -> (..., 32).
+
+    Position 2j holds byte j's low nibble and position 2j+1 its high nibble
+    (decode the low nibble first, then the high nibble; interleave before
+    flattening).
+    """
+    lo, hi = split_nibbles(packed)
+    codes = np.stack([lo, hi], axis=-1)  # (..., 16, 2)
+    return codes.reshape(codes.shape[:-2] + (2 * codes.shape[-2],))
+
+
+def scale_factor(scales: np.ndarray) -> np.ndarray:
+    """2^(s - 127) for each scale byte, in float64 (exact for all 0..255)."""
+    s = np.asarray(scales, dtype=np.uint8).astype(np.int64)
+    return np.ldexp(np.ones(s.shape, dtype=np.float64), s - SCALE_BIAS)
+
+
+def decode_rows(packed_rows: np.ndarray, scales_rows: np.ndarray) -> np.ndarray:
+    """Decode rows of one expert: packed (R, G, 16), scales (R, G) -> (R, 32G).
+
+    Each group's 32 table values are multiplied by its own scale factor and
+    the groups are concatenated in order along the input axis.
+    """
+    packed_rows = np.asarray(packed_rows, dtype=np.uint8)
+    scales_rows = np.asarray(scales_rows, dtype=np.uint8)
+    if packed_rows.ndim != 3 or packed_rows.shape[-1] != GROUP_BYTES:
+        raise ValueError("packed rows must have shape (R, G, 16)")
+    if scales_rows.shape != packed_rows.shape[:-1]:
+        raise ValueError("scales must have the packed shape without its last axis")
+    values = E2M1_TABLE[group_codes(packed_rows)]  # (R, G, 32)
+    values = values * scale_factor(scales_rows)[..., None]
+    R, G = scales_rows.shape
+    return values.reshape(R, G * GROUP_VALUES)
+
+
+def decode_expert(packed_e: np.ndarray, scales_e: np.ndarray) -> np.ndarray:
+    """The full (O, 32G) float64 matrix W_e of one expert."""
+    return decode_rows(packed_e, scales_e)
+
+
+# --------------------------------------------------------------- bucketing
+
+def bucket_pairs(sel: np.ndarray, E: int) -> dict:
+    """Count-sort of (token, slot) pairs by expert, keeping pair order.
+
+    The pairs are numbered i = t*K + k. ``count[e]`` is how many pairs chose
+    e; ``offsets`` is the exclusive prefix sum of the counts (length E+1);
+    expert e owns the sorted positions offsets[e] .. offsets[e+1]-1, filled
+    with its pairs in increasing pair number (histogram, then scatter, as
+    the bucketed expert prefill does on page "MoE Expert Kernels: Grouped
+    Prefill and Mixed-Quant Compact Experts", section 2).
+    ``perm[position] = pair`` and ``slot_of_pair[pair] = position``.
+    A pair whose index is outside [0, E) gets no position
+    (slot_of_pair = -1) and is counted in ``n_invalid``.
+    """
+    flat = np.asarray(sel).reshape(-1).astype(np.int64)
+    P = flat.size
+    count = np.zeros(E, dtype=np.int64)
+    n_invalid = 0
+    for e in flat:  # histogram
+        if 0 <= e < E:
+            count[e] += 1
+        else:
+            n_invalid += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):  # exclusive prefix sum
+        offsets[e + 1] = offsets[e] + count[e]
+    cursor = offsets[:-1].copy()
+    perm = np.full(offsets[-1], -1, dtype=np.int64)
+    slot_of_pair = np.full(P, -1, dtype=np.int64)
+    for i, e in enumerate(flat):  # stable scatter in pair order
+        if 0 <= e < E:
+            perm[cursor[e]] = i
+            slot_of_pair[i] = cursor[e]
+            cursor[e] += 1
+    return {
+        "count": count.astype(np.int32),
+        "offsets": offsets.astype(np.int32),
+        "perm": perm.astype(np.int32),
+        "slot_of_pair": slot_of_pair.astype(np.int32),
+        "n_invalid": int(n_invalid),
+    }
+
+
+# ------------------------------------------------------------- the layer
+
+def _check(x, sel, p, shared, E):
+    x = np.asarray(x)
+    sel = np.asarray(sel)
+    p = np.asarray(p)
+    shared = np.asarray(shared)
+    if x.ndim != 2 or x.shape[1] % GROUP_VALUES != 0 or x.shape[1] == 0:
+        raise ValueError("x must be (T, 32G) with G >= 1")
+    if sel.shape != p.shape or sel.ndim != 2 or sel.shape[0] != x.shape[0]:
+        raise ValueError("selected experts and mixture weights must both be (T, K)")
+    if shared.ndim != 2 or shared.shape[0] != x.shape[0]:
+        raise ValueError("shared output must be (T, O)")
+    if sel.size and (sel.min() < 0 or sel.max() >= E):
+        raise ValueError("selected expert index out of range")
+    return x, sel, p, shared
+
+
+def expert_linear(x, packed, scales, sel, p, shared) -> np.ndarray:
+    """y = shared + sum_k p[t,k] * W_{sel[t,k]} x_t, in float64.
+
+    ``packed`` and ``scales`` are anything that returns expert e's arrays for
+    ``packed[e]`` (O, G, 16) and ``scales[e]`` (O, G) - a NumPy array or a
+    lazily drawn tensor - so only the selected experts are ever read.
+    Returns a new float64 (T, O) array; no input is modified.
+    """
+    E = len(packed)
+    x, sel, p, shared = _check(x, sel, p, shared, E)
+    T, K = sel.shape
+    O = shared.shape[1]
+    x64 = x.astype(np.float64)
+    p64 = p.astype(np.float64)
+    y = shared.astype(np.float64, copy=True)  # a non-mutating copy of shared
+    contrib = np.zeros((T, K, O), dtype=np.float64)
+    for e in np.unique(sel):  # each selected expert is decoded once
+        W = decode_expert(packed[e], scales[e])
+        if W.shape != (O, x.shape[1]):
+            raise ValueError("expert matrix shape does not match x and shared")
+        ts, ks = np.nonzero(sel == e)
+        contrib[ts, ks, :] = x64[ts] @ W.T  # each row of W dotted with the token
+    routed = np.zeros((T, O), dtype=np.float64)
+    for k in range(K):  # weighted accumulation over the selected list
+        routed += p64[:, k:k + 1] * contrib[:, k, :]
+    return y + routed
+
+
+def expert_linear_rows(x, packed, scales, sel, p, shared, rows) -> np.ndarray:
+    """The same as ``expert_linear`` restricted to output coordinates ``rows``.
+
+    Returns (T, len(rows)) float64: column j is output coordinate rows[j].
+    Only those rows of the selected experts are decoded, which makes the
+    oracle usable at full size on a sample of outputs.
+    """
+    E = len(packed)
+    x, sel, p, shared = _check(x, sel, p, shared, E)
+    rows = np.asarray(rows, dtype=np.int64)
+    T, K = sel.shape
+    x64 = x.astype(np.float64)
+    p64 = p.astype(np.float64)
+    y = shared[:, rows].astype(np.float64)
+    contrib = np.zeros((T, K, rows.size), dtype=np.float64)
+    for e in np.unique(sel):
+        W = decode_rows(np.asarray(packed[e])[rows], np.asarray(scales[e])[rows])
+        ts, ks = np.nonzero(sel == e)
+        contrib[ts, ks, :] = x64[ts] @ W.T
+    routed = np.zeros((T, rows.size), dtype=np.float64)
+    for k in range(K):
+        routed += p64[:, k:k + 1] * contrib[:, k, :]
+    return y + routed
+
+
+def expert_linear_scalar(x, packed, scales, sel, p, shared) -> list:
+    """Brute force with plain Python numbers and loops (tiny shapes only).
+
+    Reads every weight from its byte and scale directly, with no arrays, no
+    table of decoded groups and no matrix products; returns a list of lists.
+    """
+    T = len(x)
+    K = len(sel[0]) if T else 0
+    O = len(shared[0]) if T else 0
+    out = []
+    for t in range(T):
+        row = []
+        for o in range(O):
+            acc = float(shared[t][o])
+            for k in range(K):
+                e = int(sel[t][k])
+                dot = 0.0
+                G = len(packed[e][o])
+                for g in range(G):
+                    factor = 2.0 ** (int(scales[e][o][g]) - SCALE_BIAS)
+                    for j in range(GROUP_BYTES):
+                        byte = int(packed[e][o][g][j])
+                        low, high = byte % 16, byte // 16
+                        dot += E2M1_VALUES[low] * factor * float(x[t][32 * g + 2 * j])
+                        dot += E2M1_VALUES[high] * factor * float(x[t][32 * g + 2 * j + 1])
+                acc += float(p[t][k]) * dot
+            row.append(acc)
+        out.append(row)
+    return out

@@ -1,0 +1,397 @@
+"""Pins of the float64 oracle to facts other than itself (CPU only).
+
+Each test ties the oracle to something the pages print (fixtures under
+tests/golden, each with its citation), to a closed form, to an invariant of
+the definition, to a library routine in a special case, or to the brute-force
+scalar version. ``test_planted_mistakes_are_caught`` plants plausible
+mistakes in the oracle and checks that the pins fail on each of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mxfp4_oracle as om
+import workloads
+from conftest import GOLDEN
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _random_case(seed, T, E, K, G, O, scale_lo=120, scale_hi=134, distinct=True):
+    rng = _rng(seed)
+    x = rng.standard_normal((T, 32 * G)).astype(np.float32)
+    shared = rng.standard_normal((T, O)).astype(np.float32)
+    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, (E, O, G), dtype=np.uint8)
+    if distinct:
+        sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    else:
+        sel = rng.integers(0, E, (T, K)).astype(np.int32)
+    p = rng.random((T, K)).astype(np.float32)
+    return x, packed, scales, sel, p, shared
+
+
+# ----------------------------------------------------------- printed values
+
+def test_table_matches_printed_list_bit_for_bit():
+    g = _golden("e2m1_table.json")
+    assert len(oracle.E2M1_TABLE) == 16
+    for i, v in enumerate(g["values"]):
+        assert oracle.E2M1_TABLE[i] == v
+        assert np.signbit(oracle.E2M1_TABLE[i]) == (math.copysign(1.0, v) < 0)
+    assert np.signbit(oracle.E2M1_TABLE[g["negative_zero_index"]])
+    # what decoding actually produces: codes 0..15 at unit scale (byte j of the
+    # group holds codes 2j (low nibble) and 2j+1 (high nibble), j < 8)
+    packed = np.zeros((1, 1, 16), np.uint8)
+    packed[0, 0, :8] = [2 * j + 16 * (2 * j + 1) for j in range(8)]
+    row = oracle.decode_rows(packed, np.array([[127]], np.uint8))[0, :16]
+    for i, v in enumerate(g["values"]):
+        assert row[i] == v and np.signbit(row[i]) == (math.copysign(1.0, v) < 0)
+
+
+def _decode_single_group(byte_values, scale):
+    packed = np.zeros((1, 1, 16), dtype=np.uint8)
+    packed[0, 0, : len(byte_values)] = byte_values
+    return oracle.decode_rows(packed, np.array([[scale]], dtype=np.uint8))[0]
+
+
+def test_byte_0x21_decodes_low_nibble_first():
+    g = _golden("byte_0x21_example.json")
+    row = _decode_single_group([g["byte"]], g["scale_byte"])
+    assert list(row[:2]) == g["decoded_in_order"]
+    assert list(row[:2]) != g["decoded_if_high_first"]
+    # through the whole layer: x = e_0 picks the first value, x = e_1 the second
+    packed = np.zeros((1, 1, 1, 16), dtype=np.uint8)
+    packed[0, 0, 0, 0] = g["byte"]
+    scales = np.full((1, 1, 1), g["scale_byte"], dtype=np.uint8)
+    for pos, want in enumerate(g["decoded_in_order"]):
+        x = np.zeros((1, 32), dtype=np.float32)
+        x[0, pos] = 1.0
+        y = oracle.expert_linear(x, packed, scales, np.array([[0]]), np.array([[1.0]], np.float32),
+                                 np.zeros((1, 1), np.float32))
+        assert y[0, 0] == want
+
+
+def test_scale_bias_examples():
+    g = _golden("scale_bias_examples.json")
+    one = 2 | (2 << 4)  # both nibbles code 2, the table's 1.0
+    for s, factor in g["factors"].items():
+        row = _decode_single_group([one] * 16, int(s))
+        assert np.all(row == factor)
+        assert np.all(oracle.scale_factor(np.array([int(s)], np.uint8)) == factor)
+
+
+def test_numeric_example_gives_32():
+    g = _golden("numeric_example.json")
+    args = [np.array(g[k]) for k in ("latent_tokens", "packed_weights", "scale_bytes",
+                                     "selected_experts", "mixture_weights", "shared_output")]
+    args[0] = args[0].astype(np.float32)
+    args[1] = args[1].astype(np.uint8)
+    args[2] = args[2].astype(np.uint8)
+    args[4] = args[4].astype(np.float32)
+    args[5] = args[5].astype(np.float32)
+    y = oracle.expert_linear(*args)
+    assert y.tolist() == g["output"]
+    assert oracle.expert_linear_scalar(*[a.tolist() for a in args]) == g["output"]
+
+
+def test_shape_examples():
+    g = _golden("shape_examples.json")
+    rng = _rng(5)
+    for case in g["cases"]:
+        T, I = case["latent_tokens"]
+        E, O, G, _ = case["packed_weights"]
+        K = case["selected_experts"][1]
+        x = rng.standard_normal((T, I)).astype(np.float32)
+        packed = rng.integers(0, 256, case["packed_weights"], dtype=np.uint8)
+        scales = rng.integers(120, 130, (E, O, G), dtype=np.uint8)
+        sel = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        p = np.full((T, K), 1.0 / K, np.float32)
+        shared = rng.standard_normal(case["shared_output"]).astype(np.float32)
+        assert list(oracle.expert_linear(x, packed, scales, sel, p, shared).shape) == case["output"]
+
+
+# ----------------------------------------------------------- exhaustive grid
+
+def test_every_code_and_scale():
+    table = _golden("e2m1_table.json")["values"]
+    for s in range(256):
+        for code in range(16):
+            row = _decode_single_group([code | (code << 4)] * 16, s)
+            want = math.ldexp(table[code], s - 127)
+            assert np.all(row == want)
+            assert np.all(np.signbit(row) == (math.copysign(1.0, want) < 0))
+
+
+def test_nibble_split_exhaustive():
+    b = np.arange(256, dtype=np.uint8)
+    lo, hi = oracle.split_nibbles(b)
+    for v in range(256):
+        assert (int(lo[v]), int(hi[v])) == (v % 16, v // 16)
+    codes = oracle.group_codes(b.reshape(16, 16))
+    for j in range(16):
+        for v in range(16):
+            byte = 16 * j + v
+            assert codes[j, 2 * v] == byte % 16 and codes[j, 2 * v + 1] == byte // 16
+
+
+# ----------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("byte,scale", [(0x21, 128), (0x22, 127), (0x9F, 125), (0x7E, 130), (0x08, 127)])
+def test_closed_form_constant_matrix(byte, scale):
+    """One byte value and one scale everywhere, x = ones: every output is
+    shared + sum_k p_k * 16 G (LUT[lo] + LUT[hi]) 2^(s-127)."""
+    table = _golden("e2m1_table.json")["values"]
+    T, E, K, G, O = 3, 5, 2, 3, 4
+    rng = _rng(byte)
+    packed = np.full((E, O, G, 16), byte, np.uint8)
+    scales = np.full((E, O, G), scale, np.uint8)
+    sel = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+    p = rng.random((T, K)).astype(np.float32)
+    shared = rng.standard_normal((T, O)).astype(np.float32)
+    y = oracle.expert_linear(np.ones((T, 32 * G), np.float32), packed, scales, sel, p, shared)
+    lo, hi = divmod(byte, 16)[1], divmod(byte, 16)[0]
+    per_expert = 16 * G * (table[lo] + table[hi]) * 2.0 ** (scale - 127)
+    for t in range(T):
+        for o in range(O):
+            want = float(shared[t, o]) + sum(float(p[t, k]) for k in range(K)) * per_expert
+            assert math.isclose(y[t, o], want, rel_tol=1e-14, abs_tol=1e-14)
+
+
+def test_encoded_matrix_is_a_plain_matvec():
+    """Draw a matrix of table values with per-group powers of two, encode it
+    into bytes by the stated layout, and compare with numpy's matmul."""
+    table = np.array(_golden("e2m1_table.json")["values"])
+    rng = _rng(11)
+    T, E, G, O = 5, 3, 4, 7
+    I = 32 * G
+    codes = rng.integers(0, 16, (E, O, I))
+    scales = rng.integers(118, 137, (E, O, G), dtype=np.uint8)
+    W = table[codes] * np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=2)
+    packed = (codes[..., 0::2] + 16 * codes[..., 1::2]).reshape(E, O, G, 16).astype(np.uint8)
+    x = rng.standard_normal((T, I)).astype(np.float32)
+    sel = rng.integers(0, E, (T, 1)).astype(np.int32)
+    p = np.ones((T, 1), np.float32)
+    y = oracle.expert_linear(x, packed, scales, sel, p, np.zeros((T, O), np.float32))
+    want = np.stack([W[sel[t, 0]] @ x[t].astype(np.float64) for t in range(T)])
+    np.testing.assert_allclose(y, want, rtol=1e-13, atol=1e-13)
+    # and the rows decoded directly
+    for e in range(E):
+        np.testing.assert_array_equal(oracle.decode_expert(packed[e], scales[e]), W[e])
+
+
+# ----------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_matches(seed):
+    rng = _rng(100 + seed)
+    T, E, K, G, O = (int(v) for v in rng.integers(1, 5, 5))
+    K = min(K, E)
+    x, packed, scales, sel, p, shared = _random_case(seed, T, E, K, G, O, distinct=seed % 2 == 0)
+    y = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    ys = np.array(oracle.expert_linear_scalar(x.tolist(), packed.tolist(), scales.tolist(),
+                                              sel.tolist(), p.tolist(), shared.tolist()))
+    np.testing.assert_allclose(y, ys, rtol=1e-12, atol=1e-12)
+
+
+def test_brute_force_matches_tiny_workload():
+    inp = workloads.make_inputs("tiny")
+    y = oracle.expert_linear(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared)
+    ys = np.array(oracle.expert_linear_scalar(inp.x.tolist(), inp.packed.materialize().tolist(),
+                                              inp.scales.materialize().tolist(), inp.sel.tolist(),
+                                              inp.p.tolist(), inp.shared.tolist()))
+    np.testing.assert_allclose(y, ys, rtol=1e-12, atol=1e-12)
+
+
+def test_rows_variant_matches_full():
+    x, packed, scales, sel, p, shared = _random_case(3, 6, 5, 3, 3, 40)
+    y = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    rows = [0, 7, 39, 12]
+    yr = oracle.expert_linear_rows(x, packed, scales, sel, p, shared, rows)
+    np.testing.assert_allclose(yr, y[:, rows], rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------- invariants
+
+def test_unselected_experts_do_not_matter():
+    x, packed, scales, sel, p, shared = _random_case(4, 4, 9, 2, 2, 8)
+    y = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    rng = _rng(44)
+    packed2, scales2 = packed.copy(), scales.copy()
+    for e in set(range(9)) - set(np.unique(sel).tolist()):
+        packed2[e] = rng.integers(0, 256, packed2[e].shape)
+        scales2[e] = 255
+    assert np.array_equal(oracle.expert_linear(x, packed2, scales2, sel, p, shared), y)
+
+
+def test_linear_in_x_and_p():
+    x1, packed, scales, sel, p1, shared = _random_case(6, 3, 4, 2, 3, 6)
+    x2, _, _, _, p2, _ = _random_case(7, 3, 4, 2, 3, 6)
+    a, b = 0.75, -1.25
+    f = lambda x, p: oracle.expert_linear(x, packed, scales, sel, p, shared) - shared
+    lhs = f(a * x1.astype(np.float64) + b * x2.astype(np.float64), p1)
+    np.testing.assert_allclose(lhs, a * f(x1, p1) + b * f(x2, p1), rtol=1e-11, atol=1e-11)
+    lhs = f(x1, a * p1.astype(np.float64) + b * p2.astype(np.float64))
+    np.testing.assert_allclose(lhs, a * f(x1, p1) + b * f(x1, p2), rtol=1e-11, atol=1e-11)
+
+
+def test_sign_flip_negates_routed_part():
+    x, packed, scales, sel, p, shared = _random_case(8, 4, 5, 2, 3, 6)
+    zero = np.zeros_like(shared)
+    y = oracle.expert_linear(x, packed, scales, sel, p, zero)
+    yn = oracle.expert_linear(x, packed ^ np.uint8(0x88), scales, sel, p, zero)
+    assert np.array_equal(yn, -y)
+
+
+def test_scale_shift_doubles_routed_part():
+    x, packed, scales, sel, p, shared = _random_case(9, 4, 5, 2, 3, 6)
+    zero = np.zeros_like(shared)
+    y = oracle.expert_linear(x, packed, scales, sel, p, zero)
+    y2 = oracle.expert_linear(x, packed, scales + np.uint8(1), sel, p, zero)
+    assert np.array_equal(y2, 2 * y)
+
+
+def test_nibble_swap_equals_input_pair_swap():
+    x, packed, scales, sel, p, shared = _random_case(10, 3, 4, 2, 2, 5)
+    swapped = ((packed & 0x0F) << 4) | (packed >> 4)
+    xs = x.copy()
+    xs[:, 0::2], xs[:, 1::2] = x[:, 1::2], x[:, 0::2]
+    np.testing.assert_allclose(oracle.expert_linear(xs, swapped, scales, sel, p, shared),
+                               oracle.expert_linear(x, packed, scales, sel, p, shared),
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_duplicate_selection_counts_twice():
+    x, packed, scales, sel, p, shared = _random_case(12, 2, 3, 1, 2, 4)
+    zero = np.zeros_like(shared)
+    single = oracle.expert_linear(x, packed, scales, sel, p, zero)
+    twice = oracle.expert_linear(x, packed, scales, np.concatenate([sel, sel], 1),
+                                 np.concatenate([p, p], 1), zero)
+    np.testing.assert_allclose(twice, 2 * single, rtol=1e-14)
+
+
+def test_inputs_not_mutated_and_fresh_output():
+    x, packed, scales, sel, p, shared = _random_case(13, 3, 4, 2, 2, 5)
+    copies = [a.copy() for a in (x, packed, scales, sel, p, shared)]
+    y = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    for a, c in zip((x, packed, scales, sel, p, shared), copies):
+        assert np.array_equal(a, c)
+    assert not np.shares_memory(y, shared)
+
+
+def test_invalid_index_raises():
+    x, packed, scales, sel, p, shared = _random_case(14, 2, 3, 1, 1, 2)
+    sel[0, 0] = 3
+    with pytest.raises(ValueError):
+        oracle.expert_linear(x, packed, scales, sel, p, shared)
+
+
+# ----------------------------------------------------------- bucketing
+
+@pytest.mark.parametrize("seed,T,K,E", [(0, 1, 4, 128), (1, 8, 8, 384), (2, 37, 3, 5), (3, 200, 8, 64)])
+def test_bucketing_is_a_stable_sort(seed, T, K, E):
+    rng = _rng(seed)
+    sel = rng.integers(0, E, (T, K)).astype(np.int32)
+    b = oracle.bucket_pairs(sel, E)
+    flat = sel.ravel()
+    assert np.array_equal(b["count"], np.bincount(flat, minlength=E))
+    assert np.array_equal(b["offsets"], np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert np.array_equal(b["perm"], np.argsort(flat, kind="stable"))
+    assert np.array_equal(b["perm"][b["slot_of_pair"]], np.arange(flat.size))
+    assert b["n_invalid"] == 0
+
+
+def test_bucketing_drops_invalid():
+    sel = np.array([[0, 5], [-1, 2], [2, 0]], np.int32)
+    b = oracle.bucket_pairs(sel, 3)
+    assert b["n_invalid"] == 2
+    assert b["count"].tolist() == [2, 0, 2]
+    assert b["perm"].tolist() == [0, 5, 3, 4]
+    assert b["slot_of_pair"].tolist() == [0, -1, -1, 2, 3, 1]
+
+
+# ----------------------------------------------------------- workloads
+
+def test_workload_shapes_and_routing():
+    for name, w in workloads.WORKLOADS.items():
+        if w.T * w.E > 4_000_000:
+            continue
+        inp = workloads.make_inputs(w, n_routing_sets=2)
+        assert inp.x.shape == (w.T, 32 * w.G) and inp.shared.shape == (w.T, w.O)
+        assert inp.sel.shape == (w.T, w.K) and inp.p.shape == (w.T, w.K)
+        assert inp.sel.dtype == np.int32 and inp.p.dtype == np.float32
+        for row in inp.sel:
+            assert len(set(row.tolist())) == w.K  # distinct experts per token
+        np.testing.assert_allclose(inp.p.sum(1), 1.0, rtol=1e-6)
+        assert inp.packed[0].shape == (w.O, w.G, 16)
+        s = inp.scales[w.E - 1]
+        assert s.min() >= w.scale_lo and s.max() <= w.scale_hi
+        assert not np.array_equal(inp.routing_sets[0][0], inp.routing_sets[1][0])
+        if w.dtype == "bf16":
+            assert np.all((inp.x.view(np.uint32) & 0xFFFF) == 0)
+
+
+# ----------------------------------------------------------- planted mistakes
+
+def _pins_pass():
+    """Run the value pins; return False as soon as one fails."""
+    checks = [test_byte_0x21_decodes_low_nibble_first, test_scale_bias_examples,
+              test_numeric_example_gives_32, test_encoded_matrix_is_a_plain_matvec,
+              test_table_matches_printed_list_bit_for_bit, test_brute_force_matches_tiny_workload]
+    checks += [lambda b=b, s=s: test_closed_form_constant_matrix(b, s) for b, s in [(0x21, 128), (0x9F, 125)]]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    assert _pins_pass()
+    orig_split = om.split_nibbles
+    orig_table = om.E2M1_TABLE.copy()
+    orig_factor = om.scale_factor
+    orig_decode_rows = om.decode_rows
+    mistakes = {
+        "high nibble first": lambda mp: mp.setattr(om, "split_nibbles", lambda b: orig_split(b)[::-1]),
+        "positive zero at index 8": lambda mp: mp.setattr(om, "E2M1_TABLE", np.where(np.arange(16) == 8, 0.0, orig_table)),
+        "wrong LUT entry": lambda mp: mp.setattr(om, "E2M1_TABLE", np.where(np.arange(16) == 6, 5.0, orig_table)),
+        "bias sign flipped": lambda mp: mp.setattr(om, "scale_factor", lambda s: 1.0 / orig_factor(s)),
+        "off-by-one bias": lambda mp: mp.setattr(om, "scale_factor", lambda s: 2.0 * orig_factor(s)),
+        "groups reversed": lambda mp: mp.setattr(
+            om, "decode_rows", lambda pk, sc: orig_decode_rows(np.asarray(pk)[:, ::-1], np.asarray(sc)[:, ::-1])),
+    }
+    for name, plant in mistakes.items():
+        with monkeypatch.context() as mp:
+            plant(mp)
+            assert not _pins_pass(), f"planted mistake not caught: {name}"
+    assert _pins_pass()
+
+
+def test_planted_combine_mistakes_are_caught(monkeypatch):
+    """Mistakes in the layer itself: dropping shared, ignoring p, or using
+    the transpose of W all change the brute-force comparison."""
+    x, packed, scales, sel, p, shared = _random_case(21, 3, 4, 2, 1, 32)
+    ys = np.array(oracle.expert_linear_scalar(x.tolist(), packed.tolist(), scales.tolist(),
+                                              sel.tolist(), p.tolist(), shared.tolist()))
+    good = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    np.testing.assert_allclose(good, ys, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(good - shared, ys, rtol=1e-6)  # dropped shared term
+    assert not np.allclose(oracle.expert_linear(x, packed, scales, sel, np.ones_like(p), shared), ys)
+    orig = om.decode_expert
+    with monkeypatch.context() as mp:  # square case: I = O = 32, transposed operand
+        mp.setattr(om, "decode_expert", lambda pk, sc: orig(pk, sc).T)
+        assert not np.allclose(oracle.expert_linear(x, packed, scales, sel, p, shared), ys)
