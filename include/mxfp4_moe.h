@@ -1,0 +1,186 @@
+/*
+ * mxfp4_moe.h - C ABI of the MXFP4 routed-expert linear on AMD MI355X (gfx950).
+ *
+ * The operation (page "MXFP4 Routed Expert Linear", Kimi K3, section
+ * "Route, weight, and add the shared path"; page "MXFP4 Experts", shape
+ * paragraph):
+ *
+ *     y[t, :] = shared[t, :] + sum_{k < K} p[t, k] * W_{sel[t, k]} x[t, :]
+ *
+ * W_e is O x I with I = 32 G. It is stored as packed bytes [E, O, G, 16]
+ * (two E2M1 codes per byte, low nibble first) and E8M0 scale bytes [E, O, G]
+ * (the packed shape without its last axis, page "MXFP4 Dequant", "How it
+ * works"). Code n of byte b is n_lo = b & 15 then n_hi = b >> 4; it maps
+ * through the E2M1 table {0, .5, 1, 1.5, 2, 3, 4, 6, -0, -.5, -1, -1.5, -2,
+ * -3, -4, -6} and is multiplied by 2^(s - 127) for its group's scale byte s
+ * (page "MXFP4 Routed Expert Linear", "What is stored in one group" and
+ * "Apply the shared group scale"). Group g fills input columns 32g..32g+31
+ * of its row ("Reconstruct the matrix in the right orientation").
+ *
+ * Only the experts that appear in sel are read ("Decode only selected
+ * experts"); no decoded weight matrix is ever written to device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.   Every tensor pointer is a device pointer owned by the caller.
+ *             The library never frees, retains or writes an input.
+ * Layout.     Dense row-major:
+ *               x       [T, 32G]  fp32 or bf16 (bf16 = raw 16-bit patterns)
+ *               packed  [E, O, G, 16] uint8
+ *               scales  [E, O, G]     uint8
+ *               sel     [T, K]    int32 expert indices
+ *               p       [T, K]    fp32 mixture weights (used as given; never
+ *                                 renormalised)
+ *               shared  [T, O]    same dtype as x
+ *               y       [T, O]    same dtype as x, fully overwritten
+ * Alignment.  packed and x must be 16-byte aligned; scales, sel, p, shared
+ *             and y need only the natural alignment of their element type.
+ * Aliasing.   y may be exactly shared (each element is read and then written
+ *             by the same thread); any other overlap of y with an input is
+ *             rejected with MXFP4_ERR_INVALID_ARG.
+ * Selection.  A token may list an expert more than once; every listed slot
+ *             contributes (list semantics). An index outside [0, E) breaks
+ *             a stated precondition: that slot contributes nothing, and it is
+ *             reported only when MXFP4_FLAG_CHECK is set.
+ * Rounding.   Products are accumulated in fp32; y is shared + (the k-ordered
+ *             fp32 sum of p * partial), rounded once to y's dtype (round to
+ *             nearest even). Results are bitwise deterministic run to run.
+ * Streams.    Work is enqueued on `stream` (0 = the null stream) of the
+ *             current HIP device; every call returns without waiting for the
+ *             GPU unless MXFP4_FLAG_CHECK is set.
+ * Errors.     Every call returns an mxfp4_status. Argument checks happen on
+ *             the host before anything is enqueued and need no GPU. T = 0 is
+ *             valid and enqueues nothing. A device that is not gfx950 gets
+ *             MXFP4_ERR_UNSUPPORTED_DEVICE: there is no fallback path.
+ * Threads.    All entry points are reentrant; the only shared state is a
+ *             per-device cache of the architecture check.
+ */
+#ifndef MXFP4_MOE_H
+#define MXFP4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mxfp4_status {
+  MXFP4_OK = 0,
+  MXFP4_ERR_INVALID_ARG = -1,        /* null pointer, bad size, misalignment, overlap */
+  MXFP4_ERR_UNSUPPORTED_DEVICE = -2, /* the current device is not gfx950 */
+  MXFP4_ERR_HIP = -3,                /* a HIP runtime call or a launch failed */
+  MXFP4_ERR_WORKSPACE_TOO_SMALL = -4,
+  MXFP4_ERR_INVALID_INDEX = -5,      /* with MXFP4_FLAG_CHECK: some sel entry outside [0, E) */
+  MXFP4_ERR_UNSUPPORTED = -6         /* a forced path that does not exist for this dtype */
+} mxfp4_status;
+
+typedef enum mxfp4_dtype {
+  MXFP4_DTYPE_F32 = 0,
+  MXFP4_DTYPE_BF16 = 1
+} mxfp4_dtype;
+
+/* Flags of the _ex entry points. */
+#define MXFP4_FLAG_FORCE_GEMV 0x1u /* decode-shaped path (dequant-GEMV, fused combine) */
+#define MXFP4_FLAG_FORCE_GEMM 0x2u /* prefill-shaped path (bucketing, MFMA grouped GEMM, combine) */
+#define MXFP4_FLAG_CHECK 0x4u      /* synchronise `stream` and report out-of-range indices */
+/* Flags of mxfp4_moe_bucket. */
+#define MXFP4_FLAG_BUCKET_ONE_BLOCK 0x10u  /* one workgroup does histogram, scan and scatter */
+#define MXFP4_FLAG_BUCKET_MULTI_BLOCK 0x20u /* per-chunk histograms, a scan, per-chunk scatter */
+
+/* Limits checked on the host. */
+#define MXFP4_MAX_EXPERTS 8192
+#define MXFP4_MAX_PAIRS (1 << 26) /* T * K */
+
+/* Path identifiers returned by mxfp4_moe_select_path. */
+#define MXFP4_PATH_GEMV 1
+#define MXFP4_PATH_GEMM 2
+
+/*
+ * mxfp4_moe_linear - y = shared + sum_k p[t,k] W_{sel[t,k]} x[t], fp32 x/shared/y.
+ * The argument list is the operation's: inputs x, packed, scales, sel, p,
+ * shared; output y; sizes T (tokens), E (experts), O (output features),
+ * G (groups per row, I = 32G), K (slots per token); the stream.
+ * Scratch memory, when the chosen path needs it, is taken with
+ * hipMallocAsync / hipFreeAsync on `stream`; use mxfp4_moe_linear_ex with a
+ * caller workspace to avoid allocation (e.g. under graph capture).
+ */
+int mxfp4_moe_linear(const float* x, const uint8_t* packed, const uint8_t* scales,
+                     const int32_t* sel, const float* p, const float* shared, float* y,
+                     int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, hipStream_t stream);
+
+/* The same with bf16 x, shared and y (raw 16-bit patterns). p stays fp32. */
+int mxfp4_moe_linear_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
+                          const int32_t* sel, const float* p, const uint16_t* shared, uint16_t* y,
+                          int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, hipStream_t stream);
+
+/*
+ * mxfp4_moe_workspace_size - bytes of device workspace that
+ * mxfp4_moe_linear_ex needs for these sizes, dtype and flags (written to
+ * *bytes; 0 is a valid answer). Host-only; needs no GPU.
+ */
+int mxfp4_moe_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype,
+                             uint32_t flags, size_t* bytes);
+
+/*
+ * mxfp4_moe_linear_ex - the operation with an explicit dtype (mxfp4_dtype),
+ * flags and a caller-owned device workspace of at least
+ * mxfp4_moe_workspace_size bytes (256-byte aligned). It allocates nothing
+ * and does not synchronise unless MXFP4_FLAG_CHECK is set, so it may be
+ * captured in a HIP graph. Calls that share one workspace must not overlap.
+ */
+int mxfp4_moe_linear_ex(const void* x, const uint8_t* packed, const uint8_t* scales,
+                        const int32_t* sel, const float* p, const void* shared, void* y,
+                        int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype,
+                        uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mxfp4_moe_select_path - which path the _ex call takes for these sizes,
+ * dtype and flags: MXFP4_PATH_GEMV or MXFP4_PATH_GEMM, or a negative
+ * mxfp4_status. Host-only.
+ */
+int mxfp4_moe_select_path(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype,
+                          uint32_t flags);
+
+/*
+ * mxfp4_moe_bucket - the token-to-expert bucketing on its own: a stable
+ * counting sort of the P = T*K pairs (pair i = t*K + k) by expert index
+ * (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
+ * Experts", section 2: histogram, then scatter into per-expert contiguous
+ * segments). Outputs (device, caller-owned, int32):
+ *   count[E]          pairs per expert
+ *   offsets[E + 1]    exclusive prefix sum of count
+ *   perm[P]           perm[offsets[e] + r] = the r-th pair (in pair order) that chose e;
+ *                     entries from offsets[E] on are left untouched (invalid pairs)
+ *   slot_of_pair[P]   inverse of perm; -1 for a pair whose index is outside [0, E)
+ *   n_invalid[1]      number of such pairs
+ * flags selects the algorithm (MXFP4_FLAG_BUCKET_*; 0 = automatic). The
+ * workspace (mxfp4_moe_bucket_workspace_size bytes) is caller-owned.
+ */
+int mxfp4_moe_bucket_workspace_size(int64_t T, int64_t K, int64_t E, uint32_t flags, size_t* bytes);
+int mxfp4_moe_bucket(const int32_t* sel, int64_t T, int64_t K, int64_t E, int32_t* count,
+                     int32_t* offsets, int32_t* perm, int32_t* slot_of_pair, int32_t* n_invalid,
+                     uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mxfp4_decode_rows - decode rows row0 .. row0+nrows-1 of expert e into
+ * out[nrows, 32G] (dtype fp32 or bf16), exactly: each value is
+ * E2M1[n] * 2^(s - 127) rounded to the output type, which is exact except
+ * where the value overflows to +-inf (s >= 253). This is the decode the
+ * product kernels use, exported so that it can be tested bit for bit. It
+ * writes decoded weights to memory and is not part of the fused path.
+ */
+int mxfp4_decode_rows(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O,
+                      int64_t G, int64_t e, int64_t row0, int64_t nrows, int dtype, void* out,
+                      hipStream_t stream);
+
+/* A static, human-readable name of a status code. */
+const char* mxfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_MOE_H */

@@ -1,0 +1,160 @@
+"""MXFP4 routed-expert linear on AMD MI355X (gfx950).
+
+    y_t = y_t^shared + sum_k p[t,k] W_{sel[t,k]} x_t
+
+with every W_e stored as packed E2M1 codes [E, O, G, 16] and E8M0 scale
+bytes [E, O, G] (page "MXFP4 Routed Expert Linear", Kimi K3). All the work
+runs in the HIP kernels of ``libmxfp4_moe.so`` behind the C ABI declared in
+include/mxfp4_moe.h; this module only checks tensor arguments, allocates the
+output and the workspace with PyTorch, and passes pointers and the current
+HIP stream through ctypes. It has no other implementation of any step: when
+the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import (  # noqa: F401
+    DTYPE_BF16, DTYPE_F32, FLAG_CHECK, FLAG_FORCE_GEMM, FLAG_FORCE_GEMV, FLAG_BUCKET_MULTI_BLOCK,
+    FLAG_BUCKET_ONE_BLOCK, PATH_GEMM, PATH_GEMV, Mxfp4Error, bucket_workspace_size, select_path,
+    status_string, workspace_size,
+)
+
+__all__ = [
+    "mxfp4_expert_linear", "moe_linear", "decode_rows", "bucket", "workspace_size", "select_path",
+    "Mxfp4Error", "library_path",
+]
+
+_DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+
+def library_path() -> str:
+    _abi.lib()
+    return _abi.LIB_PATH
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def moe_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, sel: torch.Tensor, p: torch.Tensor,
+               shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = shared + sum_k p[:,k] * W_{sel[:,k]} x on the current HIP stream.
+
+    x [T, 32G] fp32 or bf16; packed [E, O, G, 16] uint8; scales [E, O, G]
+    uint8; sel [T, K] int32; p [T, K] fp32; shared [T, O] in x's dtype. All
+    on one gfx950 device and contiguous. Returns ``out`` (allocated when not
+    given; it may be ``shared`` itself). ``workspace``, when given, is a
+    uint8 device tensor of at least ``workspace_size(...)`` bytes.
+    """
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be on a HIP device")
+    dt = _DTYPES[x.dtype]
+    _need(x, "x", x.dtype, 2, dev)
+    _need(packed, "packed", torch.uint8, 4, dev)
+    _need(scales, "scales", torch.uint8, 3, dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    _need(shared, "shared", x.dtype, 2, dev)
+    T, I = x.shape
+    E, O, G, B = packed.shape
+    K = sel.shape[1]
+    if B != 16 or I != 32 * G:
+        raise ValueError(f"packed must be [E, O, G, 16] with 32G == x.shape[1]; got {tuple(packed.shape)}, I={I}")
+    if tuple(scales.shape) != (E, O, G):
+        raise ValueError("scales must have the packed shape without its last axis")
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K) or tuple(shared.shape) != (T, O):
+        raise ValueError("sel and p must be [T, K] and shared [T, O]")
+    y = torch.empty_like(shared) if out is None else out
+    _need(y, "out", x.dtype, 2, dev)
+    if tuple(y.shape) != (T, O):
+        raise ValueError("out must be [T, O]")
+    need = workspace_size(T, E, O, G, K, dt, flags)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev:
+        raise ValueError("workspace must be a uint8 tensor on x's device")
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_linear_ex(
+            _ptr(x), _ptr(packed), _ptr(scales), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y),
+            T, E, O, G, K, dt, flags, _ptr(workspace), workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_linear_ex")
+    return y
+
+
+def mxfp4_expert_linear(latent_tokens: torch.Tensor, packed_weights: torch.Tensor, scale_bytes: torch.Tensor,
+                        selected_experts: torch.Tensor, mixture_weights: torch.Tensor,
+                        shared_output: torch.Tensor) -> torch.Tensor:
+    """The problem page's signature ("Starter Code"): returns a new tensor
+    shaped like ``shared_output`` in the latent tokens' dtype and device.
+
+    Marshalling only: the expert indices are passed as int32 and the mixture
+    weights as fp32 (copies when they arrive in another integer or float
+    type); nothing supplied is modified.
+    """
+    if shared_output.dtype != latent_tokens.dtype:
+        raise TypeError("shared_output must have the latent tokens' dtype")
+    sel = selected_experts.to(device=latent_tokens.device, dtype=torch.int32).contiguous()
+    p = mixture_weights.to(device=latent_tokens.device, dtype=torch.float32).contiguous()
+    return moe_linear(latent_tokens.contiguous(), packed_weights.contiguous(), scale_bytes.contiguous(), sel, p,
+                      shared_output.contiguous())
+
+
+def decode_rows(packed: torch.Tensor, scales: torch.Tensor, e: int, row0: int, nrows: int,
+                dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Rows row0 .. row0+nrows-1 of expert e decoded to [nrows, 32G] (exact)."""
+    dev = packed.device
+    _need(packed, "packed", torch.uint8, 4, dev)
+    _need(scales, "scales", torch.uint8, 3, dev)
+    E, O, G, _ = packed.shape
+    out = torch.empty((nrows, 32 * G), dtype=dtype, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_decode_rows(_ptr(packed), _ptr(scales), E, O, G, e, row0, nrows, _DTYPES[dtype],
+                                          _ptr(out), _stream(dev))
+    _abi.check(st, "mxfp4_decode_rows")
+    return out
+
+
+def bucket(sel: torch.Tensor, E: int, flags: int = 0) -> dict:
+    """Stable counting sort of the (token, slot) pairs by expert."""
+    dev = sel.device
+    _need(sel, "sel", torch.int32, 2, dev)
+    T, K = sel.shape
+    P = T * K
+    i32 = dict(dtype=torch.int32, device=dev)
+    count = torch.empty(E, **i32)
+    offsets = torch.empty(E + 1, **i32)
+    perm = torch.full((P,), -7, **i32)
+    slot = torch.empty(P, **i32)
+    n_invalid = torch.empty(1, **i32)
+    ws = torch.empty(max(bucket_workspace_size(T, K, E, flags), 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_bucket(_ptr(sel), T, K, E, _ptr(count), _ptr(offsets), _ptr(perm), _ptr(slot),
+                                         _ptr(n_invalid), flags, _ptr(ws), ws.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_bucket")
+    return {"count": count, "offsets": offsets, "perm": perm, "slot_of_pair": slot, "n_invalid": n_invalid}

@@ -1,0 +1,86 @@
+"""Build the gfx950 library ``libmxfp4_moe.so`` in this package directory.
+
+    python -m mxfp4_block_scaled_amd.build [-v]
+
+Every HIP source is compiled for gfx950 only with hipcc; the host C ABI
+(csrc/api.cpp) is compiled by hipcc as plain host C++. Objects go to
+``_build/`` at the repository root; the shared library lands next to this
+file, which is where the binding loads it from.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_NAME = "libmxfp4_moe.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+HIP_SOURCES = ["bucket.hip", "gemv.hip", "gemm.hip", "combine.hip"]
+HOST_SOURCES = ["api.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def _common_flags():
+    return ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _device_flags():
+    # packed fp32 VALU ops are switched off for all device code
+    return [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), "-c", path, "-o", obj] + _common_flags()
+    if src.endswith(".hip"):
+        cmd += _device_flags()
+    else:
+        cmd += ["-x", "c++", "-D__HIP_PLATFORM_AMD__"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    sources = HIP_SOURCES + HOST_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(sources), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), sources))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking {LIB_NAME} failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv[1:]))

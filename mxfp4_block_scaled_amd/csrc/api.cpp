@@ -1,0 +1,334 @@
+// C ABI of the MXFP4 routed-expert linear (declarations and conventions in
+// include/mxfp4_moe.h). This file holds the host side only: argument checks
+// that need no GPU, the workspace layout, the gfx950 check, the choice
+// between the decode-shaped and the prefill-shaped path, and the launches.
+#include "mxfp4_moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+using namespace mxfp4;
+
+// Decode-shaped path up to this many tokens (bf16): every expert's pairs
+// then fit one 16-column MFMA tile when a token lists distinct experts, so
+// each selected expert's bytes are streamed exactly once.
+constexpr int64_t kGemvMaxTokens = 16;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+  int64_t T, E, O, G, K, P, I;
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out) && *out >= 0; }
+
+int check_dims(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, Dims* d) {
+  if (T < 0 || E < 1 || O < 1 || G < 1 || K < 1) return MXFP4_ERR_INVALID_ARG;
+  if (E > MXFP4_MAX_EXPERTS || O > (int64_t(1) << 30) || G > (int64_t(1) << 24)) return MXFP4_ERR_INVALID_ARG;
+  int64_t P = 0, t = 0;
+  if (!mul_ok(T, K, &P) || P > MXFP4_MAX_PAIRS) return MXFP4_ERR_INVALID_ARG;
+  // the packed tensor's byte size and the partial buffer must be addressable
+  if (!mul_ok(E, O, &t) || !mul_ok(t, G, &t) || !mul_ok(t, 16, &t)) return MXFP4_ERR_INVALID_ARG;
+  if (!mul_ok(P, O, &t) || !mul_ok(t, 4, &t)) return MXFP4_ERR_INVALID_ARG;
+  if (!mul_ok(T, 32 * G, &t) || !mul_ok(t, 4, &t)) return MXFP4_ERR_INVALID_ARG;
+  *d = Dims{T, E, O, G, K, P, 32 * G};
+  return MXFP4_OK;
+}
+
+int dtype_size(int dtype) { return dtype == MXFP4_DTYPE_F32 ? 4 : (dtype == MXFP4_DTYPE_BF16 ? 2 : 0); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int select_path(const Dims& d, int dtype, uint32_t flags) {
+  if (dtype_size(dtype) == 0) return MXFP4_ERR_INVALID_ARG;
+  const bool fv = flags & MXFP4_FLAG_FORCE_GEMV, fm = flags & MXFP4_FLAG_FORCE_GEMM;
+  if (fv && fm) return MXFP4_ERR_INVALID_ARG;
+  if (dtype == MXFP4_DTYPE_F32) {
+    if (fm) return MXFP4_ERR_UNSUPPORTED;  // the MFMA grouped GEMM is bf16-only
+    return MXFP4_PATH_GEMV;
+  }
+  if (fv) return MXFP4_PATH_GEMV;
+  if (fm) return MXFP4_PATH_GEMM;
+  return d.T <= kGemvMaxTokens ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
+}
+
+// Workspace layout. GEMV: n_invalid only. GEMM: bucketing arrays, the M-tile
+// list and the fp32 partial rows [P, O].
+struct Layout {
+  size_t n_invalid, count, offsets, perm, slot, bcount, tiles, n_tiles, part, total;
+};
+
+Layout layout(const Dims& d, int path) {
+  Layout L{};
+  size_t off = 0;
+  L.n_invalid = off;
+  off += kAlign;
+  if (path == MXFP4_PATH_GEMM) {
+    const int64_t nch = bucket_chunks(d.P);
+    L.count = off;
+    off = align_up(off + d.E * 4);
+    L.offsets = off;
+    off = align_up(off + (d.E + 1) * 4);
+    L.perm = off;
+    off = align_up(off + d.P * 4);
+    L.slot = off;
+    off = align_up(off + d.P * 4);
+    L.bcount = off;
+    off = align_up(off + (nch * d.E + nch) * 4);
+    L.tiles = off;
+    off = align_up(off + gemm_max_tiles(d.P, d.E) * sizeof(GemmTile));
+    L.n_tiles = off;
+    off += kAlign;
+    L.part = off;
+    off = align_up(off + (size_t)d.P * d.O * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+std::atomic<int> g_arch[64];  // 0 unknown, 1 gfx950, -1 another device
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MXFP4_ERR_HIP;
+  int v = (dev >= 0 && dev < 64) ? g_arch[dev].load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXFP4_ERR_HIP;
+    v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':'))
+            ? 1
+            : -1;
+    if (dev >= 0 && dev < 64) g_arch[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? MXFP4_OK : MXFP4_ERR_UNSUPPORTED_DEVICE;
+}
+
+int check_linear_args(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
+                      const void* shared, void* y, const Dims& d, int dtype) {
+  const int es = dtype_size(dtype);
+  if (es == 0) return MXFP4_ERR_INVALID_ARG;
+  if (d.T == 0) return MXFP4_OK;
+  if (!x || !packed || !scales || !sel || !p || !shared || !y) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(sel, 4) || !aligned(p, 4) || !aligned(shared, es) ||
+      !aligned(y, es))
+    return MXFP4_ERR_INVALID_ARG;
+  const size_t ny = (size_t)d.T * d.O * es;
+  const size_t sizes[6] = {(size_t)d.T * d.I * es, (size_t)d.E * d.O * d.G * 16, (size_t)d.E * d.O * d.G,
+                           (size_t)d.P * 4, (size_t)d.P * 4, ny};
+  const void* ptrs[6] = {x, packed, scales, sel, p, shared};
+  for (int i = 0; i < 6; i++) {
+    if (i == 5 && ptrs[i] == y) continue;  // in place on shared is allowed
+    if (overlap(y, ny, ptrs[i], sizes[i])) return MXFP4_ERR_INVALID_ARG;
+  }
+  return MXFP4_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP; }
+
+int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
+               const void* shared, void* y, const Dims& d, int dtype, uint32_t flags, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
+  const int path = select_path(d, dtype, flags);
+  if (path < 0) return path;
+  const Layout L = layout(d, path);
+  if (ws_bytes < L.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!ws || !aligned(ws, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(ws);
+  int32_t* n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
+  hipError_t err = hipSuccess;
+  const int es = dtype_size(dtype);
+  if (path == MXFP4_PATH_GEMV) {
+    if (d.K > kMaxFusedPairs) return MXFP4_ERR_UNSUPPORTED;
+    // token chunks whose pairs fit one fused launch
+    const int64_t tc = kMaxFusedPairs / d.K;
+    int chunk = 0;
+    for (int64_t t0 = 0; t0 < d.T && err == hipSuccess; t0 += tc, chunk++) {
+      const int64_t tn = (d.T - t0 < tc) ? d.T - t0 : tc;
+      const char* xc = static_cast<const char*>(x) + t0 * d.I * es;
+      const int32_t* selc = sel + t0 * d.K;
+      const float* pc = p + t0 * d.K;
+      const char* shc = static_cast<const char*>(shared) + t0 * d.O * es;
+      char* yc = static_cast<char*>(y) + t0 * d.O * es;
+      if (dtype == MXFP4_DTYPE_F32)
+        err = launch_gemv_f32_fused(reinterpret_cast<const float*>(xc), packed, scales, selc, pc,
+                                    reinterpret_cast<const float*>(shc), reinterpret_cast<float*>(yc), (int)tn,
+                                    (int)d.E, (int)d.O, (int)d.G, (int)d.K, n_invalid, chunk, stream);
+      else
+        err = launch_gemv_bf16_fused(reinterpret_cast<const uint16_t*>(xc), packed, scales, selc, pc,
+                                     reinterpret_cast<const uint16_t*>(shc), reinterpret_cast<uint16_t*>(yc), (int)tn,
+                                     (int)d.E, (int)d.O, (int)d.G, (int)d.K, n_invalid, chunk, stream);
+    }
+  } else {
+    BucketOut b;
+    b.count = reinterpret_cast<int32_t*>(base + L.count);
+    b.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    b.perm = reinterpret_cast<int32_t*>(base + L.perm);
+    b.slot_of_pair = reinterpret_cast<int32_t*>(base + L.slot);
+    b.n_invalid = n_invalid;
+    b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
+    b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+    err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
+    if (err == hipSuccess)
+      err = launch_gemm_bf16(static_cast<const uint16_t*>(x), packed, scales, b.perm, b.tiles, b.n_tiles,
+                             gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.K, (int)d.O,
+                             (int)d.G, stream);
+    if (err == hipSuccess)
+      err = launch_combine(reinterpret_cast<const float*>(base + L.part), b.slot_of_pair, p, shared, y, (int)d.T,
+                           (int)d.K, (int)d.O, dtype, stream);
+  }
+  if (err != hipSuccess) return MXFP4_ERR_HIP;
+  if (flags & MXFP4_FLAG_CHECK) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+    int32_t inv = 0;
+    if (hipMemcpy(&inv, n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
+    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
+  }
+  return MXFP4_OK;
+}
+
+int linear_alloc(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
+                 const void* shared, void* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype,
+                 hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  st = check_linear_args(x, packed, scales, sel, p, shared, y, d, dtype);
+  if (st != MXFP4_OK || d.T == 0) return st;
+  const int path = select_path(d, dtype, 0);
+  if (path < 0) return path;
+  const size_t bytes = layout(d, path).total;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) return MXFP4_ERR_HIP;
+  st = run_linear(x, packed, scales, sel, p, shared, y, d, dtype, 0, ws, bytes, stream);
+  if (hipFreeAsync(ws, stream) != hipSuccess && st == MXFP4_OK) st = MXFP4_ERR_HIP;
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_moe_linear(const float* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
+                     const float* shared, float* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,
+                     hipStream_t stream) {
+  return linear_alloc(x, packed, scales, sel, p, shared, y, T, E, O, G, K, MXFP4_DTYPE_F32, stream);
+}
+
+int mxfp4_moe_linear_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                          const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+                          int64_t G, int64_t K, hipStream_t stream) {
+  return linear_alloc(x, packed, scales, sel, p, shared, y, T, E, O, G, K, MXFP4_DTYPE_BF16, stream);
+}
+
+int mxfp4_moe_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype, uint32_t flags,
+                             size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  const int path = select_path(d, dtype, flags);
+  if (path < 0) return path;
+  *bytes = (T == 0) ? 0 : layout(d, path).total;
+  return MXFP4_OK;
+}
+
+int mxfp4_moe_select_path(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype, uint32_t flags) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  return select_path(d, dtype, flags);
+}
+
+int mxfp4_moe_linear_ex(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
+                        const void* shared, void* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype,
+                        uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~(MXFP4_FLAG_FORCE_GEMV | MXFP4_FLAG_FORCE_GEMM | MXFP4_FLAG_CHECK)) return MXFP4_ERR_INVALID_ARG;
+  st = check_linear_args(x, packed, scales, sel, p, shared, y, d, dtype);
+  if (st != MXFP4_OK) return st;
+  const int path = select_path(d, dtype, flags);
+  if (path < 0) return path;
+  if (d.T == 0) return MXFP4_OK;
+  return run_linear(x, packed, scales, sel, p, shared, y, d, dtype, flags, workspace, workspace_bytes, stream);
+}
+
+int mxfp4_moe_bucket_workspace_size(int64_t T, int64_t K, int64_t E, uint32_t flags, size_t* bytes) {
+  if (!bytes || T < 0 || K < 1 || E < 1 || E > MXFP4_MAX_EXPERTS) return MXFP4_ERR_INVALID_ARG;
+  if ((flags & MXFP4_FLAG_BUCKET_ONE_BLOCK) && (flags & MXFP4_FLAG_BUCKET_MULTI_BLOCK)) return MXFP4_ERR_INVALID_ARG;
+  int64_t P = 0;
+  if (!mul_ok(T, K, &P) || P > MXFP4_MAX_PAIRS) return MXFP4_ERR_INVALID_ARG;
+  const int64_t nch = bucket_chunks(P);
+  *bytes = align_up((size_t)(nch * E + nch) * 4);
+  return MXFP4_OK;
+}
+
+int mxfp4_moe_bucket(const int32_t* sel, int64_t T, int64_t K, int64_t E, int32_t* count, int32_t* offsets,
+                     int32_t* perm, int32_t* slot_of_pair, int32_t* n_invalid, uint32_t flags, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  int st = mxfp4_moe_bucket_workspace_size(T, K, E, flags, &need);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~(MXFP4_FLAG_BUCKET_ONE_BLOCK | MXFP4_FLAG_BUCKET_MULTI_BLOCK)) return MXFP4_ERR_INVALID_ARG;
+  if (!count || !offsets || !n_invalid) return MXFP4_ERR_INVALID_ARG;
+  const int64_t P = T * K;
+  if (P > 0 && (!sel || !perm || !slot_of_pair)) return MXFP4_ERR_INVALID_ARG;
+  const bool one = (flags & MXFP4_FLAG_BUCKET_ONE_BLOCK) || (!(flags & MXFP4_FLAG_BUCKET_MULTI_BLOCK) && P <= 4096);
+  if (!one && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  BucketOut b{count, offsets, perm, slot_of_pair, n_invalid, nullptr, nullptr};
+  hipError_t err = one ? launch_bucket_one_block(sel, (int)P, (int)E, b, stream)
+                       : (P == 0 ? launch_bucket_one_block(sel, 0, (int)E, b, stream)
+                                 : launch_bucket_multi(sel, (int)P, (int)E, static_cast<int32_t*>(workspace), b, stream));
+  return hip_status(err);
+}
+
+int mxfp4_decode_rows(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, int64_t e,
+                      int64_t row0, int64_t nrows, int dtype, void* out, hipStream_t stream) {
+  Dims d;
+  int st = check_dims(0, E, O, G, 1, &d);
+  if (st != MXFP4_OK) return st;
+  if (dtype_size(dtype) == 0 || e < 0 || e >= E || row0 < 0 || nrows < 0 || row0 + nrows > O)
+    return MXFP4_ERR_INVALID_ARG;
+  if (nrows == 0) return MXFP4_OK;
+  if (!packed || !scales || !out || !aligned(packed, 16) || !aligned(out, 16)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  const int64_t row = e * O + row0;
+  return hip_status(launch_decode_rows(packed + row * G * 16, scales + row * G, nrows, G, dtype, out, stream));
+}
+
+const char* mxfp4_status_string(int status) {
+  switch (status) {
+    case MXFP4_OK: return "ok";
+    case MXFP4_ERR_INVALID_ARG: return "invalid argument";
+    case MXFP4_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case MXFP4_ERR_HIP: return "HIP runtime error";
+    case MXFP4_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MXFP4_ERR_INVALID_INDEX: return "selected expert index out of range";
+    case MXFP4_ERR_UNSUPPORTED: return "unsupported path for this dtype or shape";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+// Largest number of pairs (T*K) one fused decode-shaped launch handles: the
+// in-workgroup bucketing and the per-pair partial rows live in LDS.
+constexpr int kMaxFusedPairs = 512;
+
+// Grouped-GEMM tile sizes (pairs x output features) and the bucketing chunk.
+constexpr int kGemmTileM = 128;
+constexpr int kGemmTileN = 128;
+constexpr int kBucketChunk = 1024;
+
+// One M-tile of the grouped GEMM: expert e owns sorted positions
+// row0 .. row0+mlen-1 of this tile.
+struct GemmTile {
+  int32_t e;
+  int32_t row0;
+  int32_t mlen;
+  int32_t pad;
+};
+
+// Upper bound on the number of M-tiles: sum_e ceil(count_e / MT) <= P/MT + min(E, P).
+inline int64_t gemm_max_tiles(int64_t P, int64_t E) {
+  return P / kGemmTileM + (E < P ? E : P);
+}
+// Pairs per bucketing chunk: kBucketChunk, grown (in steps of 64) so that
+// there are never more than kMaxBucketChunks chunks.
+constexpr int64_t kMaxBucketChunks = 256;
+inline int64_t bucket_chunk_size(int64_t P) {
+  int64_t c = (P + kMaxBucketChunks - 1) / kMaxBucketChunks;
+  c = (c + 63) / 64 * 64;
+  return c < kBucketChunk ? kBucketChunk : c;
+}
+inline int64_t bucket_chunks(int64_t P) { return P <= 0 ? 0 : (P + bucket_chunk_size(P) - 1) / bucket_chunk_size(P); }
+
+// ---- bucketing (count, offsets, perm, slot_of_pair, n_invalid, GEMM tiles)
+struct BucketOut {
+  int32_t* count;         // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* perm;          // [P]
+  int32_t* slot_of_pair;  // [P]
+  int32_t* n_invalid;     // [1]
+  GemmTile* tiles;        // [gemm_max_tiles] or null
+  int32_t* n_tiles;       // [1] or null
+};
+// bcount: [bucket_chunks(P) * E] + [bucket_chunks(P)] int32 scratch
+hipError_t launch_bucket_multi(const int32_t* sel, int P, int E, int32_t* bcount, BucketOut out,
+                               hipStream_t stream);
+hipError_t launch_bucket_one_block(const int32_t* sel, int P, int E, BucketOut out, hipStream_t stream);
+
+// ---- decode-shaped fused path: bucketing in LDS + dequant-GEMV + combine.
+// n_invalid (may be null) receives the number of out-of-range indices,
+// accumulated over successive chunk launches (chunk_index 0 starts at zero).
+hipError_t launch_gemv_f32_fused(const float* x, const uint8_t* packed, const uint8_t* scales,
+                                 const int32_t* sel, const float* p, const float* shared, float* y,
+                                 int T, int E, int O, int G, int K, int32_t* n_invalid,
+                                 int chunk_index, hipStream_t stream);
+hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
+                                  const int32_t* sel, const float* p, const uint16_t* shared,
+                                  uint16_t* y, int T, int E, int O, int G, int K, int32_t* n_invalid,
+                                  int chunk_index, hipStream_t stream);
+
+// ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
+                            const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
+                            int64_t max_tiles, float* part, int K, int O, int G, hipStream_t stream);
+hipError_t launch_combine(const float* part, const int32_t* slot_of_pair, const float* p,
+                          const void* shared, void* y, int T, int K, int O, int dtype,
+                          hipStream_t stream);
+
+// ---- exported decode (test and inspection)
+hipError_t launch_decode_rows(const uint8_t* packed_rows, const uint8_t* scales_rows, int64_t nrows,
+                              int64_t G, int dtype, void* out, hipStream_t stream);
+
+}  // namespace mxfp4

@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-side checks return the documented status codes before
+anything is enqueued. No call here reaches the GPU: every call either fails
+validation or is a host-only query."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from mxfp4_block_scaled_amd import _abi
+
+HEADER = os.path.join(ROOT, "include", "mxfp4_moe.h")
+
+# fake, 256-byte aligned, never dereferenced: validation fails before any use
+A = 0x100000
+B = 0x200000
+C = 0x300000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _abi.lib()
+    names = _declared()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_abi.SIGNATURES)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (MXFP4_\w+) (0x[0-9a-f]+u?|\(1 << \d+\)|\d+)", text))
+    assert int(consts["MXFP4_FLAG_FORCE_GEMV"].rstrip("u"), 16) == _abi.FLAG_FORCE_GEMV
+    assert int(consts["MXFP4_FLAG_FORCE_GEMM"].rstrip("u"), 16) == _abi.FLAG_FORCE_GEMM
+    assert int(consts["MXFP4_FLAG_CHECK"].rstrip("u"), 16) == _abi.FLAG_CHECK
+    assert int(consts["MXFP4_MAX_EXPERTS"]) == _abi.MAX_EXPERTS
+    for name, val in re.findall(r"(MXFP4_(?:OK|ERR_\w+)) = (-?\d+)", text):
+        assert getattr(_abi, name[len("MXFP4_"):]) == int(val)
+
+
+def test_status_strings():
+    assert _abi.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5, -6):
+        assert _abi.status_string(s) not in ("ok", "unknown status")
+    assert _abi.status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes_host_only():
+    assert _abi.workspace_size(0, 4, 32, 2, 2, _abi.DTYPE_F32) == 0
+    small = _abi.workspace_size(1, 128, 5760, 90, 4, _abi.DTYPE_F32)
+    assert 0 < small <= 4096  # decode-shaped path: a status word only
+    big = _abi.workspace_size(4096, 128, 5760, 90, 4, _abi.DTYPE_BF16)
+    assert big >= 4096 * 4 * 5760 * 4  # fp32 partial rows [P, O]
+    assert _abi.bucket_workspace_size(8192, 8, 384) >= 4 * 384 * 64
+
+
+def test_path_selection():
+    f32, bf16 = _abi.DTYPE_F32, _abi.DTYPE_BF16
+    assert _abi.select_path(1, 128, 5760, 90, 4, f32) == _abi.PATH_GEMV
+    assert _abi.select_path(8, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMV
+    assert _abi.select_path(16, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMV
+    assert _abi.select_path(17, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMM
+    assert _abi.select_path(4096, 128, 5760, 90, 4, bf16) == _abi.PATH_GEMM
+    assert _abi.select_path(4096, 128, 5760, 90, 4, f32) == _abi.PATH_GEMV
+    assert _abi.select_path(8, 384, 4096, 224, 8, bf16, _abi.FLAG_FORCE_GEMM) == _abi.PATH_GEMM
+    assert _abi.select_path(4096, 128, 5760, 90, 4, bf16, _abi.FLAG_FORCE_GEMV) == _abi.PATH_GEMV
+    with pytest.raises(_abi.Mxfp4Error) as e:
+        _abi.select_path(4, 4, 32, 2, 2, f32, _abi.FLAG_FORCE_GEMM)
+    assert e.value.status == _abi.ERR_UNSUPPORTED
+    with pytest.raises(_abi.Mxfp4Error) as e:
+        _abi.select_path(4, 4, 32, 2, 2, bf16, _abi.FLAG_FORCE_GEMM | _abi.FLAG_FORCE_GEMV)
+    assert e.value.status == _abi.ERR_INVALID_ARG
+
+
+def _ex(x=A, packed=B, scales=C + 0x10000, sel=C + 0x20000, p=C + 0x30000, shared=C + 0x40000, y=C + 0x50000,
+        T=1, E=2, O=4, G=1, K=1, dtype=0, flags=0, ws=C + 0x60000, ws_bytes=1 << 20):
+    return _abi.lib().mxfp4_moe_linear_ex(x, packed, scales, sel, p, shared, y, T, E, O, G, K, dtype, flags, ws,
+                                          ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(E=0), dict(O=0), dict(G=0), dict(K=0), dict(E=_abi.MAX_EXPERTS + 1),
+    dict(T=1 << 24, K=8), dict(dtype=7), dict(x=0), dict(packed=0), dict(scales=0), dict(sel=0), dict(p=0),
+    dict(shared=0), dict(y=0), dict(x=A + 4), dict(packed=B + 8), dict(sel=C + 0x20001), dict(p=C + 0x30002),
+    dict(y=C + 0x50001), dict(y=A), dict(y=B + 64), dict(y=C + 0x10000), dict(flags=0x100),
+    dict(flags=_abi.FLAG_FORCE_GEMV | _abi.FLAG_FORCE_GEMM),
+])
+def test_invalid_arguments_rejected(kw):
+    assert _ex(**kw) == _abi.ERR_INVALID_ARG
+
+
+def test_workspace_too_small_rejected():
+    M = 1 << 28  # far apart: no fake buffer overlaps another at this size
+    kw = dict(x=1 * M, packed=2 * M, scales=3 * M, sel=4 * M, p=5 * M, shared=6 * M, y=7 * M, ws=8 * M)
+    assert _ex(T=4096, E=128, O=64, G=2, K=4, dtype=1, ws_bytes=1024, **kw) == _abi.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_fp32_forced_gemm_unsupported():
+    assert _ex(flags=_abi.FLAG_FORCE_GEMM) == _abi.ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_a_no_op():
+    # T = 0 is valid and enqueues nothing, even with null tensor pointers
+    assert _ex(T=0, x=0, packed=0, scales=0, sel=0, p=0, shared=0, y=0, ws=0, ws_bytes=0) == _abi.OK
+    lib = _abi.lib()
+    assert lib.mxfp4_moe_linear(None, None, None, None, None, None, None, 0, 2, 4, 1, 1, None) == _abi.OK
+    assert lib.mxfp4_moe_linear_bf16(None, None, None, None, None, None, None, 0, 2, 4, 1, 1, None) == _abi.OK
+
+
+def test_plain_entry_points_validate():
+    lib = _abi.lib()
+    assert lib.mxfp4_moe_linear(A, 0, C, C, C, C, C, 1, 2, 4, 1, 1, None) == _abi.ERR_INVALID_ARG
+    assert lib.mxfp4_moe_linear_bf16(A, B, C, C, C, C, C, 1, 0, 4, 1, 1, None) == _abi.ERR_INVALID_ARG
+
+
+def test_decode_rows_validates():
+    lib = _abi.lib()
+    f = lib.mxfp4_decode_rows
+    assert f(B, C, 2, 4, 1, 2, 0, 1, 0, A, None) == _abi.ERR_INVALID_ARG  # e out of range
+    assert f(B, C, 2, 4, 1, 0, 3, 2, 0, A, None) == _abi.ERR_INVALID_ARG  # rows past O
+    assert f(B, C, 2, 4, 1, 0, 0, 1, 5, A, None) == _abi.ERR_INVALID_ARG  # dtype
+    assert f(B + 1, C, 2, 4, 1, 0, 0, 1, 0, A, None) == _abi.ERR_INVALID_ARG  # misaligned packed
+    assert f(B, C, 2, 4, 1, 0, 0, 0, 0, A, None) == _abi.OK  # nothing to do
+
+
+def test_bucket_validates():
+    lib = _abi.lib()
+    f = lib.mxfp4_moe_bucket
+    assert f(A, 1, 1, 0, B, B, B, B, B, 0, C, 64, None) == _abi.ERR_INVALID_ARG
+    assert f(A, 1, 1, 4, 0, B, B, B, B, 0, C, 64, None) == _abi.ERR_INVALID_ARG
+    assert f(A, 1, 1, 4, B, B, B, B, B, _abi.FLAG_BUCKET_ONE_BLOCK | _abi.FLAG_BUCKET_MULTI_BLOCK, C, 64,
+             None) == _abi.ERR_INVALID_ARG
+    assert f(A, 1000, 8, 4, B, B, B, B, B, _abi.FLAG_BUCKET_MULTI_BLOCK, C, 4, None) == _abi.ERR_WORKSPACE_TOO_SMALL

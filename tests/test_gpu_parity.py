@@ -1,0 +1,419 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Bars (written in each check):
+* decoded weights and all bucketing outputs: bit-exact;
+* fp32 activations: max |y - y_ref| <= 1e-4 * (1 + |y_ref|), elementwise;
+* bf16 activations: relative L2 error <= 1e-2 over the compared outputs.
+Full-size workloads run the whole layer on the GPU in the launch
+configuration the benchmark times and compare a sample of output rows
+(all tokens) that the oracle computes row by row.
+"""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only machines, never run there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import mxfp4_block_scaled_amd as mx  # noqa: E402
+from mxfp4_block_scaled_amd import _abi  # noqa: E402
+
+DEV = torch.device("cuda:0")
+F32_TOL = 1e-4
+BF16_REL_L2 = 1e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ helpers
+
+class DevInputs:
+    def __init__(self, x, packed, scales, sel, p, shared, dtype):
+        self.x, self.packed, self.scales, self.sel, self.p, self.shared = x, packed, scales, sel, p, shared
+        self.dtype = dtype
+
+
+def _tdtype(name):
+    return torch.float32 if name == "fp32" else torch.bfloat16
+
+
+def upload(x, packed, scales, sel, p, shared, dtype):
+    """Host arrays (packed/scales may be lazy per-expert tensors) -> device."""
+    td = _tdtype(dtype)
+    E = len(packed)
+    pk0 = np.asarray(packed[0])
+    dpk = torch.empty((E,) + pk0.shape, dtype=torch.uint8, device=DEV)
+    dsc = torch.empty((E,) + np.asarray(scales[0]).shape, dtype=torch.uint8, device=DEV)
+    for e in range(E):
+        dpk[e].copy_(torch.from_numpy(np.ascontiguousarray(packed[e])))
+        dsc[e].copy_(torch.from_numpy(np.ascontiguousarray(scales[e])))
+    return DevInputs(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(td), dpk, dsc,
+                     torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).to(DEV),
+                     torch.from_numpy(np.ascontiguousarray(p, dtype=np.float32)).to(DEV),
+                     torch.from_numpy(np.ascontiguousarray(shared, dtype=np.float32)).to(DEV).to(td), dtype)
+
+
+def run(d: DevInputs, flags=0, sel=None, p=None, out=None):
+    y = mx.moe_linear(d.x, d.packed, d.scales, d.sel if sel is None else sel, d.p if p is None else p, d.shared,
+                      flags=flags, out=out)
+    torch.cuda.synchronize()
+    return y
+
+
+def host64(y):
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def assert_fp32_close(y, ref, what=""):
+    err = np.abs(y - ref)
+    bound = F32_TOL * (1.0 + np.abs(ref))
+    worst = np.max(err / bound) if err.size else 0.0
+    assert np.all(err <= bound), f"{what}: max err/bound {worst:.3g} (max abs err {err.max():.3g})"
+
+
+def rel_l2(y, ref):
+    return float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def assert_bf16_close(y, ref, what=""):
+    r = rel_l2(y, ref)
+    say(f"  {what}: rel L2 {r:.3e}, max abs {np.abs(y - ref).max():.3e}")
+    assert r <= BF16_REL_L2, f"{what}: relative L2 {r:.3e} > {BF16_REL_L2}"
+
+
+def assert_close(y, ref, dtype, what=""):
+    if dtype == "fp32":
+        assert_fp32_close(y, ref, what)
+    else:
+        assert_bf16_close(y, ref, what)
+
+
+def random_case(seed, T, E, K, G, O, dtype, scale_lo=118, scale_hi=130, distinct=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, 32 * G)).astype(np.float32)
+    shared = rng.standard_normal((T, O)).astype(np.float32)
+    if dtype == "bf16":
+        x, shared = workloads.round_to_bf16(x), workloads.round_to_bf16(shared)
+    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, (E, O, G), dtype=np.uint8)
+    if distinct:
+        sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    else:
+        sel = rng.integers(0, E, (T, K)).astype(np.int32)
+    p = rng.random((T, K)).astype(np.float32)
+    return x, packed, scales, sel, p, shared
+
+
+# ------------------------------------------------------------------ exact decode
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_rows_every_byte_and_scale_bit_exact(dtype):
+    say(f"decode_rows exhaustive {dtype}")
+    # row s holds every byte value (group g, byte j = 16 g + j) at scale s
+    packed = np.broadcast_to(np.arange(256, dtype=np.uint8).reshape(1, 1, 16, 16), (1, 256, 16, 16)).copy()
+    scales = np.broadcast_to(np.arange(256, dtype=np.uint8).reshape(1, 256, 1), (1, 256, 16)).copy()
+    want64 = oracle.decode_rows(packed[0], scales[0])
+    with np.errstate(over="ignore"):
+        want32 = want64.astype(np.float32)
+    got = mx.decode_rows(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV), 0, 0, 256,
+                         _tdtype(dtype))
+    torch.cuda.synchronize()
+    if dtype == "fp32":
+        g = got.cpu().numpy().view(np.uint32)
+        assert np.array_equal(g, want32.view(np.uint32))
+    else:
+        g = got.view(torch.int16).cpu().numpy().view(np.uint16)
+        wb = want32.view(np.uint32)
+        assert np.all((wb & 0xFFFF) == 0)  # every decoded value is a bf16 value (or +-inf)
+        assert np.array_equal(g, (wb >> 16).astype(np.uint16))
+    # negative zero survives
+    neg0 = (want32 == 0) & np.signbit(want32)
+    assert neg0.any()
+
+
+def test_decode_rows_window_of_a_larger_expert():
+    x, packed, scales, sel, p, shared = random_case(3, 1, 3, 1, 5, 37, "fp32", 100, 160)
+    got = mx.decode_rows(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV), 2, 11, 20)
+    want = oracle.decode_rows(packed[2, 11:31], scales[2, 11:31]).astype(np.float32)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ printed examples
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_printed_examples_on_gpu(dtype):
+    td = _tdtype(dtype)
+    # byte 0x21 at scale 128 decodes to (1.0, 2.0) in this order
+    packed = torch.zeros((1, 1, 1, 16), dtype=torch.uint8, device=DEV)
+    packed[0, 0, 0, 0] = 0x21
+    scales = torch.full((1, 1, 1), 128, dtype=torch.uint8, device=DEV)
+    for pos, want in ((0, 1.0), (1, 2.0)):
+        x = torch.zeros((1, 32), dtype=td, device=DEV)
+        x[0, pos] = 1
+        y = mx.mxfp4_expert_linear(x, packed, scales, torch.tensor([[0]], device=DEV),
+                                   torch.tensor([[1.0]], device=DEV), torch.zeros((1, 1), dtype=td, device=DEV))
+        assert y.dtype == td and y.shape == (1, 1)
+        assert float(y[0, 0]) == want
+    # every byte 0x22, scale 127, ones input: 32.0
+    y = mx.mxfp4_expert_linear(torch.ones((1, 32), dtype=td, device=DEV),
+                               torch.full((1, 1, 1, 16), 34, dtype=torch.uint8, device=DEV),
+                               torch.full((1, 1, 1), 127, dtype=torch.uint8, device=DEV),
+                               torch.tensor([[0]], device=DEV), torch.tensor([[1.0]], device=DEV),
+                               torch.zeros((1, 1), dtype=td, device=DEV))
+    assert float(y[0, 0]) == 32.0
+
+
+# ------------------------------------------------------------------ bucketing
+
+def _bucket_case(name):
+    if name in workloads.WORKLOADS:
+        return workloads.make_inputs(name).sel, workloads.WORKLOADS[name].E
+    rng = np.random.default_rng(abs(hash(name)) % 1000)
+    if name == "invalid":
+        sel = rng.integers(-3, 9, (37, 3)).astype(np.int32)
+        return sel, 6
+    if name == "one_expert":
+        return np.zeros((2000, 2), np.int32), 1
+    if name == "duplicates":
+        return rng.integers(0, 7, (300, 5)).astype(np.int32), 7
+    if name == "many_experts":
+        return rng.integers(0, 8192, (3000, 8)).astype(np.int32), 8192
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("algo", [_abi.FLAG_BUCKET_ONE_BLOCK, _abi.FLAG_BUCKET_MULTI_BLOCK])
+@pytest.mark.parametrize("case", ["tiny", "decode", "decode8", "prefill", "skewed", "invalid", "one_expert",
+                                  "duplicates", "many_experts"])
+def test_bucketing_bit_exact(case, algo):
+    sel, E = _bucket_case(case)
+    say(f"bucket {case} algo={algo:#x} P={sel.size} E={E}")
+    want = oracle.bucket_pairs(sel, E)
+    got = mx.bucket(torch.from_numpy(sel).to(DEV), E, algo)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in got.items()}
+    nv = int(want["offsets"][-1])
+    assert np.array_equal(g["count"], want["count"])
+    assert np.array_equal(g["offsets"], want["offsets"])
+    assert np.array_equal(g["perm"][:nv], want["perm"])
+    assert np.all(g["perm"][nv:] == -7)  # untouched past the valid pairs
+    assert np.array_equal(g["slot_of_pair"], want["slot_of_pair"])
+    assert int(g["n_invalid"][0]) == want["n_invalid"]
+
+
+# ------------------------------------------------------------------ workloads
+
+@functools.lru_cache(maxsize=1)
+def _workload_dev(name):
+    inp = workloads.make_inputs(name, n_routing_sets=2)
+    say(f"uploading {name}")
+    return inp, upload(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, inp.workload.dtype)
+
+
+def _sample_rows(O, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(O, size=min(n, O), replace=False).tolist())
+    rows.update({0, O - 1, min(O - 1, 127), min(O - 1, 128)})
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_small_workloads_full_oracle(name):
+    inp, d = _workload_dev(name)
+    say(f"workload {name} full oracle")
+    ref = oracle.expert_linear(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared)
+    y = run(d)
+    assert y.dtype == torch.float32 and tuple(y.shape) == ref.shape
+    assert_fp32_close(host64(y), ref, name)
+    # second routing draw on the same weights
+    sel2, p2 = inp.routing_sets[1]
+    ref2 = oracle.expert_linear(inp.x, inp.packed, inp.scales, sel2, p2, inp.shared)
+    y2 = run(d, sel=torch.from_numpy(sel2).to(DEV), p=torch.from_numpy(p2).to(DEV))
+    assert_fp32_close(host64(y2), ref2, name + " routing set 1")
+
+
+@pytest.mark.parametrize("name,nrows", [("decode8", 160), ("prefill", 48), ("skewed", 40)])
+def test_large_workloads_sampled_rows(name, nrows):
+    inp, d = _workload_dev(name)
+    w = inp.workload
+    rows = _sample_rows(w.O, nrows, 7)
+    say(f"workload {name}: GPU run, oracle on {rows.size} rows x {w.T} tokens")
+    y = run(d)
+    assert y.dtype == torch.bfloat16 and tuple(y.shape) == (w.T, w.O)
+    ref = oracle.expert_linear_rows(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
+    assert_bf16_close(host64(y)[:, rows], ref, name)
+    assert np.all(np.isfinite(host64(y)))
+
+
+def test_decode8_both_paths():
+    inp, d = _workload_dev("decode8")
+    rows = _sample_rows(inp.workload.O, 96, 8)
+    ref = oracle.expert_linear_rows(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
+    for flags in (_abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMM):
+        say(f"decode8 flags={flags}")
+        y = host64(run(d, flags=flags))
+        assert_bf16_close(y[:, rows], ref, f"decode8 flags={flags}")
+
+
+# ------------------------------------------------------------------ paths, thresholds, edges
+
+@pytest.mark.parametrize("T", [15, 16, 17])
+def test_threshold_sweep(T):
+    case = random_case(100 + T, T, 40, 4, 8, 136, "bf16")
+    d = upload(*case, "bf16")
+    E, O, G = 40, 136, 8
+    want_path = _abi.PATH_GEMV if T <= 16 else _abi.PATH_GEMM
+    assert mx.select_path(T, E, O, G, 4, _abi.DTYPE_BF16) == want_path
+    ref = oracle.expert_linear(*case)
+    results = {}
+    for flags in (0, _abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMM):
+        y = host64(run(d, flags=flags))
+        assert_bf16_close(y, ref, f"T={T} flags={flags}")
+        results[flags] = y
+    assert np.array_equal(results[0], results[_abi.FLAG_FORCE_GEMV if T <= 16 else _abi.FLAG_FORCE_GEMM])
+
+
+EDGE_CASES = [
+    # T, E, K, G, O, distinct
+    (1, 1, 1, 1, 1, True),
+    (1, 3, 1, 1, 17, True),
+    (2, 5, 5, 3, 33, True),      # every expert chosen by every token, odd G
+    (3, 8, 2, 7, 130, True),     # ragged 128-row N-tile
+    (5, 6, 4, 2, 16, False),     # duplicates within a token
+    (9, 64, 2, 5, 257, True),    # most experts empty
+    (40, 3, 2, 4, 64, False),    # many rows per expert, duplicates
+    (33, 200, 8, 3, 96, True),   # P spans a ragged 128-row M-tile
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "T{}E{}K{}G{}O{}{}".format(*c[:5], "" if c[5] else "dup"))
+def test_edge_shapes(case, dtype):
+    T, E, K, G, O, distinct = case
+    say(f"edge {case} {dtype}")
+    host = random_case(sum(case[:5]), T, E, K, G, O, dtype, distinct=distinct)
+    d = upload(*host, dtype)
+    ref = oracle.expert_linear(*host)
+    flag_sets = [0] if dtype == "fp32" else [0, _abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMM]
+    for flags in flag_sets:
+        y = run(d, flags=flags)
+        assert y.dtype == _tdtype(dtype)
+        assert_close(host64(y), ref, dtype, f"{case} flags={flags}")
+
+
+def test_fp32_many_tokens_uses_chunked_fused_launches():
+    # P > 512 pairs per launch: the fp32 path splits tokens into chunks
+    host = random_case(5, 300, 16, 3, 2, 40, "fp32")
+    d = upload(*host, "fp32")
+    assert_fp32_close(host64(run(d)), oracle.expert_linear(*host), "fp32 T=300")
+
+
+def test_empty_batch():
+    d = upload(*random_case(1, 2, 4, 2, 2, 8, "fp32"), "fp32")
+    y = mx.moe_linear(d.x[:0], d.packed, d.scales, d.sel[:0], d.p[:0], d.shared[:0])
+    assert y.shape == (0, 8)
+
+
+# ------------------------------------------------------------------ invariants
+
+@pytest.mark.parametrize("dtype,flags", [("fp32", 0), ("bf16", _abi.FLAG_FORCE_GEMV), ("bf16", _abi.FLAG_FORCE_GEMM)])
+def test_invariants(dtype, flags):
+    T, E, K, G, O = 6, 12, 3, 6, 200
+    x, packed, scales, sel, p, shared = random_case(77, T, E, K, G, O, dtype)
+    zero = np.zeros_like(shared)
+    d = upload(x, packed, scales, sel, p, zero, dtype)
+    y = run(d, flags=flags)
+    y_again = run(d, flags=flags)
+    assert torch.equal(y, y_again), "not deterministic"
+    # unselected experts do not matter, bit for bit
+    pk2, sc2 = packed.copy(), scales.copy()
+    rng = np.random.default_rng(1)
+    for e in set(range(E)) - set(np.unique(sel).tolist()):
+        pk2[e] = rng.integers(0, 256, pk2[e].shape)
+        sc2[e] = 255
+    assert torch.equal(run(upload(x, pk2, sc2, sel, p, zero, dtype), flags=flags), y)
+    # b ^ 0x88 flips every sign: the routed part is negated exactly
+    yn = run(upload(x, packed ^ np.uint8(0x88), scales, sel, p, zero, dtype), flags=flags)
+    assert torch.equal(yn, -y)
+    # every scale + 1 doubles the routed part exactly
+    y2 = run(upload(x, packed, scales + np.uint8(1), sel, p, zero, dtype), flags=flags)
+    assert torch.equal(y2, 2 * y)
+    # swapping the nibbles of every byte equals swapping inputs 2j <-> 2j+1
+    xs = x.copy()
+    xs[:, 0::2], xs[:, 1::2] = x[:, 1::2], x[:, 0::2]
+    sw = ((packed & 0x0F) << 4) | (packed >> 4)
+    ys = run(upload(xs, sw, scales, sel, p, zero, dtype), flags=flags)
+    assert_close(host64(ys), host64(y), dtype, "nibble swap")
+    # linear in p
+    p2 = np.random.default_rng(2).random(p.shape).astype(np.float32)
+    ya = host64(run(d, p=torch.from_numpy(p2).to(DEV), flags=flags))
+    yb = host64(run(d, p=torch.from_numpy(p + p2).to(DEV), flags=flags))
+    ref = oracle.expert_linear(x, packed, scales, sel, p + p2, zero)
+    assert_close(yb, ref, dtype, "p1+p2")
+    assert_close(host64(y) + ya, ref, dtype, "y(p1)+y(p2)")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_inputs_untouched_and_in_place(dtype):
+    host = random_case(9, 4, 6, 2, 3, 50, dtype)
+    d = upload(*host, dtype)
+    before = [t.clone() for t in (d.x, d.packed, d.scales, d.sel, d.p, d.shared)]
+    y = run(d)
+    for a, b in zip((d.x, d.packed, d.scales, d.sel, d.p, d.shared), before):
+        assert torch.equal(a, b)
+    assert y.data_ptr() != d.shared.data_ptr()
+    out = d.shared.clone()
+    y2 = run(d, out=None)
+    y3 = mx.moe_linear(d.x, d.packed, d.scales, d.sel, d.p, out, out=out)  # y == shared
+    torch.cuda.synchronize()
+    assert y3.data_ptr() == out.data_ptr() and torch.equal(y3, y2)
+
+
+def test_out_of_range_index_reported_with_check_flag():
+    x, packed, scales, sel, p, shared = random_case(11, 5, 7, 2, 2, 24, "fp32")
+    sel[2, 1] = 7
+    sel[4, 0] = -1
+    d = upload(x, packed, scales, sel, p, shared, "fp32")
+    with pytest.raises(mx.Mxfp4Error) as e:
+        run(d, flags=_abi.FLAG_CHECK)
+    assert e.value.status == _abi.ERR_INVALID_INDEX
+    y = run(d)  # without the flag: the bad slots contribute nothing
+    sel_ok, p_ok = sel.copy(), p.copy()
+    for t, k in ((2, 1), (4, 0)):
+        sel_ok[t, k], p_ok[t, k] = 0, 0.0
+    assert_fp32_close(host64(y), oracle.expert_linear(x, packed, scales, sel_ok, p_ok, shared), "invalid dropped")
+
+
+def test_plain_entry_points_match_ex():
+    lib = _abi.lib()
+    for dtype in ("fp32", "bf16"):
+        host = random_case(12, 3, 5, 2, 4, 40, dtype)
+        d = upload(*host, dtype)
+        y_ex = run(d)
+        y = torch.empty_like(d.shared)
+        fn = lib.mxfp4_moe_linear if dtype == "fp32" else lib.mxfp4_moe_linear_bf16
+        st = fn(d.x.data_ptr(), d.packed.data_ptr(), d.scales.data_ptr(), d.sel.data_ptr(), d.p.data_ptr(),
+                d.shared.data_ptr(), y.data_ptr(), 3, 5, 40, 4, 2, torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ex)
+    # prefill-shaped plain call (allocates its workspace on the stream)
+    host = random_case(13, 40, 6, 2, 3, 64, "bf16")
+    d = upload(*host, "bf16")
+    y = torch.empty_like(d.shared)
+    st = lib.mxfp4_moe_linear_bf16(d.x.data_ptr(), d.packed.data_ptr(), d.scales.data_ptr(), d.sel.data_ptr(),
+                                   d.p.data_ptr(), d.shared.data_ptr(), y.data_ptr(), 40, 6, 64, 3, 2,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y, run(d))
