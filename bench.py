@@ -1,0 +1,248 @@
+"""Benchmark of the MXFP4 routed-expert linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the whole layer (bucketing, dequant-GEMV or grouped
+GEMM, combine) on one batch of the workload's synthetic inputs, all resident
+in HBM before the timed region. Step i uses routing draw i mod R (R = 64
+distinct (sel, p) draws), so consecutive calls read different experts and
+the Infinity Cache cannot serve the weights from the previous call.
+
+The K timed steps are captured once in a HIP graph and replayed; the timed
+region is bracketed by device synchronisation, and HIP events on the replay
+stream give its duration. One JSON line goes to stdout; details to stderr.
+
+value:
+  decode-shaped workloads: algorithmic weight bytes per second, where a call
+    reads U * O * G * 17 bytes (16 packed + 1 scale byte per 32-weight
+    group of each of the U distinct selected experts; 4.25 bits per weight);
+  prefill-shaped workloads: 2 * T * K * O * I flops per second.
+cpu_baseline: the float64 oracle timed on the host on a bounded sample of
+  the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "packed-weight GB/s (decode) & TFLOP/s (prefill), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+N_ROUTING_SETS = 64
+DECODE_WORKLOADS = ("tiny", "decode", "decode8")
+KERNEL_SOURCES = {
+    "gemv": ["mxfp4_block_scaled_amd/csrc/gemv.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+    "gemm": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sources_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, kind: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sources_sha(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, kind, sample_seconds):
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS threads unknown
+        threads = os.cpu_count() or 1
+    w = inp.workload
+    if kind == "gemv":
+        done_bytes, calls, t0 = 0.0, 0, time.perf_counter()
+        while True:
+            sel, p = inp.routing_sets[calls % len(inp.routing_sets)]
+            oracle.expert_linear(inp.x, inp.packed, inp.scales, sel, p, inp.shared)
+            done_bytes += len(np.unique(sel)) * w.O * w.G * 17
+            calls += 1
+            if time.perf_counter() - t0 >= sample_seconds:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"{calls} full calls of the {w.name} workload (routing draws 0..{calls - 1})",
+                "seconds": round(dt, 2)}
+    # prefill: all tokens, a sample of output rows
+    rows_per_call = 16
+    done_flops, calls, t0 = 0.0, 0, time.perf_counter()
+    rng = np.random.default_rng(0)
+    while True:
+        rows = np.sort(rng.choice(w.O, rows_per_call, replace=False))
+        oracle.expert_linear_rows(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
+        done_flops += 2.0 * w.P * rows_per_call * w.I
+        calls += 1
+        if time.perf_counter() - t0 >= sample_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} x {rows_per_call} output rows of the {w.name} workload, all {w.T} tokens",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp4_block_scaled_amd as mx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.workload]
+    kind = "gemv" if args.workload in DECODE_WORKLOADS else "gemm"
+    td = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    t_gen = time.perf_counter()
+    inp = workloads.make_inputs(w, n_routing_sets=N_ROUTING_SETS)
+    packed = torch.empty((w.E, w.O, w.G, 16), dtype=torch.uint8, device=dev)
+    scales = torch.empty((w.E, w.O, w.G), dtype=torch.uint8, device=dev)
+    for e in range(w.E):
+        packed[e].copy_(torch.from_numpy(inp.packed[e]))
+        scales[e].copy_(torch.from_numpy(inp.scales[e]))
+    x = torch.from_numpy(inp.x).to(dev).to(td)
+    shared = torch.from_numpy(inp.shared).to(dev).to(td)
+    sels = torch.from_numpy(np.stack([s for s, _ in inp.routing_sets])).to(dev)
+    ps = torch.from_numpy(np.stack([p for _, p in inp.routing_sets])).to(dev)
+    y = torch.empty_like(shared)
+    ws = torch.empty(max(mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1), 1),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: inputs drawn and resident in {time.perf_counter() - t_gen:.1f} s; "
+        f"packed {packed.numel() / 1e9:.2f} GB, workspace {ws.numel() / 1e6:.1f} MB, "
+        f"path {'GEMV' if mx.select_path(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == 'fp32' else 1) == 1 else 'GEMM'}")
+
+    def step(i):
+        r = i % N_ROUTING_SETS
+        mx.moe_linear(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
+
+    # eager reference of the last timed step, for the graph replay check
+    last = (args.steps - 1) % N_ROUTING_SETS
+    step(last)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream(device=dev)
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            step(0)  # the binding allocates nothing here; this call only settles the stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, y_eager):
+            raise SystemExit("graph replay result differs from the eager call")
+        log("[bench] graph replay matches the eager call bit for bit")
+
+    # timed region
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(i)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    if not torch.equal(y, y_eager):
+        raise SystemExit("timed steps ended with a result that differs from the eager call")
+
+    uniq = [len(np.unique(inp.routing_sets[i % N_ROUTING_SETS][0])) for i in range(args.steps)]
+    bytes_per_step = float(np.mean(uniq)) * w.O * w.G * 17
+    flops_per_step = 2.0 * w.P * w.O * w.I
+    if kind == "gemv":
+        value = bytes_per_step / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4)}
+    else:
+        value = flops_per_step / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = "gemv_f32_fused_kernel" if (kind == "gemv" and w.dtype == "fp32") else (
+        "gemv_bf16_fused_kernel" if kind == "gemv" else "whole call (bucketing + gemm_bf16_kernel + combine)")
+    roof["launch_ms"] = round(ms_step, 6)
+    roof["per_launch"] = ({"bytes": bytes_per_step} if kind == "gemv" else {"flops": flops_per_step})
+    roof["traffic"] = committed_traffic(w.name, kind)
+    log(f"[bench] {args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, "
+        f"{value:.1f} {unit} ({100 * roof['frac']:.1f}% of peak); mean distinct experts {np.mean(uniq):.1f}")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if w.dtype == "fp32" else "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
+                   "x_dtype": w.dtype, "routing": w.routing if w.routing == "uniform" else f"zipf({w.zipf_s})",
+                   "routing_draws": N_ROUTING_SETS, "graph": graph is not None},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(inp, kind, args.cpu_seconds)
+        out["cpu_baseline"] = cb
+        log(f"[bench] oracle on the host: {cb['value']:.4g} {cb['unit']} with {cb['cores']} threads ({cb['sample']})")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
