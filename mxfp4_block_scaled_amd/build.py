@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,21 +46,42 @@ def _device_flags():
     return [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+def _resource_problems(remarks: str) -> list:
+    """Kernels that use scratch memory or spill registers, from the
+    compiler's resource-usage remarks."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
+        if m and int(m.group(2)) != 0:
+            bad.append(f"{name}: {m.group(1)} = {m.group(2)}")
+    return bad
+
+
 def _compile(src: str, verbose: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-c", path, "-o", obj] + _common_flags()
     if src.endswith(".hip"):
-        cmd += _device_flags()
+        cmd += _device_flags() + ["-Rpass-analysis=kernel-resource-usage"]
     else:
         cmd += ["-x", "c++", "-D__HIP_PLATFORM_AMD__"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in line)
+    text = r.stdout + r.stderr
+    out = "\n".join(line for line in text.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in line and "remark:" not in line)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{out}")
+    # every kernel must keep its state in registers and LDS: scratch memory
+    # (private arrays or spills) costs a slow memory round trip per access
+    bad = _resource_problems(text)
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory or spill:\n  " + "\n  ".join(bad))
     if verbose and out.strip():
         print(out, flush=True)
     return obj

@@ -57,13 +57,15 @@ int select_path(const Dims& d, int dtype, uint32_t flags) {
   if (dtype_size(dtype) == 0) return MXFP4_ERR_INVALID_ARG;
   const bool fv = flags & MXFP4_FLAG_FORCE_GEMV, fm = flags & MXFP4_FLAG_FORCE_GEMM;
   if (fv && fm) return MXFP4_ERR_INVALID_ARG;
+  // the decode-shaped kernel needs one token's activations and partial rows in LDS
+  const bool gemv_ok = decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype) >= 1;
   if (dtype == MXFP4_DTYPE_F32) {
-    if (fm) return MXFP4_ERR_UNSUPPORTED;  // the MFMA grouped GEMM is bf16-only
+    if (fm || !gemv_ok) return MXFP4_ERR_UNSUPPORTED;  // the MFMA grouped GEMM is bf16-only
     return MXFP4_PATH_GEMV;
   }
-  if (fv) return MXFP4_PATH_GEMV;
+  if (fv) return gemv_ok ? MXFP4_PATH_GEMV : MXFP4_ERR_UNSUPPORTED;
   if (fm) return MXFP4_PATH_GEMM;
-  return d.T <= kGemvMaxTokens ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
+  return (d.T <= kGemvMaxTokens && gemv_ok) ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
 }
 
 // Workspace layout. GEMV: n_invalid only. GEMM: bucketing arrays, the M-tile
@@ -154,25 +156,16 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
   hipError_t err = hipSuccess;
   const int es = dtype_size(dtype);
   if (path == MXFP4_PATH_GEMV) {
-    if (d.K > kMaxFusedPairs) return MXFP4_ERR_UNSUPPORTED;
-    // token chunks whose pairs fit one fused launch
-    const int64_t tc = kMaxFusedPairs / d.K;
+    // token chunks whose pairs and activations fit one fused launch
+    const int64_t tc = decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype);
+    if (tc < 1) return MXFP4_ERR_UNSUPPORTED;
     int chunk = 0;
     for (int64_t t0 = 0; t0 < d.T && err == hipSuccess; t0 += tc, chunk++) {
       const int64_t tn = (d.T - t0 < tc) ? d.T - t0 : tc;
-      const char* xc = static_cast<const char*>(x) + t0 * d.I * es;
-      const int32_t* selc = sel + t0 * d.K;
-      const float* pc = p + t0 * d.K;
-      const char* shc = static_cast<const char*>(shared) + t0 * d.O * es;
-      char* yc = static_cast<char*>(y) + t0 * d.O * es;
-      if (dtype == MXFP4_DTYPE_F32)
-        err = launch_gemv_f32_fused(reinterpret_cast<const float*>(xc), packed, scales, selc, pc,
-                                    reinterpret_cast<const float*>(shc), reinterpret_cast<float*>(yc), (int)tn,
-                                    (int)d.E, (int)d.O, (int)d.G, (int)d.K, n_invalid, chunk, stream);
-      else
-        err = launch_gemv_bf16_fused(reinterpret_cast<const uint16_t*>(xc), packed, scales, selc, pc,
-                                     reinterpret_cast<const uint16_t*>(shc), reinterpret_cast<uint16_t*>(yc), (int)tn,
-                                     (int)d.E, (int)d.O, (int)d.G, (int)d.K, n_invalid, chunk, stream);
+      err = launch_decode_fused(static_cast<const char*>(x) + t0 * d.I * es, packed, scales, sel + t0 * d.K,
+                                p + t0 * d.K, static_cast<const char*>(shared) + t0 * d.O * es,
+                                static_cast<char*>(y) + t0 * d.O * es, (int)tn, (int)d.E, (int)d.O, (int)d.G,
+                                (int)d.K, dtype, n_invalid, chunk, stream);
     }
   } else {
     BucketOut b;

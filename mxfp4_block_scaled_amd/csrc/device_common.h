@@ -92,6 +92,23 @@ __device__ __forceinline__ void decode8_bf16_slow(uint32_t w, uint32_t s, uint32
   }
 }
 
+// Scale byte 255 (2^128): decode at 2^127 in fp32 (exact), double (exact,
+// overflowing to +-inf where the value does), keep the bf16 high halves
+// (exact: every such value is a bf16 value or an infinity).
+__device__ __forceinline__ void decode8_bf16_s255(uint32_t w, uint32_t out[4]) {
+  const float sc = e8m0_operand(254);
+  f32x2 v[4];
+  v[0] = cvt_fp4x2_f32<0>(w, sc);
+  v[1] = cvt_fp4x2_f32<1>(w, sc);
+  v[2] = cvt_fp4x2_f32<2>(w, sc);
+  v[3] = cvt_fp4x2_f32<3>(w, sc);
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+    const float lo = v[b].x * 2.0f, hi = v[b].y * 2.0f;
+    out[b] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+}
+
 __device__ __forceinline__ void decode8_bf16_fast(uint32_t w, float sc, uint32_t out[4]) {
   out[0] = cvt_fp4x2_bf16<0>(w, sc);
   out[1] = cvt_fp4x2_bf16<1>(w, sc);

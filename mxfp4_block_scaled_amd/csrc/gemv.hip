@@ -1,289 +1,418 @@
-// Decode-shaped path: one launch does the bucketing, the dequant-GEMV and
-// the combine for a few tokens.
+// Decode-shaped path: routing, dequant-GEMV and combine in one launch.
 //
-// Each workgroup owns a tile of output rows and computes, for every selected
-// expert, that expert's rows of W_e x_t for all of its pairs; it keeps those
+// Each workgroup owns 16 output rows and computes, for every selected
+// expert, those rows of W_e x_t for all of the expert's pairs, keeps the
 // per-pair partial rows in LDS and finally writes
 //     y[t, o] = shared[t, o] + sum_{k<K} p[t,k] * partial[(t,k), o]
 // with the sum over k in order (page "MXFP4 Routed Expert Linear", "Route,
 // weight, and add the shared path"). Only the selected experts' bytes are
-// read; each 16-byte group is loaded once and used for every token of that
-// expert. No decoded weight leaves the registers.
+// read; each 16-byte group is loaded once (128-bit loads) and used for every
+// token of that expert. No decoded weight leaves the registers.
 //
-// Bucketing in the workgroup: every pair gets its position in the stable
-// sort by expert by counting the pairs before it (ties by pair number), so
-// the segments, their order and the positions are the same in every
-// workgroup and every run.
+// Routing: at most 64 pairs per launch (the host splits tokens into
+// chunks). Every wave finds the distinct experts itself: lane i holds pair
+// i, and log2(E) ballots give each lane the mask of pairs that chose its
+// expert. No LDS and no barrier stand between the routing load and the
+// first weight loads.
+//
+// Arithmetic: v_mfma_f32_16x16x32_bf16. The A operand is 16 weight rows by
+// 32 inputs, decoded exactly into bf16 by the scaled FP4 convert (every
+// E2M1 value times 2^(s-127) is a bf16 value unless it overflows). The B
+// operand is 16 columns, one per (pair, piece): bf16 activations are one
+// piece; fp32 activations are split exactly into three bf16 pieces by
+// truncation (x = x0 + x1 + x2 for every normal fp32 x), so every product
+// w * x_i is exact and the MFMA accumulates in fp32 -- the result keeps
+// fp32 accuracy. Lane (r, q) = (lane & 15, lane >> 4) loads the whole group
+// 4i+q of row r and feeds its dword j to MFMA j; the B operand uses the
+// same permutation of k, so each MFMA sums matching products.
+//
+// Work item = (distinct expert, chunk of 16 columns, k-split). A wave walks
+// its items as one stream of iterations (16 rows x 4 groups each) with
+// kRing 128-bit loads in flight, across item boundaries. The activations
+// are staged once per workgroup in LDS (rows padded by 16 bytes so that the
+// columns of an MFMA fall in different banks).
 #include "device_common.h"
 #include "launch.h"
 
 namespace mxfp4 {
 namespace {
 
+constexpr int kDecThreads = 512;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kRing = 8;   // iterations whose loads a wave keeps in flight
+constexpr int kRows = 16;  // output rows per workgroup (one MFMA tile)
+
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
 
-struct FusedBuckets {
-  int key[kMaxFusedPairs];           // expert of pair i, or E when out of range
-  int sorted_pair[kMaxFusedPairs];   // pair at sorted position r
-  int slot_of_pair[kMaxFusedPairs];  // sorted position of pair i, -1 if out of range
-  int seg_expert[kMaxFusedPairs];    // expert of segment u (increasing)
-  int seg_begin[kMaxFusedPairs + 1]; // first sorted position of segment u
-  int n_seg;
-  int n_invalid;
-  int wave_cnt[16];
-};
-
-template <int NT>
-__device__ void bucket_in_block(const int32_t* __restrict__ sel, int P, int E, FusedBuckets& b) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid == 0) b.n_invalid = 0;
-  __syncthreads();
-  for (int i = tid; i < P; i += NT) {
-    const int e = sel[i];
-    const bool ok = e >= 0 && e < E;
-    b.key[i] = ok ? e : E;
-    if (!ok) atomicAdd(&b.n_invalid, 1);
+// Position of the n-th set bit of m (m has more than n set bits), by a
+// branch-free binary search on popcounts.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int width = 32; width >= 1; width >>= 1) {
+    const uint64_t low = m & ((width == 64 ? 0ull : (1ull << width)) - 1ull);
+    const int c = __popcll(low);
+    const bool up = n >= c;
+    n -= up ? c : 0;
+    pos += up ? width : 0;
+    m = up ? (m >> width) : low;
   }
-  __syncthreads();
-  for (int i = tid; i < P; i += NT) {
-    const int ki = b.key[i];
-    int r = 0;
-    for (int j = 0; j < P; j++) {
-      const int kj = b.key[j];
-      r += (kj < ki) | ((kj == ki) & (j < i));
-    }
-    b.sorted_pair[r] = i;
-    b.slot_of_pair[i] = (ki < E) ? r : -1;
-  }
-  __syncthreads();
-  int base = 0;
-  for (int r0 = 0; r0 < P; r0 += NT) {
-    const int r = r0 + tid;
-    bool start = false;
-    int kr = E;
-    if (r < P) {
-      kr = b.key[b.sorted_pair[r]];
-      start = kr < E && (r == 0 || b.key[b.sorted_pair[r - 1]] != kr);
-    }
-    const uint64_t m = __ballot(start);
-    if (lane == 0) b.wave_cnt[w] = __popcll(m);
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int i = 0; i < NT / 64; i++) {
-      const int c = b.wave_cnt[i];
-      before += (i < w) ? c : 0;
-      tot += c;
-    }
-    if (start) {
-      const int u = base + before + __popcll(m & lanes_below(lane));
-      b.seg_expert[u] = kr;
-      b.seg_begin[u] = r;
-    }
-    base += tot;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    b.n_seg = base;
-    b.seg_begin[base] = P - b.n_invalid;
-  }
-  __syncthreads();
+  return pos;
 }
 
-// ------------------------------------------------------------------ fp32
-// One wave per (expert, row): lane j takes groups j, j+64, ...; the 32
-// unscaled table values of a group are dotted with x in fp32 and the group
-// partial is scaled by 2^(s-127) with ldexp (the same value as scaling every
-// weight first, up to where fp32 under- or overflows); a fixed butterfly sums
-// the 64 lanes.
-template <int R>
-__global__ void __launch_bounds__(256) gemv_f32_fused_kernel(
-    const float* __restrict__ x, const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
-    const int32_t* __restrict__ sel, const float* __restrict__ p, const float* shared, float* y, int T, int E, int O,
-    int G, int K, int32_t* __restrict__ n_invalid, int chunk_index) {
-  __shared__ FusedBuckets bk;
-  __shared__ float part[kMaxFusedPairs * R];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int P = T * K;
-  const int64_t I = 32 * (int64_t)G;
-  bucket_in_block<256>(sel, P, E, bk);
-  const int U = bk.n_seg;
-  const int o0 = blockIdx.x * R;
-  for (int it = w; it < U * R; it += 4) {
-    const int u = it / R, r = it - u * R, o = o0 + r;
-    if (o >= O) continue;
-    const int e = bk.seg_expert[u], sb = bk.seg_begin[u], n = bk.seg_begin[u + 1] - sb;
-    const uint8_t* prow = packed + ((int64_t)e * O + o) * (int64_t)G * 16;
-    const uint8_t* srow = scales + ((int64_t)e * O + o) * (int64_t)G;
-    for (int q0 = 0; q0 < n; q0 += 4) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      const float* xr[4];
-#pragma unroll
-      for (int qi = 0; qi < 4; qi++) {
-        const int pr = (q0 + qi < n) ? bk.sorted_pair[sb + q0 + qi] : 0;
-        xr[qi] = x + (int64_t)(pr / K) * I;
-      }
-      for (int g = lane; g < G; g += 64) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(prow + (int64_t)g * 16);
-        const int s = srow[g];
-        float wf[32];
-        decode8_f32_unscaled(wv.x, wf);
-        decode8_f32_unscaled(wv.y, wf + 8);
-        decode8_f32_unscaled(wv.z, wf + 16);
-        decode8_f32_unscaled(wv.w, wf + 24);
-#pragma unroll
-        for (int qi = 0; qi < 4; qi++) {
-          if (q0 + qi < n) {
-            const float4* xv = reinterpret_cast<const float4*>(xr[qi] + 32 * g);
-            float gp = 0.f;
-#pragma unroll
-            for (int v = 0; v < 8; v++) {
-              const float4 xx = xv[v];
-              gp = fmaf(wf[4 * v + 0], xx.x, gp);
-              gp = fmaf(wf[4 * v + 1], xx.y, gp);
-              gp = fmaf(wf[4 * v + 2], xx.z, gp);
-              gp = fmaf(wf[4 * v + 3], xx.w, gp);
-            }
-            acc[qi] += __builtin_amdgcn_ldexpf(gp, s - 127);
-          }
-        }
-      }
-#pragma unroll
-      for (int qi = 0; qi < 4; qi++) {
-        if (q0 + qi < n) {
-          const float v = wave_sum(acc[qi]);
-          if (lane == 0) part[(sb + q0 + qi) * R + r] = v;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < T * R; idx += 256) {
-    const int t = idx / R, r = idx - t * R, o = o0 + r;
-    if (o >= O) continue;
-    float a = 0.f;
-    for (int k = 0; k < K; k++) {
-      const int sp = bk.slot_of_pair[t * K + k];
-      if (sp >= 0) a = fmaf(p[t * K + k], part[sp * R + r], a);
-    }
-    const int64_t yo = (int64_t)t * O + o;
-    y[yo] = shared[yo] + a;
-  }
-  if (blockIdx.x == 0 && tid == 0 && n_invalid) n_invalid[0] = (chunk_index == 0 ? 0 : n_invalid[0]) + bk.n_invalid;
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int src) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// ------------------------------------------------------------------ bf16
-// One wave per (expert, 16-row tile): v_mfma_f32_16x16x32_bf16 with the
-// decoded weights as the 16 x 32 operand and up to 16 of the expert's pairs
-// as the 32 x 16 operand. Lane (r, q) = (lane & 15, lane >> 4) loads the
-// whole 16-byte group 4*it + q of row r and feeds its dword j to MFMA j;
-// the x operand uses the same permutation of k, so each MFMA still sums
-// matching weight/activation products. The scale is applied in the decode
-// (exact in bf16), so the MFMA accumulates W_e x exactly as defined.
-template <int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) gemv_bf16_fused_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
-    const int32_t* __restrict__ sel, const float* __restrict__ p, const uint16_t* shared, uint16_t* y, int T, int E,
-    int O, int G, int K, int32_t* __restrict__ n_invalid, int chunk_index) {
-  constexpr int R = 16;
-  __shared__ FusedBuckets bk;
-  __shared__ float part[kMaxFusedPairs * R];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const uint32_t lo = __shfl((uint32_t)v, src, kWave);
+  const uint32_t hi = __shfl((uint32_t)(v >> 32), src, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// fp32 -> three bf16 (bit patterns) with f = x0 + x1 + x2 exactly: each
+// piece keeps the top 8 significant bits of what is left, and the
+// subtractions are exact (both operands share sign and exponent range).
+__device__ __forceinline__ void split3(float f, uint32_t& b0, uint32_t& b1, uint32_t& b2) {
+  const uint32_t u = __float_as_uint(f);
+  const float r1 = f - __uint_as_float(u & 0xffff0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+  b0 = u >> 16;
+  b1 = u1 >> 16;
+  b2 = __float_as_uint(r2) >> 16;
+}
+
+template <bool XF32>
+__global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
+    const void* __restrict__ xv, const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+    const int32_t* __restrict__ sel, const float* __restrict__ p, const void* shared, void* y, int T, int E, int O,
+    int G, int K, int S, int nbits, int32_t* __restrict__ n_invalid, int chunk_index) {
+  constexpr int NP = XF32 ? 3 : 1;  // bf16 pieces per activation
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  __shared__ float p_lds[kMaxFusedPairs];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, kept in a scalar register
   const int r = lane & 15, q = lane >> 4;
-  const int P = T * K;
-  const int64_t I = 32 * (int64_t)G;
-  bucket_in_block<WAVES * 64>(sel, P, E, bk);
-  const int U = bk.n_seg;
-  const int o0 = blockIdx.x * R;
+  const int P = T * K, I = 32 * G, IL = I + 8;
+  const int o0 = blockIdx.x * kRows;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn);  // [T][NP][IL] bf16
+  float* part = reinterpret_cast<float*>(dyn + (((size_t)T * NP * IL * 2 + 15) & ~(size_t)15));  // [S][P*NP][16]
+
+  // ---- routing input first, then the loads that do not depend on it:
+  // p, shared and (up to two 16-byte chunks per thread of) x, written to LDS
+  // after the weight loads have been issued
+  const int e_l = lane < P ? sel[lane] : -1;
+  const float my_p = tid < P ? p[tid] : 0.f;
+  const int t_first = tid >> 4, rr_first = tid & 15;
+  const bool first_ok = t_first < T && o0 + rr_first < O;
+  float sh_first = 0.f;
+  if (first_ok) {
+    const int64_t yo = (int64_t)t_first * O + o0 + rr_first;
+    sh_first = XF32 ? static_cast<const float*>(shared)[yo] : bf16_to_f32(static_cast<const uint16_t*>(shared)[yo]);
+  }
+  const int cpr = XF32 ? I / 4 : I / 8;  // 16-byte chunks per row of x
+  const int nxc = T * cpr;
+  const u32x4* x16 = static_cast<const u32x4*>(xv);
+  u32x4 xpre0 = {0u, 0u, 0u, 0u}, xpre1 = {0u, 0u, 0u, 0u};
+  if (tid < nxc) xpre0 = x16[tid];
+  if (tid + kDecThreads < nxc) xpre1 = x16[tid + kDecThreads];
+
+  // ---- routing (every wave, registers only)
+  const bool ok = lane < P && e_l >= 0 && e_l < E;
+  uint64_t peers = __ballot(ok);
+  for (int b = 0; b < nbits; b++) {
+    const bool bit = (e_l >> b) & 1;
+    const uint64_t ones = __ballot(ok && bit);
+    peers &= bit ? ones : ~ones;
+  }
+  const uint64_t firsts = __ballot(ok && (peers & lanes_below(lane)) == 0);
+  const uint64_t valid = __ballot(ok);
+  const int U = __popcll(firsts);
+  // lane u < U describes the u-th distinct expert (in pair order of first use)
+  const int src_u = lane < U ? nth_set_bit(firsts, lane) : 0;
+  const uint64_t pm_u = shfl64(peers, src_u);
+  const int e_u = __shfl(e_l, src_u, kWave);
+  const int n4 = (G + 3) >> 2;
+  const int gs4 = (n4 + S - 1) / S;  // iterations (4 groups each) per k-split
+  const int ncol_u = lane < U ? __popcll(pm_u) * NP : 0;
+  // Usually every expert's (pair, piece) columns fit one chunk of 16, and
+  // item i is simply (expert i / S, split i % S); otherwise a prefix sum of
+  // the per-expert chunk counts maps items to experts.
+  const bool single = __ballot(ncol_u > 16) == 0;
+  int incl = 0, NI = U * S;
+  if (!single) {
+    incl = ((ncol_u + 15) >> 4) * S;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += v;
+    }
+    NI = __builtin_amdgcn_readlane(incl, 63);
+  }
+  struct Item {
+    int e, ks, cc, gbeg, nit;
+    uint64_t pm;
+  };
+  auto item_info = [&](int item) {
+    Item it;
+    int u, rem;
+    if (single) {
+      u = item / S;
+      rem = item - u * S;
+    } else {
+      u = __popcll(__ballot(lane < U && incl <= item));
+      rem = item - (u > 0 ? __builtin_amdgcn_readlane(incl, u - 1) : 0);
+    }
+    it.cc = rem / S;
+    it.ks = rem - it.cc * S;
+    it.e = __builtin_amdgcn_readlane(e_u, u);
+    it.pm = readlane64(pm_u, u);
+    it.gbeg = it.ks * gs4 * 4;
+    it.nit = (min(G, it.gbeg + gs4 * 4) - it.gbeg + 3) >> 2;
+    return it;
+  };
+  const int n_mine = NI > w ? (NI - w + kDecWaves - 1) / kDecWaves : 0;
+  int total = 0;  // iterations of this wave over all its items
+  for (int j = 0; j < n_mine; j++) {
+    const int ks = single ? (w + kDecWaves * j) % S : item_info(w + kDecWaves * j).ks;
+    const int gb = ks * gs4 * 4;
+    total += (min(G, gb + gs4 * 4) - gb + 3) >> 2;
+  }
+
+  // ---- load cursor. Every ring slot issues exactly one 16-byte weight load
+  // and one scale-byte load, always from a valid address (past the end of
+  // the wave's work: the lane's last group again, value discarded), so the
+  // number of loads in flight is static and the waits pipeline.
   const int o = o0 + r;
   const bool row_ok = o < O;
-  for (int u = w; u < U; u += WAVES) {
-    const int e = bk.seg_expert[u], sb = bk.seg_begin[u], n = bk.seg_begin[u + 1] - sb;
-    const uint8_t* prow = packed + ((int64_t)e * O + (row_ok ? o : 0)) * (int64_t)G * 16;
-    const uint8_t* srow = scales + ((int64_t)e * O + (row_ok ? o : 0)) * (int64_t)G;
-    for (int c0 = 0; c0 < n; c0 += 16) {
-      const bool col_ok = c0 + r < n;
-      const int pr = col_ok ? bk.sorted_pair[sb + c0 + r] : 0;
-      const uint16_t* xrow = x + (int64_t)(pr / K) * I;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int g0 = 0; g0 < G; g0 += 4) {
-        const int g = g0 + q;
-        const bool g_ok = g < G;
-        u32x4 wv = {0u, 0u, 0u, 0u};
-        uint32_t s = 127;
-        if (row_ok && g_ok) {
-          wv = *reinterpret_cast<const u32x4*>(prow + (int64_t)g * 16);
-          s = srow[g];
-        }
-        u32x4 xv[4];
+  int l_j = 0, l_it = 0, l_gbeg = 0, l_nit = 0, l_gend = 1;
+  bool l_done = n_mine == 0;
+  const uint8_t* l_prow = packed;
+  const uint8_t* l_srow = scales;
+  auto l_refresh = [&]() {
+    const Item it = item_info(w + kDecWaves * l_j);
+    l_gbeg = it.gbeg;
+    l_nit = it.nit;
+    l_gend = min(G, l_gbeg + 4 * l_nit);
+    const int64_t row = (int64_t)it.e * O + (row_ok ? o : 0);
+    l_prow = packed + row * (int64_t)G * 16;
+    l_srow = scales + row * (int64_t)G;
+  };
+  if (!l_done) l_refresh();
+  u32x4 rw[kRing];
+  uint8_t rs[kRing];  // kept as bytes: widened where used, not where the loop repeats
+  uint32_t rvalid = 0;  // bit s: slot s holds a real group for this lane
+  // The loaded values are used as they are; invalid slots are zeroed only
+  // when consumed, so no instruction waits on a load before then.
+  auto issue_load = [&](int s, u32x4& wv, uint8_t& sv) {
+    const int g = l_gbeg + 4 * l_it + q;
+    const bool okl = !l_done && row_ok && g < l_gend;
+    // past the end of the item: re-read one of its groups (cached)
+    const int gc = min(g, l_gend - 1);
+    wv = *reinterpret_cast<const u32x4*>(l_prow + gc * 16);
+    sv = l_srow[gc];
+    rvalid = okl ? (rvalid | (1u << s)) : (rvalid & ~(1u << s));
+    if (!l_done && ++l_it == l_nit) {
+      l_it = 0;
+      if (++l_j < n_mine) l_refresh();
+      else l_done = true;
+    }
+  };
 #pragma unroll
-        for (int j = 0; j < 4; j++) xv[j] = u32x4{0u, 0u, 0u, 0u};
-        if (col_ok && g_ok) {
-          const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + 32 * (int64_t)g);
+  for (int s = 0; s < kRing; s++) issue_load(s, rw[s], rs[s]);
+
+  // ---- x -> LDS (fp32: three bf16 pieces per value), p -> LDS
+  auto stage_chunk = [&](int idx, u32x4 v) {
+    const int t = idx / cpr, c = idx - t * cpr;
+    if constexpr (XF32) {
+      uint32_t a0, a1, a2, b0, b1, b2, c0, c1, c2, d0, d1, d2;
+      split3(__uint_as_float(v[0]), a0, a1, a2);
+      split3(__uint_as_float(v[1]), b0, b1, b2);
+      split3(__uint_as_float(v[2]), c0, c1, c2);
+      split3(__uint_as_float(v[3]), d0, d1, d2);
+      uint16_t* base = xs + (t * NP) * IL + 4 * c;
+      *reinterpret_cast<uint2*>(base) = make_uint2(a0 | (b0 << 16), c0 | (d0 << 16));
+      *reinterpret_cast<uint2*>(base + IL) = make_uint2(a1 | (b1 << 16), c1 | (d1 << 16));
+      *reinterpret_cast<uint2*>(base + 2 * IL) = make_uint2(a2 | (b2 << 16), c2 | (d2 << 16));
+    } else {
+      *reinterpret_cast<u32x4*>(xs + t * IL + 8 * c) = v;
+    }
+  };
+  if (tid < nxc) stage_chunk(tid, xpre0);
+  if (tid + kDecThreads < nxc) stage_chunk(tid + kDecThreads, xpre1);
+  // the rest of x (large activations), 8 chunks per thread in flight at a time
+  for (int base = tid + 2 * kDecThreads; base < nxc; base += 8 * kDecThreads) {
+    u32x4 v[8];
 #pragma unroll
-          for (int j = 0; j < 4; j++) xv[j] = xp[j];
-        }
+    for (int i = 0; i < 8; i++) {
+      const int idx = base + i * kDecThreads;
+      v[i] = x16[idx < nxc ? idx : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (base + i * kDecThreads < nxc) stage_chunk(base + i * kDecThreads, v[i]);
+  }
+  if (tid < P) p_lds[tid] = my_p;
+  __syncthreads();
+
+  // ---- compute cursor
+  int c_j = 0, c_it = 0, c_gbeg = 0, c_nit = 0, c_ks = 0;
+  const uint16_t* bptr = xs;  // this lane's B column (a row of xs)
+  bool col_ok = false;
+  int colidx = 0;
+  auto c_refresh = [&]() {
+    const Item it = item_info(w + kDecWaves * c_j);
+    c_gbeg = it.gbeg;
+    c_nit = it.nit;
+    c_ks = it.ks;
+    const int gc = it.cc * 16 + r;  // column of this lane: (pair, piece)
+    col_ok = gc < __popcll(it.pm) * NP;
+    const int pi = col_ok ? gc / NP : 0;
+    const int pc = col_ok ? gc - pi * NP : 0;
+    const int pair = nth_set_bit(it.pm, pi);
+    colidx = pair * NP + pc;
+    bptr = xs + ((pair / K) * NP + pc) * IL;
+  };
+  if (n_mine > 0) c_refresh();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < total; base += kRing) {
+#pragma unroll
+    for (int s = 0; s < kRing; s++) {
+      // keep each slot's work after the previous slot's: consuming slot s
+      // must wait for slot s's loads only
+      __builtin_amdgcn_sched_barrier(0);
+      if (base + s < total) {
+        // decode the 16-byte group of this lane (row r, group gbeg + 4 it + q);
+        // an invalid slot decodes zero codes, i.e. zeros
+        const bool vs = (rvalid >> s) & 1u;
+        const uint32_t sv = vs ? (uint32_t)rs[s] : 127u;
+        u32x4 wq = rw[s];
+#pragma unroll
+        for (int j = 0; j < 4; j++) wq[j] = vs ? wq[j] : 0u;
         uint32_t wd[4][4];
-        if (__builtin_expect(__ballot(s == 255) != 0, 0)) {
+        const float sc = e8m0_operand(sv < 255 ? sv : 254);
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            if (s == 255) decode8_bf16_slow(wv[j], s, wd[j]);
-            else decode8_bf16_fast(wv[j], e8m0_operand(s), wd[j]);
+        for (int j = 0; j < 4; j++) decode8_bf16_fast(wq[j], sc, wd[j]);
+        if (__builtin_expect(__ballot(sv == 255) != 0, 0)) {
+          if (sv == 255) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) decode8_bf16_s255(wq[j], wd[j]);
           }
-        } else {
-          const float sc = e8m0_operand(s);
-#pragma unroll
-          for (int j = 0; j < 4; j++) decode8_bf16_fast(wv[j], sc, wd[j]);
         }
+        const int gb = min(c_gbeg + 4 * c_it + q, G - 1);  // in bounds; a zero A covers the tail
+        const uint16_t* bp = bptr + 32 * gb;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const u32x4 a = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, xv[j]),
+          const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
+          const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
                                                         acc, 0, 0, 0);
         }
+        if (++c_it == c_nit) {
+          // acc[i] = row 4q + i of the tile, column r of this item
+          if (col_ok) {
+            float* dst = part + ((size_t)c_ks * P * NP + colidx) * kRows + 4 * q;
+            *reinterpret_cast<f32x4*>(dst) = acc;
+          }
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          c_it = 0;
+          if (++c_j < n_mine) c_refresh();
+        }
       }
-      // acc[i] = row 4q + i of the tile, column (pair) lane & 15
-      if (col_ok) {
-        const int pos = sb + c0 + r;
-#pragma unroll
-        for (int i = 0; i < 4; i++) part[pos * R + 4 * q + i] = acc[i];
-      }
+      issue_load(s, rw[s], rs[s]);
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < T * R; idx += WAVES * 64) {
-    const int t = idx / R, rr = idx - t * R, oo = o0 + rr;
+
+  // ---- combine: k-ordered fp32 sum of p * partial, then shared, one rounding
+  for (int idx = tid; idx < T * kRows; idx += kDecThreads) {
+    const int t = idx >> 4, rr = idx & 15, oo = o0 + rr;
     if (oo >= O) continue;
     float a = 0.f;
     for (int k = 0; k < K; k++) {
-      const int sp = bk.slot_of_pair[t * K + k];
-      if (sp >= 0) a = fmaf(p[t * K + k], part[sp * R + rr], a);
+      const int qp = t * K + k;
+      if (!((valid >> qp) & 1ull)) continue;
+      float v = 0.f;
+      for (int ks = 0; ks < S; ks++)
+#pragma unroll
+        for (int pc = 0; pc < NP; pc++) v += part[((size_t)ks * P * NP + qp * NP + pc) * kRows + rr];
+      a = fmaf(p_lds[qp], v, a);
     }
     const int64_t yo = (int64_t)t * O + oo;
-    y[yo] = f32_to_bf16_rne(bf16_to_f32(shared[yo]) + a);
+    float sh;
+    if (idx == tid) sh = sh_first;
+    else sh = XF32 ? static_cast<const float*>(shared)[yo] : bf16_to_f32(static_cast<const uint16_t*>(shared)[yo]);
+    if constexpr (XF32) static_cast<float*>(y)[yo] = sh + a;
+    else static_cast<uint16_t*>(y)[yo] = f32_to_bf16_rne(sh + a);
   }
-  if (blockIdx.x == 0 && tid == 0 && n_invalid) n_invalid[0] = (chunk_index == 0 ? 0 : n_invalid[0]) + bk.n_invalid;
+  if (blockIdx.x == 0 && tid == 0 && n_invalid)
+    n_invalid[0] = (chunk_index == 0 ? 0 : n_invalid[0]) + (P - __popcll(valid));
+}
+
+int bits_for_experts(int E) {
+  int nb = 0;
+  while ((1 << nb) < E) nb++;
+  return nb;
+}
+
+// k-splits: enough work items for the workgroup's waves when few experts
+// are selected, every split non-empty.
+int decode_splits(int T, int K, int E, int G) {
+  const int P = T * K;
+  const int uexp = P < E ? P : E;
+  int S = uexp >= kDecWaves ? 1 : kDecWaves / uexp;
+  const int n4 = (G + 3) / 4;
+  if (S > n4) S = n4;
+  const int per = (n4 + S - 1) / S;
+  return (n4 + per - 1) / per;
+}
+
+size_t decode_lds_bytes(int T, int K, int G, int dtype, int S) {
+  const int NP = dtype == 0 ? 3 : 1;
+  const size_t xs = ((size_t)T * NP * (32 * (size_t)G + 8) * 2 + 15) & ~(size_t)15;
+  return xs + (size_t)S * T * K * NP * kRows * 4;
 }
 
 }  // namespace
 
-hipError_t launch_gemv_f32_fused(const float* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
-                                 const float* p, const float* shared, float* y, int T, int E, int O, int G, int K,
-                                 int32_t* n_invalid, int chunk_index, hipStream_t stream) {
-  constexpr int R = 4;
-  const int nblk = (O + R - 1) / R;
-  hipLaunchKernelGGL(gemv_f32_fused_kernel<R>, dim3(nblk), dim3(256), 0, stream, x, packed, scales, sel, p, shared, y,
-                     T, E, O, G, K, n_invalid, chunk_index);
-  return hipGetLastError();
+int decode_tokens_per_launch(int K, int E, int G, int dtype) {
+  if (K > kMaxFusedPairs) return 0;
+  int tc = kMaxFusedPairs / K;
+  while (tc > 0 && decode_lds_bytes(tc, K, G, dtype, decode_splits(tc, K, E, G)) > (size_t)kDecodeMaxLds) tc--;
+  return tc;
 }
 
-hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
-                                  const float* p, const uint16_t* shared, uint16_t* y, int T, int E, int O, int G, int K,
-                                  int32_t* n_invalid, int chunk_index, hipStream_t stream) {
-  constexpr int WAVES = 8;
-  const int nblk = (O + 15) / 16;
-  hipLaunchKernelGGL(gemv_bf16_fused_kernel<WAVES>, dim3(nblk), dim3(WAVES * 64), 0, stream, x, packed, scales, sel, p,
-                     shared, y, T, E, O, G, K, n_invalid, chunk_index);
+hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                               const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
+                               int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream) {
+  if (T * K > kMaxFusedPairs) return hipErrorInvalidValue;
+  const int S = decode_splits(T, K, E, G);
+  const size_t lds = decode_lds_bytes(T, K, G, dtype, S);
+  if (lds > (size_t)kDecodeMaxLds) return hipErrorInvalidValue;
+  const int nb = bits_for_experts(E);
+  const dim3 grid((O + kRows - 1) / kRows);
+  if (dtype == 0) {
+    static bool attr = false;  // large LDS needs the opt-in once per kernel
+    if (!attr) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
+      attr = true;
+    }
+    hipLaunchKernelGGL(decode_fused_kernel<true>, grid, dim3(kDecThreads), lds, stream, x, packed, scales, sel, p,
+                       shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
+  } else {
+    static bool attr = false;
+    if (!attr) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
+      attr = true;
+    }
+    hipLaunchKernelGGL(decode_fused_kernel<false>, grid, dim3(kDecThreads), lds, stream, x, packed, scales, sel, p,
+                       shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
+  }
   return hipGetLastError();
 }
 

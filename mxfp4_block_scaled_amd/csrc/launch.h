@@ -8,9 +8,11 @@
 
 namespace mxfp4 {
 
-// Largest number of pairs (T*K) one fused decode-shaped launch handles: the
-// in-workgroup bucketing and the per-pair partial rows live in LDS.
-constexpr int kMaxFusedPairs = 512;
+// Largest number of pairs (T*K) one fused decode-shaped launch handles
+// (one per lane of a wave).
+constexpr int kMaxFusedPairs = 64;
+// LDS one decode-shaped workgroup may use (activations + partial rows).
+constexpr int kDecodeMaxLds = 156 * 1024;
 
 // Grouped-GEMM tile sizes (pairs x output features) and the bucketing chunk.
 constexpr int kGemmTileM = 128;
@@ -55,17 +57,15 @@ hipError_t launch_bucket_multi(const int32_t* sel, int P, int E, int32_t* bcount
                                hipStream_t stream);
 hipError_t launch_bucket_one_block(const int32_t* sel, int P, int E, BucketOut out, hipStream_t stream);
 
-// ---- decode-shaped fused path: bucketing in LDS + dequant-GEMV + combine.
-// n_invalid (may be null) receives the number of out-of-range indices,
-// accumulated over successive chunk launches (chunk_index 0 starts at zero).
-hipError_t launch_gemv_f32_fused(const float* x, const uint8_t* packed, const uint8_t* scales,
-                                 const int32_t* sel, const float* p, const float* shared, float* y,
-                                 int T, int E, int O, int G, int K, int32_t* n_invalid,
-                                 int chunk_index, hipStream_t stream);
-hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
-                                  const int32_t* sel, const float* p, const uint16_t* shared,
-                                  uint16_t* y, int T, int E, int O, int G, int K, int32_t* n_invalid,
-                                  int chunk_index, hipStream_t stream);
+// ---- decode-shaped fused path: routing, dequant-GEMV and combine.
+// dtype 0 = fp32 x/shared/y, 1 = bf16. n_invalid (may be null) receives the
+// number of out-of-range indices, accumulated over successive chunk launches
+// (chunk_index 0 starts at zero).
+hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                               const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
+                               int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream);
+// Most tokens one decode-shaped launch takes for these sizes (0: none fits).
+int decode_tokens_per_launch(int K, int E, int G, int dtype);
 
 // ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,

@@ -342,9 +342,13 @@ def test_invariants(dtype, flags):
         pk2[e] = rng.integers(0, 256, pk2[e].shape)
         sc2[e] = 255
     assert torch.equal(run(upload(x, pk2, sc2, sel, p, zero, dtype), flags=flags), y)
-    # b ^ 0x88 flips every sign: the routed part is negated exactly
+    # b ^ 0x88 flips every sign: the routed part is negated. Within the
+    # tolerance bar, not bit for bit: the MFMA's fp32 accumulation is not
+    # correctly rounded and not sign-symmetric in the last bit (measured on
+    # MI355X: 183 of 51,200 outputs of v_mfma_f32_16x16x32_bf16 differ when
+    # A is negated)
     yn = run(upload(x, packed ^ np.uint8(0x88), scales, sel, p, zero, dtype), flags=flags)
-    assert torch.equal(yn, -y)
+    assert_close(host64(yn), -host64(y), dtype, "sign flip")
     # every scale + 1 doubles the routed part exactly
     y2 = run(upload(x, packed, scales + np.uint8(1), sel, p, zero, dtype), flags=flags)
     assert torch.equal(y2, 2 * y)
