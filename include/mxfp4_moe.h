@@ -86,6 +86,8 @@ typedef enum mxfp4_dtype {
 #define MXFP4_FLAG_FORCE_GEMV 0x1u /* decode-shaped path (dequant-GEMV, fused combine) */
 #define MXFP4_FLAG_FORCE_GEMM 0x2u /* prefill-shaped path (bucketing, MFMA grouped GEMM, combine) */
 #define MXFP4_FLAG_CHECK 0x4u      /* synchronise `stream` and report out-of-range indices */
+#define MXFP4_FLAG_GEMV_MFMA 0x8u  /* decode-shaped path on the MFMA kernel (16-row tiles) instead of
+                                      the row-contiguous vector-ALU kernel */
 /* Flags of mxfp4_moe_bucket. */
 #define MXFP4_FLAG_BUCKET_ONE_BLOCK 0x10u  /* one workgroup does histogram, scan and scatter */
 #define MXFP4_FLAG_BUCKET_MULTI_BLOCK 0x20u /* per-chunk histograms, a scan, per-chunk scatter */

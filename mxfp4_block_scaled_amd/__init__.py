@@ -19,7 +19,7 @@ import torch
 
 from . import _abi
 from ._abi import (  # noqa: F401
-    DTYPE_BF16, DTYPE_F32, FLAG_CHECK, FLAG_FORCE_GEMM, FLAG_FORCE_GEMV, FLAG_BUCKET_MULTI_BLOCK,
+    DTYPE_BF16, DTYPE_F32, FLAG_CHECK, FLAG_FORCE_GEMM, FLAG_FORCE_GEMV, FLAG_GEMV_MFMA, FLAG_BUCKET_MULTI_BLOCK,
     FLAG_BUCKET_ONE_BLOCK, PATH_GEMM, PATH_GEMV, Mxfp4Error, bucket_workspace_size, select_path,
     status_string, workspace_size,
 )

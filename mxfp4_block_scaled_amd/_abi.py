@@ -26,6 +26,7 @@ DTYPE_BF16 = 1
 FLAG_FORCE_GEMV = 0x1
 FLAG_FORCE_GEMM = 0x2
 FLAG_CHECK = 0x4
+FLAG_GEMV_MFMA = 0x8
 FLAG_BUCKET_ONE_BLOCK = 0x10
 FLAG_BUCKET_MULTI_BLOCK = 0x20
 

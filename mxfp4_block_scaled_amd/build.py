@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmxfp4_moe.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-HIP_SOURCES = ["bucket.hip", "gemv.hip", "gemm.hip", "combine.hip"]
+HIP_SOURCES = ["bucket.hip", "gemv.hip", "gemv_rows.hip", "gemm.hip", "combine.hip"]
 HOST_SOURCES = ["api.cpp"]
 ARCH = "gfx950"
 
@@ -55,7 +55,9 @@ def _resource_problems(remarks: str) -> list:
         if m:
             name = m.group(1)
             continue
-        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
+        # SGPR spills land in VGPR lanes (no memory) unless scratch is used,
+        # which the scratch size shows
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)", line)
         if m and int(m.group(2)) != 0:
             bad.append(f"{name}: {m.group(1)} = {m.group(2)}")
     return bad
@@ -78,7 +80,7 @@ def _compile(src: str, verbose: bool) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{out}")
     # every kernel must keep its state in registers and LDS: scratch memory
-    # (private arrays or spills) costs a slow memory round trip per access
+    # (private arrays or VGPR spills) costs a slow memory round trip per access
     bad = _resource_problems(text)
     if bad:
         raise RuntimeError(f"{src}: kernels use scratch memory or spill:\n  " + "\n  ".join(bad))

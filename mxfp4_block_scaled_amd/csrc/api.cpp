@@ -53,12 +53,23 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Decode-shaped kernel: the row-contiguous one unless the MFMA one is asked
+// for or the rows kernel's 32-bit buffer offsets cannot address an expert.
+bool use_rows_kernel(const Dims& d, uint32_t flags) {
+  return !(flags & MXFP4_FLAG_GEMV_MFMA) && gemv_rows_supported((int)d.O, (int)d.G);
+}
+
+int64_t gemv_tokens_per_launch(const Dims& d, int dtype, uint32_t flags) {
+  return use_rows_kernel(d, flags) ? gemv_rows_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype)
+                                   : decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype);
+}
+
 int select_path(const Dims& d, int dtype, uint32_t flags) {
   if (dtype_size(dtype) == 0) return MXFP4_ERR_INVALID_ARG;
   const bool fv = flags & MXFP4_FLAG_FORCE_GEMV, fm = flags & MXFP4_FLAG_FORCE_GEMM;
   if (fv && fm) return MXFP4_ERR_INVALID_ARG;
-  // the decode-shaped kernel needs one token's activations and partial rows in LDS
-  const bool gemv_ok = decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype) >= 1;
+  // the decode-shaped kernels need one token's activations and partial rows in LDS
+  const bool gemv_ok = gemv_tokens_per_launch(d, dtype, flags) >= 1;
   if (dtype == MXFP4_DTYPE_F32) {
     if (fm || !gemv_ok) return MXFP4_ERR_UNSUPPORTED;  // the MFMA grouped GEMM is bf16-only
     return MXFP4_PATH_GEMV;
@@ -157,15 +168,16 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
   const int es = dtype_size(dtype);
   if (path == MXFP4_PATH_GEMV) {
     // token chunks whose pairs and activations fit one fused launch
-    const int64_t tc = decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype);
+    const int64_t tc = gemv_tokens_per_launch(d, dtype, flags);
     if (tc < 1) return MXFP4_ERR_UNSUPPORTED;
+    const auto launch = use_rows_kernel(d, flags) ? launch_gemv_rows : launch_decode_fused;
     int chunk = 0;
     for (int64_t t0 = 0; t0 < d.T && err == hipSuccess; t0 += tc, chunk++) {
       const int64_t tn = (d.T - t0 < tc) ? d.T - t0 : tc;
-      err = launch_decode_fused(static_cast<const char*>(x) + t0 * d.I * es, packed, scales, sel + t0 * d.K,
-                                p + t0 * d.K, static_cast<const char*>(shared) + t0 * d.O * es,
-                                static_cast<char*>(y) + t0 * d.O * es, (int)tn, (int)d.E, (int)d.O, (int)d.G,
-                                (int)d.K, dtype, n_invalid, chunk, stream);
+      err = launch(static_cast<const char*>(x) + t0 * d.I * es, packed, scales, sel + t0 * d.K,
+                   p + t0 * d.K, static_cast<const char*>(shared) + t0 * d.O * es,
+                   static_cast<char*>(y) + t0 * d.O * es, (int)tn, (int)d.E, (int)d.O, (int)d.G, (int)d.K, dtype,
+                   n_invalid, chunk, stream);
     }
   } else {
     BucketOut b;
@@ -256,7 +268,8 @@ int mxfp4_moe_linear_ex(const void* x, const uint8_t* packed, const uint8_t* sca
   Dims d;
   int st = check_dims(T, E, O, G, K, &d);
   if (st != MXFP4_OK) return st;
-  if (flags & ~(MXFP4_FLAG_FORCE_GEMV | MXFP4_FLAG_FORCE_GEMM | MXFP4_FLAG_CHECK)) return MXFP4_ERR_INVALID_ARG;
+  if (flags & ~(MXFP4_FLAG_FORCE_GEMV | MXFP4_FLAG_FORCE_GEMM | MXFP4_FLAG_CHECK | MXFP4_FLAG_GEMV_MFMA))
+    return MXFP4_ERR_INVALID_ARG;
   st = check_linear_args(x, packed, scales, sel, p, shared, y, d, dtype);
   if (st != MXFP4_OK) return st;
   const int path = select_path(d, dtype, flags);

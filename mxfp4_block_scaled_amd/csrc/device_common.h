@@ -26,6 +26,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -59,6 +60,18 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t w, float scale_opera
   else
     asm("v_cvt_scalef32_pk_bf16_fp4 %0, %1, %2 op_sel:[1,1,0]" : "=v"(r) : "v"(w), "v"(scale_operand));
   return r;
+}
+
+// c + a.lo * b.lo + a.hi * b.hi for two bf16 pairs, fp32 accumulate
+// (v_dot2c_f32_bf16). The operands go through memcpy: with this compiler a
+// bit cast of the 32-bit elements of a vector makes the builtin reuse one
+// element for all of them. (Not inline assembly: the compiler must see the
+// instruction to add the wait states its result needs.)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  bf16x2 av, bv;
+  __builtin_memcpy(&av, &a, 4);
+  __builtin_memcpy(&bv, &b, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(av, bv, c, false);
 }
 
 // Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).

@@ -33,6 +33,7 @@
 // columns of an MFMA fall in different banks).
 #include "device_common.h"
 #include "launch.h"
+#include "wave_routing.h"
 
 namespace mxfp4 {
 namespace {
@@ -41,36 +42,6 @@ constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kRing = 8;   // iterations whose loads a wave keeps in flight
 constexpr int kRows = 16;  // output rows per workgroup (one MFMA tile)
-
-__device__ __forceinline__ uint64_t lanes_below(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
-
-// Position of the n-th set bit of m (m has more than n set bits), by a
-// branch-free binary search on popcounts.
-__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
-  int pos = 0;
-#pragma unroll
-  for (int width = 32; width >= 1; width >>= 1) {
-    const uint64_t low = m & ((width == 64 ? 0ull : (1ull << width)) - 1ull);
-    const int c = __popcll(low);
-    const bool up = n >= c;
-    n -= up ? c : 0;
-    pos += up ? width : 0;
-    m = up ? (m >> width) : low;
-  }
-  return pos;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int src) {
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, src);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
-  const uint32_t lo = __shfl((uint32_t)v, src, kWave);
-  const uint32_t hi = __shfl((uint32_t)(v >> 32), src, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
 
 // fp32 -> three bf16 (bit patterns) with f = x0 + x1 + x2 exactly: each
 // piece keeps the top 8 significant bits of what is left, and the
@@ -121,20 +92,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
   if (tid + kDecThreads < nxc) xpre1 = x16[tid + kDecThreads];
 
   // ---- routing (every wave, registers only)
-  const bool ok = lane < P && e_l >= 0 && e_l < E;
-  uint64_t peers = __ballot(ok);
-  for (int b = 0; b < nbits; b++) {
-    const bool bit = (e_l >> b) & 1;
-    const uint64_t ones = __ballot(ok && bit);
-    peers &= bit ? ones : ~ones;
-  }
-  const uint64_t firsts = __ballot(ok && (peers & lanes_below(lane)) == 0);
-  const uint64_t valid = __ballot(ok);
-  const int U = __popcll(firsts);
-  // lane u < U describes the u-th distinct expert (in pair order of first use)
-  const int src_u = lane < U ? nth_set_bit(firsts, lane) : 0;
-  const uint64_t pm_u = shfl64(peers, src_u);
-  const int e_u = __shfl(e_l, src_u, kWave);
+  const WaveRoute rt = route_wave(e_l, lane, P, E, nbits);
+  const uint64_t valid = rt.valid, pm_u = rt.pm_u;
+  const int U = rt.U, e_u = rt.e_u;
   const int n4 = (G + 3) >> 2;
   const int gs4 = (n4 + S - 1) / S;  // iterations (4 groups each) per k-split
   const int ncol_u = lane < U ? __popcll(pm_u) * NP : 0;
@@ -277,7 +237,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     bptr = xs + ((pair / K) * NP + pc) * IL;
   };
   if (n_mine > 0) c_refresh();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_hi = {0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < total; base += kRing) {
 #pragma unroll
     for (int s = 0; s < kRing; s++) {
@@ -293,26 +253,40 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
 #pragma unroll
         for (int j = 0; j < 4; j++) wq[j] = vs ? wq[j] : 0u;
         uint32_t wd[4][4];
-        const float sc = e8m0_operand(sv < 255 ? sv : 254);
+        // scale bytes >= 253 can make E2M1 * 2^(s-127) overflow bf16: such a
+        // lane's group is decoded at 2^(s-135) into a second accumulator,
+        // multiplied by 2^8 when the item ends (exact)
+        const bool hi = sv >= 253u;
+        const float sc = e8m0_operand(hi ? sv - 8u : sv);
 #pragma unroll
         for (int j = 0; j < 4; j++) decode8_bf16_fast(wq[j], sc, wd[j]);
-        if (__builtin_expect(__ballot(sv == 255) != 0, 0)) {
-          if (sv == 255) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) decode8_bf16_s255(wq[j], wd[j]);
-          }
-        }
         const int gb = min(c_gbeg + 4 * c_it + q, G - 1);  // in bounds; a zero A covers the tail
         const uint16_t* bp = bptr + 32 * gb;
+        if (__builtin_expect(__ballot(hi) == 0, 1)) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
-          const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
-                                                        acc, 0, 0, 0);
+          for (int j = 0; j < 4; j++) {
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
+            const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
+            const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi ? z : av),
+                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi ? av : z),
+                                                             __builtin_bit_cast(bf16x8, bv), acc_hi, 0, 0, 0);
+          }
         }
         if (++c_it == c_nit) {
           // acc[i] = row 4q + i of the tile, column r of this item
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[i] = fmaf(256.f, acc_hi[i], acc[i]);
+          acc_hi = f32x4{0.f, 0.f, 0.f, 0.f};
           if (col_ok) {
             float* dst = part + ((size_t)c_ks * P * NP + colidx) * kRows + 4 * q;
             *reinterpret_cast<f32x4*>(dst) = acc;

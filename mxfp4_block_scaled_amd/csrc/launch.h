@@ -67,6 +67,14 @@ hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8
 // Most tokens one decode-shaped launch takes for these sizes (0: none fits).
 int decode_tokens_per_launch(int K, int E, int G, int dtype);
 
+// Row-contiguous decode-shaped kernel (vector ALUs, buffer loads): same
+// contract as launch_decode_fused; needs O * G * 16 < 2^31.
+bool gemv_rows_supported(int O, int G);
+int gemv_rows_tokens_per_launch(int K, int E, int G, int dtype);
+hipError_t launch_gemv_rows(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                            const float* p, const void* shared, void* y, int T, int E, int O, int G, int K, int dtype,
+                            int32_t* n_invalid, int chunk_index, hipStream_t stream);
+
 // ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
                             const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,

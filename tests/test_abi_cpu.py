@@ -41,6 +41,7 @@ def test_header_constants_match_binding():
     assert int(consts["MXFP4_FLAG_FORCE_GEMV"].rstrip("u"), 16) == _abi.FLAG_FORCE_GEMV
     assert int(consts["MXFP4_FLAG_FORCE_GEMM"].rstrip("u"), 16) == _abi.FLAG_FORCE_GEMM
     assert int(consts["MXFP4_FLAG_CHECK"].rstrip("u"), 16) == _abi.FLAG_CHECK
+    assert int(consts["MXFP4_FLAG_GEMV_MFMA"].rstrip("u"), 16) == _abi.FLAG_GEMV_MFMA
     assert int(consts["MXFP4_MAX_EXPERTS"]) == _abi.MAX_EXPERTS
     for name, val in re.findall(r"(MXFP4_(?:OK|ERR_\w+)) = (-?\d+)", text):
         assert getattr(_abi, name[len("MXFP4_"):]) == int(val)

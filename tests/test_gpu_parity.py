@@ -227,18 +227,23 @@ def _sample_rows(O, n, seed):
     return np.array(sorted(rows))
 
 
+# decode-shaped kernels: row-contiguous (default) and 16-row MFMA tiles
+GEMV_KERNELS = [0, _abi.FLAG_GEMV_MFMA]
+
+
+@pytest.mark.parametrize("kernel", GEMV_KERNELS)
 @pytest.mark.parametrize("name", ["tiny", "decode"])
-def test_small_workloads_full_oracle(name):
+def test_small_workloads_full_oracle(name, kernel):
     inp, d = _workload_dev(name)
-    say(f"workload {name} full oracle")
+    say(f"workload {name} full oracle kernel={kernel}")
     ref = oracle.expert_linear(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared)
-    y = run(d)
+    y = run(d, flags=kernel)
     assert y.dtype == torch.float32 and tuple(y.shape) == ref.shape
     assert_fp32_close(host64(y), ref, name)
     # second routing draw on the same weights
     sel2, p2 = inp.routing_sets[1]
     ref2 = oracle.expert_linear(inp.x, inp.packed, inp.scales, sel2, p2, inp.shared)
-    y2 = run(d, sel=torch.from_numpy(sel2).to(DEV), p=torch.from_numpy(p2).to(DEV))
+    y2 = run(d, sel=torch.from_numpy(sel2).to(DEV), p=torch.from_numpy(p2).to(DEV), flags=kernel)
     assert_fp32_close(host64(y2), ref2, name + " routing set 1")
 
 
@@ -259,7 +264,7 @@ def test_decode8_both_paths():
     inp, d = _workload_dev("decode8")
     rows = _sample_rows(inp.workload.O, 96, 8)
     ref = oracle.expert_linear_rows(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
-    for flags in (_abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMM):
+    for flags in (_abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMV | _abi.FLAG_GEMV_MFMA, _abi.FLAG_FORCE_GEMM):
         say(f"decode8 flags={flags}")
         y = host64(run(d, flags=flags))
         assert_bf16_close(y[:, rows], ref, f"decode8 flags={flags}")
@@ -276,7 +281,7 @@ def test_threshold_sweep(T):
     assert mx.select_path(T, E, O, G, 4, _abi.DTYPE_BF16) == want_path
     ref = oracle.expert_linear(*case)
     results = {}
-    for flags in (0, _abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMM):
+    for flags in (0, _abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMV | _abi.FLAG_GEMV_MFMA, _abi.FLAG_FORCE_GEMM):
         y = host64(run(d, flags=flags))
         assert_bf16_close(y, ref, f"T={T} flags={flags}")
         results[flags] = y
@@ -304,18 +309,40 @@ def test_edge_shapes(case, dtype):
     host = random_case(sum(case[:5]), T, E, K, G, O, dtype, distinct=distinct)
     d = upload(*host, dtype)
     ref = oracle.expert_linear(*host)
-    flag_sets = [0] if dtype == "fp32" else [0, _abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMM]
+    mf = _abi.FLAG_GEMV_MFMA
+    flag_sets = [0, mf] if dtype == "fp32" else [0, _abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMV | mf,
+                                                _abi.FLAG_FORCE_GEMM]
     for flags in flag_sets:
         y = run(d, flags=flags)
         assert y.dtype == _tdtype(dtype)
         assert_close(host64(y), ref, dtype, f"{case} flags={flags}")
 
 
-def test_fp32_many_tokens_uses_chunked_fused_launches():
-    # P > 512 pairs per launch: the fp32 path splits tokens into chunks
+@pytest.mark.parametrize("kernel", GEMV_KERNELS)
+def test_fp32_many_tokens_uses_chunked_fused_launches(kernel):
+    # more pairs than one fused launch takes: the fp32 path splits tokens into chunks
     host = random_case(5, 300, 16, 3, 2, 40, "fp32")
     d = upload(*host, "fp32")
-    assert_fp32_close(host64(run(d)), oracle.expert_linear(*host), "fp32 T=300")
+    assert_fp32_close(host64(run(d, flags=kernel)), oracle.expert_linear(*host), "fp32 T=300")
+
+
+@pytest.mark.parametrize("dtype,flags", [("fp32", 0), ("fp32", _abi.FLAG_GEMV_MFMA), ("bf16", _abi.FLAG_FORCE_GEMV),
+                                         ("bf16", _abi.FLAG_FORCE_GEMV | _abi.FLAG_GEMV_MFMA)])
+def test_largest_scales_against_oracle(dtype, flags):
+    # scale bytes 253..255 (2^126..2^128): E2M1 * 2^(s-127) overflows fp32
+    # and bf16 for the larger codes, the layer's result does not; tiny
+    # activations keep every output finite, so the exact (float64) result is
+    # the reference
+    T, E, K, G, O = 3, 4, 2, 5, 40
+    x, packed, scales, sel, p, shared = random_case(55, T, E, K, G, O, dtype)
+    x = (x * np.float32(2.0 ** -100)).astype(np.float32)
+    if dtype == "bf16":
+        x = workloads.round_to_bf16(x)
+    scales = np.broadcast_to((255 - np.arange(G) % 3).astype(np.uint8), scales.shape).copy()
+    d = upload(x, packed, scales, sel, p, shared, dtype)
+    ref = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    assert np.all(np.isfinite(ref)) and np.abs(ref).max() > 1e6
+    assert_close(host64(run(d, flags=flags)), ref, dtype, f"scales 253..255 {dtype} flags={flags}")
 
 
 def test_empty_batch():
@@ -326,7 +353,9 @@ def test_empty_batch():
 
 # ------------------------------------------------------------------ invariants
 
-@pytest.mark.parametrize("dtype,flags", [("fp32", 0), ("bf16", _abi.FLAG_FORCE_GEMV), ("bf16", _abi.FLAG_FORCE_GEMM)])
+@pytest.mark.parametrize("dtype,flags", [("fp32", 0), ("fp32", _abi.FLAG_GEMV_MFMA), ("bf16", _abi.FLAG_FORCE_GEMV),
+                                         ("bf16", _abi.FLAG_FORCE_GEMV | _abi.FLAG_GEMV_MFMA),
+                                         ("bf16", _abi.FLAG_FORCE_GEMM)])
 def test_invariants(dtype, flags):
     T, E, K, G, O = 6, 12, 3, 6, 200
     x, packed, scales, sel, p, shared = random_case(77, T, E, K, G, O, dtype)
