@@ -39,22 +39,34 @@
 namespace mxfp4 {
 namespace {
 
-constexpr int kRing = 4;  // slots whose loads a wave keeps in flight
+constexpr int kRing = 2;  // slots whose loads a wave keeps in flight
 constexpr int kRpl = 2;   // weight rows per lane in a slot
-constexpr int kTmax = 8;  // pairs per work item
+constexpr int kTmax = 2;  // pairs per work item (an expert with more pairs gets more items)
 constexpr int kXPre = 4;   // 16-byte chunks of x per thread loaded with the routing input
-constexpr int kOob = (int)0x80000000u;  // buffer offset beyond any resource: loads return zero
+// group offset beyond any expert's resource (O * G < 2^27): loads return zero
+constexpr uint32_t kOobGroup = 0x08000000u;
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+// n / d for 0 <= n < 2^24, d > 0: float estimate, then exact correction.
+__device__ __forceinline__ int div_small(int n, int d) {
+  int t = (int)((float)n * __builtin_amdgcn_rcpf((float)d));
+  while (t > 0 && t * d > n) t--;
+  while ((t + 1) * d <= n) t++;
+  return t;
+}
 
 template <bool XF32, int L, int NW>
 __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const int32_t* __restrict__ sel, const float* __restrict__ p, const void* shared, void* y, int T, int E, int O,
-    int G, int K, int R, int S, int gs, int nbits, int32_t* __restrict__ n_invalid, int chunk_index) {
+    int G, int K, int S, int gs, int nbits, int32_t* __restrict__ n_invalid, int chunk_index) {
   constexpr int RI = 64 / L;        // rows per wave-wide load
   constexpr int RW = RI * kRpl;     // rows per work item
+  constexpr int R = 2 * NW;         // rows per workgroup
+  constexpr int NRG = R / RW;       // row groups per workgroup (a power of two)
   constexpr int CH = XF32 ? 8 : 4;  // 16-byte activation chunks per group
   constexpr int kThreads = NW * 64, kWaves = NW;
+  static_assert(NRG >= 1 && (NRG & (NRG - 1)) == 0, "row groups");
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   __shared__ float p_lds[kMaxFusedPairs];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -62,7 +74,6 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
   const int j = lane % L, h = lane / L;  // group within the team's L, row team
   const int P = T * K, GP = G + 1;       // GP: group columns in LDS (last one zero)
   const int o0 = blockIdx.x * R;
-  const int NRG = R / RW;
   uint8_t* xs = dyn;  // [T][CH][GP] chunks of 16 bytes
   float* part = reinterpret_cast<float*>(dyn + (size_t)T * CH * GP * 16);  // [S][P][R]
 
@@ -76,7 +87,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
     const int64_t yo = (int64_t)t_first * O + o0 + rr_first;
     sh_first = XF32 ? static_cast<const float*>(shared)[yo] : bf16_to_f32(static_cast<const uint16_t*>(shared)[yo]);
   }
-  const int nxc = T * G * CH;  // 16-byte chunks of x
+  const int rowc = G * CH, nxc = T * rowc;  // 16-byte chunks of x per token, in all
   const u32x4* x16 = static_cast<const u32x4*>(xv);
   u32x4 xpre[kXPre];
 #pragma unroll
@@ -87,41 +98,53 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
 
   // ---- routing (every wave, registers only)
   const WaveRoute rt = route_wave(e_l, lane, P, E, nbits);
+  const int t_of_pair = div_small(lane, K);  // lane i: token of pair i
   const int U = rt.U;
-  const int per_batch = S * NRG;  // items per (expert, pair batch)
+  // Items are numbered i = q * per_batch + (ks * NRG + rg), q indexing the
+  // (expert, pair batch) pairs in expert order. Usually no expert has more
+  // than kTmax pairs and q is the expert; otherwise a prefix sum of the
+  // per-expert batch counts maps q to its expert. A wave takes items
+  // w, w + NW, ...; its cursors step through them without divisions.
+  const int per_batch = S * NRG;
   const int ntok_u = lane < U ? __popcll(rt.pm_u) : 0;
-  // Usually no expert has more than kTmax pairs and item i is simply
-  // (expert i / per_batch, ...); otherwise a prefix sum of the per-expert
-  // batch counts maps items to experts.
   const bool single = __ballot(ntok_u > kTmax) == 0;
-  int incl = 0, NI = U * per_batch;
+  int inclb = 0, NQ = U;
   if (!single) {
-    incl = ((ntok_u + kTmax - 1) / kTmax) * per_batch;
+    inclb = (ntok_u + kTmax - 1) / kTmax;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
+      const int v = __shfl_up(inclb, d, 64);
+      if (lane >= d) inclb += v;
     }
-    NI = __builtin_amdgcn_readlane(incl, 63);
+    NQ = __builtin_amdgcn_readlane(inclb, 63);
   }
+  const int NI = NQ * per_batch;
+  struct Cursor {
+    int q, within;  // (expert, batch) index and position inside it
+  };
+  auto first_item = [&]() {
+    Cursor c{0, w};
+    while (c.within >= per_batch) c.within -= per_batch, c.q++;
+    return c;
+  };
+  auto next_item = [&](Cursor& c) {
+    c.within += kWaves;
+    while (c.within >= per_batch) c.within -= per_batch, c.q++;
+  };
   struct Item {
     int e, b, ks, rg, gbeg, gend, nm;
     uint64_t pm;
   };
-  auto item_info = [&](int item) {
+  auto item_info = [&](const Cursor& c) {
     Item it;
-    int u, rem;
-    if (single) {
-      u = item / per_batch;
-      rem = item - u * per_batch;
-    } else {
-      u = __popcll(__ballot(lane < U && incl <= item));
-      rem = item - (u > 0 ? __builtin_amdgcn_readlane(incl, u - 1) : 0);
+    int u = c.q;
+    it.b = 0;
+    if (!single) {
+      u = __popcll(__ballot(lane < U && inclb <= c.q));
+      it.b = c.q - (u > 0 ? __builtin_amdgcn_readlane(inclb, u - 1) : 0);
     }
-    it.b = rem / per_batch;
-    rem -= it.b * per_batch;
-    it.ks = rem / NRG;
-    it.rg = rem - it.ks * NRG;
+    it.ks = c.within / NRG;
+    it.rg = c.within % NRG;
     it.e = __builtin_amdgcn_readlane(rt.e_u, u);
     it.pm = readlane64(rt.pm_u, u);
     it.gbeg = it.ks * gs;
@@ -131,51 +154,53 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
   };
   const int n_mine = NI > w ? (NI - w + kWaves - 1) / kWaves : 0;
   int total = 0;  // slots of this wave over all its items
-  for (int jj = 0; jj < n_mine; jj++) {
-    int ks;
-    if (single) {
-      const int rem = (w + kWaves * jj) % per_batch;
-      ks = rem / NRG;
-    } else {
-      ks = item_info(w + kWaves * jj).ks;
+  {
+    Cursor c = first_item();
+    for (int jj = 0; jj < n_mine; jj++, next_item(c)) {
+      const int gb = (c.within / NRG) * gs;
+      total += (min(G, gb + gs) - gb + L - 1) / L;
     }
-    const int gb = ks * gs;
-    total += (min(G, gb + gs) - gb + L - 1) / L;
   }
 
   // ---- load cursor: every slot issues kRpl 16-byte weight loads and kRpl
-  // scale-byte loads; lanes with nothing to load read beyond the resource.
+  // scale-byte loads, at per-row offsets fixed when the item starts. A row
+  // past the end of the matrix reads beyond the expert's buffer resource
+  // (zeros, no memory traffic); a lane past the end of its k-split reads
+  // whatever group follows, which adds nothing: its activations are the
+  // zero column.
   const int nrec_w = O * G * 16, nrec_s = O * G;
-  int l_j = 0, l_m = 0, l_nm = 1, l_gbeg = 0, l_gend = 0, l_rg = 0;
+  int l_j = 0, l_m = 0, l_nm = 1;
   bool l_done = n_mine == 0;
+  Cursor l_cur = first_item();
   const uint8_t* l_wb = packed;
   const uint8_t* l_sb = scales;
+  uint32_t l_off[kRpl];  // this lane's first group (row-major in the expert), per row
   auto l_refresh = [&]() {
-    const Item it = item_info(w + kWaves * l_j);
-    l_gbeg = it.gbeg;
-    l_gend = it.gend;
+    const Item it = item_info(l_cur);
     l_nm = it.nm;
-    l_rg = it.rg;
     l_wb = packed + (int64_t)it.e * nrec_w;
     l_sb = scales + (int64_t)it.e * nrec_s;
+#pragma unroll
+    for (int i = 0; i < kRpl; i++) {
+      const int o = o0 + it.rg * RW + i * RI + h;
+      l_off[i] = o < O ? (uint32_t)(o * G + it.gbeg + j) : kOobGroup;
+    }
   };
   if (!l_done) l_refresh();
   u32x4 rw[kRing][kRpl];
   uint8_t rs[kRing][kRpl];
   auto issue_load = [&](int s) {
-    const int g = l_gbeg + j + L * l_m;
     const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc((void*)l_wb, (short)0, nrec_w, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)l_sb, (short)0, nrec_s, kRsrcFlags);
 #pragma unroll
     for (int i = 0; i < kRpl; i++) {
-      const int o = o0 + l_rg * RW + i * RI + h;
-      const bool ok = !l_done && o < O && g < l_gend;
-      const int idx = o * G + g;
-      rw[s][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, ok ? idx * 16 : kOob, 0, 0));
-      rs[s][i] = __builtin_amdgcn_raw_buffer_load_b8(rss, ok ? idx : kOob, 0, 0);
+      const uint32_t gi = l_off[i] + (uint32_t)(L * l_m);
+      rw[s][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, 0));
+      rs[s][i] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)gi, 0, 0);
     }
     if (!l_done && ++l_m == l_nm) {
       l_m = 0;
+      next_item(l_cur);
       if (++l_j < n_mine) l_refresh();
       else l_done = true;
     }
@@ -185,8 +210,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
 
   // ---- x -> LDS as [t][c][g], plus the zero column g = G; p -> LDS
   auto stage_chunk = [&](int q, u32x4 v) {
-    const int t = q / (G * CH), r2 = q - t * (G * CH);
-    const int g = r2 / CH, c = r2 - g * CH;
+    const int t = div_small(q, rowc), r2 = q - t * rowc;
+    const int g = r2 / CH, c = r2 % CH;
     *reinterpret_cast<u32x4*>(xs + ((size_t)(t * CH + c) * GP + g) * 16) = v;
   };
 #pragma unroll
@@ -213,8 +238,9 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
   int c_j = 0, c_m = 0, c_nm = 1, c_gbeg = 0, c_gend = 0, c_ks = 0, c_rg = 0, c_nt = 0;
   int c_pt[kTmax];  // pair | token << 8 of the item's pairs
   const int xrow = CH * GP * 16;  // LDS bytes per token of x
+  Cursor c_cur = first_item();
   auto c_refresh = [&]() {
-    const Item it = item_info(w + kWaves * c_j);
+    const Item it = item_info(c_cur);
     c_gbeg = it.gbeg;
     c_gend = it.gend;
     c_nm = it.nm;
@@ -227,7 +253,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
     for (int tt = 0; tt < kTmax; tt++) {
       const int pair = m ? (int)__builtin_ctzll(m) : 0;
       m &= m - 1;
-      c_pt[tt] = pair | ((pair / K) << 8);
+      c_pt[tt] = pair | (__builtin_amdgcn_readlane(t_of_pair, pair) << 8);
     }
   };
   if (n_mine > 0) c_refresh();
@@ -332,6 +358,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
 #pragma unroll
             for (int tt = 0; tt < kTmax; tt++) acc[i][tt] = 0.f;
           c_m = 0;
+          next_item(c_cur);
           if (++c_j < n_mine) c_refresh();
         }
       }
@@ -342,7 +369,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
 
   // ---- combine: k-ordered fp32 sum of p * partial, then shared, one rounding
   for (int idx = tid; idx < T * R; idx += kThreads) {
-    const int t = idx / R, rr = idx - t * R, oo = o0 + rr;
+    const int t = idx / R, rr = idx % R, oo = o0 + rr;
     if (oo >= O) continue;
     float a = 0.f;
     for (int k = 0; k < K; k++) {
@@ -393,7 +420,7 @@ RowsPlan rows_plan(int T, int K, int E, int G, int dtype) {
   const int P = T * K, uexp = P < E ? P : E;
   const int64_t xbytes = (int64_t)T * G * 32 * (dtype == 0 ? 4 : 2);
   const bool big = xbytes > 32 * 1024;
-  const int R = big ? 16 : 8, NW = big ? 8 : 4;
+  const int NW = big ? 8 : 4, R = 2 * NW;
   RowsPlan pl{R, NW, 64, 1, G};
   for (int S = 1; S <= G; S++) {
     const int gs = (G + S - 1) / S;
@@ -422,7 +449,7 @@ hipError_t launch_rows_nw(const RowsPlan& pl, size_t lds, const void* x, const u
   }
   const dim3 grid((O + pl.R - 1) / pl.R);
   hipLaunchKernelGGL((gemv_rows_kernel<XF32, L, NW>), grid, dim3(NW * 64), lds, stream, x, packed, scales, sel, p,
-                     shared, y, T, E, O, G, K, pl.R, pl.S, pl.gs, bits_for(E), n_invalid, chunk_index);
+                     shared, y, T, E, O, G, K, pl.S, pl.gs, bits_for(E), n_invalid, chunk_index);
   return hipGetLastError();
 }
 
