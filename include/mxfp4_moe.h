@@ -178,6 +178,24 @@ int mxfp4_decode_rows(const uint8_t* packed, const uint8_t* scales, int64_t E, i
                       int64_t G, int64_t e, int64_t row0, int64_t nrows, int dtype, void* out,
                       hipStream_t stream);
 
+/*
+ * mxfp4_moe_gemm_stage - run again only the grouped GEMM of the
+ * prefill-shaped path (bf16): the bucketing results and M-tile list are the
+ * ones a previous mxfp4_moe_linear_ex call with the same sizes, dtype
+ * MXFP4_DTYPE_BF16 and the prefill-shaped path (chosen for these sizes or
+ * forced with MXFP4_FLAG_FORCE_GEMM) left in `workspace`; the fp32 partial
+ * rows it writes go to the same workspace. For timing and inspection of
+ * that one kernel (page "MoE Expert Kernels: Grouped Prefill and
+ * Mixed-Quant Compact Experts", section 2: one matmul per expert segment).
+ * Returns MXFP4_ERR_WORKSPACE_TOO_SMALL and MXFP4_ERR_INVALID_ARG as _ex
+ * does. The workspace must hold that call's results untouched: the kernel
+ * trusts the expert indices, positions and tile list it finds there, so
+ * anything else is undefined behaviour.
+ */
+int mxfp4_moe_gemm_stage(const void* x, const uint8_t* packed, const uint8_t* scales,
+                         int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* mxfp4_status_string(int status);
 

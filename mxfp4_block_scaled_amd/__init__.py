@@ -25,7 +25,7 @@ from ._abi import (  # noqa: F401
 )
 
 __all__ = [
-    "mxfp4_expert_linear", "moe_linear", "decode_rows", "bucket", "workspace_size", "select_path",
+    "mxfp4_expert_linear", "moe_linear", "decode_rows", "bucket", "gemm_stage", "workspace_size", "select_path",
     "Mxfp4Error", "library_path",
 ]
 
@@ -138,6 +138,23 @@ def decode_rows(packed: torch.Tensor, scales: torch.Tensor, e: int, row0: int, n
                                           _ptr(out), _stream(dev))
     _abi.check(st, "mxfp4_decode_rows")
     return out
+
+
+def gemm_stage(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
+               workspace: torch.Tensor) -> None:
+    """Re-run only the grouped GEMM of the prefill-shaped path on the
+    bucketing that the last ``moe_linear`` call with this workspace (bf16,
+    same sizes, prefill-shaped path) left there. For timing."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(packed, "packed", torch.uint8, 4, dev)
+    _need(scales, "scales", torch.uint8, 3, dev)
+    T = x.shape[0]
+    E, O, G, _ = packed.shape
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_gemm_stage(_ptr(x), _ptr(packed), _ptr(scales), T, E, O, G, K, _ptr(workspace),
+                                             workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_gemm_stage")
 
 
 def bucket(sel: torch.Tensor, E: int, flags: int = 0) -> dict:

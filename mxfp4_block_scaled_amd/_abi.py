@@ -52,6 +52,7 @@ SIGNATURES = {
     "mxfp4_moe_bucket_workspace_size": (_int, [_i64] * 3 + [_u32, ctypes.POINTER(_sz)]),
     "mxfp4_moe_bucket": (_int, [_vp] + [_i64] * 3 + [_vp] * 5 + [_u32, _vp, _sz, _vp]),
     "mxfp4_decode_rows": (_int, [_vp] * 2 + [_i64] * 6 + [_int, _vp, _vp]),
+    "mxfp4_moe_gemm_stage": (_int, [_vp] * 3 + [_i64] * 5 + [_vp, _sz, _vp]),
     "mxfp4_status_string": (ctypes.c_char_p, [_int]),
 }
 

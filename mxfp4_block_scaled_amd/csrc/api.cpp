@@ -278,6 +278,26 @@ int mxfp4_moe_linear_ex(const void* x, const uint8_t* packed, const uint8_t* sca
   return run_linear(x, packed, scales, sel, p, shared, y, d, dtype, flags, workspace, workspace_bytes, stream);
 }
 
+int mxfp4_moe_gemm_stage(const void* x, const uint8_t* packed, const uint8_t* scales, int64_t T, int64_t E, int64_t O,
+                         int64_t G, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (d.T == 0) return MXFP4_OK;
+  if (!x || !packed || !scales) return MXFP4_ERR_INVALID_ARG;
+  const Layout L = layout(d, MXFP4_PATH_GEMM);
+  if (workspace_bytes < L.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  const hipError_t err = launch_gemm_bf16(
+      static_cast<const uint16_t*>(x), packed, scales, reinterpret_cast<const int32_t*>(base + L.perm),
+      reinterpret_cast<const GemmTile*>(base + L.tiles), reinterpret_cast<const int32_t*>(base + L.n_tiles),
+      gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.K, (int)d.O, (int)d.G, stream);
+  return hip_status(err);
+}
+
 int mxfp4_moe_bucket_workspace_size(int64_t T, int64_t K, int64_t E, uint32_t flags, size_t* bytes) {
   if (!bytes || T < 0 || K < 1 || E < 1 || E > MXFP4_MAX_EXPERTS) return MXFP4_ERR_INVALID_ARG;
   if ((flags & MXFP4_FLAG_BUCKET_ONE_BLOCK) && (flags & MXFP4_FLAG_BUCKET_MULTI_BLOCK)) return MXFP4_ERR_INVALID_ARG;

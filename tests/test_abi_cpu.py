@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES)
@@ -140,3 +140,13 @@ def test_bucket_validates():
     assert f(A, 1, 1, 4, B, B, B, B, B, _abi.FLAG_BUCKET_ONE_BLOCK | _abi.FLAG_BUCKET_MULTI_BLOCK, C, 64,
              None) == _abi.ERR_INVALID_ARG
     assert f(A, 1000, 8, 4, B, B, B, B, B, _abi.FLAG_BUCKET_MULTI_BLOCK, C, 4, None) == _abi.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_gemm_stage_host_checks():
+    # rejected on the host before any device work: sizes, null pointers, workspace size
+    lib = _abi.lib()
+    a, b = 1 << 40, 1 << 41
+    assert lib.mxfp4_moe_gemm_stage(a, a, a, 4, 0, 32, 2, 2, b, 1 << 20, None) == _abi.ERR_INVALID_ARG
+    assert lib.mxfp4_moe_gemm_stage(None, a, a, 4, 4, 32, 2, 2, b, 1 << 20, None) == _abi.ERR_INVALID_ARG
+    assert lib.mxfp4_moe_gemm_stage(a, a, a, 4, 4, 32, 2, 2, b, 16, None) == _abi.ERR_WORKSPACE_TOO_SMALL
+    assert lib.mxfp4_moe_gemm_stage(a, a, a, 0, 4, 32, 2, 2, None, 0, None) == _abi.OK
