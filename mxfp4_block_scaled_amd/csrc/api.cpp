@@ -191,8 +191,8 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
     err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
     if (err == hipSuccess)
       err = launch_gemm_bf16(static_cast<const uint16_t*>(x), packed, scales, b.perm, b.tiles, b.n_tiles,
-                             gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.K, (int)d.O,
-                             (int)d.G, stream);
+                             gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.T, (int)d.K,
+                             (int)d.O, (int)d.G, stream);
     if (err == hipSuccess)
       err = launch_combine(reinterpret_cast<const float*>(base + L.part), b.slot_of_pair, p, shared, y, (int)d.T,
                            (int)d.K, (int)d.O, dtype, stream);
@@ -294,7 +294,8 @@ int mxfp4_moe_gemm_stage(const void* x, const uint8_t* packed, const uint8_t* sc
   const hipError_t err = launch_gemm_bf16(
       static_cast<const uint16_t*>(x), packed, scales, reinterpret_cast<const int32_t*>(base + L.perm),
       reinterpret_cast<const GemmTile*>(base + L.tiles), reinterpret_cast<const int32_t*>(base + L.n_tiles),
-      gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.K, (int)d.O, (int)d.G, stream);
+      gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.T, (int)d.K, (int)d.O, (int)d.G,
+      stream);
   return hip_status(err);
 }
 

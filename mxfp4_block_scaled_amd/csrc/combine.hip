@@ -3,8 +3,9 @@
 // Combine (page "MXFP4 Routed Expert Linear", "Route, weight, and add the
 // shared path" and "Implementation order"):
 //     y[t, o] = round(shared[t, o] + (sum over k = 0..K-1, in order, of p[t,k] * part[slot(t,k), o]))
-// One thread per output element, fp32 fused multiply-adds in slot order,
-// one rounding to y's dtype; no atomics, so the result is deterministic.
+// One thread per output element (or four, with 16-byte loads), fp32 fused
+// multiply-adds in slot order, one rounding to y's dtype; no atomics, so the
+// result is deterministic and the same in both forms.
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,6 +31,54 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       } else {
         const float sh = static_cast<const float*>(shared)[yo];
         static_cast<float*>(y)[yo] = sh + a;
+      }
+    }
+  }
+}
+
+// The same, four outputs per thread with 16-byte loads of the partial rows
+// (O % 4 == 0, so every row start is 16-byte aligned). The slots and
+// weights of token t are loaded once per thread and kept in registers.
+constexpr int kCombMaxK = 16;
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) combine4_kernel(const float* __restrict__ part,
+                                                       const int32_t* __restrict__ slot_of_pair,
+                                                       const float* __restrict__ p, const void* shared, void* y, int T,
+                                                       int K, int O) {
+  const int O4 = O >> 2;
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    int sp[kCombMaxK];
+    float pk[kCombMaxK];
+#pragma unroll
+    for (int k = 0; k < kCombMaxK; k++) {
+      sp[k] = k < K ? slot_of_pair[t * K + k] : -1;
+      pk[k] = k < K ? p[t * K + k] : 0.f;
+    }
+    for (int o4 = blockIdx.x * 256 + threadIdx.x; o4 < O4; o4 += gridDim.x * 256) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kCombMaxK; k++) {
+        if (k < K && sp[k] >= 0) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)sp[k] * O + 4 * o4);
+#pragma unroll
+          for (int i = 0; i < 4; i++) a[i] = fmaf(pk[k], v[i], a[i]);
+        }
+      }
+      const int64_t yo = (int64_t)t * O + 4 * o4;
+      if constexpr (BF16) {
+        const uint2 sh = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(shared) + yo);
+        const uint32_t r0 = f32_to_bf16_rne(bf16_to_f32((uint16_t)sh.x) + a[0]);
+        const uint32_t r1 = f32_to_bf16_rne(bf16_to_f32((uint16_t)(sh.x >> 16)) + a[1]);
+        const uint32_t r2 = f32_to_bf16_rne(bf16_to_f32((uint16_t)sh.y) + a[2]);
+        const uint32_t r3 = f32_to_bf16_rne(bf16_to_f32((uint16_t)(sh.y >> 16)) + a[3]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + yo) = make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+      } else {
+        const f32x4 sh = *reinterpret_cast<const f32x4*>(static_cast<const float*>(shared) + yo);
+        f32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; i++) r[i] = sh[i] + a[i];
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + yo) = r;
       }
     }
   }
@@ -72,8 +121,20 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(const uint8_t* __restr
 
 hipError_t launch_combine(const float* part, const int32_t* slot_of_pair, const float* p, const void* shared, void* y,
                           int T, int K, int O, int dtype, hipStream_t stream) {
-  const unsigned gx = (unsigned)((O + 255) / 256);
   const unsigned gy = (unsigned)(T < 32768 ? T : 32768);
+  const bool vec = O % 4 == 0 && K <= kCombMaxK && reinterpret_cast<uintptr_t>(part) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(shared) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
+  if (vec) {
+    const unsigned gx = (unsigned)((O / 4 + 255) / 256);
+    if (dtype == 1)
+      hipLaunchKernelGGL(combine4_kernel<true>, dim3(gx, gy), dim3(256), 0, stream, part, slot_of_pair, p, shared, y, T,
+                         K, O);
+    else
+      hipLaunchKernelGGL(combine4_kernel<false>, dim3(gx, gy), dim3(256), 0, stream, part, slot_of_pair, p, shared, y,
+                         T, K, O);
+    return hipGetLastError();
+  }
+  const unsigned gx = (unsigned)((O + 255) / 256);
   if (dtype == 1)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(gx, gy), dim3(256), 0, stream, part, slot_of_pair, p, shared, y, T, K, O);
   else

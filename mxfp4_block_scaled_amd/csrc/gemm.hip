@@ -19,7 +19,8 @@
 // for both operands; this permutes the order of k inside the stage, which
 // leaves every product x_i * w_i paired correctly.
 // Waves are 2 x 2 over the 128 x 128 tile; each owns 64 x 64 = 2 x 2 MFMA
-// tiles. Loads of the next stage overlap the MFMAs of the current one.
+// tiles (a 32-row sub-tile past the segment's end is skipped). Loads of the
+// next stage overlap the MFMAs of the current one.
 #include "device_common.h"
 #include "launch.h"
 
@@ -130,6 +131,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __res
     for (int j = 0; j < 4; j++) {
 #pragma unroll
       for (int mi = 0; mi < 2; mi++) {
+        if (64 * wm + 32 * mi >= tl.mlen) continue;  // a 32-row sub-tile past the segment
         const int ml = 64 * wm + 32 * mi + lm;
         const u32x4 av = *reinterpret_cast<const u32x4*>(&As[buf][ml * A_LD + lq * 32 + j * 8]);
 #pragma unroll
@@ -159,11 +161,13 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __res
   }
 }
 
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
-                            const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int K, int O,
-                            int G, hipStream_t stream) {
+                            const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
+                            int O, int G, hipStream_t stream) {
+  (void)T;
   const int n_ntiles = (O + NT - 1) / NT;
   const int64_t nblk = max_tiles * n_ntiles;
   if (nblk <= 0) return hipSuccess;

@@ -76,9 +76,9 @@ hipError_t launch_gemv_rows(const void* x, const uint8_t* packed, const uint8_t*
                             int32_t* n_invalid, int chunk_index, hipStream_t stream);
 
 // ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
-hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
-                            const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
-                            int64_t max_tiles, float* part, int K, int O, int G, hipStream_t stream);
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
+                            const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
+                            int O, int G, hipStream_t stream);
 hipError_t launch_combine(const float* part, const int32_t* slot_of_pair, const float* p,
                           const void* shared, void* y, int T, int K, int O, int dtype,
                           hipStream_t stream);
