@@ -22,15 +22,18 @@
 // piece; fp32 activations are split exactly into three bf16 pieces by
 // truncation (x = x0 + x1 + x2 for every normal fp32 x), so every product
 // w * x_i is exact and the MFMA accumulates in fp32 -- the result keeps
-// fp32 accuracy. Lane (r, q) = (lane & 15, lane >> 4) loads the whole group
-// 4i+q of row r and feeds its dword j to MFMA j; the B operand uses the
-// same permutation of k, so each MFMA sums matching products.
+// fp32 accuracy. For MFMA step i lane (r, q) = (lane & 15, lane >> 4)
+// holds group 4i+q of row r and feeds its dword j to MFMA j; the B operand
+// uses the same permutation of k, so each MFMA sums matching products.
 //
-// Work item = (distinct expert, chunk of 16 columns, k-split). A wave walks
-// its items as one stream of iterations (16 rows x 4 groups each) with
-// kRing 128-bit loads in flight, across item boundaries. The activations
-// are staged once per workgroup in LDS (rows padded by 16 bytes so that the
-// columns of an MFMA fall in different banks).
+// Memory: an iteration covers 8 groups of the 16 rows. Lane (lr, lg) loads
+// group lg of rows lr and 8 + lr (8 whole 128-byte row segments per load)
+// and the matching scale bytes; a per-wave LDS buffer with padded rows
+// turns that into the MFMA layout without bank conflicts. Work item =
+// (distinct expert, chunk of 16 columns, k-split). A wave walks its items as
+// one stream of iterations with kRing iterations of loads in flight, across
+// item boundaries. The activations are staged once per workgroup in LDS
+// (each row followed by an all-zero group that the lanes past a split read).
 #include "device_common.h"
 #include "launch.h"
 #include "wave_routing.h"
@@ -40,8 +43,12 @@ namespace {
 
 constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kRing = 8;   // iterations whose loads a wave keeps in flight
+constexpr int kRing = 4;   // iterations (8 groups of the 16 rows each) whose loads a wave keeps in flight
 constexpr int kRows = 16;  // output rows per workgroup (one MFMA tile)
+constexpr int kTrRow = 8 * 16 + 16;           // bytes per row of a wave's transpose buffer (padded)
+constexpr int kTrBytes = kRows * kTrRow + kRows * 8;  // weights then scale bytes
+constexpr uint32_t kOobGroup = 0x08000000u;   // group offset beyond any expert's resource
+constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
 
 // fp32 -> three bf16 (bit patterns) with f = x0 + x1 + x2 exactly: each
 // piece keeps the top 8 significant bits of what is left, and the
@@ -67,10 +74,12 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, kept in a scalar register
   const int r = lane & 15, q = lane >> 4;
-  const int P = T * K, I = 32 * G, IL = I + 8;
+  const int P = T * K, I = 32 * G, IL = I + 40;  // IL: a zero group 32G..32G+31, then 8 of padding
   const int o0 = blockIdx.x * kRows;
   uint16_t* xs = reinterpret_cast<uint16_t*>(dyn);  // [T][NP][IL] bf16
-  float* part = reinterpret_cast<float*>(dyn + (((size_t)T * NP * IL * 2 + 15) & ~(size_t)15));  // [S][P*NP][16]
+  const size_t xs_bytes = ((size_t)T * NP * IL * 2 + 15) & ~(size_t)15;
+  float* part = reinterpret_cast<float*>(dyn + xs_bytes);  // [S][P*NP][16]
+  uint8_t* tr = dyn + xs_bytes + (size_t)S * P * NP * kRows * 4 + (size_t)w * kTrBytes;  // this wave's transpose buffer
 
   // ---- routing input first, then the loads that do not depend on it:
   // p, shared and (up to two 16-byte chunks per thread of) x, written to LDS
@@ -95,8 +104,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
   const WaveRoute rt = route_wave(e_l, lane, P, E, nbits);
   const uint64_t valid = rt.valid, pm_u = rt.pm_u;
   const int U = rt.U, e_u = rt.e_u;
-  const int n4 = (G + 3) >> 2;
-  const int gs4 = (n4 + S - 1) / S;  // iterations (4 groups each) per k-split
+  const int n8 = (G + 7) >> 3;
+  const int gs8 = (n8 + S - 1) / S;  // iterations (8 groups each) per k-split
   const int ncol_u = lane < U ? __popcll(pm_u) * NP : 0;
   // Usually every expert's (pair, piece) columns fit one chunk of 16, and
   // item i is simply (expert i / S, split i % S); otherwise a prefix sum of
@@ -130,51 +139,58 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     it.ks = rem - it.cc * S;
     it.e = __builtin_amdgcn_readlane(e_u, u);
     it.pm = readlane64(pm_u, u);
-    it.gbeg = it.ks * gs4 * 4;
-    it.nit = (min(G, it.gbeg + gs4 * 4) - it.gbeg + 3) >> 2;
+    it.gbeg = it.ks * gs8 * 8;
+    it.nit = (min(G, it.gbeg + gs8 * 8) - it.gbeg + 7) >> 3;
     return it;
   };
   const int n_mine = NI > w ? (NI - w + kDecWaves - 1) / kDecWaves : 0;
   int total = 0;  // iterations of this wave over all its items
   for (int j = 0; j < n_mine; j++) {
     const int ks = single ? (w + kDecWaves * j) % S : item_info(w + kDecWaves * j).ks;
-    const int gb = ks * gs4 * 4;
-    total += (min(G, gb + gs4 * 4) - gb + 3) >> 2;
+    const int gb = ks * gs8 * 8;
+    total += (min(G, gb + gs8 * 8) - gb + 7) >> 3;
   }
 
-  // ---- load cursor. Every ring slot issues exactly one 16-byte weight load
-  // and one scale-byte load, always from a valid address (past the end of
-  // the wave's work: the lane's last group again, value discarded), so the
-  // number of loads in flight is static and the waits pipeline.
-  const int o = o0 + r;
-  const bool row_ok = o < O;
-  int l_j = 0, l_it = 0, l_gbeg = 0, l_nit = 0, l_gend = 1;
+  // ---- load cursor. An iteration covers 8 groups of the 16 rows: lane
+  // (lr, lg) = (lane >> 3, lane & 7) loads group gbase + lg of rows lr and
+  // 8 + lr (two loads of 8 whole 128-byte row segments each) and their scale
+  // bytes. Loads go through buffer resources sized to the selected expert; a
+  // row past O and every load past the wave's last item use an offset beyond
+  // the resource and read zeros without memory traffic, so every slot issues
+  // the same loads and the waits pipeline.
+  const int lr = lane >> 3, lg = lane & 7;
+  const int nrec_w = O * G * 16, nrec_s = O * G;
+  int l_j = 0, l_it = 0, l_nit = 1;
   bool l_done = n_mine == 0;
-  const uint8_t* l_prow = packed;
-  const uint8_t* l_srow = scales;
+  const uint8_t* l_wb = packed;
+  const uint8_t* l_sb = scales;
+  uint32_t l_off[2];  // group offset (row-major in the expert) of this lane's first group, per load
   auto l_refresh = [&]() {
     const Item it = item_info(w + kDecWaves * l_j);
-    l_gbeg = it.gbeg;
     l_nit = it.nit;
-    l_gend = min(G, l_gbeg + 4 * l_nit);
-    const int64_t row = (int64_t)it.e * O + (row_ok ? o : 0);
-    l_prow = packed + row * (int64_t)G * 16;
-    l_srow = scales + row * (int64_t)G;
+    l_wb = packed + (int64_t)it.e * nrec_w;
+    l_sb = scales + (int64_t)it.e * nrec_s;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int o = o0 + 8 * t + lr;
+      l_off[t] = o < O ? (uint32_t)(o * G + it.gbeg + lg) : kOobGroup;
+    }
   };
   if (!l_done) l_refresh();
-  u32x4 rw[kRing];
-  uint8_t rs[kRing];  // kept as bytes: widened where used, not where the loop repeats
-  uint32_t rvalid = 0;  // bit s: slot s holds a real group for this lane
-  // The loaded values are used as they are; invalid slots are zeroed only
-  // when consumed, so no instruction waits on a load before then.
-  auto issue_load = [&](int s, u32x4& wv, uint8_t& sv) {
-    const int g = l_gbeg + 4 * l_it + q;
-    const bool okl = !l_done && row_ok && g < l_gend;
-    // past the end of the item: re-read one of its groups (cached)
-    const int gc = min(g, l_gend - 1);
-    wv = *reinterpret_cast<const u32x4*>(l_prow + gc * 16);
-    sv = l_srow[gc];
-    rvalid = okl ? (rvalid | (1u << s)) : (rvalid & ~(1u << s));
+  u32x4 rw[kRing][2];
+  uint8_t rs[kRing][2];
+  auto issue_load = [&](int s) {
+    const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc((void*)l_wb, (short)0, nrec_w, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)l_sb, (short)0, nrec_s, kRsrcFlags);
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      // a lane past its split reads the following group (the next row at the
+      // end of a row; beyond the resource at the end of the expert); it
+      // meets the zero activation group, so it adds nothing
+      const uint32_t gi = l_done ? kOobGroup : l_off[t] + (uint32_t)(8 * l_it);
+      rw[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, 0));
+      rs[s][t] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)gi, 0, 0);
+    }
     if (!l_done && ++l_it == l_nit) {
       l_it = 0;
       if (++l_j < n_mine) l_refresh();
@@ -182,7 +198,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     }
   };
 #pragma unroll
-  for (int s = 0; s < kRing; s++) issue_load(s, rw[s], rs[s]);
+  for (int s = 0; s < kRing; s++) issue_load(s);
 
   // ---- x -> LDS (fp32: three bf16 pieces per value), p -> LDS
   auto stage_chunk = [&](int idx, u32x4 v) {
@@ -215,11 +231,13 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     for (int i = 0; i < 8; i++)
       if (base + i * kDecThreads < nxc) stage_chunk(base + i * kDecThreads, v[i]);
   }
+  for (int i = tid; i < T * NP * 4; i += kDecThreads)  // the zero group of every row
+    *reinterpret_cast<u32x4*>(xs + (i >> 2) * IL + I + 8 * (i & 3)) = u32x4{0u, 0u, 0u, 0u};
   if (tid < P) p_lds[tid] = my_p;
   __syncthreads();
 
   // ---- compute cursor
-  int c_j = 0, c_it = 0, c_gbeg = 0, c_nit = 0, c_ks = 0;
+  int c_j = 0, c_it = 0, c_gbeg = 0, c_gend = 0, c_nit = 0, c_ks = 0;
   const uint16_t* bptr = xs;  // this lane's B column (a row of xs)
   bool col_ok = false;
   int colidx = 0;
@@ -227,6 +245,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     const Item it = item_info(w + kDecWaves * c_j);
     c_gbeg = it.gbeg;
     c_nit = it.nit;
+    c_gend = min(G, it.gbeg + 8 * it.nit);
     c_ks = it.ks;
     const int gc = it.cc * 16 + r;  // column of this lane: (pair, piece)
     col_ok = gc < __popcll(it.pm) * NP;
@@ -245,41 +264,48 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
       // must wait for slot s's loads only
       __builtin_amdgcn_sched_barrier(0);
       if (base + s < total) {
-        // decode the 16-byte group of this lane (row r, group gbeg + 4 it + q);
-        // an invalid slot decodes zero codes, i.e. zeros
-        const bool vs = (rvalid >> s) & 1u;
-        const uint32_t sv = vs ? (uint32_t)rs[s] : 127u;
-        u32x4 wq = rw[s];
+        // transpose through this wave's LDS buffer: rows as loaded (8 groups
+        // each, padded rows: conflict-free both ways), then lane (r, q) takes
+        // group 4i + q of row r for MFMA step i
 #pragma unroll
-        for (int j = 0; j < 4; j++) wq[j] = vs ? wq[j] : 0u;
-        uint32_t wd[4][4];
-        // scale bytes >= 253 can make E2M1 * 2^(s-127) overflow bf16: such a
-        // lane's group is decoded at 2^(s-135) into a second accumulator,
-        // multiplied by 2^8 when the item ends (exact)
-        const bool hi = sv >= 253u;
-        const float sc = e8m0_operand(hi ? sv - 8u : sv);
+        for (int t = 0; t < 2; t++) {
+          *reinterpret_cast<u32x4*>(tr + (8 * t + lr) * kTrRow + lg * 16) = rw[s][t];
+          tr[kRows * kTrRow + (8 * t + lr) * 8 + lg] = rs[s][t];
+        }
 #pragma unroll
-        for (int j = 0; j < 4; j++) decode8_bf16_fast(wq[j], sc, wd[j]);
-        const int gb = min(c_gbeg + 4 * c_it + q, G - 1);  // in bounds; a zero A covers the tail
-        const uint16_t* bp = bptr + 32 * gb;
-        if (__builtin_expect(__ballot(hi) == 0, 1)) {
+        for (int i = 0; i < 2; i++) {
+          const u32x4 wq = *reinterpret_cast<const u32x4*>(tr + r * kTrRow + (4 * i + q) * 16);
+          const uint32_t sv = tr[kRows * kTrRow + r * 8 + 4 * i + q];
+          uint32_t wd[4][4];
+          // scale bytes >= 253 can make E2M1 * 2^(s-127) overflow bf16: such a
+          // lane's group is decoded at 2^(s-135) into a second accumulator,
+          // multiplied by 2^8 when the item ends (exact)
+          const bool hi = sv >= 253u;
+          const float sc = e8m0_operand(hi ? sv - 8u : sv);
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
-            const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-          }
-        } else {
+          for (int j = 0; j < 4; j++) decode8_bf16_fast(wq[j], sc, wd[j]);
+          // activations of this group; past the split: the zero group
+          const int g = c_gbeg + 8 * c_it + 4 * i + q;
+          const uint16_t* bp = bptr + 32 * (g < c_gend ? g : G);
+          if (__builtin_expect(__ballot(hi) == 0, 1)) {
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
-            const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi ? z : av),
-                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-            acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi ? av : z),
-                                                             __builtin_bit_cast(bf16x8, bv), acc_hi, 0, 0, 0);
+            for (int j = 0; j < 4; j++) {
+              const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
+              const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                            __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + 8 * j);
+              const u32x4 av = {wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
+              const u32x4 z = {0u, 0u, 0u, 0u};
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi ? z : av),
+                                                            __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+              acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi ? av : z),
+                                                               __builtin_bit_cast(bf16x8, bv), acc_hi, 0, 0, 0);
+            }
           }
         }
         if (++c_it == c_nit) {
@@ -296,7 +322,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
           if (++c_j < n_mine) c_refresh();
         }
       }
-      issue_load(s, rw[s], rs[s]);
+      issue_load(s);
     }
   }
   __syncthreads();
@@ -338,16 +364,16 @@ int decode_splits(int T, int K, int E, int G) {
   const int P = T * K;
   const int uexp = P < E ? P : E;
   int S = uexp >= kDecWaves ? 1 : kDecWaves / uexp;
-  const int n4 = (G + 3) / 4;
-  if (S > n4) S = n4;
-  const int per = (n4 + S - 1) / S;
-  return (n4 + per - 1) / per;
+  const int n8 = (G + 7) / 8;
+  if (S > n8) S = n8;
+  const int per = (n8 + S - 1) / S;
+  return (n8 + per - 1) / per;
 }
 
 size_t decode_lds_bytes(int T, int K, int G, int dtype, int S) {
   const int NP = dtype == 0 ? 3 : 1;
-  const size_t xs = ((size_t)T * NP * (32 * (size_t)G + 8) * 2 + 15) & ~(size_t)15;
-  return xs + (size_t)S * T * K * NP * kRows * 4;
+  const size_t xs = ((size_t)T * NP * (32 * (size_t)G + 40) * 2 + 15) & ~(size_t)15;
+  return xs + (size_t)S * T * K * NP * kRows * 4 + (size_t)kDecWaves * kTrBytes;
 }
 
 }  // namespace

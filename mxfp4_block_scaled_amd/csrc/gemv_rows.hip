@@ -194,7 +194,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)l_sb, (short)0, nrec_s, kRsrcFlags);
 #pragma unroll
     for (int i = 0; i < kRpl; i++) {
-      const uint32_t gi = l_off[i] + (uint32_t)(L * l_m);
+      // past the wave's last item: beyond the resource (zeros, no memory traffic)
+      const uint32_t gi = l_done ? kOobGroup : l_off[i] + (uint32_t)(L * l_m);
       rw[s][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, 0));
       rs[s][i] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)gi, 0, 0);
     }
