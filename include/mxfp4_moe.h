@@ -74,7 +74,10 @@ typedef enum mxfp4_status {
   MXFP4_ERR_HIP = -3,                /* a HIP runtime call or a launch failed */
   MXFP4_ERR_WORKSPACE_TOO_SMALL = -4,
   MXFP4_ERR_INVALID_INDEX = -5,      /* with MXFP4_FLAG_CHECK: some sel entry outside [0, E) */
-  MXFP4_ERR_UNSUPPORTED = -6         /* a forced path that does not exist for this dtype */
+  MXFP4_ERR_UNSUPPORTED = -6         /* a forced path that does not exist for these sizes or dtype:
+                                        the decode-shaped path needs one expert's packed bytes
+                                        O*G*16 < 2^31 and one token's rows in LDS; the
+                                        prefill-shaped path is bf16-only */
 } mxfp4_status;
 
 typedef enum mxfp4_dtype {

@@ -54,14 +54,14 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // Decode-shaped kernel: the row-contiguous one unless the MFMA one is asked
-// for or the rows kernel's 32-bit buffer offsets cannot address an expert.
-bool use_rows_kernel(const Dims& d, uint32_t flags) {
-  return !(flags & MXFP4_FLAG_GEMV_MFMA) && gemv_rows_supported((int)d.O, (int)d.G);
-}
+// for. Both address an expert's packed bytes with 32-bit buffer offsets, so
+// the decode-shaped path needs O * G * 16 < 2^31.
+bool use_rows_kernel(uint32_t flags) { return !(flags & MXFP4_FLAG_GEMV_MFMA); }
 
 int64_t gemv_tokens_per_launch(const Dims& d, int dtype, uint32_t flags) {
-  return use_rows_kernel(d, flags) ? gemv_rows_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype)
-                                   : decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype);
+  if (!gemv_rows_supported((int)d.O, (int)d.G)) return 0;
+  return use_rows_kernel(flags) ? gemv_rows_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype)
+                                : decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype);
 }
 
 int select_path(const Dims& d, int dtype, uint32_t flags) {
@@ -170,7 +170,7 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
     // token chunks whose pairs and activations fit one fused launch
     const int64_t tc = gemv_tokens_per_launch(d, dtype, flags);
     if (tc < 1) return MXFP4_ERR_UNSUPPORTED;
-    const auto launch = use_rows_kernel(d, flags) ? launch_gemv_rows : launch_decode_fused;
+    const auto launch = use_rows_kernel(flags) ? launch_gemv_rows : launch_decode_fused;
     int chunk = 0;
     for (int64_t t0 = 0; t0 < d.T && err == hipSuccess; t0 += tc, chunk++) {
       const int64_t tn = (d.T - t0 < tc) ? d.T - t0 : tc;

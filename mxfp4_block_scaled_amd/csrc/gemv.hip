@@ -388,7 +388,7 @@ int decode_tokens_per_launch(int K, int E, int G, int dtype) {
 hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
                                const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
                                int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream) {
-  if (T * K > kMaxFusedPairs) return hipErrorInvalidValue;
+  if (T * K > kMaxFusedPairs || !gemv_rows_supported(O, G)) return hipErrorInvalidValue;
   const int S = decode_splits(T, K, E, G);
   const size_t lds = decode_lds_bytes(T, K, G, dtype, S);
   if (lds > (size_t)kDecodeMaxLds) return hipErrorInvalidValue;

@@ -58,6 +58,7 @@ hipError_t launch_bucket_multi(const int32_t* sel, int P, int E, int32_t* bcount
 hipError_t launch_bucket_one_block(const int32_t* sel, int P, int E, BucketOut out, hipStream_t stream);
 
 // ---- decode-shaped fused path: routing, dequant-GEMV and combine.
+// Both decode-shaped kernels need O * G * 16 < 2^31 (gemv_rows_supported).
 // dtype 0 = fp32 x/shared/y, 1 = bf16. n_invalid (may be null) receives the
 // number of out-of-range indices, accumulated over successive chunk launches
 // (chunk_index 0 starts at zero).
