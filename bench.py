@@ -75,6 +75,73 @@ def committed_traffic(workload: str, kind: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def copy_calibration(mib: int, reps: int = 8):
+    """A plain elementwise kernel of known traffic (reads and writes mib MiB
+    per launch): the calibration run for the HBM byte counters."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} launches of a {mib} MiB read + {mib} MiB write")
+
+
+def _counter_means(run_dir: str, counter: str, kernel_part: str):
+    """Mean of one rocprofv3 counter over the dispatches of the kernels whose
+    name contains kernel_part, from the counter_collection.csv files under
+    run_dir."""
+    import csv
+    import glob
+
+    vals = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") == counter and kernel_part in row.get("Kernel_Name", ""):
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} values for kernels named *{kernel_part}* under {run_dir}")
+    return float(np.mean(vals)), len(vals)
+
+
+def record_traffic(args):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the
+    workload's dominant kernel, the same two of the copy calibration) into
+    HBM bytes per launch, stored in profiles/traffic.json with the hash of
+    the kernel's sources; prints a summary."""
+    w = workloads.WORKLOADS[args.workload]
+    kind = "gemv" if args.workload in DECODE_WORKLOADS else "gemm"
+    kname = "gemv_rows_kernel" if kind == "gemv" else "gemm_bf16_kernel"
+    fdir, wdir, cfdir, cwdir = args.record_traffic
+    copy_kib = args.copy_mib * 1024.0
+    k_fetch, n_f = _counter_means(fdir, "FETCH_SIZE", kname)
+    k_write, n_w = _counter_means(wdir, "WRITE_SIZE", kname)
+    c_fetch, _ = _counter_means(cfdir, "FETCH_SIZE", "neg_kernel")
+    c_write, _ = _counter_means(cwdir, "WRITE_SIZE", "neg_kernel")
+    f_fac, w_fac = copy_kib / c_fetch, copy_kib / c_write
+    hbm = (k_fetch * f_fac + k_write * w_fac) * 1024.0
+    rec = {"kernel": kname, "source_sha": sources_sha(kind), "hbm_bytes_per_launch": round(hbm),
+           "fetch_kib_per_dispatch": round(k_fetch, 1), "write_kib_per_dispatch": round(k_write, 1),
+           "dispatches": [n_f, n_w], "copy_mib": args.copy_mib,
+           "copy_fetch_kib": round(c_fetch, 1), "copy_write_kib": round(c_write, 1),
+           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[w.name] = rec
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({w.name: rec}))
+
+
 def cpu_baseline(inp, kind, sample_seconds):
     import oracle
 
@@ -124,13 +191,27 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run only the copy calibration kernel of this size (for the byte counters)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="host only: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload and of "
+                         "the copy calibration (--copy-mib) into profiles/traffic.json")
     args = ap.parse_args()
+    if args.record_traffic:
+        if args.copy_mib <= 0:
+            raise SystemExit("--record-traffic needs the --copy-mib size the calibration ran with")
+        record_traffic(args)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib)
+        return
 
     import torch
 
@@ -213,20 +294,26 @@ def main():
         # the grouped GEMM alone, on the bucketing the last timed step left in
         # the workspace: K launches captured in a graph, timed like the steps
         r_last = (args.steps - 1) % N_ROUTING_SETS
-        g2 = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             mx.gemm_stage(x, packed, scales, w.K, ws)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g2, stream=stream):
-            for _ in range(args.steps):
-                mx.gemm_stage(x, packed, scales, w.K, ws)
-        g2.replay()
-        torch.cuda.synchronize()
+        g2 = None
+        if graph is not None:
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2, stream=stream):
+                for _ in range(args.steps):
+                    mx.gemm_stage(x, packed, scales, w.K, ws)
+            g2.replay()
+            torch.cuda.synchronize()
         e2a = torch.cuda.Event(enable_timing=True)
         e2b = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
             e2a.record(stream)
-            g2.replay()
+            if g2 is not None:
+                g2.replay()
+            else:
+                for _ in range(args.steps):
+                    mx.gemm_stage(x, packed, scales, w.K, ws)
             e2b.record(stream)
         torch.cuda.synchronize()
         gemm_ms = e2a.elapsed_time(e2b) / args.steps

@@ -74,9 +74,11 @@ int select_path(const Dims& d, int dtype, uint32_t flags) {
     if (fm || !gemv_ok) return MXFP4_ERR_UNSUPPORTED;  // the MFMA grouped GEMM is bf16-only
     return MXFP4_PATH_GEMV;
   }
+  const bool gemm_ok = gemm_supported(d.T, d.O, d.G);
   if (fv) return gemv_ok ? MXFP4_PATH_GEMV : MXFP4_ERR_UNSUPPORTED;
-  if (fm) return MXFP4_PATH_GEMM;
-  return (d.T <= kGemvMaxTokens && gemv_ok) ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
+  if (fm) return gemm_ok ? MXFP4_PATH_GEMM : MXFP4_ERR_UNSUPPORTED;
+  if (gemv_ok && (d.T <= kGemvMaxTokens || !gemm_ok)) return MXFP4_PATH_GEMV;
+  return gemm_ok ? MXFP4_PATH_GEMM : MXFP4_ERR_UNSUPPORTED;
 }
 
 // Workspace layout. GEMV: n_invalid only. GEMM: bucketing arrays, the M-tile
@@ -285,6 +287,7 @@ int mxfp4_moe_gemm_stage(const void* x, const uint8_t* packed, const uint8_t* sc
   if (st != MXFP4_OK) return st;
   if (d.T == 0) return MXFP4_OK;
   if (!x || !packed || !scales) return MXFP4_ERR_INVALID_ARG;
+  if (!gemm_supported(d.T, d.O, d.G)) return MXFP4_ERR_UNSUPPORTED;
   const Layout L = layout(d, MXFP4_PATH_GEMM);
   if (workspace_bytes < L.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;

@@ -129,6 +129,18 @@ __device__ __forceinline__ void decode8_bf16_fast(uint32_t w, float sc, uint32_t
   out[3] = cvt_fp4x2_bf16<3>(w, sc);
 }
 
+// The same 8 values as an MFMA operand. Built from the builtin's vector
+// elements, which this compiler keeps intact (unlike a bit cast of the pair
+// to 32 bits): the four converts then write the operand registers directly,
+// with no copies.
+__device__ __forceinline__ bf16x8 decode8_bf16x8(uint32_t w, float sc) {
+  const bf16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  return bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
 // Unscaled E2M1 values of the 8 codes of w as fp32 (exact).
 __device__ __forceinline__ void decode8_f32_unscaled(uint32_t w, float out[8]) {
   f32x2 a = cvt_fp4x2_f32<0>(w, 1.0f), b = cvt_fp4x2_f32<1>(w, 1.0f);

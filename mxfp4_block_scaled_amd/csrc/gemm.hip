@@ -7,8 +7,11 @@
 // (page "MXFP4 Routed Expert Linear", "Reconstruct the matrix in the right
 // orientation": each output coordinate is a row of W_e dotted with the
 // token). Per K-stage of two groups (64 inputs) the workgroup stages in LDS
-// the gathered bf16 token rows (128 x 64) and the raw packed bytes and scale
-// bytes of its 128 weight rows; every wave then decodes its own weight
+// the gathered bf16 token rows (128 x 64) and the raw packed bytes of its
+// 128 weight rows. Scale bytes go to LDS in chunks of 16 groups (8 stages),
+// each row's 16 bytes with a few dword loads, prefetched a chunk ahead
+// (one byte per lane per stage would touch a cache line per row per stage);
+// every wave then decodes its own weight
 // fragments from LDS straight into MFMA operand registers (exact in bf16:
 // every E2M1 value times a power of two up to 2^127 is a bf16 value), so no
 // decoded weight is ever stored, in LDS or in HBM.
@@ -31,14 +34,21 @@ constexpr int MT = kGemmTileM;
 constexpr int NT = kGemmTileN;
 constexpr int A_LD = 64 + 8;  // bf16 elements per LDS row (144 B: conflict-free 16-B reads)
 constexpr int B_LD = 48;      // bytes per LDS row of packed weights (32 used)
+constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
+constexpr uint32_t kOobByte = 0x80000000u;    // byte offset past the activation and weight resources
+constexpr int kScGroups = 16;                   // scale bytes per row and chunk
+constexpr int kScStages = kScGroups / 2;        // stages per chunk
+constexpr int kScPitch = 5;                     // dwords per LDS row of a chunk (16 bytes at offset 0..3)
+constexpr int kScSlots = (kGemmTileN * kScPitch + 255) / 256;
+static_assert(kGemmTileN * kScPitch <= 1020, "q / 5 by multiply-shift");
 
-__global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __restrict__ x,
+__global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __restrict__ x,
                                                            const uint8_t* __restrict__ packed,
                                                            const uint8_t* __restrict__ scales,
                                                            const int32_t* __restrict__ perm,
                                                            const GemmTile* __restrict__ tiles,
                                                            const int32_t* __restrict__ n_tiles, float* __restrict__ part,
-                                                           int K, int O, int G, int n_ntiles) {
+                                                           int K, int O, int G, int n_ntiles, uint32_t x_bytes) {
   const int ti = blockIdx.x / n_ntiles;
   const int nt = blockIdx.x - ti * n_ntiles;
   if (ti >= n_tiles[0]) return;
@@ -48,52 +58,79 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __res
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * A_LD];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][NT * B_LD];
-  __shared__ uint8_t Ss[2][NT * 2];
+  __shared__ __attribute__((aligned(16))) uint32_t Sc[NT * kScPitch];  // scale chunk: row r at dword kScPitch r
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int lm = lane & 31, lq = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
 
   // A loader: rows (tid >> 3) + 32 i, 16-byte column tid & 7 of the stage slice
-  const uint16_t* arow[4];
-  bool aok[4];
+  // activations through a buffer resource: 32-bit byte offsets, an invalid
+  // row gets an offset past the resource (zeros, no memory traffic)
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRsrcFlags);
+  uint32_t a_off[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int m = (tid >> 3) + 32 * i;
-    aok[i] = m < tl.mlen;
-    const int pr = aok[i] ? perm[tl.row0 + m] : 0;
-    arow[i] = x + (int64_t)(pr / K) * I + (tid & 7) * 8;
+    a_off[i] = m < tl.mlen ? (uint32_t)(perm[tl.row0 + m] / K) * (uint32_t)(64 * G) + 16u * (tid & 7) : kOobByte;
   }
   // B loader: row tid >> 1, group (tid & 1) of the stage
   const int bn = n0 + (tid >> 1);
-  const bool bok = bn < O;
-  const uint8_t* brow = packed + ((int64_t)tl.e * O + (bok ? bn : 0)) * (int64_t)G * 16 + (tid & 1) * 16;
-  const uint8_t* srow = scales + ((int64_t)tl.e * O + (bok ? bn : 0)) * (int64_t)G + (tid & 1);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(packed + (int64_t)tl.e * O * G * 16), (short)0, O * G * 16, kRsrcFlags);
+  const uint32_t b_off = bn < O ? ((uint32_t)bn * (uint32_t)G + (uint32_t)(tid & 1)) * 16u : kOobByte;
+  // Scale chunk loader: thread slot i covers (row, dword) = ((tid + 256 i) / 5, (tid + 256 i) % 5) of
+  // the chunk; row r's 16 bytes of chunk c start at byte rb_r + 16 c of the scales, read from the
+  // dword boundary below (the first byte sits at offset rb_r & 3 of the LDS row).
+  const int64_t srun = ((int64_t)tl.e * O + n0) * (int64_t)G;  // byte offset of row n0 in the scales
+  const uintptr_t s_first = reinterpret_cast<uintptr_t>(scales) + (uintptr_t)srun;
+  const uint32_t* s_al = reinterpret_cast<const uint32_t*>(s_first & ~(uintptr_t)3);  // wave-uniform
+  const int s_mis = (int)(s_first & 3);
+  const int nchunk = (G + kScGroups - 1) / kScGroups;
+  const int nrows = min(NT, O - n0);
+  uint32_t sreg[kScSlots];
+  auto sc_load = [&](int c) {
+    const int len = min(kScGroups, G - kScGroups * c);
+#pragma unroll
+    for (int i = 0; i < kScSlots; i++) {
+      const int q = tid + 256 * i, r = (q * 205) >> 10, k = q - r * kScPitch;  // q / 5 for q < 1020
+      const int a = s_mis + r * G + kScGroups * c;  // byte offset from s_al
+      sreg[i] = 0u;
+      if (r < nrows && 4 * k < (a & 3) + len) sreg[i] = s_al[(a >> 2) + k];
+    }
+  };
+  auto sc_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < kScSlots; i++) {
+      const int q = tid + 256 * i;
+      if (q < NT * kScPitch) Sc[q] = sreg[i];  // rows past nrows get zeros (never read for a product)
+    }
+  };
+  // this lane's two weight rows: first byte offset of their chunk rows in Sc
+  int s_row[2];
+#pragma unroll
+  for (int nj = 0; nj < 2; nj++) {
+    const int nl = 64 * wn + 32 * nj + lm;
+    s_row[nj] = 4 * kScPitch * nl + ((s_mis + nl * G) & 3);
+  }
+  const uint8_t* scb = reinterpret_cast<const uint8_t*>(Sc);
 
   u32x4 ra[4], rb;
-  uint32_t rs;
   auto gload = [&](int st) {
     const int g0 = 2 * st;
-    const bool ag = g0 + ((tid & 7) >> 2) < G;
+    // past G: the sign bit of G - 1 - group moves the offset past the resource
+    const uint32_t past = (uint32_t)(G - 1 - (g0 + ((tid & 7) >> 2))) >> 31 << 31;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      ra[i] = u32x4{0u, 0u, 0u, 0u};
-      if (aok[i] && ag) ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + 64 * (int64_t)st);
-    }
-    const bool bg = g0 + (tid & 1) < G;
-    rb = u32x4{0u, 0u, 0u, 0u};
-    rs = 127;
-    if (bok && bg) {
-      rb = *reinterpret_cast<const u32x4*>(brow + (int64_t)g0 * 16);
-      rs = srow[g0];
-    }
+    for (int i = 0; i < 4; i++)
+      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((a_off[i] + 128u * st) | past), 0, 0));
+    const uint32_t bpast = (uint32_t)(G - 1 - (g0 + (tid & 1))) >> 31 << 31;
+    rb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((b_off + 32u * st) | bpast), 0, 0));
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; i++)
       *reinterpret_cast<u32x4*>(&As[buf][((tid >> 3) + 32 * i) * A_LD + (tid & 7) * 8]) = ra[i];
     *reinterpret_cast<u32x4*>(&Bs[buf][(tid >> 1) * B_LD + (tid & 1) * 16]) = rb;
-    Ss[buf][(tid >> 1) * 2 + (tid & 1)] = (uint8_t)rs;
   };
 
   f32x16 acc[2][2];
@@ -104,46 +141,58 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __res
 
   const int nst = (G + 1) / 2;
   gload(0);
+  sc_load(0);
   sstore(0);
+  sc_store();
   __syncthreads();
   for (int st = 0; st < nst; st++) {
     const int buf = st & 1;
+    const int sst = st % kScStages;  // stage within the scale chunk
     if (st + 1 < nst) gload(st + 1);
-    uint32_t bw[2][4][4];
+    if (sst == 0 && st / kScStages + 1 < nchunk) sc_load(st / kScStages + 1);
+    u32x4 wv[2];
+    float sc[2];
+    bool s255[2];
 #pragma unroll
     for (int nj = 0; nj < 2; nj++) {
       const int nl = 64 * wn + 32 * nj + lm;
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(&Bs[buf][nl * B_LD + lq * 16]);
-      const uint32_t s = Ss[buf][nl * 2 + lq];
-      if (__builtin_expect(__ballot(s == 255) != 0, 0)) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          if (s == 255) decode8_bf16_slow(wv[j], s, bw[nj][j]);
-          else decode8_bf16_fast(wv[j], e8m0_operand(s), bw[nj][j]);
-        }
-      } else {
-        const float sc = e8m0_operand(s);
-#pragma unroll
-        for (int j = 0; j < 4; j++) decode8_bf16_fast(wv[j], sc, bw[nj][j]);
-      }
+      wv[nj] = *reinterpret_cast<const u32x4*>(&Bs[buf][nl * B_LD + lq * 16]);
+      // a group past G (odd G, last stage) has zero weights; its byte is unused
+      const uint32_t sb = scb[s_row[nj] + 2 * sst + lq];
+      sc[nj] = e8m0_operand(sb);
+      s255[nj] = sb == 255;
     }
+    // a scale byte of 255 anywhere in the wave (never on ordinary data): those lanes decode exactly
+    const bool slow = __ballot(s255[0] | s255[1]) != 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
+      bf16x8 bw[2];
+#pragma unroll
+      for (int nj = 0; nj < 2; nj++) {
+        bw[nj] = decode8_bf16x8(wv[nj][j], sc[nj]);
+        if (__builtin_expect(slow, 0) && s255[nj]) {
+          uint32_t t[4];
+          decode8_bf16_slow(wv[nj][j], 255u, t);
+          bw[nj] = __builtin_bit_cast(bf16x8, (u32x4{t[0], t[1], t[2], t[3]}));
+        }
+      }
 #pragma unroll
       for (int mi = 0; mi < 2; mi++) {
         if (64 * wm + 32 * mi >= tl.mlen) continue;  // a 32-row sub-tile past the segment
         const int ml = 64 * wm + 32 * mi + lm;
         const u32x4 av = *reinterpret_cast<const u32x4*>(&As[buf][ml * A_LD + lq * 32 + j * 8]);
 #pragma unroll
-        for (int nj = 0; nj < 2; nj++) {
-          const u32x4 bv = {bw[nj][j][0], bw[nj][j][1], bw[nj][j][2], bw[nj][j][3]};
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                __builtin_bit_cast(bf16x8, bv), acc[mi][nj], 0, 0, 0);
-        }
+        for (int nj = 0; nj < 2; nj++)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bw[nj], acc[mi][nj],
+                                                                0, 0, 0);
       }
     }
     if (st + 1 < nst) sstore(buf ^ 1);
     __syncthreads();
+    if (sst == kScStages - 1 && st + 1 < nst) {  // every wave is past the chunk's last stage
+      sc_store();
+      __syncthreads();
+    }
   }
   // D layout of the 32x32 MFMA: element i of lane l is row 8(i/4) + 4(l/32) + i%4, column l%32.
 #pragma unroll
@@ -164,15 +213,21 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __res
 
 }  // namespace
 
+bool gemm_supported(int64_t T, int64_t O, int64_t G) {
+  // 32-bit byte offsets into the activations and into one expert's packed bytes
+  return T * 64 * G < ((int64_t)1 << 31) && O * G * 16 < ((int64_t)1 << 31);
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                             const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
                             int O, int G, hipStream_t stream) {
-  (void)T;
+  if (!gemm_supported(T, O, G)) return hipErrorInvalidValue;
   const int n_ntiles = (O + NT - 1) / NT;
   const int64_t nblk = max_tiles * n_ntiles;
   if (nblk <= 0) return hipSuccess;
+  const uint32_t x_bytes = (uint32_t)((int64_t)T * 64 * G);
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, x, packed, scales, perm, tiles,
-                     n_tiles, part, K, O, G, n_ntiles);
+                     n_tiles, part, K, O, G, n_ntiles, x_bytes);
   return hipGetLastError();
 }
 

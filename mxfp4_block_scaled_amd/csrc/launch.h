@@ -77,6 +77,9 @@ hipError_t launch_gemv_rows(const void* x, const uint8_t* packed, const uint8_t*
                             int32_t* n_invalid, int chunk_index, hipStream_t stream);
 
 // ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
+// The grouped GEMM addresses the activations and one expert's packed bytes
+// with 32-bit byte offsets: T * 32G * 2 < 2^31 and O * G * 16 < 2^31.
+bool gemm_supported(int64_t T, int64_t O, int64_t G);
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                             const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
                             int O, int G, hipStream_t stream);

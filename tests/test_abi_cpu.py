@@ -79,15 +79,24 @@ def test_path_selection():
     with pytest.raises(_abi.Mxfp4Error) as e:
         _abi.select_path(4, 4, 32, 2, 2, bf16, _abi.FLAG_FORCE_GEMM | _abi.FLAG_FORCE_GEMV)
     assert e.value.status == _abi.ERR_INVALID_ARG
-    # one expert of 2^31 packed bytes or more: beyond the decode-shaped
-    # kernels' 32-bit buffer offsets (both of them)
+    # one expert of 2^31 packed bytes or more: beyond every kernel's 32-bit
+    # buffer offsets
     O, G = 1 << 16, 1 << 11
     for flags in (0, _abi.FLAG_GEMV_MFMA):
         assert _abi.select_path(1, 2, O, G - 1, 1, bf16, flags) == _abi.PATH_GEMV
-        assert _abi.select_path(1, 2, O, G, 1, bf16, flags) == _abi.PATH_GEMM
-        with pytest.raises(_abi.Mxfp4Error) as e:
-            _abi.select_path(1, 2, O, G, 1, f32, flags)
-        assert e.value.status == _abi.ERR_UNSUPPORTED
+        assert _abi.select_path(1, 2, O, G - 1, 1, bf16, flags | _abi.FLAG_FORCE_GEMM) == _abi.PATH_GEMM
+        for dt in (f32, bf16):
+            with pytest.raises(_abi.Mxfp4Error) as e:
+                _abi.select_path(1, 2, O, G, 1, dt, flags)
+            assert e.value.status == _abi.ERR_UNSUPPORTED
+    # activations of 2^31 bytes or more: beyond the grouped GEMM's offsets;
+    # the decode-shaped path takes them in token chunks
+    T, G = 1 << 16, 1 << 9
+    assert _abi.select_path(T - 1, 8, 64, G, 1, bf16) == _abi.PATH_GEMM
+    assert _abi.select_path(T, 8, 64, G, 1, bf16) == _abi.PATH_GEMV
+    with pytest.raises(_abi.Mxfp4Error) as e:
+        _abi.select_path(T, 8, 64, G, 1, bf16, _abi.FLAG_FORCE_GEMM)
+    assert e.value.status == _abi.ERR_UNSUPPORTED
 
 
 def _ex(x=A, packed=B, scales=C + 0x10000, sel=C + 0x20000, p=C + 0x30000, shared=C + 0x40000, y=C + 0x50000,
