@@ -298,6 +298,9 @@ EDGE_CASES = [
     (9, 64, 2, 5, 257, True),    # most experts empty
     (40, 3, 2, 4, 64, False),    # many rows per expert, duplicates
     (33, 200, 8, 3, 96, True),   # P spans a ragged 128-row M-tile
+    (20, 4, 2, 33, 40, True),    # odd G over three 16-group scale chunks
+    (17, 3, 3, 47, 129, True),   # odd G, ragged N-tile, scale rows at every byte offset
+    (6, 5, 2, 32, 36, True),     # G an exact multiple of the scale chunk
 ]
 
 
@@ -352,6 +355,29 @@ def test_empty_batch():
 
 
 # ------------------------------------------------------------------ invariants
+
+@pytest.mark.parametrize("flags", [_abi.FLAG_FORCE_GEMM, _abi.FLAG_FORCE_GEMV, _abi.FLAG_FORCE_GEMV | _abi.FLAG_GEMV_MFMA])
+def test_largest_scales_with_bf16_weights_in_range(flags):
+    # scale bytes 253..255 with codes small enough that every decoded weight
+    # is a finite bf16 value (|E2M1| <= 1.5 at 253/254, <= 0.5 at 255): the
+    # grouped GEMM's bf16 weights are then exact too, and its scale-255 path
+    # (the slow exact decode) is checked against the float64 oracle
+    T, E, K, G, O = 20, 3, 2, 37, 70
+    x, packed, scales, sel, p, shared = random_case(91, T, E, K, G, O, "bf16")
+    x = workloads.round_to_bf16((x * np.float32(2.0 ** -110)).astype(np.float32))
+    scales = np.random.default_rng(92).integers(253, 256, scales.shape).astype(np.uint8)
+    small = np.array([0, 1, 8, 9], np.uint8)        # 0, 0.5, -0, -0.5
+    mid = np.array([0, 1, 2, 3, 8, 9, 10, 11], np.uint8)  # |E2M1| <= 1.5
+    rng = np.random.default_rng(93)
+    lo255, hi255 = rng.choice(small, packed.shape), rng.choice(small, packed.shape)
+    lo, hi = rng.choice(mid, packed.shape), rng.choice(mid, packed.shape)
+    is255 = (scales == 255)[..., None]
+    packed = np.where(is255, lo255 | (hi255 << 4), lo | (hi << 4)).astype(np.uint8)
+    d = upload(x, packed, scales, sel, p, shared, "bf16")
+    ref = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    assert np.all(np.isfinite(ref))
+    assert_close(host64(run(d, flags=flags)), ref, "bf16", f"scales 253..255, finite weights, flags={flags}")
+
 
 @pytest.mark.parametrize("dtype,flags", [("fp32", 0), ("fp32", _abi.FLAG_GEMV_MFMA), ("bf16", _abi.FLAG_FORCE_GEMV),
                                          ("bf16", _abi.FLAG_FORCE_GEMV | _abi.FLAG_GEMV_MFMA),
