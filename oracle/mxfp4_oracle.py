@@ -45,6 +45,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * an expert index outside [0, E) violates a stated precondition; the oracle
   raises ValueError.
 
+The SwiGLU expert block (``expert_swiglu``, at the end of this module)
+composes two such projections per routed pair with silu(gate) * up between
+them (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
+Experts", section 1; gate and up stacked along the output rows, gate first).
+
 Parity status: every function here is pinned by tests against values the
 pages print, closed forms, invariants and a brute-force scalar version.
 """
@@ -260,5 +265,126 @@ def expert_linear_scalar(x, packed, scales, sel, p, shared) -> list:
                         dot += E2M1_VALUES[high] * factor * float(x[t][32 * g + 2 * j + 1])
                 acc += float(p[t][k]) * dot
             row.append(acc)
+        out.append(row)
+    return out
+
+
+# ------------------------------------------------------- the SwiGLU expert
+#
+# Page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact Experts",
+# section "1. The shared building blocks: routers and the SwiGLU expert
+# shape": every routed expert is a SwiGLU - gate and up projections of the
+# token, silu(gate) times up elementwise, then the down projection - and the
+# routed outputs are weighted by the mixture weights and accumulated. The exo
+# pull request page ("Summary") stacks each expert's gate and up matrices
+# along their output rows; the plainest reading, taken here, is gate rows
+# first: rows [0, F) of the stacked matrix are the gate, rows [F, 2F) the up
+# projection. Both matrices are MXFP4 like the routed linear's. The oracle
+# keeps the intermediate exact in float64.
+
+def silu(v):
+    """silu(v) = v * sigmoid(v) = v / (1 + e^-v), float64 (0 for v -> -inf)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def _swiglu_shapes(gu_packed, dn_packed, x, shared):
+    two_f = np.asarray(gu_packed[0]).shape[0]
+    if two_f % 2 != 0:
+        raise ValueError("the stacked gate/up matrix needs an even row count")
+    F = two_f // 2
+    if np.asarray(dn_packed[0]).shape[1] * GROUP_VALUES != F:
+        raise ValueError("the down projection's input width must be F")
+    if np.asarray(gu_packed[0]).shape[1] * GROUP_VALUES != np.asarray(x).shape[1]:
+        raise ValueError("the gate/up input width must match x")
+    if np.asarray(dn_packed[0]).shape[0] != np.asarray(shared).shape[1]:
+        raise ValueError("the down projection's output width must match shared")
+    return F
+
+
+def swiglu_hidden(x_rows, gu_packed_e, gu_scales_e):
+    """h = silu(gate x) * (up x) for the token rows x_rows (n, I) of one
+    expert: (n, F) float64."""
+    W = decode_expert(gu_packed_e, gu_scales_e)  # (2F, I)
+    F = W.shape[0] // 2
+    gu = np.asarray(x_rows, dtype=np.float64) @ W.T
+    return silu(gu[:, :F]) * gu[:, F:]
+
+
+def expert_swiglu(x, gu_packed, gu_scales, dn_packed, dn_scales, sel, p, shared) -> np.ndarray:
+    """y_t = shared_t + sum_k p[t,k] * D_e (silu(Gate_e x_t) * (Up_e x_t)),
+    e = sel[t,k], in float64. gu_packed (E, 2F, G, 16) / gu_scales (E, 2F, G)
+    hold gate then up; dn_packed (E, O, F/32, 16) / dn_scales (E, O, F/32)
+    the down projection. Returns a new (T, O) float64 array."""
+    E = len(gu_packed)
+    x, sel, p, shared = _check(x, sel, p, shared, E)
+    _swiglu_shapes(gu_packed, dn_packed, x, shared)
+    T, K = sel.shape
+    O = shared.shape[1]
+    x64 = x.astype(np.float64)
+    p64 = p.astype(np.float64)
+    y = shared.astype(np.float64, copy=True)
+    contrib = np.zeros((T, K, O), dtype=np.float64)
+    for e in np.unique(sel):
+        ts, ks = np.nonzero(sel == e)
+        h = swiglu_hidden(x64[ts], gu_packed[e], gu_scales[e])
+        D = decode_expert(dn_packed[e], dn_scales[e])  # (O, F)
+        contrib[ts, ks, :] = h @ D.T
+    routed = np.zeros((T, O), dtype=np.float64)
+    for k in range(K):
+        routed += p64[:, k:k + 1] * contrib[:, k, :]
+    return y + routed
+
+
+def expert_swiglu_rows(x, gu_packed, gu_scales, dn_packed, dn_scales, sel, p, shared, rows) -> np.ndarray:
+    """``expert_swiglu`` restricted to output coordinates ``rows``: every
+    pair's full hidden vector, but only those rows of the down projections."""
+    E = len(gu_packed)
+    x, sel, p, shared = _check(x, sel, p, shared, E)
+    rows = np.asarray(rows, dtype=np.int64)
+    T, K = sel.shape
+    x64 = x.astype(np.float64)
+    p64 = p.astype(np.float64)
+    y = shared[:, rows].astype(np.float64)
+    contrib = np.zeros((T, K, rows.size), dtype=np.float64)
+    for e in np.unique(sel):
+        ts, ks = np.nonzero(sel == e)
+        h = swiglu_hidden(x64[ts], gu_packed[e], gu_scales[e])
+        D = decode_rows(np.asarray(dn_packed[e])[rows], np.asarray(dn_scales[e])[rows])
+        contrib[ts, ks, :] = h @ D.T
+    routed = np.zeros((T, rows.size), dtype=np.float64)
+    for k in range(K):
+        routed += p64[:, k:k + 1] * contrib[:, k, :]
+    return y + routed
+
+
+def expert_swiglu_scalar(x, gu_packed, gu_scales, dn_packed, dn_scales, sel, p, shared) -> list:
+    """Brute force with plain Python numbers and loops (tiny shapes only)."""
+    import math
+
+    def weight(packed, scales, e, o, i):
+        byte = int(packed[e][o][i // 32][(i % 32) // 2])
+        code = byte % 16 if i % 2 == 0 else byte // 16
+        return E2M1_VALUES[code] * 2.0 ** (int(scales[e][o][i // 32]) - SCALE_BIAS)
+
+    T = len(x)
+    K = len(sel[0]) if T else 0
+    O = len(shared[0]) if T else 0
+    I = len(x[0]) if T else 0
+    F = len(gu_packed[0]) // 2
+    out = []
+    for t in range(T):
+        row = [float(shared[t][o]) for o in range(O)]
+        for k in range(K):
+            e = int(sel[t][k])
+            h = []
+            for f in range(F):
+                g = sum(weight(gu_packed, gu_scales, e, f, i) * float(x[t][i]) for i in range(I))
+                u = sum(weight(gu_packed, gu_scales, e, F + f, i) * float(x[t][i]) for i in range(I))
+                h.append(g / (1.0 + math.exp(-g)) * u)
+            for o in range(O):
+                d = sum(weight(dn_packed, dn_scales, e, o, f) * h[f] for f in range(F))
+                row[o] += float(p[t][k]) * d
         out.append(row)
     return out

@@ -395,3 +395,126 @@ def test_planted_combine_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as mp:  # square case: I = O = 32, transposed operand
         mp.setattr(om, "decode_expert", lambda pk, sc: orig(pk, sc).T)
         assert not np.allclose(oracle.expert_linear(x, packed, scales, sel, p, shared), ys)
+
+
+# ------------------------------------------------------- the SwiGLU expert
+
+def _swiglu_case(seed, T, E, K, G, F, O, scale_lo=118, scale_hi=126, distinct=True):
+    """Random gate/up (E, 2F, G, 16) and down (E, O, F/32, 16) experts."""
+    rng = _rng(seed)
+    x, _, _, sel, p, shared = _random_case(seed, T, E, K, G, O, distinct=distinct)
+    gu_p = rng.integers(0, 256, (E, 2 * F, G, 16), dtype=np.uint8)
+    gu_s = rng.integers(scale_lo, scale_hi + 1, (E, 2 * F, G), dtype=np.uint8)
+    dn_p = rng.integers(0, 256, (E, O, F // 32, 16), dtype=np.uint8)
+    dn_s = rng.integers(scale_lo, scale_hi + 1, (E, O, F // 32), dtype=np.uint8)
+    return x, gu_p, gu_s, dn_p, dn_s, sel, p, shared
+
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    v = np.linspace(-30, 30, 121)
+    # silu(-v) = silu(v) - v, and silu(v) -> v, -> 0 at the ends
+    np.testing.assert_allclose(oracle.silu(-v), oracle.silu(v) - v, rtol=0, atol=1e-12)
+    assert oracle.silu(60.0) == pytest.approx(60.0, rel=1e-15)
+    assert abs(oracle.silu(-60.0)) < 1e-20
+    assert oracle.silu(-1e6) == 0.0
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_swiglu_brute_force_matches(seed):
+    T, E, K, G, F, O = 3, 3, 2, 1, 32, 5
+    args = _swiglu_case(seed, T, E, K, G, F, O, distinct=seed == 0)
+    ys = np.array(oracle.expert_swiglu_scalar(*[a.tolist() for a in args]))
+    y = oracle.expert_swiglu(*args)
+    np.testing.assert_allclose(y, ys, rtol=1e-11, atol=1e-9)
+
+
+def test_swiglu_closed_form_pins_gate_then_up():
+    # x = ones (I = 32); gate rows all 0.5 -> g = 16; up rows all -1 -> u = -32;
+    # down rows all 1 -> every output is F * silu(16) * (-32). With gate and
+    # up swapped it would be F * silu(-32) * 16, which is tiny.
+    F, O = 32, 3
+    x = np.ones((1, 32), np.float32)
+    gu_p = np.zeros((1, 2 * F, 1, 16), np.uint8)
+    gu_p[0, :F] = 0x11       # code 1 = 0.5 in both nibbles
+    gu_p[0, F:] = 0xAA       # code 10 = -1
+    gu_s = np.full((1, 2 * F, 1), 127, np.uint8)
+    dn_p = np.full((1, O, 1, 16), 0x22, np.uint8)  # code 2 = 1
+    dn_s = np.full((1, O, 1), 127, np.uint8)
+    sel = np.zeros((1, 1), np.int32)
+    p = np.ones((1, 1), np.float32)
+    shared = np.zeros((1, O), np.float32)
+    y = oracle.expert_swiglu(x, gu_p, gu_s, dn_p, dn_s, sel, p, shared)
+    want = F * (16.0 / (1.0 + math.exp(-16.0))) * -32.0
+    np.testing.assert_allclose(y, np.full((1, O), want), rtol=1e-14)
+
+
+def test_swiglu_zero_gate_or_up_gives_shared():
+    args = list(_swiglu_case(3, 4, 5, 2, 2, 64, 7))
+    x, gu_p, gu_s, dn_p, dn_s, sel, p, shared = args
+    for half in (slice(0, 64), slice(64, 128)):
+        z = gu_p.copy()
+        z[:, half] = 0
+        y = oracle.expert_swiglu(x, z, gu_s, dn_p, dn_s, sel, p, shared)
+        assert np.array_equal(y, shared.astype(np.float64))
+
+
+def test_swiglu_scale_shifts_double_the_routed_part():
+    x, gu_p, gu_s, dn_p, dn_s, sel, p, shared = _swiglu_case(4, 4, 5, 2, 2, 64, 7)
+    base = oracle.expert_swiglu(x, gu_p, gu_s, dn_p, dn_s, sel, p, shared) - shared
+    up_s = gu_s.copy()
+    up_s[:, 64:] += 1  # up doubles: h doubles (h is linear in up)
+    y_up = oracle.expert_swiglu(x, gu_p, up_s, dn_p, dn_s, sel, p, shared) - shared
+    np.testing.assert_allclose(y_up, 2 * base, rtol=1e-12, atol=1e-12)
+    y_dn = oracle.expert_swiglu(x, gu_p, gu_s, dn_p, dn_s + np.uint8(1), sel, p, shared) - shared
+    np.testing.assert_allclose(y_dn, 2 * base, rtol=1e-12, atol=1e-12)
+    # doubling the gate does not double the result (silu is not linear)
+    g_s = gu_s.copy()
+    g_s[:, :64] += 1
+    y_g = oracle.expert_swiglu(x, gu_p, g_s, dn_p, dn_s, sel, p, shared) - shared
+    assert not np.allclose(y_g, 2 * base, rtol=1e-3)
+
+
+def test_swiglu_is_the_composition_of_two_expert_linears():
+    # gate, up and down each computed by the (pinned) routed linear with one
+    # slot per pair and unit weights, then combined by hand
+    x, gu_p, gu_s, dn_p, dn_s, sel, p, shared = _swiglu_case(5, 3, 4, 2, 2, 32, 6)
+    T, K = sel.shape
+    y = shared.astype(np.float64).copy()
+    for k in range(K):
+        one = np.ones((T, 1), np.float32)
+        s1 = sel[:, k:k + 1]
+        g = oracle.expert_linear(x, gu_p[:, :32], gu_s[:, :32], s1, one, np.zeros((T, 32), np.float32))
+        u = oracle.expert_linear(x, gu_p[:, 32:], gu_s[:, 32:], s1, one, np.zeros((T, 32), np.float32))
+        h = g / (1.0 + np.exp(-g)) * u
+        d = oracle.expert_linear(h, dn_p, dn_s, s1, one, np.zeros((T, 6), np.float32))
+        y += p[:, k:k + 1].astype(np.float64) * d
+    np.testing.assert_allclose(oracle.expert_swiglu(x, gu_p, gu_s, dn_p, dn_s, sel, p, shared), y,
+                               rtol=1e-12, atol=1e-9)
+
+
+def test_swiglu_rows_variant_matches_full():
+    args = _swiglu_case(6, 5, 6, 3, 2, 64, 40)
+    full = oracle.expert_swiglu(*args)
+    rows = np.array([0, 7, 8, 39])
+    np.testing.assert_allclose(oracle.expert_swiglu_rows(*args, rows), full[:, rows], rtol=1e-13, atol=1e-12)
+
+
+def test_swiglu_planted_mistakes_are_caught(monkeypatch):
+    args = _swiglu_case(7, 3, 3, 2, 1, 32, 4)
+    ys = np.array(oracle.expert_swiglu_scalar(*[a.tolist() for a in args]))
+    np.testing.assert_allclose(oracle.expert_swiglu(*args), ys, rtol=1e-11, atol=1e-9)
+    orig_silu, orig_hidden = om.silu, om.swiglu_hidden
+    mistakes = {
+        "sigmoid instead of silu": lambda mp: mp.setattr(om, "silu", lambda v: 1.0 / (1.0 + np.exp(-np.asarray(v)))),
+        "gate and up swapped": lambda mp: mp.setattr(
+            om, "swiglu_hidden", lambda xr, pk, sc: orig_hidden(xr, np.roll(np.asarray(pk), 32, axis=0),
+                                                                np.roll(np.asarray(sc), 32, axis=0))),
+        "silu dropped (identity)": lambda mp: mp.setattr(
+            om, "silu", lambda v: orig_silu(v) * 0 + np.asarray(v, dtype=np.float64)),
+    }
+    for name, plant in mistakes.items():
+        with monkeypatch.context() as mp:
+            plant(mp)
+            assert not np.allclose(oracle.expert_swiglu(*args), ys, rtol=1e-6), f"planted mistake not caught: {name}"
