@@ -199,6 +199,37 @@ int mxfp4_moe_gemm_stage(const void* x, const uint8_t* packed, const uint8_t* sc
                          int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * mxfp4_moe_swiglu_ex - the routed SwiGLU expert block, bf16 x, shared, y
+ * (raw 16-bit patterns), p fp32:
+ *   y[t] = shared[t] + sum_k p[t,k] * Down_e(silu(Gate_e x[t]) * (Up_e x[t])),  e = sel[t,k],
+ * silu(v) = v / (1 + e^-v) (page "MoE Expert Kernels: Grouped Prefill and
+ * Mixed-Quant Compact Experts", section 1: every routed expert is a SwiGLU
+ * whose routing-weighted outputs are summed; the exo pull request page
+ * stacks gate and up along the output rows, read here as gate first).
+ *   gu_packed (E, 2F, G, 16), gu_scales (E, 2F, G): rows [0, F) gate, rows
+ *     [F, 2F) up, over I = 32G inputs (x is (T, I));
+ *   dn_packed (E, O, F/32, 16), dn_scales (E, O, F/32): the down projection;
+ *   shared, y: (T, O).
+ * F must be a positive multiple of 32. Each pair's intermediate silu(gate) *
+ * up is rounded to bf16 (the down projection's MFMA operand); the
+ * projections accumulate in fp32 and the K slots are summed in order in fp32,
+ * as in mxfp4_moe_linear_ex. Work: bucketing, a grouped GEMM with the SwiGLU
+ * in its epilogue, a grouped GEMM of the down projection over the sorted
+ * rows, the combine. Caller-owned device workspace of
+ * mxfp4_moe_swiglu_workspace_size bytes (256-byte aligned); flags 0 or
+ * MXFP4_FLAG_CHECK. Allocates nothing; may be captured in a graph. Errors as
+ * mxfp4_moe_linear_ex; MXFP4_ERR_UNSUPPORTED when T*I*2, T*K*F*2, 2F*G*16 or
+ * O*F/2 bytes reach 2^31. Same aliasing rule: y may be shared, nothing else.
+ */
+int mxfp4_moe_swiglu_workspace_size(int64_t T, int64_t E, int64_t F, int64_t G, int64_t O, int64_t K,
+                                    size_t* bytes);
+int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales,
+                        const uint8_t* dn_packed, const uint8_t* dn_scales, const int32_t* sel,
+                        const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E,
+                        int64_t F, int64_t G, int64_t O, int64_t K, uint32_t flags, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* mxfp4_status_string(int status);
 

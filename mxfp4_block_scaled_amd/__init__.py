@@ -21,12 +21,12 @@ from . import _abi
 from ._abi import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, FLAG_CHECK, FLAG_FORCE_GEMM, FLAG_FORCE_GEMV, FLAG_GEMV_MFMA, FLAG_BUCKET_MULTI_BLOCK,
     FLAG_BUCKET_ONE_BLOCK, PATH_GEMM, PATH_GEMV, Mxfp4Error, bucket_workspace_size, select_path,
-    status_string, workspace_size,
+    status_string, swiglu_workspace_size, workspace_size,
 )
 
 __all__ = [
-    "mxfp4_expert_linear", "moe_linear", "decode_rows", "bucket", "gemm_stage", "workspace_size", "select_path",
-    "Mxfp4Error", "library_path",
+    "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
+    "swiglu_workspace_size", "select_path", "Mxfp4Error", "library_path",
 ]
 
 _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
@@ -104,6 +104,59 @@ def moe_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, sel:
             _ptr(x), _ptr(packed), _ptr(scales), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y),
             T, E, O, G, K, dt, flags, _ptr(workspace), workspace.numel(), _stream(dev))
     _abi.check(st, "mxfp4_moe_linear_ex")
+    return y
+
+
+def moe_swiglu(x: torch.Tensor, gu_packed: torch.Tensor, gu_scales: torch.Tensor, dn_packed: torch.Tensor,
+               dn_scales: torch.Tensor, sel: torch.Tensor, p: torch.Tensor, shared: torch.Tensor, *,
+               out: torch.Tensor | None = None, flags: int = 0,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The routed SwiGLU expert block on the current HIP stream (bf16):
+    y = shared + sum_k p[:,k] * Down_e(silu(Gate_e x) * Up_e x), e = sel[:,k].
+
+    x [T, 32G] bf16; gu_packed [E, 2F, G, 16] / gu_scales [E, 2F, G] uint8
+    (gate rows first, then up); dn_packed [E, O, F/32, 16] / dn_scales
+    [E, O, F/32] uint8; sel [T, K] int32; p [T, K] fp32; shared [T, O] bf16.
+    Returns ``out`` (allocated when not given; it may be ``shared``).
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be on a HIP device")
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(gu_packed, "gu_packed", torch.uint8, 4, dev)
+    _need(gu_scales, "gu_scales", torch.uint8, 3, dev)
+    _need(dn_packed, "dn_packed", torch.uint8, 4, dev)
+    _need(dn_scales, "dn_scales", torch.uint8, 3, dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    _need(shared, "shared", torch.bfloat16, 2, dev)
+    T, I = x.shape
+    E, F2, G, B = gu_packed.shape
+    K = sel.shape[1]
+    O = dn_packed.shape[1]
+    if B != 16 or I != 32 * G or F2 % 2 != 0:
+        raise ValueError(f"gu_packed must be [E, 2F, G, 16] with 32G == x.shape[1]; got {tuple(gu_packed.shape)}")
+    F = F2 // 2
+    if tuple(gu_scales.shape) != (E, F2, G):
+        raise ValueError("gu_scales must have gu_packed's shape without its last axis")
+    if F % 32 != 0 or tuple(dn_packed.shape) != (E, O, F // 32, 16) or tuple(dn_scales.shape) != (E, O, F // 32):
+        raise ValueError(f"dn_packed must be [E, O, F/32, 16] with F = {F} a multiple of 32, dn_scales [E, O, F/32]")
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K) or tuple(shared.shape) != (T, O):
+        raise ValueError("sel and p must be [T, K] and shared [T, O]")
+    y = torch.empty_like(shared) if out is None else out
+    _need(y, "out", torch.bfloat16, 2, dev)
+    if tuple(y.shape) != (T, O):
+        raise ValueError("out must be [T, O]")
+    need = _abi.swiglu_workspace_size(T, E, F, G, O, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev:
+        raise ValueError("workspace must be a uint8 tensor on x's device")
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_swiglu_ex(
+            _ptr(x), _ptr(gu_packed), _ptr(gu_scales), _ptr(dn_packed), _ptr(dn_scales), _ptr(sel), _ptr(p),
+            _ptr(shared), _ptr(y), T, E, F, G, O, K, flags, _ptr(workspace), workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_swiglu_ex")
     return y
 
 

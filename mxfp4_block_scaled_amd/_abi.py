@@ -53,6 +53,8 @@ SIGNATURES = {
     "mxfp4_moe_bucket": (_int, [_vp] + [_i64] * 3 + [_vp] * 5 + [_u32, _vp, _sz, _vp]),
     "mxfp4_decode_rows": (_int, [_vp] * 2 + [_i64] * 6 + [_int, _vp, _vp]),
     "mxfp4_moe_gemm_stage": (_int, [_vp] * 3 + [_i64] * 5 + [_vp, _sz, _vp]),
+    "mxfp4_moe_swiglu_workspace_size": (_int, [_i64] * 6 + [ctypes.POINTER(_sz)]),
+    "mxfp4_moe_swiglu_ex": (_int, [_vp] * 9 + [_i64] * 6 + [_u32, _vp, _sz, _vp]),
     "mxfp4_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -92,6 +94,12 @@ def check(status: int, what: str = "") -> None:
 def workspace_size(T, E, O, G, K, dtype, flags=0) -> int:
     out = _sz(0)
     check(lib().mxfp4_moe_workspace_size(T, E, O, G, K, dtype, flags, ctypes.byref(out)), "workspace_size")
+    return out.value
+
+
+def swiglu_workspace_size(T, E, F, G, O, K) -> int:
+    out = _sz(0)
+    check(lib().mxfp4_moe_swiglu_workspace_size(T, E, F, G, O, K, ctypes.byref(out)), "swiglu_workspace_size")
     return out.value
 
 

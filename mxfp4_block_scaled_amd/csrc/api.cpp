@@ -229,9 +229,132 @@ int linear_alloc(const void* x, const uint8_t* packed, const uint8_t* scales, co
   return st;
 }
 
+// ---- SwiGLU expert block: two grouped GEMMs over one bucketing.
+struct SwDims {
+  Dims gu, dn;  // gate/up: (T, E, 2F, G, K); down: (T, E, O, F/32, K)
+  int64_t F;
+};
+
+int check_swiglu_dims(int64_t T, int64_t E, int64_t F, int64_t G, int64_t O, int64_t K, SwDims* d) {
+  if (F < 32 || F % 32 != 0 || F > (int64_t(1) << 29)) return MXFP4_ERR_INVALID_ARG;
+  int st = check_dims(T, E, 2 * F, G, K, &d->gu);
+  if (st != MXFP4_OK) return st;
+  st = check_dims(T, E, O, F / 32, K, &d->dn);
+  if (st != MXFP4_OK) return st;
+  int64_t t = 0;
+  if (!mul_ok(d->gu.P, F, &t) || !mul_ok(t, 2, &t)) return MXFP4_ERR_INVALID_ARG;
+  d->F = F;
+  return MXFP4_OK;
+}
+
+// The down stage's GEMM layout (bucketing arrays, tiles, fp32 part [P, O]),
+// then h [P, F] bf16.
+struct SwLayout {
+  Layout L;
+  size_t h, total;
+};
+
+SwLayout swiglu_layout(const SwDims& d) {
+  SwLayout S;
+  S.L = layout(d.dn, MXFP4_PATH_GEMM);
+  S.h = S.L.total;
+  S.total = align_up(S.h + (size_t)d.dn.P * d.F * 2);
+  return S;
+}
+
+bool swiglu_supported(const SwDims& d) {
+  return gemm_supported(d.gu.T, d.gu.O, d.gu.G) && gemm_supported(d.dn.P, d.dn.O, d.dn.G);
+}
+
+int check_swiglu_args(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales, const uint8_t* dn_packed,
+                      const uint8_t* dn_scales, const int32_t* sel, const float* p, const uint16_t* shared,
+                      const uint16_t* y, const SwDims& d) {
+  if (d.gu.T == 0) return MXFP4_OK;
+  if (!x || !gu_packed || !gu_scales || !dn_packed || !dn_scales || !sel || !p || !shared || !y)
+    return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(gu_packed, 16) || !aligned(dn_packed, 16) || !aligned(sel, 4) || !aligned(p, 4) ||
+      !aligned(shared, 2) || !aligned(y, 2))
+    return MXFP4_ERR_INVALID_ARG;
+  const Dims& a = d.gu;
+  const Dims& b = d.dn;
+  const size_t ny = (size_t)b.T * b.O * 2;
+  const size_t sizes[8] = {(size_t)a.T * a.I * 2, (size_t)a.E * a.O * a.G * 16, (size_t)a.E * a.O * a.G,
+                           (size_t)b.E * b.O * b.G * 16, (size_t)b.E * b.O * b.G, (size_t)a.P * 4,
+                           (size_t)a.P * 4, ny};
+  const void* ptrs[8] = {x, gu_packed, gu_scales, dn_packed, dn_scales, sel, p, shared};
+  for (int i = 0; i < 8; i++) {
+    if (i == 7 && ptrs[i] == y) continue;  // in place on shared is allowed
+    if (overlap(y, ny, ptrs[i], sizes[i])) return MXFP4_ERR_INVALID_ARG;
+  }
+  return MXFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mxfp4_moe_swiglu_workspace_size(int64_t T, int64_t E, int64_t F, int64_t G, int64_t O, int64_t K,
+                                    size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  SwDims d;
+  int st = check_swiglu_dims(T, E, F, G, O, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (!swiglu_supported(d)) return MXFP4_ERR_UNSUPPORTED;
+  *bytes = (T == 0) ? 0 : swiglu_layout(d).total;
+  return MXFP4_OK;
+}
+
+int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales,
+                        const uint8_t* dn_packed, const uint8_t* dn_scales, const int32_t* sel, const float* p,
+                        const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t F, int64_t G, int64_t O,
+                        int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  SwDims d;
+  int st = check_swiglu_dims(T, E, F, G, O, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~MXFP4_FLAG_CHECK) return MXFP4_ERR_INVALID_ARG;
+  st = check_swiglu_args(x, gu_packed, gu_scales, dn_packed, dn_scales, sel, p, shared, y, d);
+  if (st != MXFP4_OK) return st;
+  if (!swiglu_supported(d)) return MXFP4_ERR_UNSUPPORTED;
+  if (d.gu.T == 0) return MXFP4_OK;
+  const SwLayout S = swiglu_layout(d);
+  if (workspace_bytes < S.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  const Layout& L = S.L;
+  BucketOut b;
+  b.count = reinterpret_cast<int32_t*>(base + L.count);
+  b.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  b.perm = reinterpret_cast<int32_t*>(base + L.perm);
+  b.slot_of_pair = reinterpret_cast<int32_t*>(base + L.slot);
+  b.n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
+  b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
+  b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + S.h);
+  float* part = reinterpret_cast<float*>(base + L.part);
+  const int64_t max_tiles = gemm_max_tiles(d.gu.P, d.gu.E);
+  hipError_t err = launch_bucket_multi(sel, (int)d.gu.P, (int)d.gu.E, reinterpret_cast<int32_t*>(base + L.bcount), b,
+                                       stream);
+  if (err == hipSuccess)
+    err = launch_gemm_swiglu(x, gu_packed, gu_scales, b.perm, b.tiles, b.n_tiles, max_tiles, h, (int)d.gu.T,
+                             (int)d.gu.K, (int)d.F, (int)d.gu.G, stream);
+  if (err == hipSuccess)
+    err = launch_gemm_direct(h, dn_packed, dn_scales, b.tiles, b.n_tiles, max_tiles, part, d.dn.P, (int)d.dn.O,
+                             (int)d.dn.G, stream);
+  if (err == hipSuccess)
+    err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.dn.T, (int)d.dn.K, (int)d.dn.O, MXFP4_DTYPE_BF16,
+                         stream);
+  if (err != hipSuccess) return MXFP4_ERR_HIP;
+  if (flags & MXFP4_FLAG_CHECK) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+    int32_t inv = 0;
+    if (hipMemcpy(&inv, b.n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
+    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
+  }
+  return MXFP4_OK;
+}
+
 
 int mxfp4_moe_linear(const float* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
                      const float* shared, float* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,

@@ -42,19 +42,43 @@ constexpr int kScPitch = 5;                     // dwords per LDS row of a chunk
 constexpr int kScSlots = (kGemmTileN * kScPitch + 255) / 256;
 static_assert(kGemmTileN * kScPitch <= 1020, "q / 5 by multiply-shift");
 
+// What the kernel's rows and columns are:
+//  kGather: A rows are the tokens of the tile's pairs (perm / K), the
+//           128 columns are weight rows n0 .. n0+127, output fp32 part rows.
+//  kSwiGLU: A rows as kGather; the weight matrix stacks gate (rows [0, F))
+//           over up (rows [F, 2F)), and the tile's 128 columns are the gate
+//           and up rows of 64 features f0 .. f0+63 arranged so that each
+//           lane's two 32-column MFMA tiles hold the gate and the up value
+//           of the same feature; the epilogue writes bf16
+//           h[row, f] = silu(gate) * up (page "MoE Expert Kernels: Grouped
+//           Prefill and Mixed-Quant Compact Experts", section 1).
+//  kDirect: A rows are the sorted positions themselves (rows of h), output
+//           fp32 part rows.
+enum GemmMode { kGather = 0, kSwiGLU = 1, kDirect = 2 };
+
+template <int MODE>
 __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __restrict__ x,
                                                            const uint8_t* __restrict__ packed,
                                                            const uint8_t* __restrict__ scales,
                                                            const int32_t* __restrict__ perm,
                                                            const GemmTile* __restrict__ tiles,
-                                                           const int32_t* __restrict__ n_tiles, float* __restrict__ part,
-                                                           int K, int O, int G, int n_ntiles, uint32_t x_bytes) {
+                                                           const int32_t* __restrict__ n_tiles, void* __restrict__ out,
+                                                           int K, int O, int G, int n_ntiles, uint32_t x_bytes, int F) {
   const int ti = blockIdx.x / n_ntiles;
   const int nt = blockIdx.x - ti * n_ntiles;
   if (ti >= n_tiles[0]) return;
   const GemmTile tl = tiles[ti];
-  const int n0 = nt * NT;
-  const int64_t I = 32 * (int64_t)G;
+  const int n0 = nt * NT;           // kGather / kDirect: first weight row of the tile
+  const int f0 = nt * (NT / 2);     // kSwiGLU: first feature of the tile
+  // weight row of LDS row r of the tile (-1: none)
+  auto wrow = [&](int r) -> int {
+    if constexpr (MODE == kSwiGLU) {
+      const int f = f0 + 32 * (r >> 6) + (r & 31);
+      return f < F ? (((r >> 5) & 1) ? F + f : f) : -1;
+    } else {
+      return n0 + r < O ? n0 + r : -1;
+    }
+  };
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * A_LD];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][NT * B_LD];
@@ -72,38 +96,39 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int m = (tid >> 3) + 32 * i;
-    a_off[i] = m < tl.mlen ? (uint32_t)(perm[tl.row0 + m] / K) * (uint32_t)(64 * G) + 16u * (tid & 7) : kOobByte;
+    const int arow = m < tl.mlen ? (MODE == kDirect ? tl.row0 + m : perm[tl.row0 + m] / K) : -1;
+    a_off[i] = arow >= 0 ? (uint32_t)arow * (uint32_t)(64 * G) + 16u * (tid & 7) : kOobByte;
   }
-  // B loader: row tid >> 1, group (tid & 1) of the stage
-  const int bn = n0 + (tid >> 1);
+  // B loader: LDS row tid >> 1, group (tid & 1) of the stage
+  const int bn = wrow(tid >> 1);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(packed + (int64_t)tl.e * O * G * 16), (short)0, O * G * 16, kRsrcFlags);
-  const uint32_t b_off = bn < O ? ((uint32_t)bn * (uint32_t)G + (uint32_t)(tid & 1)) * 16u : kOobByte;
-  // Scale chunk loader: thread slot i covers (row, dword) = ((tid + 256 i) / 5, (tid + 256 i) % 5) of
-  // the chunk; row r's 16 bytes of chunk c start at byte rb_r + 16 c of the scales, read from the
-  // dword boundary below (the first byte sits at offset rb_r & 3 of the LDS row).
-  const int64_t srun = ((int64_t)tl.e * O + n0) * (int64_t)G;  // byte offset of row n0 in the scales
-  const uintptr_t s_first = reinterpret_cast<uintptr_t>(scales) + (uintptr_t)srun;
+  const uint32_t b_off = bn >= 0 ? ((uint32_t)bn * (uint32_t)G + (uint32_t)(tid & 1)) * 16u : kOobByte;
+  // Scale chunk loader: thread slot i covers (LDS row, dword) = ((tid + 256 i) / 5, (tid + 256 i) % 5)
+  // of the chunk; the 16 bytes of chunk c of weight row w start at byte w G + 16 c of the expert's
+  // scales and are read from the dword boundary below (the first byte sits at offset (w G) & 3 of
+  // the LDS row, counted from that boundary).
+  const uintptr_t s_first = reinterpret_cast<uintptr_t>(scales) + (uintptr_t)((int64_t)tl.e * O * G);
   const uint32_t* s_al = reinterpret_cast<const uint32_t*>(s_first & ~(uintptr_t)3);  // wave-uniform
   const int s_mis = (int)(s_first & 3);
   const int nchunk = (G + kScGroups - 1) / kScGroups;
-  const int nrows = min(NT, O - n0);
   uint32_t sreg[kScSlots];
   auto sc_load = [&](int c) {
     const int len = min(kScGroups, G - kScGroups * c);
 #pragma unroll
     for (int i = 0; i < kScSlots; i++) {
       const int q = tid + 256 * i, r = (q * 205) >> 10, k = q - r * kScPitch;  // q / 5 for q < 1020
-      const int a = s_mis + r * G + kScGroups * c;  // byte offset from s_al
+      const int w = q < NT * kScPitch ? wrow(r) : -1;
+      const int a = s_mis + w * G + kScGroups * c;  // byte offset from s_al
       sreg[i] = 0u;
-      if (r < nrows && 4 * k < (a & 3) + len) sreg[i] = s_al[(a >> 2) + k];
+      if (w >= 0 && 4 * k < (a & 3) + len) sreg[i] = s_al[(a >> 2) + k];
     }
   };
   auto sc_store = [&]() {
 #pragma unroll
     for (int i = 0; i < kScSlots; i++) {
       const int q = tid + 256 * i;
-      if (q < NT * kScPitch) Sc[q] = sreg[i];  // rows past nrows get zeros (never read for a product)
+      if (q < NT * kScPitch) Sc[q] = sreg[i];  // rows without a weight row get zeros (their weights are zero)
     }
   };
   // this lane's two weight rows: first byte offset of their chunk rows in Sc
@@ -111,7 +136,8 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
 #pragma unroll
   for (int nj = 0; nj < 2; nj++) {
     const int nl = 64 * wn + 32 * nj + lm;
-    s_row[nj] = 4 * kScPitch * nl + ((s_mis + nl * G) & 3);
+    const int w = wrow(nl);
+    s_row[nj] = 4 * kScPitch * nl + (w >= 0 ? (s_mis + w * G) & 3 : 0);
   }
   const uint8_t* scb = reinterpret_cast<const uint8_t*>(Sc);
 
@@ -195,16 +221,36 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
     }
   }
   // D layout of the 32x32 MFMA: element i of lane l is row 8(i/4) + 4(l/32) + i%4, column l%32.
+  if constexpr (MODE == kSwiGLU) {
+    // acc[mi][0] holds the gate and acc[mi][1] the up value of feature f, at the same places
+    const int f = f0 + 32 * wn + lm;
+    if (f < F) {
+      uint16_t* h = static_cast<uint16_t*>(out);
 #pragma unroll
-  for (int mi = 0; mi < 2; mi++) {
+      for (int mi = 0; mi < 2; mi++) {
 #pragma unroll
-    for (int nj = 0; nj < 2; nj++) {
-      const int n = n0 + 64 * wn + 32 * nj + lm;
-      if (n >= O) continue;
+        for (int i = 0; i < 16; i++) {
+          const int m = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * lq + (i & 3);
+          if (m < tl.mlen) {
+            const float g = acc[mi][0][i], u = acc[mi][1][i];
+            h[(int64_t)(tl.row0 + m) * F + f] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
+          }
+        }
+      }
+    }
+  } else {
+    float* part = static_cast<float*>(out);
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int m = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * lq + (i & 3);
-        if (m < tl.mlen) part[(int64_t)(tl.row0 + m) * O + n] = acc[mi][nj][i];
+    for (int mi = 0; mi < 2; mi++) {
+#pragma unroll
+      for (int nj = 0; nj < 2; nj++) {
+        const int n = n0 + 64 * wn + 32 * nj + lm;
+        if (n >= O) continue;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int m = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * lq + (i & 3);
+          if (m < tl.mlen) part[(int64_t)(tl.row0 + m) * O + n] = acc[mi][nj][i];
+        }
       }
     }
   }
@@ -218,17 +264,40 @@ bool gemm_supported(int64_t T, int64_t O, int64_t G) {
   return T * 64 * G < ((int64_t)1 << 31) && O * G * 16 < ((int64_t)1 << 31);
 }
 
+namespace {
+template <int MODE>
+hipError_t launch_mode(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
+                       const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, void* out, int64_t x_rows,
+                       int K, int O, int G, int F, int n_ntiles, hipStream_t stream) {
+  if (!gemm_supported(x_rows, O, G)) return hipErrorInvalidValue;
+  const int64_t nblk = max_tiles * n_ntiles;
+  if (nblk <= 0) return hipSuccess;
+  const uint32_t x_bytes = (uint32_t)(x_rows * 64 * G);
+  hipLaunchKernelGGL(gemm_bf16_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, stream, x, packed, scales, perm, tiles,
+                     n_tiles, out, K, O, G, n_ntiles, x_bytes, F);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                             const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
                             int O, int G, hipStream_t stream) {
-  if (!gemm_supported(T, O, G)) return hipErrorInvalidValue;
-  const int n_ntiles = (O + NT - 1) / NT;
-  const int64_t nblk = max_tiles * n_ntiles;
-  if (nblk <= 0) return hipSuccess;
-  const uint32_t x_bytes = (uint32_t)((int64_t)T * 64 * G);
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, x, packed, scales, perm, tiles,
-                     n_tiles, part, K, O, G, n_ntiles, x_bytes);
-  return hipGetLastError();
+  return launch_mode<kGather>(x, packed, scales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0,
+                              (O + NT - 1) / NT, stream);
+}
+
+hipError_t launch_gemm_swiglu(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales,
+                              const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                              uint16_t* h, int T, int K, int F, int G, hipStream_t stream) {
+  return launch_mode<kSwiGLU>(x, gu_packed, gu_scales, perm, tiles, n_tiles, max_tiles, h, T, K, 2 * F, G, F,
+                              (F + NT / 2 - 1) / (NT / 2), stream);
+}
+
+hipError_t launch_gemm_direct(const uint16_t* h, const uint8_t* packed, const uint8_t* scales, const GemmTile* tiles,
+                              const int32_t* n_tiles, int64_t max_tiles, float* part, int64_t P, int O, int G,
+                              hipStream_t stream) {
+  return launch_mode<kDirect>(h, packed, scales, nullptr, tiles, n_tiles, max_tiles, part, P, 1, O, G, 0,
+                              (O + NT - 1) / NT, stream);
 }
 
 }  // namespace mxfp4

@@ -83,6 +83,17 @@ bool gemm_supported(int64_t T, int64_t O, int64_t G);
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                             const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
                             int O, int G, hipStream_t stream);
+// SwiGLU expert block, gate/up stage: weights (E, 2F, G, 16) with gate rows
+// [0, F) over up rows [F, 2F); writes h[sorted position, f] = bf16 of
+// silu(gate) * up, h being (P, F).
+hipError_t launch_gemm_swiglu(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales,
+                              const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                              uint16_t* h, int T, int K, int F, int G, hipStream_t stream);
+// Down stage: A rows are the rows of h at the sorted positions themselves
+// (h is (P, 32G) bf16); writes fp32 part rows like launch_gemm_bf16.
+hipError_t launch_gemm_direct(const uint16_t* h, const uint8_t* packed, const uint8_t* scales, const GemmTile* tiles,
+                              const int32_t* n_tiles, int64_t max_tiles, float* part, int64_t P, int O, int G,
+                              hipStream_t stream);
 hipError_t launch_combine(const float* part, const int32_t* slot_of_pair, const float* p,
                           const void* shared, void* y, int T, int K, int O, int dtype,
                           hipStream_t stream);

@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES)
@@ -168,3 +168,39 @@ def test_gemm_stage_host_checks():
     assert lib.mxfp4_moe_gemm_stage(None, a, a, 4, 4, 32, 2, 2, b, 1 << 20, None) == _abi.ERR_INVALID_ARG
     assert lib.mxfp4_moe_gemm_stage(a, a, a, 4, 4, 32, 2, 2, b, 16, None) == _abi.ERR_WORKSPACE_TOO_SMALL
     assert lib.mxfp4_moe_gemm_stage(a, a, a, 0, 4, 32, 2, 2, None, 0, None) == _abi.OK
+
+
+
+# ---- the SwiGLU expert block
+
+def _sw(x=A, gu_p=B, gu_s=C + 0x10000, dn_p=B + 0x80000, dn_s=C + 0x18000, sel=C + 0x20000, p=C + 0x30000,
+        shared=C + 0x40000, y=C + 0x50000, T=2, E=3, F=32, G=1, O=8, K=2, flags=0, ws=C + 0x60000,
+        ws_bytes=1 << 24):
+    return _abi.lib().mxfp4_moe_swiglu_ex(x, gu_p, gu_s, dn_p, dn_s, sel, p, shared, y, T, E, F, G, O, K, flags,
+                                          ws, ws_bytes, None)
+
+
+def test_swiglu_workspace_size():
+    assert _abi.swiglu_workspace_size(0, 4, 32, 2, 8, 2) == 0
+    T, E, F, G, O, K = 4096, 128, 2048, 90, 5760, 4
+    ws = _abi.swiglu_workspace_size(T, E, F, G, O, K)
+    assert ws >= T * K * O * 4 + T * K * F * 2  # fp32 partial rows and the bf16 intermediate
+    with pytest.raises(_abi.Mxfp4Error) as e:  # the intermediate h reaches 2^31 bytes
+        _abi.swiglu_workspace_size(1 << 16, 8, 1 << 11, 2, 8, 8)
+    assert e.value.status == _abi.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(E=0), dict(F=0), dict(F=48), dict(F=16), dict(G=0), dict(O=0), dict(K=0),
+    dict(E=_abi.MAX_EXPERTS + 1), dict(flags=_abi.FLAG_FORCE_GEMM), dict(flags=0x100),
+    dict(x=0), dict(gu_p=0), dict(gu_s=0), dict(dn_p=0), dict(dn_s=0), dict(sel=0), dict(p=0), dict(shared=0),
+    dict(y=0), dict(x=A + 4), dict(gu_p=B + 8), dict(dn_p=B + 0x80008), dict(sel=C + 0x20001), dict(p=C + 0x30002),
+    dict(y=C + 0x50001), dict(y=A), dict(y=B + 64), dict(y=C + 0x18000), dict(y=B + 0x80000),
+])
+def test_swiglu_host_checks_reject(kw):
+    assert _sw(**kw) == _abi.ERR_INVALID_ARG
+
+
+def test_swiglu_host_checks_workspace_and_empty():
+    assert _sw(ws_bytes=16) == _abi.ERR_WORKSPACE_TOO_SMALL
+    assert _sw(T=0, x=0, y=0, shared=0, sel=0, p=0) == _abi.OK  # nothing to do, nothing enqueued

@@ -476,3 +476,126 @@ def test_plain_entry_points_match_ex():
     assert st == 0
     torch.cuda.synchronize()
     assert torch.equal(y, run(d))
+
+
+# ------------------------------------------------------------------ SwiGLU expert block
+
+def swiglu_case(seed, T, E, K, G, F, O, scale_lo=118, scale_hi=126, distinct=True):
+    rng = np.random.default_rng(seed)
+    x = workloads.round_to_bf16(rng.standard_normal((T, 32 * G)).astype(np.float32))
+    shared = workloads.round_to_bf16(rng.standard_normal((T, O)).astype(np.float32))
+    gu_p = rng.integers(0, 256, (E, 2 * F, G, 16), dtype=np.uint8)
+    gu_s = rng.integers(scale_lo, scale_hi + 1, (E, 2 * F, G), dtype=np.uint8)
+    dn_p = rng.integers(0, 256, (E, O, F // 32, 16), dtype=np.uint8)
+    dn_s = rng.integers(scale_lo, scale_hi + 1, (E, O, F // 32), dtype=np.uint8)
+    if distinct:
+        sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    else:
+        sel = rng.integers(0, E, (T, K)).astype(np.int32)
+    p = rng.random((T, K)).astype(np.float32)
+    return x, gu_p, gu_s, dn_p, dn_s, sel, p, shared
+
+
+def upload_swiglu(x, gu_p, gu_s, dn_p, dn_s, sel, p, shared):
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+
+    return (bf(x), u8(gu_p), u8(gu_s), u8(dn_p), u8(dn_s), u8(sel.astype(np.int32)),
+            torch.from_numpy(np.ascontiguousarray(p, dtype=np.float32)).to(DEV), bf(shared))
+
+
+def run_swiglu(d, out=None):
+    y = mx.moe_swiglu(*d, out=out)
+    torch.cuda.synchronize()
+    return y
+
+
+SWIGLU_CASES = [
+    # T, E, K, G, F, O, distinct
+    (1, 3, 1, 1, 32, 8, True),
+    (5, 4, 2, 2, 64, 40, True),
+    (33, 6, 3, 3, 96, 130, True),     # F = 1.5 feature tiles, ragged N-tile of the down projection
+    (70, 16, 4, 5, 160, 72, True),    # P spans several 128-row M-tiles, odd G
+    (40, 3, 2, 17, 64, 33, False),    # duplicates within a token, G over two scale chunks
+]
+
+
+@pytest.mark.parametrize("case", SWIGLU_CASES, ids=lambda c: "T{}E{}K{}G{}F{}O{}{}".format(*c[:6], "" if c[6] else "dup"))
+def test_swiglu_against_oracle(case):
+    T, E, K, G, F, O, distinct = case
+    say(f"swiglu {case}")
+    host = swiglu_case(sum(case[:6]), T, E, K, G, F, O, distinct=distinct)
+    y = run_swiglu(upload_swiglu(*host))
+    assert y.dtype == torch.bfloat16 and tuple(y.shape) == (T, O)
+    assert_bf16_close(host64(y), oracle.expert_swiglu(*host), f"swiglu {case}")
+
+
+def test_swiglu_invariants():
+    host = list(swiglu_case(7, 24, 10, 3, 3, 96, 50))
+    x, gu_p, gu_s, dn_p, dn_s, sel, p, shared = host
+    d = upload_swiglu(*host)
+    y = run_swiglu(d)
+    assert torch.equal(y, run_swiglu(d)), "not deterministic"
+    # unselected experts do not matter, bit for bit
+    gu2, dn2, gs2, ds2 = gu_p.copy(), dn_p.copy(), gu_s.copy(), dn_s.copy()
+    rng = np.random.default_rng(8)
+    for e in set(range(10)) - set(np.unique(sel).tolist()):
+        gu2[e] = rng.integers(0, 256, gu2[e].shape)
+        dn2[e] = rng.integers(0, 256, dn2[e].shape)
+        gs2[e] = 255
+        ds2[e] = 255
+    assert torch.equal(run_swiglu(upload_swiglu(x, gu2, gs2, dn2, ds2, sel, p, shared)), y)
+    # in place on shared
+    y2 = d[7].clone()
+    run_swiglu(d[:7] + (y2,), out=y2)
+    assert torch.equal(y2, y)
+    # zero gate rows: the routed part vanishes, y = shared exactly
+    gz = gu_p.copy()
+    gz[:, :96] = 0
+    assert torch.equal(run_swiglu(upload_swiglu(x, gz, gu_s, dn_p, dn_s, sel, p, shared)), d[7])
+
+
+def test_swiglu_full_shapes_sampled():
+    # the gate/up shape of the decode8 workload (I = 7168, 2F = 4096) feeding
+    # the skewed workload's down shape (F = 2048 -> O = 7168), E = 384, K = 8;
+    # only the selected experts are drawn (the others are never read), and the
+    # oracle checks two tokens on a sample of output rows
+    T, E, K, G, F, O = 8, 384, 8, 224, 2048, 7168
+    rng = np.random.default_rng(2026)
+    x = workloads.round_to_bf16(rng.standard_normal((T, 32 * G)).astype(np.float32))
+    shared = workloads.round_to_bf16(rng.standard_normal((T, O)).astype(np.float32))
+    sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    p = rng.random((T, K)).astype(np.float32)
+    used = np.unique(sel)
+    gu_p = torch.empty((E, 2 * F, G, 16), dtype=torch.uint8, device=DEV)
+    gu_s = torch.empty((E, 2 * F, G), dtype=torch.uint8, device=DEV)
+    dn_p = torch.empty((E, O, F // 32, 16), dtype=torch.uint8, device=DEV)
+    dn_s = torch.empty((E, O, F // 32), dtype=torch.uint8, device=DEV)
+    hp = {}
+    for e in used:
+        r = np.random.default_rng(int(e) + 99)
+        hp[e] = (r.integers(0, 256, (2 * F, G, 16), dtype=np.uint8), r.integers(118, 125, (2 * F, G), dtype=np.uint8),
+                 r.integers(0, 256, (O, F // 32, 16), dtype=np.uint8), r.integers(118, 125, (O, F // 32), dtype=np.uint8))
+        for dst, src in zip((gu_p, gu_s, dn_p, dn_s), hp[e]):
+            dst[int(e)].copy_(torch.from_numpy(src))
+    bf = lambda a: torch.from_numpy(a).to(DEV).to(torch.bfloat16)  # noqa: E731
+    d = (bf(x), gu_p, gu_s, dn_p, dn_s, torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV), bf(shared))
+    y = host64(run_swiglu(d))
+    toks = [0, 5]
+    rows = np.sort(np.random.default_rng(3).choice(O, 96, replace=False))
+
+    class Lazy:
+        def __init__(self, i):
+            self.i = i
+
+        def __len__(self):
+            return E
+
+        def __getitem__(self, e):
+            return hp[int(e)][self.i]
+
+    ref = oracle.expert_swiglu_rows(x[toks], Lazy(0), Lazy(1), Lazy(2), Lazy(3), sel[toks], p[toks], shared[toks], rows)
+    assert_bf16_close(y[toks][:, rows], ref, "swiglu full shapes, 2 tokens x 96 rows")
