@@ -16,7 +16,8 @@ value:
   decode-shaped workloads: algorithmic weight bytes per second, where a call
     reads U * O * G * 17 bytes (16 packed + 1 scale byte per 32-weight
     group of each of the U distinct selected experts; 4.25 bits per weight);
-  prefill-shaped workloads: 2 * T * K * O * I flops per second.
+  prefill-shaped workloads: 2 * T * K * O * I flops per second;
+  the SwiGLU expert block: 2 * T * K * (2F * I + O * F) flops per second.
 cpu_baseline: the float64 oracle timed on the host on a bounded sample of
   the same workload.
 """
@@ -46,6 +47,7 @@ KERNEL_SOURCES = {
     "gemv": ["mxfp4_block_scaled_amd/csrc/gemv_rows.hip", "mxfp4_block_scaled_amd/csrc/device_common.h",
              "mxfp4_block_scaled_amd/csrc/wave_routing.h"],
     "gemm": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+    "swiglu": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
 }
 
 
@@ -142,6 +144,12 @@ def record_traffic(args):
     print(json.dumps({w.name: rec}))
 
 
+def _kind(w) -> str:
+    if w.F:
+        return "swiglu"
+    return "gemv" if w.name in DECODE_WORKLOADS else "gemm"
+
+
 def cpu_baseline(inp, kind, sample_seconds):
     import oracle
 
@@ -152,6 +160,24 @@ def cpu_baseline(inp, kind, sample_seconds):
     except Exception:  # threadpoolctl missing: numpy's BLAS threads unknown
         threads = os.cpu_count() or 1
     w = inp.workload
+    if kind == "swiglu":
+        # one token's full SwiGLU (all K pairs) on a sample of output rows
+        rows_per_call = 16
+        done_flops, calls, t0 = 0.0, 0, time.perf_counter()
+        rng = np.random.default_rng(0)
+        while True:
+            t = calls % w.T
+            rows = np.sort(rng.choice(w.O, rows_per_call, replace=False))
+            oracle.expert_swiglu_rows(inp.x[t:t + 1], inp.packed, inp.scales, inp.dn_packed, inp.dn_scales,
+                                      inp.sel[t:t + 1], inp.p[t:t + 1], inp.shared[t:t + 1], rows)
+            done_flops += 2.0 * w.K * (2 * w.F * w.I + rows_per_call * w.F)
+            calls += 1
+            if time.perf_counter() - t0 >= sample_seconds:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{calls} tokens (all {w.K} pairs each) x {rows_per_call} output rows of the {w.name} "
+                          "workload", "seconds": round(dt, 2)}
     if kind == "gemv":
         done_bytes, calls, t0 = 0.0, 0, time.perf_counter()
         while True:
@@ -180,6 +206,12 @@ def cpu_baseline(inp, kind, sample_seconds):
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{calls} x {rows_per_call} output rows of the {w.name} workload, all {w.T} tokens",
             "seconds": round(dt, 2)}
+
+
+def _path_name(mx, w, kind) -> str:
+    if kind == "swiglu":
+        return "SwiGLU block (bucketing, gate/up GEMM, down GEMM, combine)"
+    return "GEMV" if mx.select_path(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1) == 1 else "GEMM"
 
 
 def main():
@@ -220,30 +252,43 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.WORKLOADS[args.workload]
-    kind = "gemv" if args.workload in DECODE_WORKLOADS else "gemm"
+    kind = _kind(w)
     td = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     t_gen = time.perf_counter()
     inp = workloads.make_inputs(w, n_routing_sets=N_ROUTING_SETS)
-    packed = torch.empty((w.E, w.O, w.G, 16), dtype=torch.uint8, device=dev)
-    scales = torch.empty((w.E, w.O, w.G), dtype=torch.uint8, device=dev)
+    packed = torch.empty(inp.packed.shape, dtype=torch.uint8, device=dev)
+    scales = torch.empty(inp.scales.shape, dtype=torch.uint8, device=dev)
     for e in range(w.E):
         packed[e].copy_(torch.from_numpy(inp.packed[e]))
         scales[e].copy_(torch.from_numpy(inp.scales[e]))
+    dn_packed = dn_scales = None
+    if kind == "swiglu":
+        dn_packed = torch.empty(inp.dn_packed.shape, dtype=torch.uint8, device=dev)
+        dn_scales = torch.empty(inp.dn_scales.shape, dtype=torch.uint8, device=dev)
+        for e in range(w.E):
+            dn_packed[e].copy_(torch.from_numpy(inp.dn_packed[e]))
+            dn_scales[e].copy_(torch.from_numpy(inp.dn_scales[e]))
     x = torch.from_numpy(inp.x).to(dev).to(td)
     shared = torch.from_numpy(inp.shared).to(dev).to(td)
     sels = torch.from_numpy(np.stack([s for s, _ in inp.routing_sets])).to(dev)
     ps = torch.from_numpy(np.stack([p for _, p in inp.routing_sets])).to(dev)
     y = torch.empty_like(shared)
-    ws = torch.empty(max(mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1), 1),
-                     dtype=torch.uint8, device=dev)
+    if kind == "swiglu":
+        ws_bytes = mx.swiglu_workspace_size(w.T, w.E, w.F, w.G, w.O, w.K)
+    else:
+        ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs drawn and resident in {time.perf_counter() - t_gen:.1f} s; "
         f"packed {packed.numel() / 1e9:.2f} GB, workspace {ws.numel() / 1e6:.1f} MB, "
-        f"path {'GEMV' if mx.select_path(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == 'fp32' else 1) == 1 else 'GEMM'}")
+        f"path {_path_name(mx, w, kind)}")
 
     def step(i):
         r = i % N_ROUTING_SETS
-        mx.moe_linear(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
+        if kind == "swiglu":
+            mx.moe_swiglu(x, packed, scales, dn_packed, dn_scales, sels[r], ps[r], shared, out=y, workspace=ws)
+        else:
+            mx.moe_linear(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
 
     # eager reference of the last timed step, for the graph replay check
     last = (args.steps - 1) % N_ROUTING_SETS
@@ -322,7 +367,18 @@ def main():
     uniq = [len(np.unique(inp.routing_sets[i % N_ROUTING_SETS][0])) for i in range(args.steps)]
     bytes_per_step = float(np.mean(uniq)) * w.O * w.G * 17
     flops_per_step = 2.0 * w.P * w.O * w.I
-    if kind == "gemv":
+    if kind == "swiglu":
+        flops_per_step = 2.0 * w.P * (2 * w.F * w.I + w.O * w.F)
+    if kind == "swiglu":
+        # the block's two grouped GEMMs are its work; timed here as the whole
+        # call (bucketing and combine included), a lower bound on the GEMMs
+        value = flops_per_step / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4)}
+        roof["kernel"] = "gemm_bf16_kernel<1> + gemm_bf16_kernel<2> (whole call)"
+        roof["launch_ms"] = round(ms_step, 6)
+    elif kind == "gemv":
         # one launch per step: the fused kernel is the whole call
         value = bytes_per_step / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -339,7 +395,10 @@ def main():
         roof["kernel"] = "gemm_bf16_kernel"
         roof["launch_ms"] = round(gemm_ms, 6)
     roof["per_launch"] = ({"bytes": bytes_per_step} if kind == "gemv" else {"flops": flops_per_step})
-    roof["traffic"] = committed_traffic(w.name, kind)
+    if kind == "swiglu":
+        roof["traffic"] = None
+    if kind != "swiglu":
+        roof["traffic"] = committed_traffic(w.name, kind)
     log(f"[bench] {args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, "
         f"{value:.1f} {unit} ({100 * roof['frac']:.1f}% of peak); mean distinct experts {np.mean(uniq):.1f}")
 
@@ -348,6 +407,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32" if w.dtype == "fp32" else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
+                   **({"F": w.F} if w.F else {}),
                    "x_dtype": w.dtype, "routing": w.routing if w.routing == "uniform" else f"zipf({w.zipf_s})",
                    "routing_draws": N_ROUTING_SETS, "graph": graph is not None},
         "roofline": roof,

@@ -335,7 +335,12 @@ def test_workload_shapes_and_routing():
         for row in inp.sel:
             assert len(set(row.tolist())) == w.K  # distinct experts per token
         np.testing.assert_allclose(inp.p.sum(1), 1.0, rtol=1e-6)
-        assert inp.packed[0].shape == (w.O, w.G, 16)
+        if w.F:  # SwiGLU block: stacked gate/up, then the down projection
+            assert inp.packed[0].shape == (2 * w.F, w.G, 16)
+            assert inp.dn_packed[1].shape == (w.O, w.F // 32, 16)
+            assert inp.dn_scales[2].shape == (w.O, w.F // 32)
+        else:
+            assert inp.packed[0].shape == (w.O, w.G, 16) and inp.dn_packed is None
         s = inp.scales[w.E - 1]
         assert s.min() >= w.scale_lo and s.max() <= w.scale_hi
         assert not np.array_equal(inp.routing_sets[0][0], inp.routing_sets[1][0])

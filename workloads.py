@@ -6,8 +6,8 @@ no combine. The float64 oracle (under ``oracle/``) and the GPU library (under
 ``mxfp4_block_scaled_amd/``) both take their inputs from here and from nowhere
 else, so the two sides never share code.
 
-The five named workloads are the shapes and value distributions of the
-problem statement on the pages (page "MXFP4 Routed Expert Linear", section
+The five routed-linear workloads are the shapes and value distributions of
+the problem statement on the pages (page "MXFP4 Routed Expert Linear", section
 "Route, weight, and add the shared path"; page "MXFP4 Experts", the shape
 paragraph): latent tokens x (T, I=32G), selected experts and mixture weights
 (T, K), shared output (T, O), packed codes (E, O, G, 16) and scale bytes
@@ -15,8 +15,10 @@ paragraph): latent tokens x (T, I=32G), selected experts and mixture weights
 
 Recipe (fixed order, NumPy PCG64):
 
-* ``SeedSequence(20261202 + index).spawn(6)`` gives the streams
-  [0] x, [1] shared, [2] packed, [3] scales, [4] routing, [5] logits.
+* ``SeedSequence(20261202 + index).spawn(8)`` gives the streams
+  [0] x, [1] shared, [2] packed, [3] scales, [4] routing, [5] logits, and
+  for the SwiGLU expert block [6] and [7], the down projection's packed and
+  scale bytes ([2] and [3] then hold the stacked gate/up matrices).
 * Packed codes and scale bytes are drawn per expert, each expert from its own
   child of stream [2] / [3], so any expert can be regenerated alone.
 * x and shared are standard normal, drawn in float64, stored as float32; for
@@ -58,6 +60,7 @@ class Workload:
     routing: str = "uniform"  # "uniform" or "zipf"
     zipf_s: float = 0.0
     logit_std: float = 1.0
+    F: int = 0  # SwiGLU expert block: intermediate width (0: the routed linear alone)
 
     @property
     def I(self) -> int:  # noqa: E743 - the pages' name for the input width
@@ -71,7 +74,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads. Names say what each is; sizes are in the fields.
+# The workloads. Names say what each is; sizes are in the fields.
 WORKLOADS = {
     "tiny": Workload("tiny", 0, T=4, E=4, K=2, G=2, O=32, dtype="fp32",
                      scale_lo=124, scale_hi=130),
@@ -84,6 +87,12 @@ WORKLOADS = {
     "skewed": Workload("skewed", 4, T=8192, E=384, K=8, G=64, O=7168, dtype="bf16",
                        scale_lo=110, scale_hi=135, routing="zipf", zipf_s=1.2,
                        logit_std=math.sqrt(2.0)),
+    # SwiGLU expert block: decode8's gate/up shape (I = 7168, 2F = 4096)
+    # feeding the skewed workload's down shape (F = 2048 -> O = 7168), with
+    # the skewed workload's tokens and routing
+    "swiglu": Workload("swiglu", 5, T=8192, E=384, K=8, G=224, O=7168, dtype="bf16",
+                       scale_lo=118, scale_hi=128, routing="zipf", zipf_s=1.2,
+                       logit_std=math.sqrt(2.0), F=2048),
 }
 
 
@@ -154,11 +163,13 @@ class Inputs:
     workload: Workload
     x: np.ndarray  # float32 (T, I); bfloat16-exact values for bf16 workloads
     shared: np.ndarray  # float32 (T, O); bfloat16-exact for bf16 workloads
-    packed: ExpertTensor  # (E, O, G, 16) uint8, lazily drawn
-    scales: ExpertTensor  # (E, O, G) uint8, lazily drawn
+    packed: ExpertTensor  # (E, O, G, 16) uint8, lazily drawn; SwiGLU: gate/up (E, 2F, G, 16)
+    scales: ExpertTensor  # (E, O, G) uint8, lazily drawn; SwiGLU: (E, 2F, G)
     sel: np.ndarray  # int32 (T, K)
     p: np.ndarray  # float32 (T, K)
     routing_sets: list  # further (sel, p) draws; [0] is (sel, p)
+    dn_packed: ExpertTensor | None = None  # SwiGLU: down projection (E, O, F/32, 16)
+    dn_scales: ExpertTensor | None = None  # SwiGLU: (E, O, F/32)
 
 
 def make_inputs(w: Workload | str, n_routing_sets: int = 1) -> Inputs:
@@ -169,7 +180,8 @@ def make_inputs(w: Workload | str, n_routing_sets: int = 1) -> Inputs:
         raise ValueError("scale range must lie in 0..255")
     if w.routing != "uniform" and w.K > w.E:
         raise ValueError("K distinct experts need K <= E")
-    s_x, s_sh, s_pk, s_sc, s_rt, s_lg = np.random.SeedSequence(SEED_BASE + w.index).spawn(6)
+    # children 0..5 as always; 6 and 7 draw the SwiGLU down projection
+    s_x, s_sh, s_pk, s_sc, s_rt, s_lg, s_dp, s_ds = np.random.SeedSequence(SEED_BASE + w.index).spawn(8)
     x = np.random.Generator(np.random.PCG64(s_x)).standard_normal((w.T, w.I)).astype(np.float32)
     shared = np.random.Generator(np.random.PCG64(s_sh)).standard_normal((w.T, w.O)).astype(np.float32)
     if w.dtype == "bf16":
@@ -177,13 +189,20 @@ def make_inputs(w: Workload | str, n_routing_sets: int = 1) -> Inputs:
         shared = round_to_bf16(shared)
     elif w.dtype != "fp32":
         raise ValueError(f"unknown dtype {w.dtype!r}")
-    packed = ExpertTensor(s_pk, w.E, (w.O, w.G, 16), 0, 255)
-    scales = ExpertTensor(s_sc, w.E, (w.O, w.G), w.scale_lo, w.scale_hi)
+    rows = 2 * w.F if w.F else w.O
+    packed = ExpertTensor(s_pk, w.E, (rows, w.G, 16), 0, 255)
+    scales = ExpertTensor(s_sc, w.E, (rows, w.G), w.scale_lo, w.scale_hi)
+    dn_packed = dn_scales = None
+    if w.F:
+        if w.F % 32:
+            raise ValueError("the SwiGLU intermediate width must be a multiple of 32")
+        dn_packed = ExpertTensor(s_dp, w.E, (w.O, w.F // 32, 16), 0, 255)
+        dn_scales = ExpertTensor(s_ds, w.E, (w.O, w.F // 32), w.scale_lo, w.scale_hi)
     rng_route = np.random.Generator(np.random.PCG64(s_rt))
     rng_logit = np.random.Generator(np.random.PCG64(s_lg))
     logw = _log_weights(w)
     sets = [_draw_routing(w, rng_route, rng_logit, logw) for _ in range(max(1, n_routing_sets))]
-    return Inputs(w, x, shared, packed, scales, sets[0][0], sets[0][1], sets)
+    return Inputs(w, x, shared, packed, scales, sets[0][0], sets[0][1], sets, dn_packed, dn_scales)
 
 
 def unique_experts(sel: np.ndarray) -> np.ndarray:
