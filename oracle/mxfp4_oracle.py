@@ -388,3 +388,91 @@ def expert_swiglu_scalar(x, gu_packed, gu_scales, dn_packed, dn_scales, sel, p, 
                 row[o] += float(p[t][k]) * d
         out.append(row)
     return out
+
+
+# ----------------------------------------------------------------- routers
+#
+# What produces sel and p upstream of the layer. Two routers are described:
+# the CPU kernels page (section 1) gives a softmax router - softmax over all
+# experts, the top k of it, their probabilities divided by
+# max(their sum, 6.103515625e-5), times a scaling factor - and a sigmoid
+# router whose correction bias steers the selection only (the weights are
+# gathered from the unbiased scores); the Metal PR page ("Summary", the
+# router bullets) ranks with ties going to the lower expert index, keeps the
+# selection in that descending order, sums the chosen scores left to right,
+# divides by (sum + 1e-20) and multiplies by the scaling factor. Readings:
+# the selection is made on the exact (float64) quantities - for the softmax
+# router that is the logits themselves, which rank exactly like the exact
+# probabilities - and the sigmoid router has no expert groups (one group).
+
+SOFTMAX_MASS_FLOOR = 6.103515625e-5  # the CPU kernels page's lower bound on the selected mass
+SIGMOID_EPS = 1e-20                  # the Metal PR page's addend to the sum of the chosen scores
+
+
+def _topk_desc(keys: np.ndarray, K: int) -> np.ndarray:
+    """Indices of the K largest keys per row, largest first, ties to the
+    lower index (a stable sort of the negated keys)."""
+    return np.argsort(-keys, axis=1, kind="stable")[:, :K]
+
+
+def route_softmax(logits, K: int, scale: float = 1.0):
+    """Softmax router: returns (sel int32 [T, K], p float64 [T, K])."""
+    l = np.asarray(logits, dtype=np.float64)
+    if l.ndim != 2 or not 1 <= K <= l.shape[1]:
+        raise ValueError("logits must be (T, E) with 1 <= K <= E")
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    prob = z / z.sum(axis=1, keepdims=True)
+    sel = _topk_desc(l, K)
+    chosen = np.take_along_axis(prob, sel, axis=1)
+    p = chosen / np.maximum(chosen.sum(axis=1, keepdims=True), SOFTMAX_MASS_FLOOR) * scale
+    return sel.astype(np.int32), p
+
+
+def route_sigmoid(logits, bias, K: int, scale: float = 1.0):
+    """Sigmoid router with a selection-only bias: returns (sel, p)."""
+    l = np.asarray(logits, dtype=np.float64)
+    if l.ndim != 2 or not 1 <= K <= l.shape[1]:
+        raise ValueError("logits must be (T, E) with 1 <= K <= E")
+    b = np.zeros(l.shape[1]) if bias is None else np.asarray(bias, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-l))
+    sel = _topk_desc(s + b[None, :], K)
+    chosen = np.take_along_axis(s, sel, axis=1)
+    total = np.zeros((l.shape[0], 1))
+    for k in range(K):  # left to right
+        total += chosen[:, k:k + 1]
+    p = chosen / (total + SIGMOID_EPS) * scale
+    return sel.astype(np.int32), p
+
+
+def route_scalar(logits, bias, K: int, mode: str, scale: float = 1.0):
+    """Brute force with plain Python numbers (tiny shapes): repeated
+    selection of the largest remaining key, lower index on ties."""
+    import math
+    out_sel, out_p = [], []
+    for row in logits:
+        E = len(row)
+        if mode == "softmax":
+            m = max(row)
+            z = [math.exp(float(v) - m) for v in row]
+            prob = [v / sum(z) for v in z]
+            keys = [float(v) for v in row]
+        else:
+            prob = [1.0 / (1.0 + math.exp(-float(v))) for v in row]
+            keys = [prob[e] + (0.0 if bias is None else float(bias[e])) for e in range(E)]
+        left = list(range(E))
+        sel = []
+        for _ in range(K):
+            best = left[0]
+            for e in left[1:]:
+                if keys[e] > keys[best]:
+                    best = e
+            sel.append(best)
+            left.remove(best)
+        mass = 0.0
+        for e in sel:
+            mass += prob[e]
+        den = max(mass, SOFTMAX_MASS_FLOOR) if mode == "softmax" else mass + SIGMOID_EPS
+        out_sel.append(sel)
+        out_p.append([prob[e] / den * scale for e in sel])
+    return out_sel, out_p

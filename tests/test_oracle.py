@@ -523,3 +523,82 @@ def test_swiglu_planted_mistakes_are_caught(monkeypatch):
         with monkeypatch.context() as mp:
             plant(mp)
             assert not np.allclose(oracle.expert_swiglu(*args), ys, rtol=1e-6), f"planted mistake not caught: {name}"
+
+
+# ----------------------------------------------------------------- routers
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("mode", ["softmax", "sigmoid"])
+def test_router_brute_force_matches(seed, mode):
+    rng = _rng(seed)
+    logits = rng.standard_normal((6, 12)) * 2
+    bias = rng.standard_normal(12) * 0.3 if mode == "sigmoid" else None
+    K = 4
+    sel, p = (oracle.route_softmax(logits, K, 2.5) if mode == "softmax" else oracle.route_sigmoid(logits, bias, K, 2.5))
+    s2, p2 = oracle.route_scalar(logits.tolist(), None if bias is None else bias.tolist(), K, mode, 2.5)
+    assert sel.tolist() == s2
+    np.testing.assert_allclose(p, np.array(p2), rtol=1e-14)
+
+
+def test_router_ties_go_to_the_lower_index_in_order():
+    logits = np.array([[0.0, 3.0, 1.0, 3.0, 1.0, 3.0]])
+    sel, p = oracle.route_softmax(logits, 4)
+    assert sel.tolist() == [[1, 3, 5, 2]]
+    sel, _ = oracle.route_sigmoid(logits, None, 4)
+    assert sel.tolist() == [[1, 3, 5, 2]]
+    # the three tied experts share the selected mass equally
+    np.testing.assert_allclose(p[0, :3], p[0, 0], rtol=1e-15)
+
+
+def test_softmax_router_closed_forms():
+    rng = _rng(4)
+    logits = rng.standard_normal((5, 9))
+    sel, p = oracle.route_softmax(logits, 9)  # every expert: the weights are the softmax itself
+    z = np.exp(logits - logits.max(1, keepdims=True))
+    np.testing.assert_allclose(p, np.take_along_axis(z / z.sum(1, keepdims=True), sel, 1), rtol=1e-14)
+    np.testing.assert_allclose(p.sum(1), 1.0, rtol=1e-14)
+    sel, p = oracle.route_softmax(logits, 3, scale=2.0)  # renormalised over the chosen three, times 2
+    np.testing.assert_allclose(p.sum(1), 2.0, rtol=1e-14)
+    e = np.exp(np.take_along_axis(logits, sel, 1))
+    np.testing.assert_allclose(p, 2.0 * e / e.sum(1, keepdims=True), rtol=1e-13)
+    # K = 1: weight = scale, whatever the logits
+    _, p1 = oracle.route_softmax(logits, 1, scale=1.5)
+    np.testing.assert_allclose(p1, 1.5, rtol=1e-15)
+
+
+def test_sigmoid_router_bias_steers_selection_only():
+    logits = np.array([[2.0, 1.0, 0.0]])
+    bias = np.array([0.0, 0.0, 0.9])  # sigmoid(0) + 0.9 = 1.4 > sigmoid(2) = 0.88
+    sel, p = oracle.route_sigmoid(logits, bias, 2)
+    assert sel.tolist() == [[2, 0]]
+    s = 1.0 / (1.0 + np.exp(-np.array([0.0, 2.0])))
+    np.testing.assert_allclose(p[0], s / (s.sum() + oracle.SIGMOID_EPS), rtol=1e-15)  # unbiased scores
+    sel0, _ = oracle.route_sigmoid(logits, None, 2)
+    assert sel0.tolist() == [[0, 1]]
+
+
+def test_router_planted_mistakes_are_caught(monkeypatch):
+    rng = _rng(5)
+    logits = np.round(rng.standard_normal((8, 10)), 1)  # rounded: ties among the largest
+    bias = np.round(rng.standard_normal(10) * 0.2, 1) * 0  # a zero bias keeps the ties
+    want_s, want_p = oracle.route_scalar(logits.tolist(), bias.tolist(), 3, "sigmoid", 1.0)
+    got_s, got_p = oracle.route_sigmoid(logits, bias, 3)
+    assert got_s.tolist() == want_s
+    assert any(len(set(np.round(np.sort(r)[-4:], 6))) < 4 for r in logits)  # the case has a tie near the top
+    orig = om._topk_desc
+    mistakes = {
+        "ties to the higher index": lambda mp: mp.setattr(
+            om, "_topk_desc", lambda k, K: (k.shape[1] - 1 - np.argsort(-k[:, ::-1], axis=1, kind="stable"))[:, :K]),
+        "ascending order": lambda mp: mp.setattr(om, "_topk_desc", lambda k, K: orig(k, K)[:, ::-1]),
+    }
+    for name, plant in mistakes.items():
+        with monkeypatch.context() as mp:
+            plant(mp)
+            s, _ = oracle.route_sigmoid(logits, bias, 3)
+            assert s.tolist() != want_s, f"planted mistake not caught: {name}"
+    # weights from the biased scores would differ from the brute force
+    bias2 = rng.standard_normal(10) * 0.2
+    want_s2, want_p2 = oracle.route_scalar(logits.tolist(), bias2.tolist(), 3, "sigmoid", 1.0)
+    s = 1.0 / (1.0 + np.exp(-logits))
+    biased = np.take_along_axis(s + bias2, np.array(want_s2), 1)
+    assert not np.allclose(biased / biased.sum(1, keepdims=True), np.array(want_p2), rtol=1e-6)
