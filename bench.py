@@ -1,6 +1,7 @@
 """Benchmark of the MXFP4 routed-expert linear on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --router softmax|sigmoid --workload NAME   (the router alone)
 
 A step is one call of the whole layer (bucketing, dequant-GEMV or grouped
 GEMM, combine) on one batch of the workload's synthetic inputs, all resident
@@ -214,6 +215,106 @@ def _path_name(mx, w, kind) -> str:
     return "GEMV" if mx.select_path(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1) == 1 else "GEMM"
 
 
+def bench_router(args, w):
+    """The router alone (mxfp4_moe_route) at the workload's T, E and K.
+    Algorithmic bytes per launch: the fp32 logits (T * E * 4), the bias
+    (E * 4, sigmoid only) and the outputs (T * K * 8). Successive steps read
+    different logits buffers, together larger than the 256 MB Infinity Cache,
+    so the logits come from HBM."""
+    import torch
+
+    import mxfp4_block_scaled_amd as mx
+    import oracle
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mode = args.router
+    T, E, K = w.T, w.E, w.K
+    per_set = T * E * 4
+    n_sets = max(2, min(256, -(-512 * 2**20 // per_set)))
+    t_gen = time.perf_counter()
+    logits = torch.empty((n_sets, T, E), dtype=torch.float32, device=dev)
+    host = []
+    for i in range(n_sets):
+        lg, bias = workloads.router_logits(T, E, seed=100 + i, std=2.0, bias_std=0.1 if mode == "sigmoid" else None)
+        logits[i].copy_(torch.from_numpy(lg))
+        if i == 0:
+            host = (lg, bias)
+    dbias = None if host[1] is None else torch.from_numpy(host[1]).to(dev)
+    sel = torch.empty((T, K), dtype=torch.int32, device=dev)
+    p = torch.empty((T, K), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] router {mode} at {w.name} (T={T} E={E} K={K}): {n_sets} logits buffers of "
+        f"{per_set / 1e6:.1f} MB drawn in {time.perf_counter() - t_gen:.1f} s")
+
+    def step(i):
+        mx.route(logits[i % n_sets], K, mode, dbias, 1.0, sel=sel, p=p)
+
+    step((args.steps - 1) % n_sets)
+    torch.cuda.synchronize()
+    sel_eager, p_eager = sel.clone(), p.clone()
+    for i in range(args.warmup):
+        step(i)
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            step(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(sel, sel_eager) and torch.equal(p, p_eager)):
+            raise SystemExit("graph replay result differs from the eager call")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(i)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    nbytes = T * E * 4 + (E * 4 if mode == "sigmoid" else 0) + T * K * 8
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "route_kernel",
+            "launch_ms": round(ms_step, 6), "per_launch": {"bytes": nbytes}}
+    log(f"[bench] router: {ms_step * 1e3:.2f} us per launch, {value:.1f} GB/s, "
+        f"{T / (ms_step * 1e-3) / 1e6:.1f} M tokens/s")
+    out = {
+        "metric": f"router ({mode}) logits GB/s, % of HBM roofline", "value": round(value, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"router-{mode}-{w.name}", "T": T, "E": E, "K": K, "logits_buffers": n_sets,
+                   "graph": graph is not None},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        threads = os.cpu_count() or 1
+        fn = (lambda: oracle.route_softmax(host[0], K)) if mode == "softmax" else \
+             (lambda: oracle.route_sigmoid(host[0], host[1], K))
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            calls += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(calls * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{calls} full router calls on one logits buffer",
+                               "seconds": round(dt, 2)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +329,8 @@ def main():
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="host only: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload and of "
                          "the copy calibration (--copy-mib) into profiles/traffic.json")
+    ap.add_argument("--router", choices=["softmax", "sigmoid"],
+                    help="time the router alone at the workload's T, E and K instead of the layer")
     args = ap.parse_args()
     if args.record_traffic:
         if args.copy_mib <= 0:
@@ -243,6 +346,9 @@ def main():
 
     if args.copy_mib > 0:
         copy_calibration(args.copy_mib)
+        return
+    if args.router:
+        bench_router(args, workloads.WORKLOADS[args.workload])
         return
 
     import torch

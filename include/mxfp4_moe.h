@@ -230,6 +230,38 @@ int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8
                         int64_t F, int64_t G, int64_t O, int64_t K, uint32_t flags, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * mxfp4_moe_route - the router that produces sel and p from router logits
+ * (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
+ * Experts", section 1, for both router kinds and the floor on the selected
+ * mass; the exo pull request page, router bullets, for the tie order, the
+ * left-to-right sum, the 1e-20 addend and the scale).
+ *   logits (T, E) fp32 device, row-major; bias (E) fp32 device or NULL;
+ *   sel (T, K) int32 and p (T, K) fp32 device outputs, row-major.
+ * mode MXFP4_ROUTE_SOFTMAX: prob = softmax(logits[t]) over all E experts;
+ *   the K experts with the largest logits are chosen (the same order as
+ *   their probabilities); p[t,k] = prob[sel] / max(sum of the K chosen probs,
+ *   2^-14) * scale. bias must be NULL.
+ * mode MXFP4_ROUTE_SIGMOID: s = 1 / (1 + e^-logits[t]); the K experts with
+ *   the largest s + bias are chosen (bias NULL reads as zeros); p[t,k] =
+ *   s[sel] / (s[sel_0] + ... + s[sel_{K-1}] + 1e-20) * scale, summed left to
+ *   right. The bias steers the choice only, never the weights.
+ * In both modes sel[t] lists K distinct experts by descending key, equal keys
+ * in ascending index order; a NaN key counts as -inf and -0 as +0. Without a
+ * bias the sigmoid router ranks by the logits (the same order as the exact
+ * scores). Arithmetic is fp32; the sigmoid uses the hardware reciprocal. Needs 1 <= K <= min(E, MXFP4_ROUTE_MAX_K), E <= MXFP4_ROUTE_MAX_EXPERTS,
+ * T < 2^30, scale finite, 4-byte aligned buffers and outputs that overlap
+ * neither each other nor the inputs; anything else is MXFP4_ERR_INVALID_ARG.
+ * T = 0 does nothing. Enqueued on `stream`, no synchronisation, no
+ * allocation; may be captured in a graph.
+ */
+#define MXFP4_ROUTE_SOFTMAX 0
+#define MXFP4_ROUTE_SIGMOID 1
+#define MXFP4_ROUTE_MAX_EXPERTS 1024
+#define MXFP4_ROUTE_MAX_K 64
+int mxfp4_moe_route(const float* logits, const float* bias, int64_t T, int64_t E, int64_t K, int mode, float scale,
+                    int32_t* sel, float* p, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* mxfp4_status_string(int status);
 

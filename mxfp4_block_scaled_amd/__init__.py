@@ -20,13 +20,14 @@ import torch
 from . import _abi
 from ._abi import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, FLAG_CHECK, FLAG_FORCE_GEMM, FLAG_FORCE_GEMV, FLAG_GEMV_MFMA, FLAG_BUCKET_MULTI_BLOCK,
-    FLAG_BUCKET_ONE_BLOCK, PATH_GEMM, PATH_GEMV, Mxfp4Error, bucket_workspace_size, select_path,
+    FLAG_BUCKET_ONE_BLOCK, PATH_GEMM, PATH_GEMV, ROUTE_SIGMOID, ROUTE_SOFTMAX, Mxfp4Error, bucket_workspace_size,
+    select_path,
     status_string, swiglu_workspace_size, workspace_size,
 )
 
 __all__ = [
     "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
-    "swiglu_workspace_size", "select_path", "Mxfp4Error", "library_path",
+    "swiglu_workspace_size", "select_path", "route", "Mxfp4Error", "library_path",
 ]
 
 _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
@@ -208,6 +209,37 @@ def gemm_stage(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: i
         st = _abi.lib().mxfp4_moe_gemm_stage(_ptr(x), _ptr(packed), _ptr(scales), T, E, O, G, K, _ptr(workspace),
                                              workspace.numel(), _stream(dev))
     _abi.check(st, "mxfp4_moe_gemm_stage")
+
+
+def route(logits: torch.Tensor, K: int, mode: str = "softmax", bias: torch.Tensor | None = None,
+          scale: float = 1.0, *, sel: torch.Tensor | None = None,
+          p: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Router: fp32 logits (T, E) -> (sel int32 (T, K), p fp32 (T, K)).
+    mode "softmax" (bias must be None) or "sigmoid" (bias (E,) fp32 steers
+    the choice only)."""
+    modes = {"softmax": ROUTE_SOFTMAX, "sigmoid": ROUTE_SIGMOID}
+    if mode not in modes:
+        raise ValueError(f"mode must be one of {sorted(modes)}, got {mode!r}")
+    dev = logits.device
+    _need(logits, "logits", torch.float32, 2, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1, dev)
+        if bias.shape[0] != logits.shape[1]:
+            raise ValueError(f"bias has {bias.shape[0]} entries, logits have {logits.shape[1]} experts")
+    T = logits.shape[0]
+    if sel is None:
+        sel = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if p is None:
+        p = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K):
+        raise ValueError(f"sel and p must be ({T}, {K})")
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_route(_ptr(logits), _ptr(bias), T, logits.shape[1], K, modes[mode],
+                                        float(scale), _ptr(sel), _ptr(p), _stream(dev))
+    _abi.check(st, "mxfp4_moe_route")
+    return sel, p
 
 
 def bucket(sel: torch.Tensor, E: int, flags: int = 0) -> dict:

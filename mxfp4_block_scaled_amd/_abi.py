@@ -36,6 +36,11 @@ MAX_PAIRS = 1 << 26
 PATH_GEMV = 1
 PATH_GEMM = 2
 
+ROUTE_SOFTMAX = 0
+ROUTE_SIGMOID = 1
+ROUTE_MAX_EXPERTS = 1024
+ROUTE_MAX_K = 64
+
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -55,6 +60,7 @@ SIGNATURES = {
     "mxfp4_moe_gemm_stage": (_int, [_vp] * 3 + [_i64] * 5 + [_vp, _sz, _vp]),
     "mxfp4_moe_swiglu_workspace_size": (_int, [_i64] * 6 + [ctypes.POINTER(_sz)]),
     "mxfp4_moe_swiglu_ex": (_int, [_vp] * 9 + [_i64] * 6 + [_u32, _vp, _sz, _vp]),
+    "mxfp4_moe_route": (_int, [_vp] * 2 + [_i64] * 3 + [_int, ctypes.c_float, _vp, _vp, _vp]),
     "mxfp4_status_string": (ctypes.c_char_p, [_int]),
 }
 

@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <cmath>
 #include <cstring>
 
 #include "launch.h"
@@ -355,6 +356,25 @@ int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8
   return MXFP4_OK;
 }
 
+int mxfp4_moe_route(const float* logits, const float* bias, int64_t T, int64_t E, int64_t K, int mode, float scale,
+                    int32_t* sel, float* p, hipStream_t stream) {
+  if (T < 0 || T > (int64_t(1) << 30) || E < 1 || E > MXFP4_ROUTE_MAX_EXPERTS || K < 1 || K > E ||
+      K > MXFP4_ROUTE_MAX_K)
+    return MXFP4_ERR_INVALID_ARG;
+  if (mode != MXFP4_ROUTE_SOFTMAX && mode != MXFP4_ROUTE_SIGMOID) return MXFP4_ERR_INVALID_ARG;
+  if (mode == MXFP4_ROUTE_SOFTMAX && bias) return MXFP4_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MXFP4_ERR_INVALID_ARG;
+  if (T == 0) return MXFP4_OK;
+  if (!logits || !sel || !p) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(sel, 4) || !aligned(p, 4) || (bias && !aligned(bias, 4)))
+    return MXFP4_ERR_INVALID_ARG;
+  const size_t nl = size_t(T) * size_t(E) * 4, no = size_t(T) * size_t(K) * 4, nb = size_t(E) * 4;
+  if (overlap(sel, no, p, no) || overlap(sel, no, logits, nl) || overlap(p, no, logits, nl)) return MXFP4_ERR_INVALID_ARG;
+  if (bias && (overlap(sel, no, bias, nb) || overlap(p, no, bias, nb))) return MXFP4_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != MXFP4_OK) return st;
+  return hip_status(launch_route(logits, bias, (int)T, (int)E, (int)K, mode, scale, sel, p, stream));
+}
 
 int mxfp4_moe_linear(const float* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
                      const float* shared, float* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,

@@ -76,6 +76,16 @@ hipError_t launch_gemv_rows(const void* x, const uint8_t* packed, const uint8_t*
                             const float* p, const void* shared, void* y, int T, int E, int O, int G, int K, int dtype,
                             int32_t* n_invalid, int chunk_index, hipStream_t stream);
 
+// ---- router: logits (T, E) fp32 -> sel (T, K) int32, p (T, K) fp32.
+// mode 0 softmax, 1 sigmoid with a selection-only bias (may be null).
+// One token per group of `lanes` lanes (32 or 64; 0 = route_lanes' choice).
+// Needs 1 <= E <= 1024 and 1 <= K <= min(E, 64); route_lanes returns a group
+// width that holds them (K <= lanes, E <= 64 * lanes).
+int route_values_per_lane(int E, int lanes);
+int route_lanes(int64_t T, int E, int K);
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, int mode, float scale,
+                        int32_t* sel, float* p, hipStream_t stream, int lanes = 0);
+
 // ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
 // The grouped GEMM addresses the activations and one expert's packed bytes
 // with 32-bit byte offsets: T * 32G * 2 < 2^31 and O * G * 16 < 2^31.

@@ -3,5 +3,5 @@ from .mxfp4_oracle import (  # noqa: F401
     E2M1_VALUES, E2M1_TABLE, SCALE_BIAS, split_nibbles, group_codes, scale_factor,
     decode_rows, decode_expert, bucket_pairs, expert_linear, expert_linear_rows,
     expert_linear_scalar, silu, swiglu_hidden, expert_swiglu, expert_swiglu_rows, expert_swiglu_scalar,
-    route_softmax, route_sigmoid, route_scalar, SOFTMAX_MASS_FLOOR, SIGMOID_EPS,
+    route_softmax, route_sigmoid, route_scalar, route_keys, route_weights, SOFTMAX_MASS_FLOOR, SIGMOID_EPS,
 )

@@ -415,34 +415,62 @@ def _topk_desc(keys: np.ndarray, K: int) -> np.ndarray:
     return np.argsort(-keys, axis=1, kind="stable")[:, :K]
 
 
-def route_softmax(logits, K: int, scale: float = 1.0):
-    """Softmax router: returns (sel int32 [T, K], p float64 [T, K])."""
+def _logits2d(logits, K: int) -> np.ndarray:
     l = np.asarray(logits, dtype=np.float64)
     if l.ndim != 2 or not 1 <= K <= l.shape[1]:
         raise ValueError("logits must be (T, E) with 1 <= K <= E")
-    z = np.exp(l - l.max(axis=1, keepdims=True))
-    prob = z / z.sum(axis=1, keepdims=True)
-    sel = _topk_desc(l, K)
-    chosen = np.take_along_axis(prob, sel, axis=1)
-    p = chosen / np.maximum(chosen.sum(axis=1, keepdims=True), SOFTMAX_MASS_FLOOR) * scale
-    return sel.astype(np.int32), p
+    return l
+
+
+def _sigmoid(l: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-l))
+
+
+def route_keys(logits, bias, mode: str) -> np.ndarray:
+    """The float64 quantity each router ranks by: the logits (softmax; they
+    order like the exact probabilities) or sigmoid(logits) + bias."""
+    l = np.asarray(logits, dtype=np.float64)
+    if mode == "softmax":
+        return l.copy()
+    if mode == "sigmoid":
+        b = np.zeros(l.shape[1]) if bias is None else np.asarray(bias, dtype=np.float64)
+        return _sigmoid(l) + b[None, :]
+    raise ValueError(f"unknown router {mode!r}")
+
+
+def route_weights(logits, sel, mode: str, scale: float = 1.0) -> np.ndarray:
+    """float64 mixture weights (T, K) of the selection ``sel``: the chosen
+    softmax probabilities over max(their sum, floor), or the chosen sigmoid
+    scores over (their left-to-right sum + 1e-20); times ``scale``."""
+    l = np.asarray(logits, dtype=np.float64)
+    sel = np.asarray(sel, dtype=np.int64)
+    if mode == "softmax":
+        z = np.exp(l - l.max(axis=1, keepdims=True))
+        prob = z / z.sum(axis=1, keepdims=True)
+        chosen = np.take_along_axis(prob, sel, axis=1)
+        return chosen / np.maximum(chosen.sum(axis=1, keepdims=True), SOFTMAX_MASS_FLOOR) * scale
+    if mode == "sigmoid":
+        chosen = np.take_along_axis(_sigmoid(l), sel, axis=1)
+        total = np.zeros((l.shape[0], 1))
+        for k in range(sel.shape[1]):  # left to right
+            total += chosen[:, k:k + 1]
+        return chosen / (total + SIGMOID_EPS) * scale
+    raise ValueError(f"unknown router {mode!r}")
+
+
+def route_softmax(logits, K: int, scale: float = 1.0):
+    """Softmax router: returns (sel int32 [T, K], p float64 [T, K])."""
+    l = _logits2d(logits, K)
+    sel = _topk_desc(route_keys(l, None, "softmax"), K)
+    return sel.astype(np.int32), route_weights(l, sel, "softmax", scale)
 
 
 def route_sigmoid(logits, bias, K: int, scale: float = 1.0):
     """Sigmoid router with a selection-only bias: returns (sel, p)."""
-    l = np.asarray(logits, dtype=np.float64)
-    if l.ndim != 2 or not 1 <= K <= l.shape[1]:
-        raise ValueError("logits must be (T, E) with 1 <= K <= E")
-    b = np.zeros(l.shape[1]) if bias is None else np.asarray(bias, dtype=np.float64)
-    with np.errstate(over="ignore"):
-        s = 1.0 / (1.0 + np.exp(-l))
-    sel = _topk_desc(s + b[None, :], K)
-    chosen = np.take_along_axis(s, sel, axis=1)
-    total = np.zeros((l.shape[0], 1))
-    for k in range(K):  # left to right
-        total += chosen[:, k:k + 1]
-    p = chosen / (total + SIGMOID_EPS) * scale
-    return sel.astype(np.int32), p
+    l = _logits2d(logits, K)
+    sel = _topk_desc(route_keys(l, bias, "sigmoid"), K)
+    return sel.astype(np.int32), route_weights(l, sel, "sigmoid", scale)
 
 
 def route_scalar(logits, bias, K: int, mode: str, scale: float = 1.0):

@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES)
@@ -43,6 +43,10 @@ def test_header_constants_match_binding():
     assert int(consts["MXFP4_FLAG_CHECK"].rstrip("u"), 16) == _abi.FLAG_CHECK
     assert int(consts["MXFP4_FLAG_GEMV_MFMA"].rstrip("u"), 16) == _abi.FLAG_GEMV_MFMA
     assert int(consts["MXFP4_MAX_EXPERTS"]) == _abi.MAX_EXPERTS
+    assert int(consts["MXFP4_ROUTE_SOFTMAX"]) == _abi.ROUTE_SOFTMAX
+    assert int(consts["MXFP4_ROUTE_SIGMOID"]) == _abi.ROUTE_SIGMOID
+    assert int(consts["MXFP4_ROUTE_MAX_EXPERTS"]) == _abi.ROUTE_MAX_EXPERTS
+    assert int(consts["MXFP4_ROUTE_MAX_K"]) == _abi.ROUTE_MAX_K
     for name, val in re.findall(r"(MXFP4_(?:OK|ERR_\w+)) = (-?\d+)", text):
         assert getattr(_abi, name[len("MXFP4_"):]) == int(val)
 
@@ -204,3 +208,25 @@ def test_swiglu_host_checks_reject(kw):
 def test_swiglu_host_checks_workspace_and_empty():
     assert _sw(ws_bytes=16) == _abi.ERR_WORKSPACE_TOO_SMALL
     assert _sw(T=0, x=0, y=0, shared=0, sel=0, p=0) == _abi.OK  # nothing to do, nothing enqueued
+
+
+# ---- the router
+
+def _route(logits=A, bias=0, T=2, E=8, K=2, mode=0, scale=1.0, sel=B, p=C):
+    return _abi.lib().mxfp4_moe_route(logits, bias, T, E, K, mode, scale, sel, p, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(E=0), dict(K=0), dict(K=9), dict(E=_abi.ROUTE_MAX_EXPERTS + 1, K=2),
+    dict(E=128, K=_abi.ROUTE_MAX_K + 1), dict(mode=2), dict(mode=-1), dict(bias=C + 0x1000),
+    dict(scale=float("inf")), dict(scale=float("nan")), dict(logits=0), dict(sel=0), dict(p=0),
+    dict(logits=A + 2), dict(sel=B + 1), dict(p=C + 3), dict(mode=1, bias=C + 0x1002),
+    dict(p=B + 8), dict(sel=A + 32), dict(p=A), dict(mode=1, bias=B + 4), dict(mode=1, bias=C + 12),
+])
+def test_route_host_checks_reject(kw):
+    assert _route(**kw) == _abi.ERR_INVALID_ARG
+
+
+def test_route_empty_batch_is_a_no_op():
+    assert _route(T=0, logits=0, sel=0, p=0) == _abi.OK
+    assert _route(T=0, mode=1, bias=C + 0x1000) == _abi.OK

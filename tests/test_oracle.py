@@ -602,3 +602,29 @@ def test_router_planted_mistakes_are_caught(monkeypatch):
     s = 1.0 / (1.0 + np.exp(-logits))
     biased = np.take_along_axis(s + bias2, np.array(want_s2), 1)
     assert not np.allclose(biased / biased.sum(1, keepdims=True), np.array(want_p2), rtol=1e-6)
+
+
+@pytest.mark.parametrize("mode", ["softmax", "sigmoid"])
+def test_router_weights_of_any_selection_brute_force(mode):
+    """route_weights on a selection that is not the top k (the GPU may pick
+    another member of a near tie): plain-Python weights of that selection."""
+    rng = _rng(6)
+    logits = rng.standard_normal((5, 11)) * 1.5
+    sel = np.stack([rng.permutation(11)[:4] for _ in range(5)])
+    p = oracle.route_weights(logits, sel, mode, 0.75)
+    for t in range(5):
+        row = [float(v) for v in logits[t]]
+        if mode == "softmax":
+            m = max(row)
+            z = [math.exp(v - m) for v in row]
+            score = [v / sum(z) for v in z]
+        else:
+            score = [1.0 / (1.0 + math.exp(-v)) for v in row]
+        mass = 0.0
+        for e in sel[t]:
+            mass += score[int(e)]
+        den = max(mass, oracle.SOFTMAX_MASS_FLOOR) if mode == "softmax" else mass + oracle.SIGMOID_EPS
+        np.testing.assert_allclose(p[t], [score[int(e)] / den * 0.75 for e in sel[t]], rtol=1e-14)
+    keys = oracle.route_keys(logits, np.arange(11) * 0.1, mode)
+    want = logits if mode == "softmax" else 1.0 / (1.0 + np.exp(-logits)) + np.arange(11) * 0.1
+    np.testing.assert_allclose(keys, want, rtol=1e-15)

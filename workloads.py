@@ -205,6 +205,26 @@ def make_inputs(w: Workload | str, n_routing_sets: int = 1) -> Inputs:
     return Inputs(w, x, shared, packed, scales, sets[0][0], sets[0][1], sets, dn_packed, dn_scales)
 
 
+def router_logits(T: int, E: int, seed: int, std: float = 1.0, grid: float | None = None,
+                  bias_std: float | None = None):
+    """Router inputs: logits (T, E) float32 ~ N(0, std^2) and, when bias_std
+    is given, a per-expert bias (E,) float32 ~ N(0, bias_std^2), else None.
+    ``grid`` rounds the logits to multiples of itself (and the bias to
+    multiples of grid / 16), which plants exact ties. Streams: children 0
+    (logits) and 1 (bias) of SeedSequence(SEED_BASE + 1000 + seed)."""
+    s_l, s_b = np.random.SeedSequence(SEED_BASE + 1000 + seed).spawn(2)
+    logits = np.random.Generator(np.random.PCG64(s_l)).normal(0.0, std, size=(T, E))
+    bias = None
+    if bias_std is not None:
+        bias = np.random.Generator(np.random.PCG64(s_b)).normal(0.0, bias_std, size=E)
+    if grid is not None:
+        logits = np.round(logits / grid) * grid
+        if bias is not None:
+            bias = np.round(bias / (grid / 16)) * (grid / 16)
+    logits = np.ascontiguousarray(logits.astype(np.float32))
+    return logits, (None if bias is None else np.ascontiguousarray(bias.astype(np.float32)))
+
+
 def unique_experts(sel: np.ndarray) -> np.ndarray:
     """Sorted distinct expert indices that appear in ``sel`` (routing summary)."""
     return np.unique(np.asarray(sel).ravel())
