@@ -36,7 +36,7 @@ start from a copy of the shared output, decode each selected expert once,
 multiply each token by its selected experts, weight and accumulate the
 contributions, then add them to the shared output.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * every scale byte 0..255 follows 2^(s-127); 255 is not treated as NaN;
 * a token that lists the same expert twice gets both contributions
@@ -504,3 +504,115 @@ def route_scalar(logits, bias, K: int, mode: str, scale: float = 1.0):
         out_sel.append(sel)
         out_p.append([prob[e] / den * scale for e in sel])
     return out_sel, out_p
+
+
+# ------------------------------------------- MXFP8 activations (variant)
+#
+# The block-scaled variant multiplies the packed weights as they are by
+# activations that are themselves block-scaled. The pages fix the family and
+# its block structure: MXFP4 is a member of the OCP Microscaling formats, in
+# which blocks of 32 element codes share one E8M0 scale byte (page "MXFP4
+# Dequant", "Overview"); the CPU kernels page quantises activations to 8-bit
+# blocks of 32 for its integer dot products (its Q8_1 row provider). Readings
+# for the activations, the pages being silent:
+#
+# * element format: the 8-bit float of that family with 4 exponent bits
+#   (bias 7) and 3 mantissa bits, subnormals with quantum 2^-9, largest
+#   finite value 448 = 1.75 * 2^8, no infinities, S.1111.111 the only NaN;
+# * block: 32 consecutive inputs of one token (input columns 32b .. 32b+31,
+#   the same columns as weight group b);
+# * scale: the smallest power of two 2^X with max|block| <= 448 * 2^X, so no
+#   element saturates; X clamped to [-127, 127] and stored as the byte
+#   X + 127; an all-zero block takes X = -127;
+# * elements: v / 2^X rounded to the nearest representable value, ties to
+#   the even code, then clamped to +-448 (reachable only through the clamp of
+#   X); the sign of v is kept, also when the magnitude rounds to zero.
+#
+# The variant's defining result is the routed linear of the dequantised
+# activations, exact in float64: expert_linear(dequantize(quantize(x)), ...).
+
+E4M3_MAX = 448.0
+E4M3_MIN_NORMAL_EXP = -6   # smallest normal 2^-6
+E4M3_MANTISSA_BITS = 3
+E4M3_BIAS = 7
+
+
+def e4m3_value(code: int) -> float:
+    """Real value of one E4M3 code (NaN for 0x7f and 0xff)."""
+    code = int(code)
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** (E4M3_MIN_NORMAL_EXP - E4M3_MANTISSA_BITS)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - E4M3_BIAS)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def mxfp8_block_exponent(amax) -> np.ndarray:
+    """Smallest integer X with amax <= 448 * 2^X, clamped to [-127, 127];
+    -127 for amax == 0. Exact: amax = f * 2^e with f in [0.5, 1), and
+    448 = 0.875 * 2^9, so X = e - 9 when f <= 0.875 and e - 8 otherwise."""
+    a = np.asarray(amax, dtype=np.float64)
+    f, e = np.frexp(a)
+    X = np.where(f <= 0.875, e - 9, e - 8)
+    X = np.where(a == 0, -127, X)
+    return np.clip(X, -127, 127).astype(np.int64)
+
+
+def quantize_e4m3(v) -> np.ndarray:
+    """E4M3 codes of float64 values already divided by their block scale:
+    round to nearest, ties to even, clamp to +-448, keep the sign."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                       # a = f * 2^e, f in [0.5, 1): exponent e - 1
+    E = np.maximum(e - 1, E4M3_MIN_NORMAL_EXP)
+    quantum = np.ldexp(1.0, E - E4M3_MANTISSA_BITS)
+    aq = np.minimum(np.rint(a / quantum) * quantum, E4M3_MAX)   # np.rint: ties to even
+    # encode the exact grid value: below 2^-6 the code is aq / 2^-9 (0..8,
+    # and 8 is also the code of 2^-6); above, exponent and 3 mantissa bits
+    _, eq = np.frexp(aq)
+    Eq = eq - 1
+    normal = aq >= 2.0 ** E4M3_MIN_NORMAL_EXP
+    mant = np.where(normal, np.ldexp(aq, -Eq) - 1.0, 0.0) * 8.0
+    code = np.where(normal, ((Eq + E4M3_BIAS) << 3) | mant.astype(np.int64),
+                    np.ldexp(aq, 9).astype(np.int64))
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_mxfp8(x) -> tuple:
+    """Activations (T, I), I a multiple of 32 -> (codes uint8 (T, I),
+    scale bytes uint8 (T, I/32)), one scale per token and block of 32."""
+    x = np.asarray(x, dtype=np.float64)
+    T, I = x.shape
+    if I % GROUP_VALUES:
+        raise ValueError("the input width must be a multiple of 32")
+    blocks = x.reshape(T, I // GROUP_VALUES, GROUP_VALUES)
+    X = mxfp8_block_exponent(np.abs(blocks).max(axis=2))
+    codes = quantize_e4m3(blocks / np.ldexp(1.0, X)[:, :, None])
+    return codes.reshape(T, I), (X + SCALE_BIAS).astype(np.uint8)
+
+
+def dequantize_mxfp8(codes, scale_bytes) -> np.ndarray:
+    """float64 values of MXFP8 activations: E4M3 value times 2^(s - 127)."""
+    codes = np.asarray(codes)
+    T, I = codes.shape
+    vals = E4M3_TABLE[codes].reshape(T, I // GROUP_VALUES, GROUP_VALUES)
+    f = np.ldexp(1.0, np.asarray(scale_bytes, dtype=np.int64) - SCALE_BIAS)
+    return (vals * f[:, :, None]).reshape(T, I)
+
+
+def expert_linear_mxfp8(x, packed, scales, sel, p, shared) -> np.ndarray:
+    """The block-scaled variant: the routed linear of the MXFP8-quantised
+    activations, exact in float64."""
+    xh = dequantize_mxfp8(*quantize_mxfp8(x))
+    return expert_linear(xh, packed, scales, sel, p, shared)
+
+
+def expert_linear_mxfp8_rows(x, packed, scales, sel, p, shared, rows) -> np.ndarray:
+    """expert_linear_mxfp8 restricted to the output rows ``rows``."""
+    xh = dequantize_mxfp8(*quantize_mxfp8(x))
+    return expert_linear_rows(xh, packed, scales, sel, p, shared, rows)

@@ -628,3 +628,141 @@ def test_router_weights_of_any_selection_brute_force(mode):
     keys = oracle.route_keys(logits, np.arange(11) * 0.1, mode)
     want = logits if mode == "softmax" else 1.0 / (1.0 + np.exp(-logits)) + np.arange(11) * 0.1
     np.testing.assert_allclose(keys, want, rtol=1e-15)
+
+
+# ------------------------------------------- MXFP8 activations (variant)
+
+def test_e4m3_table_facts():
+    t = oracle.E4M3_TABLE
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0x80] == 0.0 and math.copysign(1.0, t[0x80]) == -1.0
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)  # 0x00 .. 0x7e strictly increasing
+    np.testing.assert_array_equal(t[0x80:0xFF], -pos)
+    # eight steps per binade from 2^-6 up; the subnormals are multiples of 2^-9
+    for e in range(-6, 9):
+        codes = [c for c in range(0x7F) if 2.0 ** e <= t[c] < 2.0 ** (e + 1)]
+        assert len(codes) == (8 if e < 8 else 7), e
+        np.testing.assert_allclose(np.diff(t[codes]), 2.0 ** (e - 3))
+    np.testing.assert_array_equal(t[:8], np.arange(8) * 2.0 ** -9)
+
+
+def test_e4m3_round_trip_every_finite_code():
+    t = oracle.E4M3_TABLE
+    fin = [c for c in range(256) if not np.isnan(t[c])]
+    assert oracle.quantize_e4m3(t[fin]).tolist() == fin
+
+
+def _nearest_e4m3_brute(v):
+    """Nearest finite E4M3 value by search; ties to the even code; beyond
+    448 the clamp; the sign kept."""
+    t = oracle.E4M3_TABLE
+    a = min(abs(v), 448.0)
+    best = None
+    for c in range(0x7F):
+        d = abs(t[c] - a)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (0x80 if math.copysign(1.0, v) < 0 else 0)
+
+
+def test_e4m3_quantize_brute_force():
+    rng = _rng(7)
+    mags = np.ldexp(rng.uniform(0.5, 1.0, 400), rng.integers(-12, 11, 400))
+    vals = mags * rng.choice([-1.0, 1.0], 400)
+    # exact ties between neighbours, and the top of the range
+    t = oracle.E4M3_TABLE
+    ties = [(t[c] + t[c + 1]) / 2 for c in range(0, 0x7E, 3)]
+    vals = np.concatenate([vals, ties, [-x for x in ties], [447.0, 448.0, 455.9, 456.0, 463.9, 464.0, 500.0, 1e9]])
+    got = oracle.quantize_e4m3(vals)
+    want = [_nearest_e4m3_brute(float(v)) for v in vals]
+    assert got.tolist() == want
+
+
+def test_mxfp8_block_exponent_brute_force():
+    rng = _rng(8)
+    amax = np.concatenate([np.ldexp(rng.uniform(0.5, 1.0, 300), rng.integers(-140, 130, 300)),
+                           [448.0, np.nextafter(448.0, 1e9), 1.0, 0.875 * 2.0 ** 9, 2.0 ** -140, 0.0]])
+    got = oracle.mxfp8_block_exponent(amax)
+    for a, X in zip(amax, got):
+        if a == 0:
+            assert X == -127
+            continue
+        want = next(x for x in range(-127, 128) if a <= 448.0 * 2.0 ** x) if a <= 448.0 * 2.0 ** 127 else 127
+        assert X == want, (a, X, want)
+    assert got[-6:-1].tolist() == [0, 1, -8, 0, -127]
+
+
+def test_mxfp8_quantize_blocks():
+    rng = _rng(9)
+    x = rng.standard_normal((5, 96)) * np.ldexp(1.0, rng.integers(-20, 20, (5, 1)))
+    x[2, 32:64] = 0.0  # an all-zero block
+    x[3, 0:32] = np.linspace(-448.0, 448.0, 32)  # a block that fits at X = 0 exactly
+    codes, sb = oracle.quantize_mxfp8(x)
+    assert codes.shape == (5, 96) and sb.shape == (5, 3)
+    assert sb[2, 1] == 0 and np.all(codes[2, 32:64] == 0)
+    assert sb[3, 0] == 127
+    xh = oracle.dequantize_mxfp8(codes, sb)
+    blocks = np.abs(x).reshape(5, 3, 32)
+    X = sb.astype(np.int64) - 127
+    # the block max fits without clamping: within 448 * 2^X and above half of it
+    nz = blocks.max(2) > 0
+    assert np.all(blocks.max(2)[nz] <= 448.0 * np.ldexp(1.0, X[nz]))
+    assert np.all(blocks.max(2)[nz] > 224.0 * np.ldexp(1.0, X[nz]))
+    # error: half a quantum of the element's binade (2^-4 relative for normals,
+    # 2^(X-10) absolute below 2^(X-6))
+    err = np.abs(xh - x).reshape(5, 3, 32)
+    scale = np.ldexp(1.0, X)[:, :, None]
+    bound = np.maximum(blocks * 2.0 ** -4, scale * 2.0 ** -10)
+    assert np.all(err <= bound)
+    # values already on the grid come back unchanged
+    r = np.ldexp(1.0, rng.integers(-5, 5, (4, 1)))
+    ong = oracle.E4M3_TABLE[rng.integers(0, 0x7F, (4, 64))] * r
+    ong[:, 0] = ong[:, 32] = 448.0 * r[:, 0]  # each block's maximum fixes its scale at r
+    np.testing.assert_array_equal(oracle.dequantize_mxfp8(*oracle.quantize_mxfp8(ong)), ong)
+
+
+def test_mxfp8_linear_composition_and_error():
+    """On grid activations the variant equals the exact layer; on normal
+    activations it differs by the activation rounding only (relative L2 a few
+    percent, far above the exact layer's rounding)."""
+    rng = _rng(10)
+    T, E, K, G, O = 6, 5, 2, 3, 24
+    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
+    scales = rng.integers(120, 131, (E, O, G), dtype=np.uint8)
+    sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    p = rng.uniform(0.1, 1.0, (T, K))
+    shared = rng.standard_normal((T, O))
+    r = np.ldexp(1.0, rng.integers(-3, 3, (T, 1)))
+    xg = oracle.E4M3_TABLE[rng.integers(0, 0x7F, (T, 32 * G))] * r
+    xg[:, ::32] = 448.0 * r  # each block's maximum fixes its scale at r
+    np.testing.assert_array_equal(oracle.expert_linear_mxfp8(xg, packed, scales, sel, p, shared),
+                                  oracle.expert_linear(xg, packed, scales, sel, p, shared))
+    x = rng.standard_normal((T, 32 * G))
+    ya = oracle.expert_linear_mxfp8(x, packed, scales, sel, p, shared * 0)
+    ye = oracle.expert_linear(x, packed, scales, sel, p, shared * 0)
+    rel = np.linalg.norm(ya - ye) / np.linalg.norm(ye)
+    assert 1e-3 < rel < 5e-2, rel
+    rows = np.array([0, 7, 23])
+    np.testing.assert_array_equal(oracle.expert_linear_mxfp8_rows(x, packed, scales, sel, p, shared, rows),
+                                  oracle.expert_linear_mxfp8(x, packed, scales, sel, p, shared)[:, rows])
+
+
+def test_mxfp8_planted_mistakes_are_caught(monkeypatch):
+    rng = _rng(11)
+    vals = np.concatenate([(oracle.E4M3_TABLE[1:0x7E] + oracle.E4M3_TABLE[2:0x7F]) / 2, rng.uniform(-500, 500, 50)])
+    want = [_nearest_e4m3_brute(float(v)) for v in vals]
+    mistakes = {
+        "ties away from zero": lambda mp: mp.setattr(om.np, "rint", lambda a: np.floor(np.asarray(a) + 0.5)),
+        "bias 8": lambda mp: mp.setattr(om, "E4M3_BIAS", 8),
+        "no subnormal floor": lambda mp: mp.setattr(om, "E4M3_MIN_NORMAL_EXP", -60),
+    }
+    for name, plant in mistakes.items():
+        with monkeypatch.context() as mp:
+            plant(mp)
+            assert om.quantize_e4m3(vals).tolist() != want, f"planted mistake not caught: {name}"
+    # the standard's floor(log2 amax) - 8 scale rule instead of the fitting one
+    amax = np.array([300.0, 448.0, 500.0, 1.0])
+    floor_rule = np.floor(np.log2(amax)).astype(np.int64) - 8
+    assert not np.array_equal(floor_rule, oracle.mxfp8_block_exponent(amax))
