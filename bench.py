@@ -42,6 +42,7 @@ import workloads  # noqa: E402
 METRIC = "packed-weight GB/s (decode) & TFLOP/s (prefill), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 MFMA, published (the fp4 x fp8 scaled MFMA runs at this rate)
 N_ROUTING_SETS = 64
 DECODE_WORKLOADS = ("tiny", "decode", "decode8")
 KERNEL_SOURCES = {
@@ -49,6 +50,7 @@ KERNEL_SOURCES = {
              "mxfp4_block_scaled_amd/csrc/wave_routing.h"],
     "gemm": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "swiglu": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+    "mx": ["mxfp4_block_scaled_amd/csrc/gemm_mx.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
 }
 
 
@@ -145,7 +147,11 @@ def record_traffic(args):
     print(json.dumps({w.name: rec}))
 
 
-def _kind(w) -> str:
+def _kind(w, variant=None) -> str:
+    if variant == "mxfp8":
+        if w.F or w.dtype != "bf16":
+            raise SystemExit("the MXFP8 variant runs the bf16 routed linear workloads only")
+        return "mx"
     if w.F:
         return "swiglu"
     return "gemv" if w.name in DECODE_WORKLOADS else "gemm"
@@ -198,7 +204,8 @@ def cpu_baseline(inp, kind, sample_seconds):
     rng = np.random.default_rng(0)
     while True:
         rows = np.sort(rng.choice(w.O, rows_per_call, replace=False))
-        oracle.expert_linear_rows(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
+        rows_fn = oracle.expert_linear_mxfp8_rows if kind == "mx" else oracle.expert_linear_rows
+        rows_fn(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
         done_flops += 2.0 * w.P * rows_per_call * w.I
         calls += 1
         if time.perf_counter() - t0 >= sample_seconds:
@@ -210,6 +217,8 @@ def cpu_baseline(inp, kind, sample_seconds):
 
 
 def _path_name(mx, w, kind) -> str:
+    if kind == "mx":
+        return "MXFP8 variant (bucketing, quantisation, scaled-MFMA grouped GEMM, combine)"
     if kind == "swiglu":
         return "SwiGLU block (bucketing, gate/up GEMM, down GEMM, combine)"
     return "GEMV" if mx.select_path(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1) == 1 else "GEMM"
@@ -329,6 +338,8 @@ def main():
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="host only: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload and of "
                          "the copy calibration (--copy-mib) into profiles/traffic.json")
+    ap.add_argument("--variant", choices=["mxfp8"],
+                    help="time the block-scaled variant (MXFP8 activations on the scaled MFMA) instead of the layer")
     ap.add_argument("--router", choices=["softmax", "sigmoid"],
                     help="time the router alone at the workload's T, E and K instead of the layer")
     args = ap.parse_args()
@@ -358,7 +369,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.WORKLOADS[args.workload]
-    kind = _kind(w)
+    kind = _kind(w, args.variant)
     td = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     t_gen = time.perf_counter()
     inp = workloads.make_inputs(w, n_routing_sets=N_ROUTING_SETS)
@@ -381,6 +392,8 @@ def main():
     y = torch.empty_like(shared)
     if kind == "swiglu":
         ws_bytes = mx.swiglu_workspace_size(w.T, w.E, w.F, w.G, w.O, w.K)
+    elif kind == "mx":
+        ws_bytes = mx.mxfp8_workspace_size(w.T, w.E, w.O, w.G, w.K)
     else:
         ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -393,6 +406,8 @@ def main():
         r = i % N_ROUTING_SETS
         if kind == "swiglu":
             mx.moe_swiglu(x, packed, scales, dn_packed, dn_scales, sels[r], ps[r], shared, out=y, workspace=ws)
+        elif kind == "mx":
+            mx.moe_linear_mxfp8(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
         else:
             mx.moe_linear(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
 
@@ -475,7 +490,16 @@ def main():
     flops_per_step = 2.0 * w.P * w.O * w.I
     if kind == "swiglu":
         flops_per_step = 2.0 * w.P * (2 * w.F * w.I + w.O * w.F)
-    if kind == "swiglu":
+    if kind == "mx":
+        # the variant's grouped GEMM on the scaled MFMA is its work; timed as
+        # the whole call (bucketing, quantisation and combine included)
+        value = flops_per_step / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(value / MFMA_FP8_PEAK_TFLOPS, 4)}
+        roof["kernel"] = "gemm_mx_kernel (whole call)"
+        roof["launch_ms"] = round(ms_step, 6)
+    elif kind == "swiglu":
         # the block's two grouped GEMMs are its work; timed here as the whole
         # call (bucketing and combine included), a lower bound on the GEMMs
         value = flops_per_step / (ms_step * 1e-3) / 1e12
@@ -501,9 +525,9 @@ def main():
         roof["kernel"] = "gemm_bf16_kernel"
         roof["launch_ms"] = round(gemm_ms, 6)
     roof["per_launch"] = ({"bytes": bytes_per_step} if kind == "gemv" else {"flops": flops_per_step})
-    if kind == "swiglu":
+    if kind in ("swiglu", "mx"):
         roof["traffic"] = None
-    if kind != "swiglu":
+    else:
         roof["traffic"] = committed_traffic(w.name, kind)
     log(f"[bench] {args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, "
         f"{value:.1f} {unit} ({100 * roof['frac']:.1f}% of peak); mean distinct experts {np.mean(uniq):.1f}")
@@ -511,8 +535,9 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if w.dtype == "fp32" else "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
+        "vs_baseline": None, "dtype": "fp4xfp8" if kind == "mx" else ("f32" if w.dtype == "fp32" else "bf16"),
+        "data": "synthetic",
+        "config": {"workload": w.name + ("-mxfp8" if kind == "mx" else ""), "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
                    **({"F": w.F} if w.F else {}),
                    "x_dtype": w.dtype, "routing": w.routing if w.routing == "uniform" else f"zipf({w.zipf_s})",
                    "routing_draws": N_ROUTING_SETS, "graph": graph is not None},

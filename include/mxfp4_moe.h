@@ -231,6 +231,47 @@ int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mxfp4_quantize_mxfp8 - activations to MXFP8: per token and block of 32
+ * inputs one E8M0 scale byte s (2^(s-127)) and 32 E4M3 codes (OCP
+ * Microscaling family, blocks of 32 codes sharing one E8M0 scale: page
+ * "MXFP4 Dequant", "Overview"). Readings, the pages being silent: E4M3 has
+ * bias 7, 3 mantissa bits, largest value 448; the scale is the smallest power
+ * of two 2^X with max|block| <= 448 * 2^X (X clamped to [-127, 127]; an
+ * all-zero block takes -127); each code is x / 2^X rounded to nearest, ties
+ * to even, sign kept.
+ *   x (T, I) bf16 raw bits, I a positive multiple of 32, 8-byte aligned;
+ *   codes (T, ld) and scale_bytes (T, ld / 32), ld >= I a multiple of 32,
+ *   codes 4-byte aligned; columns [I, ld) get zero codes and scale bytes 0.
+ * T * ld < 2^31; no overlap. MXFP4_ERR_INVALID_ARG otherwise. Enqueued on
+ * `stream`, no allocation.
+ */
+int mxfp4_quantize_mxfp8(const uint16_t* x, int64_t T, int64_t I, int64_t ld, uint8_t* codes, uint8_t* scale_bytes,
+                         hipStream_t stream);
+
+/*
+ * mxfp4_moe_linear_mxfp8_ex - the block-scaled variant of the layer (bf16
+ * x, shared, y; p fp32): the routed linear of mxfp4_moe_linear_ex computed
+ * with the activations quantised to MXFP8 as mxfp4_quantize_mxfp8 does and
+ * multiplied by the packed weights and scale bytes as stored on gfx950's
+ * block-scaled MFMA (no weight dequantisation):
+ *   y[t] = shared[t] + sum_k p[t,k] * W_sel[t,k] q(x[t]).
+ * This is an approximation of mxfp4_moe_linear_ex (the activation rounding,
+ * relative L2 error a few percent), reported separately from it. Weight
+ * scale bytes must be below 255 (the MFMA reads 255 as NaN). Needs O % 4 == 0,
+ * T * 128 * ceil(32G / 128) < 2^31 and O * G * 16 < 2^31, else
+ * MXFP4_ERR_UNSUPPORTED. Work: bucketing, quantisation, a grouped GEMM on the
+ * scaled MFMA, the combine. Caller-owned workspace of
+ * mxfp4_moe_mxfp8_workspace_size bytes (256-byte aligned); flags 0 or
+ * MXFP4_FLAG_CHECK. Allocates nothing; may be captured in a graph. Other
+ * errors and the aliasing rule as mxfp4_moe_linear_ex.
+ */
+int mxfp4_moe_mxfp8_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, size_t* bytes);
+int mxfp4_moe_linear_mxfp8_ex(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                              const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+                              int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * mxfp4_moe_route - the router that produces sel and p from router logits
  * (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
  * Experts", section 1, for both router kinds and the floor on the selected

@@ -21,13 +21,14 @@ from . import _abi
 from ._abi import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, FLAG_CHECK, FLAG_FORCE_GEMM, FLAG_FORCE_GEMV, FLAG_GEMV_MFMA, FLAG_BUCKET_MULTI_BLOCK,
     FLAG_BUCKET_ONE_BLOCK, PATH_GEMM, PATH_GEMV, ROUTE_SIGMOID, ROUTE_SOFTMAX, Mxfp4Error, bucket_workspace_size,
-    select_path,
+    mxfp8_workspace_size, select_path,
     status_string, swiglu_workspace_size, workspace_size,
 )
 
 __all__ = [
     "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
-    "swiglu_workspace_size", "select_path", "route", "Mxfp4Error", "library_path",
+    "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
+    "Mxfp4Error", "library_path",
 ]
 
 _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
@@ -158,6 +159,62 @@ def moe_swiglu(x: torch.Tensor, gu_packed: torch.Tensor, gu_scales: torch.Tensor
             _ptr(x), _ptr(gu_packed), _ptr(gu_scales), _ptr(dn_packed), _ptr(dn_scales), _ptr(sel), _ptr(p),
             _ptr(shared), _ptr(y), T, E, F, G, O, K, flags, _ptr(workspace), workspace.numel(), _stream(dev))
     _abi.check(st, "mxfp4_moe_swiglu_ex")
+    return y
+
+
+def quantize_mxfp8(x: torch.Tensor, ld: int | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 activations [T, I] -> (E4M3 codes uint8 [T, ld], E8M0 scale
+    bytes uint8 [T, ld/32]), one scale per token and block of 32 inputs;
+    columns past I hold zeros. ld defaults to I."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    T, I = x.shape
+    ld = I if ld is None else ld
+    codes = torch.empty((T, ld), dtype=torch.uint8, device=dev)
+    sb = torch.empty((T, ld // 32), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_quantize_mxfp8(_ptr(x), T, I, ld, _ptr(codes), _ptr(sb), _stream(dev))
+    _abi.check(st, "mxfp4_quantize_mxfp8")
+    return codes, sb
+
+
+def moe_linear_mxfp8(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, sel: torch.Tensor,
+                     p: torch.Tensor, shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The block-scaled variant of ``moe_linear`` (bf16 only): activations
+    quantised to MXFP8, multiplied by the packed weights as stored on the
+    block-scaled MFMA. An approximation of ``moe_linear`` (activation
+    rounding), reported separately. Shapes as ``moe_linear``."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be on a HIP device")
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(packed, "packed", torch.uint8, 4, dev)
+    _need(scales, "scales", torch.uint8, 3, dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    _need(shared, "shared", torch.bfloat16, 2, dev)
+    T, I = x.shape
+    E, O, G, B = packed.shape
+    K = sel.shape[1]
+    if B != 16 or I != 32 * G or tuple(scales.shape) != (E, O, G):
+        raise ValueError(f"packed must be [E, O, G, 16] with 32G == x.shape[1] and scales [E, O, G]")
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K) or tuple(shared.shape) != (T, O):
+        raise ValueError("sel and p must be [T, K] and shared [T, O]")
+    y = torch.empty_like(shared) if out is None else out
+    _need(y, "out", torch.bfloat16, 2, dev)
+    if tuple(y.shape) != (T, O):
+        raise ValueError("out must be [T, O]")
+    need = _abi.mxfp8_workspace_size(T, E, O, G, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev:
+        raise ValueError("workspace must be a uint8 tensor on x's device")
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_linear_mxfp8_ex(
+            _ptr(x), _ptr(packed), _ptr(scales), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, O, G, K, flags,
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_linear_mxfp8_ex")
     return y
 
 

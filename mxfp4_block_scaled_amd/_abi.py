@@ -61,6 +61,9 @@ SIGNATURES = {
     "mxfp4_moe_swiglu_workspace_size": (_int, [_i64] * 6 + [ctypes.POINTER(_sz)]),
     "mxfp4_moe_swiglu_ex": (_int, [_vp] * 9 + [_i64] * 6 + [_u32, _vp, _sz, _vp]),
     "mxfp4_moe_route": (_int, [_vp] * 2 + [_i64] * 3 + [_int, ctypes.c_float, _vp, _vp, _vp]),
+    "mxfp4_quantize_mxfp8": (_int, [_vp] + [_i64] * 3 + [_vp, _vp, _vp]),
+    "mxfp4_moe_mxfp8_workspace_size": (_int, [_i64] * 5 + [ctypes.POINTER(_sz)]),
+    "mxfp4_moe_linear_mxfp8_ex": (_int, [_vp] * 7 + [_i64] * 5 + [_u32, _vp, _sz, _vp]),
     "mxfp4_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -106,6 +109,12 @@ def workspace_size(T, E, O, G, K, dtype, flags=0) -> int:
 def swiglu_workspace_size(T, E, F, G, O, K) -> int:
     out = _sz(0)
     check(lib().mxfp4_moe_swiglu_workspace_size(T, E, F, G, O, K, ctypes.byref(out)), "swiglu_workspace_size")
+    return out.value
+
+
+def mxfp8_workspace_size(T, E, O, G, K) -> int:
+    out = _sz(0)
+    check(lib().mxfp4_moe_mxfp8_workspace_size(T, E, O, G, K, ctypes.byref(out)), "mxfp8_workspace_size")
     return out.value
 
 

@@ -290,6 +290,24 @@ int check_swiglu_args(const uint16_t* x, const uint8_t* gu_packed, const uint8_t
   return MXFP4_OK;
 }
 
+// the block-scaled variant: the bucketing and partial rows of the prefill
+// layout, then the MXFP8 codes (T, Kp) and scale bytes (T, Kp / 32)
+struct MxLayout {
+  Layout L;
+  int Kp;
+  size_t xq, xs, total;
+};
+
+MxLayout mx_layout(const Dims& d) {
+  MxLayout M;
+  M.L = layout(d, MXFP4_PATH_GEMM);
+  M.Kp = mx_row_bytes(d.I);
+  M.xq = M.L.total;
+  M.xs = align_up(M.xq + (size_t)d.T * M.Kp);
+  M.total = align_up(M.xs + (size_t)d.T * M.Kp / 32);
+  return M;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +364,76 @@ int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8
   if (err == hipSuccess)
     err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.dn.T, (int)d.dn.K, (int)d.dn.O, MXFP4_DTYPE_BF16,
                          stream);
+  if (err != hipSuccess) return MXFP4_ERR_HIP;
+  if (flags & MXFP4_FLAG_CHECK) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+    int32_t inv = 0;
+    if (hipMemcpy(&inv, b.n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
+    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
+  }
+  return MXFP4_OK;
+}
+
+int mxfp4_quantize_mxfp8(const uint16_t* x, int64_t T, int64_t I, int64_t ld, uint8_t* codes, uint8_t* scale_bytes,
+                         hipStream_t stream) {
+  if (T < 0 || I < 32 || I % 32 || ld < I || ld % 32 || T * ld >= (int64_t(1) << 31)) return MXFP4_ERR_INVALID_ARG;
+  if (T == 0) return MXFP4_OK;
+  if (!x || !codes || !scale_bytes || !aligned(x, 8) || !aligned(codes, 4)) return MXFP4_ERR_INVALID_ARG;
+  const size_t nx = size_t(T) * I * 2, nc = size_t(T) * ld, ns = nc / 32;
+  if (overlap(codes, nc, x, nx) || overlap(scale_bytes, ns, x, nx) || overlap(codes, nc, scale_bytes, ns))
+    return MXFP4_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != MXFP4_OK) return st;
+  return hip_status(launch_quant_mxfp8(x, (int)T, (int)I, (int)ld, codes, scale_bytes, stream));
+}
+
+int mxfp4_moe_mxfp8_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  Dims d;
+  const int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  *bytes = (T == 0) ? 0 : mx_layout(d).total;
+  return MXFP4_OK;
+}
+
+int mxfp4_moe_linear_mxfp8_ex(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                              const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+                              int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~MXFP4_FLAG_CHECK) return MXFP4_ERR_INVALID_ARG;
+  st = check_linear_args(x, packed, scales, sel, p, shared, y, d, MXFP4_DTYPE_BF16);
+  if (st != MXFP4_OK) return st;
+  if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  if (d.T == 0) return MXFP4_OK;
+  const MxLayout M = mx_layout(d);
+  if (workspace_bytes < M.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  const Layout& L = M.L;
+  BucketOut b;
+  b.count = reinterpret_cast<int32_t*>(base + L.count);
+  b.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  b.perm = reinterpret_cast<int32_t*>(base + L.perm);
+  b.slot_of_pair = reinterpret_cast<int32_t*>(base + L.slot);
+  b.n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
+  b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
+  b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + M.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(base + M.xs);
+  float* part = reinterpret_cast<float*>(base + L.part);
+  hipError_t err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
+  if (err == hipSuccess) err = launch_quant_mxfp8(x, (int)d.T, (int)d.I, M.Kp, xq, xs, stream);
+  if (err == hipSuccess)
+    err = launch_gemm_mx(xq, xs, packed, scales, b.perm, b.tiles, b.n_tiles, gemm_max_tiles(d.P, d.E), part, (int)d.T,
+                         (int)d.K, (int)d.O, (int)d.G, stream);
+  if (err == hipSuccess)
+    err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.T, (int)d.K, (int)d.O, MXFP4_DTYPE_BF16, stream);
   if (err != hipSuccess) return MXFP4_ERR_HIP;
   if (flags & MXFP4_FLAG_CHECK) {
     if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;

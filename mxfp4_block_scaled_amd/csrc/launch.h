@@ -76,6 +76,16 @@ hipError_t launch_gemv_rows(const void* x, const uint8_t* packed, const uint8_t*
                             const float* p, const void* shared, void* y, int T, int E, int O, int G, int K, int dtype,
                             int32_t* n_invalid, int chunk_index, hipStream_t stream);
 
+// ---- block-scaled variant: MXFP8 activations x MXFP4 weights on the scaled MFMA.
+// Activation rows are padded to mx_row_bytes(I) = 128 * ceil(I / 128) codes.
+int mx_row_bytes(int64_t I);
+bool gemm_mx_supported(int64_t T, int64_t O, int64_t G);  // O % 4 == 0, T * Kp and O * G * 16 below 2^31
+hipError_t launch_quant_mxfp8(const uint16_t* x, int T, int I, int Kp, uint8_t* codes, uint8_t* sb,
+                              hipStream_t stream);
+hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* packed, const uint8_t* scales,
+                          const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                          float* part, int T, int K, int O, int G, hipStream_t stream);
+
 // ---- router: logits (T, E) fp32 -> sel (T, K) int32, p (T, K) fp32.
 // mode 0 softmax, 1 sigmoid with a selection-only bias (may be null).
 // One token per group of `lanes` lanes (32 or 64; 0 = route_lanes' choice).

@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES)
@@ -230,3 +230,51 @@ def test_route_host_checks_reject(kw):
 def test_route_empty_batch_is_a_no_op():
     assert _route(T=0, logits=0, sel=0, p=0) == _abi.OK
     assert _route(T=0, mode=1, bias=C + 0x1000) == _abi.OK
+
+
+# ---- the block-scaled variant
+
+def _mx(x=A, packed=B, scales=C, sel=C + 0x10000, p=C + 0x20000, shared=C + 0x30000, y=C + 0x40000, T=2, E=3,
+        O=8, G=2, K=2, flags=0, ws=C + 0x60000, ws_bytes=1 << 24):
+    return _abi.lib().mxfp4_moe_linear_mxfp8_ex(x, packed, scales, sel, p, shared, y, T, E, O, G, K, flags, ws,
+                                                ws_bytes, None)
+
+
+def test_mxfp8_workspace_size():
+    assert _abi.mxfp8_workspace_size(0, 4, 8, 2, 2) == 0
+    T, E, O, G, K = 4096, 128, 5760, 90, 4
+    ws = _abi.mxfp8_workspace_size(T, E, O, G, K)
+    assert ws >= T * K * O * 4 + T * 2944 + T * 2944 // 32  # fp32 partial rows, codes and scales of 128-padded rows
+    with pytest.raises(_abi.Mxfp4Error) as e:  # O % 4 != 0
+        _abi.mxfp8_workspace_size(4, 4, 6, 2, 2)
+    assert e.value.status == _abi.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(E=0), dict(O=0), dict(G=0), dict(K=0), dict(flags=_abi.FLAG_FORCE_GEMM), dict(flags=0x100),
+    dict(x=0), dict(packed=0), dict(scales=0), dict(sel=0), dict(p=0), dict(shared=0), dict(y=0),
+    dict(x=A + 2), dict(sel=C + 0x10001), dict(y=A), dict(y=B + 16),
+])
+def test_mxfp8_host_checks_reject(kw):
+    assert _mx(**kw) == _abi.ERR_INVALID_ARG
+
+
+def test_mxfp8_host_checks_workspace_unsupported_and_empty():
+    assert _mx(ws_bytes=16) == _abi.ERR_WORKSPACE_TOO_SMALL
+    assert _mx(O=6) == _abi.ERR_UNSUPPORTED
+    assert _mx(T=0, x=0, y=0, shared=0, sel=0, p=0) == _abi.OK
+
+
+@pytest.mark.parametrize("args", [
+    (A, -1, 64, 64, B, C), (A, 2, 48, 64, B, C), (A, 2, 64, 48, B, C), (A, 2, 64, 80, B, C), (A, 2, 0, 32, B, C),
+    (0, 2, 64, 64, B, C), (A, 2, 64, 64, 0, C), (A, 2, 64, 64, B, 0), (A + 4, 2, 64, 64, B, C),
+    (A, 2, 64, 64, B + 2, C), (A, 2, 64, 64, A + 64, C), (A, 2, 64, 64, B, A + 8),
+    (A, 1 << 25, 64, 64, B, C),
+])
+def test_quantize_mxfp8_host_checks(args):
+    x, T, I, ld, codes, sb = args
+    assert _abi.lib().mxfp4_quantize_mxfp8(x, T, I, ld, codes, sb, None) == _abi.ERR_INVALID_ARG
+
+
+def test_quantize_mxfp8_empty():
+    assert _abi.lib().mxfp4_quantize_mxfp8(0, 0, 64, 64, 0, 0, None) == _abi.OK
