@@ -340,6 +340,8 @@ def main():
                          "the copy calibration (--copy-mib) into profiles/traffic.json")
     ap.add_argument("--variant", choices=["mxfp8"],
                     help="time the block-scaled variant (MXFP8 activations on the scaled MFMA) instead of the layer")
+    ap.add_argument("--prepared", action="store_true",
+                    help="with --variant mxfp8: weights repacked once (outside the timed region) by prepare_mx")
     ap.add_argument("--router", choices=["softmax", "sigmoid"],
                     help="time the router alone at the workload's T, E and K instead of the layer")
     args = ap.parse_args()
@@ -397,6 +399,11 @@ def main():
     else:
         ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    prepared = None
+    if args.prepared:
+        if kind != "mx":
+            raise SystemExit("--prepared goes with --variant mxfp8")
+        prepared = mx.prepare_mx(packed, scales)
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs drawn and resident in {time.perf_counter() - t_gen:.1f} s; "
         f"packed {packed.numel() / 1e9:.2f} GB, workspace {ws.numel() / 1e6:.1f} MB, "
@@ -406,6 +413,8 @@ def main():
         r = i % N_ROUTING_SETS
         if kind == "swiglu":
             mx.moe_swiglu(x, packed, scales, dn_packed, dn_scales, sels[r], ps[r], shared, out=y, workspace=ws)
+        elif kind == "mx" and prepared is not None:
+            mx.moe_linear_mxfp8_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "mx":
             mx.moe_linear_mxfp8(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
         else:
@@ -497,7 +506,7 @@ def main():
         unit = "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(value / MFMA_FP8_PEAK_TFLOPS, 4)}
-        roof["kernel"] = "gemm_mx_kernel (whole call)"
+        roof["kernel"] = "gemm_mx_kernel<%s> (whole call)" % ("true" if prepared is not None else "false")
         roof["launch_ms"] = round(ms_step, 6)
     elif kind == "swiglu":
         # the block's two grouped GEMMs are its work; timed here as the whole
@@ -537,7 +546,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp4xfp8" if kind == "mx" else ("f32" if w.dtype == "fp32" else "bf16"),
         "data": "synthetic",
-        "config": {"workload": w.name + ("-mxfp8" if kind == "mx" else ""), "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
+        "config": {"workload": w.name + ("-mxfp8" if kind == "mx" else "") + ("-prepared" if prepared is not None else ""),
+                   "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
                    **({"F": w.F} if w.F else {}),
                    "x_dtype": w.dtype, "routing": w.routing if w.routing == "uniform" else f"zipf({w.zipf_s})",
                    "routing_draws": N_ROUTING_SETS, "graph": graph is not None},

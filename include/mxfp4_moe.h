@@ -272,6 +272,35 @@ int mxfp4_moe_linear_mxfp8_ex(const uint16_t* x, const uint8_t* packed, const ui
                               hipStream_t stream);
 
 /*
+ * Load-time weight repack for the block-scaled variant. The prepared buffer
+ * holds, per expert, per N-tile of 128 output rows, per chunk of 128 inputs
+ * (4 groups) and per 16-row fragment, 64 group slots of 16 code bytes in the
+ * order the scaled MFMA's weight operand takes them (slot l: row 16 f + (l mod
+ * 16) of the tile, group 4 q + l / 16), so that every wave-wide weight request
+ * reads 1 KB of consecutive bytes; after all code slots come the slots' scale
+ * bytes in the same order (64 consecutive bytes per request). Rows past O and
+ * groups past G are zero. The canonical [E, O, G, 16] / [E, O, G] arrays are
+ * the pages' format (page "MXFP4 Experts", shape paragraph); this is a byte
+ * permutation of them plus zero padding, nothing is decoded.
+ *   mxfp4_mx_prepared_size: bytes of the prepared buffer (17 per slot).
+ *   mxfp4_prepare_mx: packed (E, O, G, 16) and scales (E, O, G) device arrays
+ *     (packed 16-byte aligned) -> prepared (16-byte aligned, bytes >= the
+ *     size; no overlap). Enqueued on `stream`; call once per weight set.
+ *   mxfp4_moe_linear_mxfp8_prepared_ex: mxfp4_moe_linear_mxfp8_ex reading the
+ *     prepared buffer instead of packed and scales; the same workspace size,
+ *     flags, errors and results bit for bit.
+ * Sizes as mxfp4_moe_linear_mxfp8_ex (MXFP4_ERR_UNSUPPORTED also when one
+ * expert's prepared codes reach 2^31 bytes).
+ */
+int mxfp4_mx_prepared_size(int64_t E, int64_t O, int64_t G, size_t* bytes);
+int mxfp4_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, void* prepared,
+                     size_t bytes, hipStream_t stream);
+int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,
+                                       const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+                                       int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * mxfp4_moe_route - the router that produces sel and p from router logits
  * (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
  * Experts", section 1, for both router kinds and the floor on the selected

@@ -28,6 +28,7 @@ from ._abi import (  # noqa: F401
 __all__ = [
     "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
+    "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared",
     "Mxfp4Error", "library_path",
 ]
 
@@ -215,6 +216,66 @@ def moe_linear_mxfp8(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
             _ptr(x), _ptr(packed), _ptr(scales), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, O, G, K, flags,
             _ptr(workspace), workspace.numel(), _stream(dev))
     _abi.check(st, "mxfp4_moe_linear_mxfp8_ex")
+    return y
+
+
+class PreparedMx:
+    """Weights repacked for the block-scaled variant (``prepare_mx``): a
+    uint8 device buffer and the (E, O, G) it was made from."""
+
+    def __init__(self, buf: torch.Tensor, E: int, O: int, G: int):
+        self.buf, self.E, self.O, self.G = buf, E, O, G
+
+
+def prepare_mx(packed: torch.Tensor, scales: torch.Tensor) -> PreparedMx:
+    """Load-time repack of [E, O, G, 16] codes and [E, O, G] scale bytes into
+    the fragment-major layout the block-scaled variant streams (a byte
+    permutation plus zero padding)."""
+    dev = packed.device
+    _need(packed, "packed", torch.uint8, 4, dev)
+    _need(scales, "scales", torch.uint8, 3, dev)
+    E, O, G, B = packed.shape
+    if B != 16 or tuple(scales.shape) != (E, O, G):
+        raise ValueError("packed must be [E, O, G, 16] and scales [E, O, G]")
+    n = _abi.mx_prepared_size(E, O, G)
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_prepare_mx(_ptr(packed), _ptr(scales), E, O, G, _ptr(buf), n, _stream(dev))
+    _abi.check(st, "mxfp4_prepare_mx")
+    return PreparedMx(buf, E, O, G)
+
+
+def moe_linear_mxfp8_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.Tensor, p: torch.Tensor,
+                              shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+                              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``moe_linear_mxfp8`` on weights repacked by ``prepare_mx`` (the same
+    result bit for bit)."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    _need(shared, "shared", torch.bfloat16, 2, dev)
+    if not isinstance(prepared, PreparedMx) or prepared.buf.device != dev:
+        raise ValueError("prepared must come from prepare_mx on x's device")
+    T, I = x.shape
+    E, O, G = prepared.E, prepared.O, prepared.G
+    K = sel.shape[1]
+    if I != 32 * G:
+        raise ValueError(f"x has {I} inputs; the prepared weights have 32 * {G}")
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K) or tuple(shared.shape) != (T, O):
+        raise ValueError("sel and p must be [T, K] and shared [T, O]")
+    y = torch.empty_like(shared) if out is None else out
+    _need(y, "out", torch.bfloat16, 2, dev)
+    if tuple(y.shape) != (T, O):
+        raise ValueError("out must be [T, O]")
+    need = _abi.mxfp8_workspace_size(T, E, O, G, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_linear_mxfp8_prepared_ex(
+            _ptr(x), _ptr(prepared.buf), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, O, G, K, flags,
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_linear_mxfp8_prepared_ex")
     return y
 
 

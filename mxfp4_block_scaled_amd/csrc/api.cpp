@@ -308,6 +308,52 @@ MxLayout mx_layout(const Dims& d) {
   return M;
 }
 
+int run_mxfp8(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, bool prepared, const int32_t* sel,
+              const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O, int64_t G,
+              int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~MXFP4_FLAG_CHECK) return MXFP4_ERR_INVALID_ARG;
+  st = check_linear_args(x, packed, scales, sel, p, shared, y, d, MXFP4_DTYPE_BF16);
+  if (st != MXFP4_OK) return st;
+  if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  if (d.T == 0) return MXFP4_OK;
+  const MxLayout M = mx_layout(d);
+  if (workspace_bytes < M.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  const Layout& L = M.L;
+  BucketOut b;
+  b.count = reinterpret_cast<int32_t*>(base + L.count);
+  b.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  b.perm = reinterpret_cast<int32_t*>(base + L.perm);
+  b.slot_of_pair = reinterpret_cast<int32_t*>(base + L.slot);
+  b.n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
+  b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
+  b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + M.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(base + M.xs);
+  float* part = reinterpret_cast<float*>(base + L.part);
+  hipError_t err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
+  if (err == hipSuccess) err = launch_quant_mxfp8(x, (int)d.T, (int)d.I, M.Kp, xq, xs, stream);
+  if (err == hipSuccess)
+    err = launch_gemm_mx(xq, xs, packed, scales, b.perm, b.tiles, b.n_tiles, gemm_max_tiles(d.P, d.E), part, (int)d.T,
+                         (int)d.K, (int)d.O, (int)d.G, stream, prepared);
+  if (err == hipSuccess)
+    err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.T, (int)d.K, (int)d.O, MXFP4_DTYPE_BF16, stream);
+  if (err != hipSuccess) return MXFP4_ERR_HIP;
+  if (flags & MXFP4_FLAG_CHECK) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+    int32_t inv = 0;
+    if (hipMemcpy(&inv, b.n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
+    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
+  }
+  return MXFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -401,47 +447,49 @@ int mxfp4_moe_linear_mxfp8_ex(const uint16_t* x, const uint8_t* packed, const ui
                               const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
                               int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
+  return run_mxfp8(x, packed, scales, false, sel, p, shared, y, T, E, O, G, K, flags, workspace, workspace_bytes,
+                   stream);
+}
+
+int mxfp4_mx_prepared_size(int64_t E, int64_t O, int64_t G, size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
   Dims d;
-  int st = check_dims(T, E, O, G, K, &d);
+  const int st = check_dims(1, E, O, G, 1, &d);
   if (st != MXFP4_OK) return st;
-  if (flags & ~MXFP4_FLAG_CHECK) return MXFP4_ERR_INVALID_ARG;
-  st = check_linear_args(x, packed, scales, sel, p, shared, y, d, MXFP4_DTYPE_BF16);
+  if (!gemm_mx_supported(1, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  *bytes = mx_prepared_bytes(E, O, G);
+  return MXFP4_OK;
+}
+
+int mxfp4_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, void* prepared,
+                     size_t bytes, hipStream_t stream) {
+  Dims d;
+  int st = check_dims(1, E, O, G, 1, &d);
   if (st != MXFP4_OK) return st;
-  if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
-  if (d.T == 0) return MXFP4_OK;
-  const MxLayout M = mx_layout(d);
-  if (workspace_bytes < M.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
-  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  if (!gemm_mx_supported(1, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  const size_t need = mx_prepared_bytes(E, O, G);
+  if (bytes < need) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!packed || !scales || !prepared || !aligned(packed, 16) || !aligned(prepared, 16)) return MXFP4_ERR_INVALID_ARG;
+  if (overlap(prepared, need, packed, (size_t)E * O * G * 16) || overlap(prepared, need, scales, (size_t)E * O * G))
+    return MXFP4_ERR_INVALID_ARG;
   st = check_device();
   if (st != MXFP4_OK) return st;
-  char* base = static_cast<char*>(workspace);
-  const Layout& L = M.L;
-  BucketOut b;
-  b.count = reinterpret_cast<int32_t*>(base + L.count);
-  b.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
-  b.perm = reinterpret_cast<int32_t*>(base + L.perm);
-  b.slot_of_pair = reinterpret_cast<int32_t*>(base + L.slot);
-  b.n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
-  b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
-  b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
-  uint8_t* xq = reinterpret_cast<uint8_t*>(base + M.xq);
-  uint8_t* xs = reinterpret_cast<uint8_t*>(base + M.xs);
-  float* part = reinterpret_cast<float*>(base + L.part);
-  hipError_t err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
-  if (err == hipSuccess) err = launch_quant_mxfp8(x, (int)d.T, (int)d.I, M.Kp, xq, xs, stream);
-  if (err == hipSuccess)
-    err = launch_gemm_mx(xq, xs, packed, scales, b.perm, b.tiles, b.n_tiles, gemm_max_tiles(d.P, d.E), part, (int)d.T,
-                         (int)d.K, (int)d.O, (int)d.G, stream);
-  if (err == hipSuccess)
-    err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.T, (int)d.K, (int)d.O, MXFP4_DTYPE_BF16, stream);
-  if (err != hipSuccess) return MXFP4_ERR_HIP;
-  if (flags & MXFP4_FLAG_CHECK) {
-    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
-    int32_t inv = 0;
-    if (hipMemcpy(&inv, b.n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
-    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
-  }
-  return MXFP4_OK;
+  return hip_status(launch_prepare_mx(packed, scales, E, (int)O, (int)G, static_cast<uint8_t*>(prepared), stream));
+}
+
+int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,
+                                       const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+                                       int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  Dims d;
+  const int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  const uint8_t* pp = static_cast<const uint8_t*>(prepared);
+  const size_t pbytes = mx_prepared_bytes(E, O, G);
+  if (T > 0 && pp && y && overlap(y, (size_t)T * O * 2, pp, pbytes)) return MXFP4_ERR_INVALID_ARG;
+  return run_mxfp8(x, pp, pp ? pp + pbytes / 17 * 16 : nullptr, true, sel, p, shared, y, T, E, O, G, K, flags,
+                   workspace, workspace_bytes, stream);
 }
 
 int mxfp4_moe_route(const float* logits, const float* bias, int64_t T, int64_t E, int64_t K, int mode, float scale,

@@ -23,7 +23,8 @@
 // 16c .. 16c+15 and 64+16c .. 64+16c+15 of the chunk for pair p, and the
 // scale byte of block 4q + c (the hardware applies the scale of lane group c
 // to inputs 32c .. 32c+31 of both operands). Activation rows are gathered
-// (row = perm / K) into LDS once per workgroup and chunk (144-byte rows:
+// (row = perm / K; each wave-wide request reads eight whole 128-byte row
+// pieces) into LDS once per workgroup and chunk (144-byte rows:
 // conflict-free 16-byte reads), double-buffered with one barrier a chunk
 // and fetched two chunks ahead (held a chunk in registers before the LDS
 // store); weights and their scales are loaded three chunks ahead into a
@@ -102,6 +103,10 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
 
 // ---- grouped GEMM
 
+// PREP: the weights come in the prepared layout of prepare_mx_kernel (one
+// contiguous 1 KB block per 16-row fragment and chunk, and a 64-byte block of
+// its scales) instead of the canonical [E, O, G, 16] / [E, O, G].
+template <bool PREP>
 __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                          const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ scales,
@@ -123,53 +128,74 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   const int wm = w >> 1, wn = w & 1;
   const int lr = lane & 15, lc = lane >> 4;
 
-  // activation loader: pair row tid >> 1, bytes 64 (tid & 1) .. +63 of the chunk
-  const int m_ld = tid >> 1, half = tid & 1;
-  const int tok = m_ld < tl.mlen ? perm[tl.row0 + m_ld] / K : -1;
+  // activation loader: wave w, request j covers pair rows 32 w + 8 j .. +7,
+  // eight lanes a row, 16 bytes a lane (the row's 128 bytes of the chunk)
+  const int ld_ch = lane & 7;
+  uint32_t x_off[4], s_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int m = 32 * w + 8 * j + (lane >> 3);
+    const int tok = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
+    x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 16u * ld_ch : kOob;
+    s_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)(Kp / 32) : kOob;
+  }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, (int)xq_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xs, (short)0, (int)xs_bytes, kRsrcFlags);
-  const uint32_t x_off = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 64u * half : kOob;
-  const uint32_t s_off = tok >= 0 ? (uint32_t)tok * (uint32_t)(Kp / 32) : kOob;
 
   // weight fragments: rows f0 + 64 wn + 16 i + lr, group 4 q + lc
-  const int64_t ebase = (int64_t)tl.e * O * G;
-  const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(packed + ebase * 16), (short)0, O * G * 16, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rsc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(scales + ebase), (short)0, O * G, kRsrcFlags);
-  uint32_t w_grp[4];  // group index (row * G + lc) of chunk 0, or kOob
+  const int nq = Kp / KC;
+  const int64_t ebase = (int64_t)tl.e * O * G;                   // canonical layout
+  const int64_t pbase = (int64_t)tl.e * n_ntiles * nq * 512;     // prepared layout: groups before expert e
+  const __amdgpu_buffer_rsrc_t rw = PREP
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)(packed + pbase * 16), (short)0, n_ntiles * nq * 8192, kRsrcFlags)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)(packed + ebase * 16), (short)0, O * G * 16, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rsc = PREP
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)(scales + pbase), (short)0, n_ntiles * nq * 512, kRsrcFlags)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)(scales + ebase), (short)0, O * G, kRsrcFlags);
+  // a wave whose 64 pairs are all past the tile's end multiplies nothing:
+  // its weight requests go past the resource (no memory traffic)
+  const bool w_live = 64 * wm < tl.mlen;
+  uint32_t w_grp[4];  // canonical: group index (row * G + lc) of chunk 0; prepared: group slot of chunk 0; or kOob
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int f = f0 + 64 * wn + 16 * i + lr;
-    // a wave whose 64 pairs are all past the tile's end multiplies nothing:
-    // its weight requests go past the resource (no memory traffic)
-    w_grp[i] = (f < O && 64 * wm < tl.mlen) ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
+    if constexpr (PREP)
+      w_grp[i] = w_live ? (uint32_t)((nt * nq * 8 + 4 * wn + i) * 64 + lane) : kOob;
+    else
+      w_grp[i] = (f < O && w_live) ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
   }
 
   u32x4 xa[4];
-  uint32_t xsc = 0;
+  uint32_t xsc[4];
   u32x4 wf[kWRing][4];
   uint32_t wsc[kWRing][4];
   auto load_x = [&](int q) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-      xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(x_off + 128u * q + 16u * j), 0, 0));
-    xsc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(s_off + 4u * q), 0, 0);
+    for (int j = 0; j < 4; j++) {
+      xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(x_off[j] + 128u * q), 0, 0));
+      xsc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(s_off[j] + 4u * q), 0, 0);
+    }
   };
   auto load_w = [&](int q, int slot) {
-    // a group past G: the sign bit of G - 1 - group moves the offset past the resource
-    const uint32_t past = (uint32_t)(G - 1 - (4 * q + lc)) >> 31 << 31;
+    // canonical: a group past G moves the offset past the resource (the sign
+    // bit of G - 1 - group); prepared: padding groups hold zeros, chunk q is
+    // 8 fragments x 64 group slots further on
+    const uint32_t past = PREP ? 0u : (uint32_t)(G - 1 - (4 * q + lc)) >> 31 << 31;
+    const uint32_t step_q = PREP ? 512u : 4u;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint32_t g = (w_grp[i] + 4u * q) | past;  // kOob stays past the resource
+      const uint32_t g = (w_grp[i] + step_q * q) | past;  // kOob stays past the resource
       wf[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(g << 4 | (g & kOob)), 0, 0));
       wsc[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, (int)g, 0, 0);
     }
   };
   auto store_x = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) *reinterpret_cast<u32x4*>(&Xs[buf][m_ld * kPitch + 64 * half + 16 * j]) = xa[j];
-    Ss[buf][m_ld] = xsc;  // both halves of a row write the same dword: no branch
+    for (int j = 0; j < 4; j++) {
+      const int m = 32 * w + 8 * j + (lane >> 3);
+      *reinterpret_cast<u32x4*>(&Xs[buf][m * kPitch + 16 * ld_ch]) = xa[j];
+      Ss[buf][m] = xsc[j];  // the eight lanes of a row write the same dword: no branch
+    }
   };
 
   v4f acc[4][4];
@@ -178,7 +204,6 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int nq = Kp / KC;
   // One chunk q; W = q mod 4 (compile-time) is its weight register slot and
   // W mod 2 its LDS buffer, so no register array is indexed at run time.
   // The activations of chunk q + 1 (loaded during chunk q - 1) go to the
@@ -246,13 +271,59 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   }
 }
 
+// Prepared layout, per expert e, N-tile n (128 rows), chunk q (4 groups) and
+// 16-row fragment f: 64 group slots of 16 bytes (slot l = row 16 f + (l & 15)
+// of the tile, group 4 q + (l >> 4): exactly what lane l of the MFMA's A
+// operand takes) and, in a second array, their 64 scale bytes in the same
+// order. Rows past O and groups past G are zero. One thread per group slot.
+__global__ void __launch_bounds__(256) prepare_mx_kernel(const uint8_t* __restrict__ packed,
+                                                         const uint8_t* __restrict__ scales, int64_t n_slots, int O,
+                                                         int G, int n_ntiles, int nq, uint8_t* __restrict__ pp,
+                                                         uint8_t* __restrict__ ps) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n_slots) return;
+  const int l = (int)(idx & 63), fr = (int)((idx >> 6) & 7);
+  const int64_t rest = idx >> 9;  // (e * n_ntiles + n) * nq + q
+  const int q = (int)(rest % nq);
+  const int64_t en = rest / nq;
+  const int n = (int)(en % n_ntiles);
+  const int64_t e = en / n_ntiles;
+  const int row = 128 * n + 16 * fr + (l & 15), g = 4 * q + (l >> 4);
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  uint8_t sc = 0;
+  if (row < O && g < G) {
+    const int64_t src = (e * O + row) * G + g;
+    v = *reinterpret_cast<const u32x4*>(packed + src * 16);
+    sc = scales[src];
+  }
+  *reinterpret_cast<u32x4*>(pp + idx * 16) = v;
+  ps[idx] = sc;
+}
+
 }  // namespace
+
+size_t mx_prepared_bytes(int64_t E, int64_t O, int64_t G) {
+  const int64_t slots = E * ((O + NT - 1) / NT) * (mx_row_bytes(32 * G) / KC) * 512;
+  return (size_t)slots * 17;
+}
+
+hipError_t launch_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int O, int G, uint8_t* prepared,
+                             hipStream_t stream) {
+  const int n_ntiles = (O + NT - 1) / NT, nq = mx_row_bytes(32 * (int64_t)G) / KC;
+  const int64_t slots = E * n_ntiles * nq * 512;
+  if (slots == 0) return hipSuccess;
+  hipLaunchKernelGGL(prepare_mx_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream, packed, scales,
+                     slots, O, G, n_ntiles, nq, prepared, prepared + slots * 16);
+  return hipGetLastError();
+}
 
 int mx_row_bytes(int64_t I) { return (int)(KC * ((I + KC - 1) / KC)); }
 
 bool gemm_mx_supported(int64_t T, int64_t O, int64_t G) {
   const int64_t Kp = mx_row_bytes(32 * G);
-  return O % 4 == 0 && T * Kp < (int64_t(1) << 31) && O * G * 16 < (int64_t(1) << 31);
+  const int64_t per_expert_prepared = ((O + NT - 1) / NT) * (Kp / KC) * 8192;
+  return O % 4 == 0 && T * Kp < (int64_t(1) << 31) && O * G * 16 < (int64_t(1) << 31) &&
+         per_expert_prepared < (int64_t(1) << 31);
 }
 
 hipError_t launch_quant_mxfp8(const uint16_t* x, int T, int I, int Kp, uint8_t* codes, uint8_t* sb,
@@ -267,13 +338,18 @@ hipError_t launch_quant_mxfp8(const uint16_t* x, int T, int I, int Kp, uint8_t* 
 
 hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* packed, const uint8_t* scales,
                           const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
-                          float* part, int T, int K, int O, int G, hipStream_t stream) {
+                          float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared) {
   const int Kp = mx_row_bytes(32 * (int64_t)G);
   const int n_ntiles = (O + NT - 1) / NT;
   const int64_t nblk = max_tiles * n_ntiles;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_mx_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, xq, xs, packed, scales, perm, tiles,
-                     n_tiles, part, K, O, G, Kp, n_ntiles, (uint32_t)((int64_t)T * Kp), (uint32_t)((int64_t)T * Kp / 32));
+  const uint32_t xq_bytes = (uint32_t)((int64_t)T * Kp), xs_bytes = (uint32_t)((int64_t)T * Kp / 32);
+  if (prepared)
+    hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3((unsigned)nblk), dim3(256), 0, stream, xq, xs, packed, scales, perm,
+                       tiles, n_tiles, part, K, O, G, Kp, n_ntiles, xq_bytes, xs_bytes);
+  else
+    hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3((unsigned)nblk), dim3(256), 0, stream, xq, xs, packed, scales, perm,
+                       tiles, n_tiles, part, K, O, G, Kp, n_ntiles, xq_bytes, xs_bytes);
   return hipGetLastError();
 }
 

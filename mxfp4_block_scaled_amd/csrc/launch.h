@@ -82,9 +82,16 @@ int mx_row_bytes(int64_t I);
 bool gemm_mx_supported(int64_t T, int64_t O, int64_t G);  // O % 4 == 0, T * Kp and O * G * 16 below 2^31
 hipError_t launch_quant_mxfp8(const uint16_t* x, int T, int I, int Kp, uint8_t* codes, uint8_t* sb,
                               hipStream_t stream);
+// prepared = true: `packed` is a buffer written by launch_prepare_mx (its scale
+// array follows the packed slots) and `scales` points at that scale array.
 hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* packed, const uint8_t* scales,
                           const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
-                          float* part, int T, int K, int O, int G, hipStream_t stream);
+                          float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared = false);
+// the prepared weight layout of the block-scaled variant: 16 bytes of codes and
+// one scale byte per group slot, slots = E * ceil(O / 128) * (Kp / 128) * 512
+size_t mx_prepared_bytes(int64_t E, int64_t O, int64_t G);
+hipError_t launch_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int O, int G, uint8_t* prepared,
+                             hipStream_t stream);
 
 // ---- router: logits (T, E) fp32 -> sel (T, K) int32, p (T, K) fp32.
 // mode 0 softmax, 1 sigmoid with a selection-only bias (may be null).

@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES)
@@ -278,3 +278,26 @@ def test_quantize_mxfp8_host_checks(args):
 
 def test_quantize_mxfp8_empty():
     assert _abi.lib().mxfp4_quantize_mxfp8(0, 0, 64, 64, 0, 0, None) == _abi.OK
+
+
+def test_mx_prepared_size_and_host_checks():
+    E, O, G = 128, 5760, 90
+    n = _abi.mx_prepared_size(E, O, G)
+    assert n == E * 45 * 23 * 512 * 17  # 45 N-tiles, 23 chunks of 4 groups, 512 slots of 17 bytes
+    with pytest.raises(_abi.Mxfp4Error) as e:
+        _abi.mx_prepared_size(4, 6, 2)  # O % 4 != 0
+    assert e.value.status == _abi.ERR_UNSUPPORTED
+    lib = _abi.lib()
+    small = _abi.mx_prepared_size(2, 8, 2)
+    assert lib.mxfp4_prepare_mx(B, C, 2, 8, 2, A, small - 1, None) == _abi.ERR_WORKSPACE_TOO_SMALL
+    for args in [(0, C, A), (B, 0, A), (B, C, 0), (B + 4, C, A), (B, C, A + 8), (B, C, B + 64)]:
+        assert lib.mxfp4_prepare_mx(args[0], args[1], 2, 8, 2, args[2], small, None) == _abi.ERR_INVALID_ARG
+    # the prepared layer: same argument rules as the canonical one
+    ws = C + 0x60000
+    assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(A, B, C + 0x10000, C + 0x20000, C + 0x30000, C + 0x40000, 2, 2, 8,
+                                                  2, 2, 0, ws, 16, None) == _abi.ERR_WORKSPACE_TOO_SMALL
+    assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(A, 0, C + 0x10000, C + 0x20000, C + 0x30000, C + 0x40000, 2, 2, 8,
+                                                  2, 2, 0, ws, 1 << 24, None) == _abi.ERR_INVALID_ARG
+    assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(A, B, C + 0x10000, C + 0x20000, C + 0x30000, B + 32, 2, 2, 8,
+                                                  2, 2, 0, ws, 1 << 24, None) == _abi.ERR_INVALID_ARG
+    assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(0, 0, 0, 0, 0, 0, 0, 2, 8, 2, 2, 0, 0, 0, None) == _abi.OK

@@ -241,3 +241,60 @@ def test_variant_full_workloads_sampled_rows(name, nrows):
     say(f"  {name}: rel L2 vs variant oracle {r:.3e}; variant vs exact layer (routed part) {rq:.3e}")
     assert r <= BF16_REL_L2
     assert rq <= VS_EXACT_REL_L2
+
+
+# ------------------------------------------------------------------ prepared weights
+
+def _prepared_layout_numpy(packed, scales):
+    """The documented prepared layout, built with numpy: slot (e, n, q, f, l)
+    holds group 4q + l // 16 of row 128n + 16f + l % 16, zeros past O / G."""
+    E, O, G, _ = packed.shape
+    NT, NQ = -(-O // 128), -(-(32 * G) // 128)
+    e, n, q, f, l = np.meshgrid(np.arange(E), np.arange(NT), np.arange(NQ), np.arange(8), np.arange(64), indexing="ij")
+    row = 128 * n + 16 * f + l % 16
+    g = 4 * q + l // 16
+    ok = (row < O) & (g < G)
+    codes = np.zeros(e.shape + (16,), np.uint8)
+    sc = np.zeros(e.shape, np.uint8)
+    codes[ok] = packed[e[ok], row[ok], g[ok]]
+    sc[ok] = scales[e[ok], row[ok], g[ok]]
+    return np.concatenate([codes.reshape(-1), sc.reshape(-1)])
+
+
+@pytest.mark.parametrize("E,O,G", [(2, 40, 1), (3, 132, 9), (2, 256, 6)])
+def test_prepared_layout_bytes(E, O, G):
+    rng = np.random.default_rng(E * O + G)
+    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
+    scales = rng.integers(0, 255, (E, O, G), dtype=np.uint8)
+    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(prep.buf.cpu().numpy(), _prepared_layout_numpy(packed, scales))
+
+
+def run_prepared(x, packed, scales, sel, p, shared):
+    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    y = mx.moe_linear_mxfp8_prepared(bf16_dev(x), prep, torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV),
+                                     bf16_dev(shared))
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"T{c[1]}E{c[2]}K{c[3]}G{c[4]}O{c[5]}" for c in CASES])
+def test_prepared_matches_canonical_bit_for_bit(c):
+    args = case(*c)
+    say(f"prepared weights, case {c}")
+    y0 = run_case(*args)
+    y1 = run_prepared(*args)
+    assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("name", ["prefill", "skewed"])
+def test_prepared_full_workloads_match_canonical(name):
+    inp, packed, scales = _workload(name)
+    say(f"prepared weights on {name}")
+    x, sel, p, sh = bf16_dev(inp.x), torch.from_numpy(inp.sel).to(DEV), torch.from_numpy(inp.p).to(DEV), bf16_dev(inp.shared)
+    y0 = mx.moe_linear_mxfp8(x, packed, scales, sel, p, sh)
+    prep = mx.prepare_mx(packed, scales)
+    y1 = mx.moe_linear_mxfp8_prepared(x, prep, sel, p, sh)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
