@@ -278,7 +278,9 @@ int mxfp4_moe_linear_mxfp8_ex(const uint16_t* x, const uint8_t* packed, const ui
  * order the scaled MFMA's weight operand takes them (slot l: row 16 f + (l mod
  * 16) of the tile, group 4 q + l / 16), so that every wave-wide weight request
  * reads 1 KB of consecutive bytes; after all code slots come the slots' scale
- * bytes in the same order (64 consecutive bytes per request). Rows past O and
+ * bytes, per (expert, tile, chunk) and half of the 8 fragments as 64 lanes x 4
+ * bytes (byte 4 l + f mod 4 for fragment f, slot l), so that one 4-byte
+ * request per lane brings a lane its four fragments' scales. Rows past O and
  * groups past G are zero. The canonical [E, O, G, 16] / [E, O, G] arrays are
  * the pages' format (page "MXFP4 Experts", shape paragraph); this is a byte
  * permutation of them plus zero padding, nothing is decoded.

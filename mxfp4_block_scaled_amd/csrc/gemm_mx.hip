@@ -23,14 +23,16 @@
 // 16c .. 16c+15 and 64+16c .. 64+16c+15 of the chunk for pair p, and the
 // scale byte of block 4q + c (the hardware applies the scale of lane group c
 // to inputs 32c .. 32c+31 of both operands). Activation rows are gathered
-// (row = perm / K; each wave-wide request reads eight whole 128-byte row
-// pieces) into LDS once per workgroup and chunk (144-byte rows:
-// conflict-free 16-byte reads), double-buffered with one barrier a chunk
-// and fetched two chunks ahead (held a chunk in registers before the LDS
-// store); weights and their scales are loaded three chunks ahead into a
-// ring of four register slots. Groups
-// past G and rows past O read through an offset beyond the buffer resource
-// (zeros). Output: fp32 rows of `part` at sorted positions, as the bf16 GEMM.
+// (row = perm / K) by LDS DMA (buffer loads that write LDS directly, no
+// registers) into a ring of three chunk slots, two chunks ahead, each
+// wave-wide request filling eight whole 128-byte row pieces; the pieces of a
+// row sit XOR-swizzled so that the 16-byte fragment reads are conflict-free
+// without padding. Weights and their scales go to a ring of three register
+// slots, two chunks ahead. Every chunk issues the same number of requests,
+// so one counted wait per chunk (this wave's DMA of the next chunk) and a
+// bare barrier replace a full fence. Groups past G and rows past O read
+// through an offset beyond the buffer resource (zeros). Output: fp32 rows of
+// `part` at sorted positions, as the bf16 GEMM.
 #include <type_traits>
 
 #include "device_common.h"
@@ -47,8 +49,13 @@ constexpr uint32_t kOob = 0x80000000u;
 constexpr int MT = kGemmTileM;  // 128 pairs
 constexpr int NT = 128;         // features
 constexpr int KC = 128;         // inputs per chunk
-constexpr int kPitch = KC + 16; // bytes per LDS activation row
-constexpr int kWRing = 4;       // weight chunks held in registers: three in flight while one is used
+constexpr int kRing = 3;         // chunk slots: activations (LDS) and weights (registers), two in flight
+// vector-memory requests per wave and chunk: 4 activation + 1 scale DMA, then
+// 4 weight loads and 4 scale-byte loads (canonical) or 1 scale dword (prepared)
+template <bool PREP>
+constexpr int kWeightLoads = PREP ? 5 : 8;
+template <bool PREP>
+constexpr int kLoadsPerChunk = 5 + kWeightLoads<PREP>;
 
 // ---- quantisation
 
@@ -121,23 +128,39 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   const GemmTile tl = tiles[ti];
   const int f0 = nt * NT;
 
-  __shared__ __attribute__((aligned(16))) uint8_t Xs[2][MT * kPitch];
-  __shared__ uint32_t Ss[2][MT];
+  // Activation ring: three chunk slots, each 128 rows x 128 bytes with the
+  // 16-byte pieces of row m stored at position piece ^ (m & 7) (conflict-free
+  // 16-byte reads without padding), and 4 x 64 scale dwords (wave w's dword
+  // l < 32 is row 32 w + l). Three separate arrays, so that the compiler can
+  // tell a slot being read from the slots the DMA is filling.
+  __shared__ __attribute__((aligned(16))) uint8_t X0[MT * KC];
+  __shared__ __attribute__((aligned(16))) uint8_t X1[MT * KC];
+  __shared__ __attribute__((aligned(16))) uint8_t X2[MT * KC];
+  __shared__ __attribute__((aligned(16))) uint32_t S0[256];
+  __shared__ __attribute__((aligned(16))) uint32_t S1[256];
+  __shared__ __attribute__((aligned(16))) uint32_t S2[256];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int wm = w >> 1, wn = w & 1;
   const int lr = lane & 15, lc = lane >> 4;
 
-  // activation loader: wave w, request j covers pair rows 32 w + 8 j .. +7,
-  // eight lanes a row, 16 bytes a lane (the row's 128 bytes of the chunk)
-  const int ld_ch = lane & 7;
-  uint32_t x_off[4], s_off[4];
+  // activation DMA: wave w, request j fills rows 32 w + 8 j .. +7 of a slot
+  // (1 KB); lane l lands at row l >> 3, position l & 7 and so fetches piece
+  // (l & 7) ^ (l >> 3) of its row. Scale DMA: lane l < 32 fetches the dword of
+  // row 32 w + l (blocks 4q .. 4q+3); lanes 32 .. 63 read past the resource
+  // and write zeros into the unused half of the wave's 64 dwords.
+  uint32_t x_off[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int m = 32 * w + 8 * j + (lane >> 3);
     const int tok = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
-    x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 16u * ld_ch : kOob;
-    s_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)(Kp / 32) : kOob;
+    x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 16u * (uint32_t)((lane & 7) ^ (lane >> 3)) : kOob;
+  }
+  uint32_t s_off;
+  {
+    const int m = 32 * w + lane;
+    const int tok = (lane < 32 && m < tl.mlen) ? perm[tl.row0 + m] / K : -1;
+    s_off = tok >= 0 ? (uint32_t)tok * (uint32_t)(Kp / 32) : kOob;
   }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, (int)xq_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xs, (short)0, (int)xs_bytes, kRsrcFlags);
@@ -155,6 +178,8 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   // a wave whose 64 pairs are all past the tile's end multiplies nothing:
   // its weight requests go past the resource (no memory traffic)
   const bool w_live = 64 * wm < tl.mlen;
+  // prepared: byte offset of this lane's scale dword in chunk 0
+  const uint32_t w_sc = w_live ? (uint32_t)(((nt * nq * 2 + wn) * 64 + lane) * 4) : kOob;
   uint32_t w_grp[4];  // canonical: group index (row * G + lc) of chunk 0; prepared: group slot of chunk 0; or kOob
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -165,16 +190,17 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
       w_grp[i] = (f < O && w_live) ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
   }
 
-  u32x4 xa[4];
-  uint32_t xsc[4];
-  u32x4 wf[kWRing][4];
-  uint32_t wsc[kWRing][4];
-  auto load_x = [&](int q) {
+  u32x4 wf[kRing][4];
+  uint32_t wsc[kRing][4];  // canonical: one scale byte per fragment
+  uint32_t wsp[kRing];     // prepared: the four fragments' scale bytes in one dword
+  // exactly kLoadsPerChunk vector-memory requests per chunk, in this order
+  auto dma_x = [&](int q, uint8_t* xdst, uint32_t* sdst) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(x_off[j] + 128u * q), 0, 0));
-      xsc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(s_off[j] + 4u * q), 0, 0);
-    }
+    for (int j = 0; j < 4; j++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xdst + (32 * w + 8 * j) * KC),
+                                               16, (int)(x_off[j] + 128u * q), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sdst + 64 * w), 4,
+                                             (int)(s_off + 4u * q), 0, 0, 0);
   };
   auto load_w = [&](int q, int slot) {
     // canonical: a group past G moves the offset past the resource (the sign
@@ -186,16 +212,15 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
     for (int i = 0; i < 4; i++) {
       const uint32_t g = (w_grp[i] + step_q * q) | past;  // kOob stays past the resource
       wf[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(g << 4 | (g & kOob)), 0, 0));
-      wsc[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, (int)g, 0, 0);
+      if constexpr (!PREP) wsc[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, (int)g, 0, 0);
     }
+    if constexpr (PREP) wsp[slot] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)(w_sc + 512u * q), 0, 0);
   };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int m = 32 * w + 8 * j + (lane >> 3);
-      *reinterpret_cast<u32x4*>(&Xs[buf][m * kPitch + 16 * ld_ch]) = xa[j];
-      Ss[buf][m] = xsc[j];  // the eight lanes of a row write the same dword: no branch
-    }
+  // wait until this wave's DMA of the next chunk has landed: it was followed
+  // by that chunk's weight requests and by one whole chunk of requests
+  auto wait_next_x = [&]() {
+    constexpr int n = kWeightLoads<PREP> + kLoadsPerChunk<PREP>;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
   };
 
   v4f acc[4][4];
@@ -204,58 +229,59 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // One chunk q; W = q mod 4 (compile-time) is its weight register slot and
-  // W mod 2 its LDS buffer, so no register array is indexed at run time.
-  // The activations of chunk q + 1 (loaded during chunk q - 1) go to the
-  // other LDS buffer first, then chunk q + 2's activations and chunk q + 3's
-  // weights are requested (the weights stream from HBM: three chunks in
-  // flight cover its latency), then chunk q is multiplied. Past the last
-  // chunk the same requests repeat the last chunk (harmless, never read), so
-  // that no load or store in the steady state sits behind a branch and the
-  // compiler's wait counts stay exact.
+  // One chunk q in ring slot R = q mod 3 (compile-time: no register array or
+  // LDS slot is chosen at run time): request chunk q + 2 (activations by DMA
+  // into slot (q + 2) mod 3, read last during chunk q - 1; weights into
+  // register slot (q + 2) mod 3), multiply chunk q, wait for this wave's DMA
+  // of chunk q + 1, barrier. Past the last chunk the requests repeat the
+  // last chunk into a slot nobody reads again, so the number of requests per
+  // chunk - and with it every wait count - is fixed.
   auto step = [&](int q, auto slot) {
-    constexpr int W = decltype(slot)::value, S = W & 1;
-    store_x(S ^ 1);
-    load_x(min(q + 2, nq - 1));
-    load_w(min(q + 3, nq - 1), (W + 3) % kWRing);
+    constexpr int R = decltype(slot)::value, RN = (R + 2) % kRing;
+    uint8_t* xn = RN == 0 ? X0 : (RN == 1 ? X1 : X2);
+    uint32_t* sn = RN == 0 ? S0 : (RN == 1 ? S1 : S2);
+    const uint8_t* xc = R == 0 ? X0 : (R == 1 ? X1 : X2);
+    const uint32_t* sc = R == 0 ? S0 : (R == 1 ? S1 : S2);
+    dma_x(min(q + 2, nq - 1), xn, sn);
+    load_w(min(q + 2, nq - 1), RN);
     __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       if (64 * wm + 16 * j >= tl.mlen) break;  // 16-pair fragments past the tile's end (wave-uniform)
       const int p = 64 * wm + 16 * j + lr;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(&Xs[S][p * kPitch + 16 * lc]);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(&Xs[S][p * kPitch + 64 + 16 * lc]);
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * (lc ^ (p & 7))]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * ((4 + lc) ^ (p & 7))]);
       const v8i bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int bs = (int)((Ss[S][p] >> (8 * lc)) & 0xFFu);
+      const int bs = (int)((sc[(p >> 5) * 64 + (p & 31)] >> (8 * lc)) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const v8i a = v8i{(int)wf[W][i][0], (int)wf[W][i][1], (int)wf[W][i][2], (int)wf[W][i][3], 0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, 0, 0, (int)wsc[W][i], 0, bs);
+        const v8i a = v8i{(int)wf[R][i][0], (int)wf[R][i][1], (int)wf[R][i][2], (int)wf[R][i][3], 0, 0, 0, 0};
+        const int as = PREP ? (int)((wsp[R] >> (8 * i)) & 0xFFu) : (int)wsc[R][i];
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, 0, 0, as, 0, bs);
       }
     }
-    __syncthreads();
+    wait_next_x();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
-  using C3 = std::integral_constant<int, 3>;
+  dma_x(0, X0, S0);
   load_w(0, 0);
+  dma_x(min(1, nq - 1), X1, S1);
   load_w(min(1, nq - 1), 1);
-  load_w(min(2, nq - 1), 2);
-  load_x(0);
-  store_x(0);
-  load_x(min(1, nq - 1));
-  __syncthreads();
+  wait_next_x();  // chunk 0's DMA: followed by chunk 0's weights and all of chunk 1's requests
+  __builtin_amdgcn_s_barrier();
   int q = 0;
-  for (; q + 3 < nq; q += 4) {
+  for (; q + 2 < nq; q += 3) {
     step(q, C0{});
     step(q + 1, C1{});
     step(q + 2, C2{});
-    step(q + 3, C3{});
   }
   if (q < nq) step(q, C0{});
   if (q + 1 < nq) step(q + 1, C1{});
-  if (q + 2 < nq) step(q + 2, C2{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
 
   // lane (lr, lc) of fragment (i, j): pair 64 wm + 16 j + lr, features 64 wn + 16 i + 4 lc .. +3
 #pragma unroll
@@ -297,7 +323,9 @@ __global__ void __launch_bounds__(256) prepare_mx_kernel(const uint8_t* __restri
     sc = scales[src];
   }
   *reinterpret_cast<u32x4*>(pp + idx * 16) = v;
-  ps[idx] = sc;
+  // scales: per (tile, chunk, half of the 8 fragments) 64 lanes x 4 bytes,
+  // byte 4 l + (fr & 3): one dword per lane holds its four fragments' scales
+  ps[((rest * 2 + (fr >> 2)) * 64 + l) * 4 + (fr & 3)] = sc;
 }
 
 }  // namespace

@@ -247,7 +247,8 @@ def test_variant_full_workloads_sampled_rows(name, nrows):
 
 def _prepared_layout_numpy(packed, scales):
     """The documented prepared layout, built with numpy: slot (e, n, q, f, l)
-    holds group 4q + l // 16 of row 128n + 16f + l % 16, zeros past O / G."""
+    holds group 4q + l // 16 of row 128n + 16f + l % 16, zeros past O / G;
+    its scale byte sits at (((e, n, q) * 2 + f // 4) * 64 + l) * 4 + f % 4."""
     E, O, G, _ = packed.shape
     NT, NQ = -(-O // 128), -(-(32 * G) // 128)
     e, n, q, f, l = np.meshgrid(np.arange(E), np.arange(NT), np.arange(NQ), np.arange(8), np.arange(64), indexing="ij")
@@ -258,6 +259,8 @@ def _prepared_layout_numpy(packed, scales):
     sc = np.zeros(e.shape, np.uint8)
     codes[ok] = packed[e[ok], row[ok], g[ok]]
     sc[ok] = scales[e[ok], row[ok], g[ok]]
+    # scales: (e, n, q, half, l, f % 4)
+    sc = sc.reshape(E, NT, NQ, 2, 4, 64).transpose(0, 1, 2, 3, 5, 4)
     return np.concatenate([codes.reshape(-1), sc.reshape(-1)])
 
 
