@@ -15,7 +15,9 @@
 // assembly of the code), so the codes equal the oracle's bit for bit.
 //
 // Grouped GEMM (gemm_mx_kernel): the M-tiles of the bucketing (<= 128 pairs
-// of one expert) x N-tiles of 128 features; 2 x 2 waves of 64 x 64. MFMA
+// of one expert) x N-tiles of 128 features; the 4 waves split the features
+// (each wave: all 128 pairs x 32 features), so no two waves load the same
+// weights - the activations, shared by all four, come from LDS. MFMA
 // operand A = weights: lane (r, c) = (lane & 15, lane >> 4) holds the 16
 // packed bytes of group 4q + c of weight row r of its 16-row fragment (one
 // 16-byte load straight from memory into the operand registers) and that
@@ -49,11 +51,13 @@ constexpr uint32_t kOob = 0x80000000u;
 constexpr int MT = kGemmTileM;  // 128 pairs
 constexpr int NT = 128;         // features
 constexpr int KC = 128;         // inputs per chunk
+constexpr int kWI = 2;           // weight fragments (16 features each) per wave: the 4 waves split the 128 features
+constexpr int kWJ = 8;           // activation fragments (16 pairs each) per wave: every wave covers all 128 pairs
 constexpr int kRing = 3;         // chunk slots: activations (LDS) and weights (registers), two in flight
 // vector-memory requests per wave and chunk: 4 activation + 1 scale DMA, then
 // 4 weight loads and 4 scale-byte loads (canonical) or 1 scale dword (prepared)
 template <bool PREP>
-constexpr int kWeightLoads = PREP ? 5 : 8;
+constexpr int kWeightLoads = PREP ? kWI + 1 : 2 * kWI;
 template <bool PREP>
 constexpr int kLoadsPerChunk = 5 + kWeightLoads<PREP>;
 
@@ -141,7 +145,6 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   __shared__ __attribute__((aligned(16))) uint32_t S2[256];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
   const int lr = lane & 15, lc = lane >> 4;
 
   // activation DMA: wave w, request j fills rows 32 w + 8 j .. +7 of a slot
@@ -165,7 +168,7 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, (int)xq_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xs, (short)0, (int)xs_bytes, kRsrcFlags);
 
-  // weight fragments: rows f0 + 64 wn + 16 i + lr, group 4 q + lc
+  // weight fragments: rows f0 + 32 w + 16 i + lr, group 4 q + lc
   const int nq = Kp / KC;
   const int64_t ebase = (int64_t)tl.e * O * G;                   // canonical layout
   const int64_t pbase = (int64_t)tl.e * n_ntiles * nq * 512;     // prepared layout: groups before expert e
@@ -177,21 +180,20 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
       : __builtin_amdgcn_make_buffer_rsrc((void*)(scales + ebase), (short)0, O * G, kRsrcFlags);
   // a wave whose 64 pairs are all past the tile's end multiplies nothing:
   // its weight requests go past the resource (no memory traffic)
-  const bool w_live = 64 * wm < tl.mlen;
   // prepared: byte offset of this lane's scale dword in chunk 0
-  const uint32_t w_sc = w_live ? (uint32_t)(((nt * nq * 2 + wn) * 64 + lane) * 4) : kOob;
-  uint32_t w_grp[4];  // canonical: group index (row * G + lc) of chunk 0; prepared: group slot of chunk 0; or kOob
+  const uint32_t w_sc = (uint32_t)(((nt * nq * 2 + (w >> 1)) * 64 + lane) * 4);
+  uint32_t w_grp[kWI];  // canonical: group index (row * G + lc) of chunk 0; prepared: group slot of chunk 0; or kOob
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int f = f0 + 64 * wn + 16 * i + lr;
+  for (int i = 0; i < kWI; i++) {
+    const int f = f0 + 32 * w + 16 * i + lr;
     if constexpr (PREP)
-      w_grp[i] = w_live ? (uint32_t)((nt * nq * 8 + 4 * wn + i) * 64 + lane) : kOob;
+      w_grp[i] = (uint32_t)((nt * nq * 8 + kWI * w + i) * 64 + lane);
     else
-      w_grp[i] = (f < O && w_live) ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
+      w_grp[i] = f < O ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
   }
 
-  u32x4 wf[kRing][4];
-  uint32_t wsc[kRing][4];  // canonical: one scale byte per fragment
+  u32x4 wf[kRing][kWI];
+  uint32_t wsc[kRing][kWI];  // canonical: one scale byte per fragment
   uint32_t wsp[kRing];     // prepared: the four fragments' scale bytes in one dword
   // exactly kLoadsPerChunk vector-memory requests per chunk, in this order
   auto dma_x = [&](int q, uint8_t* xdst, uint32_t* sdst) {
@@ -209,7 +211,7 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
     const uint32_t past = PREP ? 0u : (uint32_t)(G - 1 - (4 * q + lc)) >> 31 << 31;
     const uint32_t step_q = PREP ? 512u : 4u;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < kWI; i++) {
       const uint32_t g = (w_grp[i] + step_q * q) | past;  // kOob stays past the resource
       wf[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(g << 4 | (g & kOob)), 0, 0));
       if constexpr (!PREP) wsc[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, (int)g, 0, 0);
@@ -223,11 +225,11 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
   };
 
-  v4f acc[4][4];
+  v4f acc[kWI][kWJ];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < kWI; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kWJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // One chunk q in ring slot R = q mod 3 (compile-time: no register array or
   // LDS slot is chosen at run time): request chunk q + 2 (activations by DMA
@@ -246,17 +248,17 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
     load_w(min(q + 2, nq - 1), RN);
     __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (64 * wm + 16 * j >= tl.mlen) break;  // 16-pair fragments past the tile's end (wave-uniform)
-      const int p = 64 * wm + 16 * j + lr;
+    for (int j = 0; j < kWJ; j++) {
+      if (16 * j >= tl.mlen) break;  // 16-pair fragments past the tile's end (wave-uniform)
+      const int p = 16 * j + lr;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * (lc ^ (p & 7))]);
       const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * ((4 + lc) ^ (p & 7))]);
       const v8i bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       const int bs = (int)((sc[(p >> 5) * 64 + (p & 31)] >> (8 * lc)) & 0xFFu);
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < kWI; i++) {
         const v8i a = v8i{(int)wf[R][i][0], (int)wf[R][i][1], (int)wf[R][i][2], (int)wf[R][i][3], 0, 0, 0, 0};
-        const int as = PREP ? (int)((wsp[R] >> (8 * i)) & 0xFFu) : (int)wsc[R][i];
+        const int as = PREP ? (int)((wsp[R] >> (8 * ((kWI * w + i) & 3))) & 0xFFu) : (int)wsc[R][i];
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, 0, 0, as, 0, bs);
       }
     }
@@ -283,15 +285,15 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   if (q + 1 < nq) step(q + 1, C1{});
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
 
-  // lane (lr, lc) of fragment (i, j): pair 64 wm + 16 j + lr, features 64 wn + 16 i + 4 lc .. +3
+  // lane (lr, lc) of fragment (i, j): pair 16 j + lr, features 32 w + 16 i + 4 lc .. +3
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int p = 64 * wm + 16 * j + lr;
+  for (int j = 0; j < kWJ; j++) {
+    const int p = 16 * j + lr;
     if (p >= tl.mlen) continue;
     float* row = part + (int64_t)(tl.row0 + p) * O;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int f = f0 + 64 * wn + 16 * i + 4 * lc;
+    for (int i = 0; i < kWI; i++) {
+      const int f = f0 + 32 * w + 16 * i + 4 * lc;
       if (f < O) *reinterpret_cast<v4f*>(row + f) = acc[i][j];
     }
   }
