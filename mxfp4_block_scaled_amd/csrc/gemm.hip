@@ -111,6 +111,9 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
   const uintptr_t s_first = reinterpret_cast<uintptr_t>(scales) + (uintptr_t)((int64_t)tl.e * O * G);
   const uint32_t* s_al = reinterpret_cast<const uint32_t*>(s_first & ~(uintptr_t)3);  // wave-uniform
   const int s_mis = (int)(s_first & 3);
+  // the expert's scale bytes from the dword boundary below them, whole dwords
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)s_al, (short)0, (s_mis + O * G + 3) & ~3, kRsrcFlags);
   const int nchunk = (G + kScGroups - 1) / kScGroups;
   uint32_t sreg[kScSlots];
   auto sc_load = [&](int c) {
@@ -120,8 +123,11 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
       const int q = tid + 256 * i, r = (q * 205) >> 10, k = q - r * kScPitch;  // q / 5 for q < 1020
       const int w = q < NT * kScPitch ? wrow(r) : -1;
       const int a = s_mis + w * G + kScGroups * c;  // byte offset from s_al
-      sreg[i] = 0u;
-      if (w >= 0 && 4 * k < (a & 3) + len) sreg[i] = s_al[(a >> 2) + k];
+      // a buffer load (not a flat one) so that the compiler's wait counts stay
+      // exact; a dword with none of the chunk's bytes reads past the resource
+      const bool need = w >= 0 && 4 * k < (a & 3) + len;
+      sreg[i] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(need ? (uint32_t)((a >> 2) + k) * 4u : kOobByte), 0,
+                                                     0);
     }
   };
   auto sc_store = [&]() {
