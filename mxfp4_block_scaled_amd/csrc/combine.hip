@@ -37,34 +37,41 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 }
 
 // The same, four outputs per thread with 16-byte loads of the partial rows
-// (O % 4 == 0, so every row start is 16-byte aligned). The slots and
-// weights of token t are loaded once per thread and kept in registers.
+// (O % 4 == 0, so every row start is 16-byte aligned). Each slot's partial
+// row is read through a buffer resource of its own (a dropped slot gets an
+// empty resource: zeros, no traffic, weight 0), so the KT loads of an output
+// quad are issued back to back and waited for once, instead of one load and
+// one wait per slot behind a branch. KT = K at compile time for the common
+// K; KT = 0 takes K at run time (up to kCombMaxK).
 constexpr int kCombMaxK = 16;
-
-template <bool BF16>
+constexpr int kRsrcFlags = 0x00020000;
+template <bool BF16, int KT>
 __global__ void __launch_bounds__(256) combine4_kernel(const float* __restrict__ part,
                                                        const int32_t* __restrict__ slot_of_pair,
                                                        const float* __restrict__ p, const void* shared, void* y, int T,
                                                        int K, int O) {
+  constexpr int KM = KT > 0 ? KT : kCombMaxK;
+  if constexpr (KT > 0) K = KT;
   const int O4 = O >> 2;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
-    int sp[kCombMaxK];
-    float pk[kCombMaxK];
+    __amdgpu_buffer_rsrc_t rk[KM];
+    float pk[KM];
 #pragma unroll
-    for (int k = 0; k < kCombMaxK; k++) {
-      sp[k] = k < K ? slot_of_pair[t * K + k] : -1;
-      pk[k] = k < K ? p[t * K + k] : 0.f;
+    for (int k = 0; k < KM; k++) {
+      const int sp = k < K ? slot_of_pair[t * K + k] : -1;
+      pk[k] = sp >= 0 ? p[t * K + k] : 0.f;
+      rk[k] = __builtin_amdgcn_make_buffer_rsrc((void*)(part + (int64_t)(sp >= 0 ? sp : 0) * O), (short)0,
+                                                sp >= 0 ? O * 4 : 0, kRsrcFlags);
     }
     for (int o4 = blockIdx.x * 256 + threadIdx.x; o4 < O4; o4 += gridDim.x * 256) {
+      f32x4 v[KM];
+#pragma unroll
+      for (int k = 0; k < KM; k++) v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk[k], 16 * o4, 0, 0));
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < kCombMaxK; k++) {
-        if (k < K && sp[k] >= 0) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)sp[k] * O + 4 * o4);
+      for (int k = 0; k < KM; k++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) a[i] = fmaf(pk[k], v[i], a[i]);
-        }
-      }
+        for (int i = 0; i < 4; i++) a[i] = fmaf(pk[k], v[k][i], a[i]);
       const int64_t yo = (int64_t)t * O + 4 * o4;
       if constexpr (BF16) {
         const uint2 sh = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(shared) + yo);
@@ -119,19 +126,30 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(const uint8_t* __restr
 
 }  // namespace
 
+template <int KT>
+void launch_combine4(dim3 grid, const float* part, const int32_t* slot_of_pair, const float* p, const void* shared,
+                     void* y, int T, int K, int O, int dtype, hipStream_t stream) {
+  if (dtype == 1)
+    hipLaunchKernelGGL((combine4_kernel<true, KT>), grid, dim3(256), 0, stream, part, slot_of_pair, p, shared, y, T, K, O);
+  else
+    hipLaunchKernelGGL((combine4_kernel<false, KT>), grid, dim3(256), 0, stream, part, slot_of_pair, p, shared, y, T, K,
+                       O);
+}
+
 hipError_t launch_combine(const float* part, const int32_t* slot_of_pair, const float* p, const void* shared, void* y,
                           int T, int K, int O, int dtype, hipStream_t stream) {
   const unsigned gy = (unsigned)(T < 32768 ? T : 32768);
   const bool vec = O % 4 == 0 && K <= kCombMaxK && reinterpret_cast<uintptr_t>(part) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(shared) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
   if (vec) {
-    const unsigned gx = (unsigned)((O / 4 + 255) / 256);
-    if (dtype == 1)
-      hipLaunchKernelGGL(combine4_kernel<true>, dim3(gx, gy), dim3(256), 0, stream, part, slot_of_pair, p, shared, y, T,
-                         K, O);
-    else
-      hipLaunchKernelGGL(combine4_kernel<false>, dim3(gx, gy), dim3(256), 0, stream, part, slot_of_pair, p, shared, y,
-                         T, K, O);
+    const dim3 grid((unsigned)((O / 4 + 255) / 256), gy);
+    switch (K) {
+      case 1: launch_combine4<1>(grid, part, slot_of_pair, p, shared, y, T, K, O, dtype, stream); break;
+      case 2: launch_combine4<2>(grid, part, slot_of_pair, p, shared, y, T, K, O, dtype, stream); break;
+      case 4: launch_combine4<4>(grid, part, slot_of_pair, p, shared, y, T, K, O, dtype, stream); break;
+      case 8: launch_combine4<8>(grid, part, slot_of_pair, p, shared, y, T, K, O, dtype, stream); break;
+      default: launch_combine4<0>(grid, part, slot_of_pair, p, shared, y, T, K, O, dtype, stream); break;
+    }
     return hipGetLastError();
   }
   const unsigned gx = (unsigned)((O + 255) / 256);
