@@ -126,8 +126,14 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
                                                          const int32_t* __restrict__ n_tiles, float* __restrict__ part,
                                                          int K, int O, int G, int Kp, int n_ntiles, uint32_t xq_bytes,
                                                          uint32_t xs_bytes) {
-  const int ti = blockIdx.x / n_ntiles;
-  const int nt = blockIdx.x - ti * n_ntiles;
+  // Workgroup i runs on XCD i mod 8. XCD x takes M-tiles x, x + 8, ... with
+  // all their N-tiles back to back, so the N-tiles of an M-tile share its
+  // gathered activation rows in one L2 instead of every XCD fetching them,
+  // while neighbouring M-tiles (full and partial ones) still spread over all
+  // XCDs.
+  const int xcd_step = blockIdx.x >> 3;
+  const int ti = (blockIdx.x & 7) + 8 * (xcd_step / n_ntiles);
+  const int nt = xcd_step % n_ntiles;
   if (ti >= n_tiles[0]) return;
   const GemmTile tl = tiles[ti];
   const int f0 = nt * NT;
@@ -371,7 +377,8 @@ hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* p
                           float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared) {
   const int Kp = mx_row_bytes(32 * (int64_t)G);
   const int n_ntiles = (O + NT - 1) / NT;
-  const int64_t nblk = max_tiles * n_ntiles;
+  // 8 XCDs x ceil(max_tiles / 8) M-tiles x the N-tiles
+  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_ntiles;
   if (nblk == 0) return hipSuccess;
   const uint32_t xq_bytes = (uint32_t)((int64_t)T * Kp), xs_bytes = (uint32_t)((int64_t)T * Kp / 32);
   if (prepared)
