@@ -15,9 +15,10 @@
 // assembly of the code), so the codes equal the oracle's bit for bit.
 //
 // Grouped GEMM (gemm_mx_kernel): the M-tiles of the bucketing (<= 128 pairs
-// of one expert) x N-tiles of 128 features; the 4 waves split the features
+// of one expert) x N-tiles of 256 features; the 8 waves split the features
 // (each wave: all 128 pairs x 32 features), so no two waves load the same
-// weights - the activations, shared by all four, come from LDS. MFMA
+// weights, and the activations, shared by all eight, come from LDS once per
+// 256 features. MFMA
 // operand A = weights: lane (r, c) = (lane & 15, lane >> 4) holds the 16
 // packed bytes of group 4q + c of weight row r of its 16-row fragment (one
 // 16-byte load straight from memory into the operand registers) and that
@@ -49,17 +50,19 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOob = 0x80000000u;
 constexpr int MT = kGemmTileM;  // 128 pairs
-constexpr int NT = 128;         // features
+constexpr int NT = 128;         // rows of a prepared weight tile
+constexpr int kWaves = 8;       // waves per workgroup
+constexpr int NW = 32 * kWaves; // features per workgroup (each wave: all 128 pairs x 32 features)
 constexpr int KC = 128;         // inputs per chunk
-constexpr int kWI = 2;           // weight fragments (16 features each) per wave: the 4 waves split the 128 features
+constexpr int kWI = 2;           // weight fragments (16 features each) per wave: the waves split the features
 constexpr int kWJ = 8;           // activation fragments (16 pairs each) per wave: every wave covers all 128 pairs
 constexpr int kRing = 3;         // chunk slots: activations (LDS) and weights (registers), two in flight
-// vector-memory requests per wave and chunk: 4 activation + 1 scale DMA, then
-// 4 weight loads and 4 scale-byte loads (canonical) or 1 scale dword (prepared)
+// vector-memory requests per wave and chunk: 2 activation + 1 scale DMA, then
+// kWI weight loads and kWI scale-byte loads (canonical) or 1 scale dword (prepared)
 template <bool PREP>
 constexpr int kWeightLoads = PREP ? kWI + 1 : 2 * kWI;
 template <bool PREP>
-constexpr int kLoadsPerChunk = 5 + kWeightLoads<PREP>;
+constexpr int kLoadsPerChunk = 3 + kWeightLoads<PREP>;
 
 // ---- quantisation
 
@@ -118,13 +121,13 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
 // contiguous 1 KB block per 16-row fragment and chunk, and a 64-byte block of
 // its scales) instead of the canonical [E, O, G, 16] / [E, O, G].
 template <bool PREP>
-__global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+__global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                          const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ scales,
                                                          const int32_t* __restrict__ perm,
                                                          const GemmTile* __restrict__ tiles,
                                                          const int32_t* __restrict__ n_tiles, float* __restrict__ part,
-                                                         int K, int O, int G, int Kp, int n_ntiles, uint32_t xq_bytes,
+                                                         int K, int O, int G, int Kp, int n_ntiles, int n_wg, uint32_t xq_bytes,
                                                          uint32_t xs_bytes) {
   // Workgroup i runs on XCD i mod 8. XCD x takes M-tiles x, x + 8, ... with
   // all their N-tiles back to back, so the N-tiles of an M-tile share its
@@ -132,11 +135,11 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   // while neighbouring M-tiles (full and partial ones) still spread over all
   // XCDs.
   const int xcd_step = blockIdx.x >> 3;
-  const int ti = (blockIdx.x & 7) + 8 * (xcd_step / n_ntiles);
-  const int nt = xcd_step % n_ntiles;
+  const int ti = (blockIdx.x & 7) + 8 * (xcd_step / n_wg);
+  const int nt = xcd_step % n_wg;  // feature tile of NW features
   if (ti >= n_tiles[0]) return;
   const GemmTile tl = tiles[ti];
-  const int f0 = nt * NT;
+  const int f0 = nt * NW;
 
   // Activation ring: three chunk slots, each 128 rows x 128 bytes with the
   // 16-byte pieces of row m stored at position piece ^ (m & 7) (conflict-free
@@ -146,29 +149,29 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   __shared__ __attribute__((aligned(16))) uint8_t X0[MT * KC];
   __shared__ __attribute__((aligned(16))) uint8_t X1[MT * KC];
   __shared__ __attribute__((aligned(16))) uint8_t X2[MT * KC];
-  __shared__ __attribute__((aligned(16))) uint32_t S0[256];
-  __shared__ __attribute__((aligned(16))) uint32_t S1[256];
-  __shared__ __attribute__((aligned(16))) uint32_t S2[256];
+  __shared__ __attribute__((aligned(16))) uint32_t S0[64 * kWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t S1[64 * kWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t S2[64 * kWaves];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lc = lane >> 4;
 
-  // activation DMA: wave w, request j fills rows 32 w + 8 j .. +7 of a slot
+  // activation DMA: wave w, request j fills rows 16 w + 8 j .. +7 of a slot
   // (1 KB); lane l lands at row l >> 3, position l & 7 and so fetches piece
-  // (l & 7) ^ (l >> 3) of its row. Scale DMA: lane l < 32 fetches the dword of
-  // row 32 w + l (blocks 4q .. 4q+3); lanes 32 .. 63 read past the resource
-  // and write zeros into the unused half of the wave's 64 dwords.
-  uint32_t x_off[4];
+  // (l & 7) ^ (l >> 3) of its row. Scale DMA: lane l < 16 fetches the dword of
+  // row 16 w + l (blocks 4q .. 4q+3); lanes 16 .. 63 read past the resource
+  // and write zeros into the unused part of the wave's 64 dwords.
+  uint32_t x_off[2];
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int m = 32 * w + 8 * j + (lane >> 3);
+  for (int j = 0; j < 2; j++) {
+    const int m = 16 * w + 8 * j + (lane >> 3);
     const int tok = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
     x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 16u * (uint32_t)((lane & 7) ^ (lane >> 3)) : kOob;
   }
   uint32_t s_off;
   {
-    const int m = 32 * w + lane;
-    const int tok = (lane < 32 && m < tl.mlen) ? perm[tl.row0 + m] / K : -1;
+    const int m = 16 * w + lane;
+    const int tok = (lane < 16 && m < tl.mlen) ? perm[tl.row0 + m] / K : -1;
     s_off = tok >= 0 ? (uint32_t)tok * (uint32_t)(Kp / 32) : kOob;
   }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, (int)xq_bytes, kRsrcFlags);
@@ -187,13 +190,16 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   // a wave whose 64 pairs are all past the tile's end multiplies nothing:
   // its weight requests go past the resource (no memory traffic)
   // prepared: byte offset of this lane's scale dword in chunk 0
-  const uint32_t w_sc = (uint32_t)(((nt * nq * 2 + (w >> 1)) * 64 + lane) * 4);
+  // prepared: this wave's 32 features lie in 128-row tile pt, fragments 2 (w & 3) + i
+  const int pt = 2 * nt + (w >> 2);
+  const bool pt_live = pt < n_ntiles;  // the second half of the last workgroup may lie past O
+  const uint32_t w_sc = pt_live ? (uint32_t)(((pt * nq * 2 + ((w & 3) >> 1)) * 64 + lane) * 4) : kOob;
   uint32_t w_grp[kWI];  // canonical: group index (row * G + lc) of chunk 0; prepared: group slot of chunk 0; or kOob
 #pragma unroll
   for (int i = 0; i < kWI; i++) {
     const int f = f0 + 32 * w + 16 * i + lr;
     if constexpr (PREP)
-      w_grp[i] = (uint32_t)((nt * nq * 8 + kWI * w + i) * 64 + lane);
+      w_grp[i] = pt_live ? (uint32_t)((pt * nq * 8 + kWI * (w & 3) + i) * 64 + lane) : kOob;
     else
       w_grp[i] = f < O ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
   }
@@ -204,8 +210,8 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
   // exactly kLoadsPerChunk vector-memory requests per chunk, in this order
   auto dma_x = [&](int q, uint8_t* xdst, uint32_t* sdst) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xdst + (32 * w + 8 * j) * KC),
+    for (int j = 0; j < 2; j++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xdst + (16 * w + 8 * j) * KC),
                                                16, (int)(x_off[j] + 128u * q), 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sdst + 64 * w), 4,
                                              (int)(s_off + 4u * q), 0, 0, 0);
@@ -260,11 +266,11 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_kernel(const uint8_t* __restri
       const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * (lc ^ (p & 7))]);
       const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * ((4 + lc) ^ (p & 7))]);
       const v8i bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int bs = (int)((sc[(p >> 5) * 64 + (p & 31)] >> (8 * lc)) & 0xFFu);
+      const int bs = (int)((sc[(p >> 4) * 64 + (p & 15)] >> (8 * lc)) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < kWI; i++) {
         const v8i a = v8i{(int)wf[R][i][0], (int)wf[R][i][1], (int)wf[R][i][2], (int)wf[R][i][3], 0, 0, 0, 0};
-        const int as = PREP ? (int)((wsp[R] >> (8 * ((kWI * w + i) & 3))) & 0xFFu) : (int)wsc[R][i];
+        const int as = PREP ? (int)((wsp[R] >> (8 * ((kWI * (w & 3) + i) & 3))) & 0xFFu) : (int)wsc[R][i];
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, 0, 0, as, 0, bs);
       }
     }
@@ -376,17 +382,17 @@ hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* p
                           const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
                           float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared) {
   const int Kp = mx_row_bytes(32 * (int64_t)G);
-  const int n_ntiles = (O + NT - 1) / NT;
-  // 8 XCDs x ceil(max_tiles / 8) M-tiles x the N-tiles
-  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_ntiles;
+  const int n_ntiles = (O + NT - 1) / NT, n_wg = (O + NW - 1) / NW;
+  // 8 XCDs x ceil(max_tiles / 8) M-tiles x the feature tiles
+  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_wg;
   if (nblk == 0) return hipSuccess;
   const uint32_t xq_bytes = (uint32_t)((int64_t)T * Kp), xs_bytes = (uint32_t)((int64_t)T * Kp / 32);
   if (prepared)
-    hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3((unsigned)nblk), dim3(256), 0, stream, xq, xs, packed, scales, perm,
-                       tiles, n_tiles, part, K, O, G, Kp, n_ntiles, xq_bytes, xs_bytes);
+    hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, xq, xs, packed, scales,
+                       perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles, n_wg, xq_bytes, xs_bytes);
   else
-    hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3((unsigned)nblk), dim3(256), 0, stream, xq, xs, packed, scales, perm,
-                       tiles, n_tiles, part, K, O, G, Kp, n_ntiles, xq_bytes, xs_bytes);
+    hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, xq, xs, packed, scales,
+                       perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles, n_wg, xq_bytes, xs_bytes);
   return hipGetLastError();
 }
 
