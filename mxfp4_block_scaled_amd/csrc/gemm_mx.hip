@@ -15,10 +15,10 @@
 // assembly of the code), so the codes equal the oracle's bit for bit.
 //
 // Grouped GEMM (gemm_mx_kernel): the M-tiles of the bucketing (<= 128 pairs
-// of one expert) x N-tiles of 256 features; the 8 waves split the features
-// (each wave: all 128 pairs x 32 features), so no two waves load the same
+// of one expert) x N-tiles of 512 features; the 8 waves split the features
+// (each wave: all 128 pairs x 64 features), so no two waves load the same
 // weights, and the activations, shared by all eight, come from LDS once per
-// 256 features. MFMA
+// 512 features. MFMA
 // operand A = weights: lane (r, c) = (lane & 15, lane >> 4) holds the 16
 // packed bytes of group 4q + c of weight row r of its 16-row fragment (one
 // 16-byte load straight from memory into the operand registers) and that
@@ -52,9 +52,9 @@ constexpr uint32_t kOob = 0x80000000u;
 constexpr int MT = kGemmTileM;  // 128 pairs
 constexpr int NT = 128;         // rows of a prepared weight tile
 constexpr int kWaves = 8;       // waves per workgroup
-constexpr int NW = 32 * kWaves; // features per workgroup (each wave: all 128 pairs x 32 features)
+constexpr int kWI = 4;          // weight fragments (16 features each) per wave: the waves split the features
+constexpr int NW = 16 * kWI * kWaves;  // features per workgroup (each wave: all 128 pairs x 64 features)
 constexpr int KC = 128;         // inputs per chunk
-constexpr int kWI = 2;           // weight fragments (16 features each) per wave: the waves split the features
 constexpr int kWJ = 8;           // activation fragments (16 pairs each) per wave: every wave covers all 128 pairs
 constexpr int kRing = 3;         // chunk slots: activations (LDS) and weights (registers), two in flight
 // vector-memory requests per wave and chunk: 2 activation + 1 scale DMA, then
@@ -190,16 +190,16 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   // a wave whose 64 pairs are all past the tile's end multiplies nothing:
   // its weight requests go past the resource (no memory traffic)
   // prepared: byte offset of this lane's scale dword in chunk 0
-  // prepared: this wave's 32 features lie in 128-row tile pt, fragments 2 (w & 3) + i
-  const int pt = 2 * nt + (w >> 2);
+  // prepared: this wave's 64 features lie in 128-row tile pt, fragments 4 (w & 1) + i
+  const int pt = 4 * nt + (w >> 1);
   const bool pt_live = pt < n_ntiles;  // the second half of the last workgroup may lie past O
-  const uint32_t w_sc = pt_live ? (uint32_t)(((pt * nq * 2 + ((w & 3) >> 1)) * 64 + lane) * 4) : kOob;
+  const uint32_t w_sc = pt_live ? (uint32_t)(((pt * nq * 2 + (w & 1)) * 64 + lane) * 4) : kOob;
   uint32_t w_grp[kWI];  // canonical: group index (row * G + lc) of chunk 0; prepared: group slot of chunk 0; or kOob
 #pragma unroll
   for (int i = 0; i < kWI; i++) {
-    const int f = f0 + 32 * w + 16 * i + lr;
+    const int f = f0 + 16 * kWI * w + 16 * i + lr;
     if constexpr (PREP)
-      w_grp[i] = pt_live ? (uint32_t)((pt * nq * 8 + kWI * (w & 3) + i) * 64 + lane) : kOob;
+      w_grp[i] = pt_live ? (uint32_t)((pt * nq * 8 + kWI * (w & 1) + i) * 64 + lane) : kOob;
     else
       w_grp[i] = f < O ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
   }
@@ -261,8 +261,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
     __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
 #pragma unroll
     for (int j = 0; j < kWJ; j++) {
-      if (16 * j >= tl.mlen) break;  // 16-pair fragments past the tile's end (wave-uniform)
-      const int p = 16 * j + lr;
+      const int p = 16 * j + lr;  // rows past the tile's end hold zeros (their DMA read past the resource)
       const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * (lc ^ (p & 7))]);
       const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * ((4 + lc) ^ (p & 7))]);
       const v8i bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -270,9 +269,16 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
 #pragma unroll
       for (int i = 0; i < kWI; i++) {
         const v8i a = v8i{(int)wf[R][i][0], (int)wf[R][i][1], (int)wf[R][i][2], (int)wf[R][i][3], 0, 0, 0, 0};
-        const int as = PREP ? (int)((wsp[R] >> (8 * ((kWI * (w & 3) + i) & 3))) & 0xFFu) : (int)wsc[R][i];
+        const int as = PREP ? (int)((wsp[R] >> (8 * i)) & 0xFFu) : (int)wsc[R][i];
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, 0, 0, as, 0, bs);
       }
+    }
+    // interleave each fragment's three LDS reads with its MFMAs, so that only
+    // a few activation fragments are live at once (registers)
+#pragma unroll
+    for (int j = 0; j < kWJ; j++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kWI, 0);
     }
     wait_next_x();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
@@ -305,7 +311,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
     float* row = part + (int64_t)(tl.row0 + p) * O;
 #pragma unroll
     for (int i = 0; i < kWI; i++) {
-      const int f = f0 + 32 * w + 16 * i + 4 * lc;
+      const int f = f0 + 16 * kWI * w + 16 * i + 4 * lc;
       if (f < O) *reinterpret_cast<v4f*>(row + f) = acc[i][j];
     }
   }
