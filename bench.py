@@ -51,7 +51,9 @@ KERNEL_SOURCES = {
     "gemm": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "swiglu": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "mx": ["mxfp4_block_scaled_amd/csrc/gemm_mx.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+    "gemmp": ["mxfp4_block_scaled_amd/csrc/gemm_regdec.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
 }
+KERNEL_NAMES = {"gemv": "gemv_rows_kernel", "gemm": "gemm_bf16_kernel", "gemmp": "gemm_regdec_kernel"}
 
 
 def log(*a):
@@ -119,8 +121,8 @@ def record_traffic(args):
     HBM bytes per launch, stored in profiles/traffic.json with the hash of
     the kernel's sources; prints a summary."""
     w = workloads.WORKLOADS[args.workload]
-    kind = "gemv" if args.workload in DECODE_WORKLOADS else "gemm"
-    kname = "gemv_rows_kernel" if kind == "gemv" else "gemm_bf16_kernel"
+    kind = "gemv" if args.workload in DECODE_WORKLOADS else ("gemmp" if args.prepared else "gemm")
+    kname = KERNEL_NAMES[kind]
     fdir, wdir, cfdir, cwdir = args.record_traffic
     copy_kib = args.copy_mib * 1024.0
     k_fetch, n_f = _counter_means(fdir, "FETCH_SIZE", kname)
@@ -140,21 +142,28 @@ def record_traffic(args):
             allrec = json.load(f)
     except (OSError, ValueError):
         allrec = {}
-    allrec[w.name] = rec
+    key = w.name + ("-prepared" if kind == "gemmp" else "")
+    allrec[key] = rec
     with open(path, "w") as f:
         json.dump(allrec, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps({w.name: rec}))
+    print(json.dumps({key: rec}))
 
 
-def _kind(w, variant=None) -> str:
+def _kind(w, variant=None, prepared=False) -> str:
     if variant == "mxfp8":
         if w.F or w.dtype != "bf16":
             raise SystemExit("the MXFP8 variant runs the bf16 routed linear workloads only")
         return "mx"
     if w.F:
+        if prepared:
+            raise SystemExit("--prepared runs the routed linear workloads only")
         return "swiglu"
-    return "gemv" if w.name in DECODE_WORKLOADS else "gemm"
+    if w.name in DECODE_WORKLOADS:
+        if prepared:
+            raise SystemExit("--prepared runs the prefill-shaped workloads only")
+        return "gemv"
+    return "gemmp" if prepared else "gemm"
 
 
 def cpu_baseline(inp, kind, sample_seconds):
@@ -219,6 +228,8 @@ def cpu_baseline(inp, kind, sample_seconds):
 def _path_name(mx, w, kind) -> str:
     if kind == "mx":
         return "MXFP8 variant (bucketing, quantisation, scaled-MFMA grouped GEMM, combine)"
+    if kind == "gemmp":
+        return "GEMM on prepared weights (bucketing, register-decode grouped GEMM, combine)"
     if kind == "swiglu":
         return "SwiGLU block (bucketing, gate/up GEMM, down GEMM, combine)"
     return "GEMV" if mx.select_path(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1) == 1 else "GEMM"
@@ -341,7 +352,8 @@ def main():
     ap.add_argument("--variant", choices=["mxfp8"],
                     help="time the block-scaled variant (MXFP8 activations on the scaled MFMA) instead of the layer")
     ap.add_argument("--prepared", action="store_true",
-                    help="with --variant mxfp8: weights repacked once (outside the timed region) by prepare_mx")
+                    help="weights repacked once (outside the timed region) by prepare_mx: the bf16 GEMM on "
+                         "prepared weights, or with --variant mxfp8 the variant's")
     ap.add_argument("--router", choices=["softmax", "sigmoid"],
                     help="time the router alone at the workload's T, E and K instead of the layer")
     args = ap.parse_args()
@@ -371,7 +383,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.WORKLOADS[args.workload]
-    kind = _kind(w, args.variant)
+    kind = _kind(w, args.variant, args.prepared)
     td = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     t_gen = time.perf_counter()
     inp = workloads.make_inputs(w, n_routing_sets=N_ROUTING_SETS)
@@ -396,13 +408,13 @@ def main():
         ws_bytes = mx.swiglu_workspace_size(w.T, w.E, w.F, w.G, w.O, w.K)
     elif kind == "mx":
         ws_bytes = mx.mxfp8_workspace_size(w.T, w.E, w.O, w.G, w.K)
+    elif kind == "gemmp":
+        ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM)
     else:
         ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     prepared = None
     if args.prepared:
-        if kind != "mx":
-            raise SystemExit("--prepared goes with --variant mxfp8")
         prepared = mx.prepare_mx(packed, scales)
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs drawn and resident in {time.perf_counter() - t_gen:.1f} s; "
@@ -417,6 +429,8 @@ def main():
             mx.moe_linear_mxfp8_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "mx":
             mx.moe_linear_mxfp8(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
+        elif kind == "gemmp":
+            mx.moe_linear_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         else:
             mx.moe_linear(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
 
@@ -465,19 +479,25 @@ def main():
         raise SystemExit("timed steps ended with a result that differs from the eager call")
 
     gemm_ms = None
-    if kind == "gemm":
+    if kind in ("gemm", "gemmp"):
+        def gemm_alone():
+            if kind == "gemmp":
+                mx.gemm_stage_prepared(x, prepared, w.K, ws)
+            else:
+                mx.gemm_stage(x, packed, scales, w.K, ws)
+
         # the grouped GEMM alone, on the bucketing the last timed step left in
         # the workspace: K launches captured in a graph, timed like the steps
         r_last = (args.steps - 1) % N_ROUTING_SETS
         with torch.cuda.stream(stream):
-            mx.gemm_stage(x, packed, scales, w.K, ws)
+            gemm_alone()
         torch.cuda.synchronize()
         g2 = None
         if graph is not None:
             g2 = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g2, stream=stream):
                 for _ in range(args.steps):
-                    mx.gemm_stage(x, packed, scales, w.K, ws)
+                    gemm_alone()
             g2.replay()
             torch.cuda.synchronize()
         e2a = torch.cuda.Event(enable_timing=True)
@@ -488,7 +508,7 @@ def main():
                 g2.replay()
             else:
                 for _ in range(args.steps):
-                    mx.gemm_stage(x, packed, scales, w.K, ws)
+                    gemm_alone()
             e2b.record(stream)
         torch.cuda.synchronize()
         gemm_ms = e2a.elapsed_time(e2b) / args.steps
@@ -531,13 +551,13 @@ def main():
         ach = flops_per_step / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
-        roof["kernel"] = "gemm_bf16_kernel"
+        roof["kernel"] = KERNEL_NAMES[kind]
         roof["launch_ms"] = round(gemm_ms, 6)
     roof["per_launch"] = ({"bytes": bytes_per_step} if kind == "gemv" else {"flops": flops_per_step})
     if kind in ("swiglu", "mx"):
         roof["traffic"] = None
     else:
-        roof["traffic"] = committed_traffic(w.name, kind)
+        roof["traffic"] = committed_traffic(w.name + ("-prepared" if kind == "gemmp" else ""), kind)
     log(f"[bench] {args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, "
         f"{value:.1f} {unit} ({100 * roof['frac']:.1f}% of peak); mean distinct experts {np.mean(uniq):.1f}")
 

@@ -303,6 +303,34 @@ int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, 
                                        hipStream_t stream);
 
 /*
+ * The bf16 routed linear on prepared weights (the buffer of mxfp4_prepare_mx,
+ * a load-time byte permutation of packed and scales; page "MXFP4 Routed
+ * Expert Linear", "Reconstruct the matrix in the right orientation", for the
+ * product): the prefill-shaped path - bucketing, a grouped GEMM that brings
+ * each 1 KB block of prepared codes into LDS with one request, decodes it in
+ * registers and multiplies on bf16 MFMA with fp32 accumulation, and the
+ * combine.
+ *   mxfp4_moe_linear_prepared_ex: x (T, 32G), shared and y (T, O) bf16 as
+ *     mxfp4_moe_linear_ex with MXFP4_DTYPE_BF16; the workspace is
+ *     mxfp4_moe_workspace_size(T, E, O, G, K, MXFP4_DTYPE_BF16,
+ *     MXFP4_FLAG_FORCE_GEMM, ...) bytes; flags 0 or MXFP4_FLAG_CHECK; errors
+ *     as mxfp4_moe_linear_ex. Results within the bf16 bar of the exact layer
+ *     (the same products as the canonical path, summed in another order).
+ *   mxfp4_moe_gemm_stage_prepared: the grouped GEMM of that path alone, on
+ *     the bucketing a previous mxfp4_moe_linear_prepared_ex call with the
+ *     same sizes left in `workspace` (as mxfp4_moe_gemm_stage).
+ * MXFP4_ERR_UNSUPPORTED unless O % 4 == 0, T * 64G < 2^31 and one expert's
+ * prepared codes stay below 2^31 bytes. Allocates nothing; may be captured
+ * in a graph.
+ */
+int mxfp4_moe_linear_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,
+                                  const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O, int64_t G,
+                                  int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+int mxfp4_moe_gemm_stage_prepared(const uint16_t* x, const void* prepared, int64_t T, int64_t E, int64_t O,
+                                  int64_t G, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * mxfp4_moe_route - the router that produces sel and p from router logits
  * (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
  * Experts", section 1, for both router kinds and the floor on the selected

@@ -28,7 +28,7 @@ from ._abi import (  # noqa: F401
 __all__ = [
     "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
-    "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared",
+    "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared", "moe_linear_prepared", "gemm_stage_prepared",
     "Mxfp4Error", "library_path",
 ]
 
@@ -220,8 +220,9 @@ def moe_linear_mxfp8(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
 
 
 class PreparedMx:
-    """Weights repacked for the block-scaled variant (``prepare_mx``): a
-    uint8 device buffer and the (E, O, G) it was made from."""
+    """Weights repacked by ``prepare_mx`` (read by the block-scaled variant
+    and by the bf16 prepared path): a uint8 device buffer and the (E, O, G)
+    it was made from."""
 
     def __init__(self, buf: torch.Tensor, E: int, O: int, G: int):
         self.buf, self.E, self.O, self.G = buf, E, O, G
@@ -277,6 +278,58 @@ def moe_linear_mxfp8_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.
             _ptr(workspace), workspace.numel(), _stream(dev))
     _abi.check(st, "mxfp4_moe_linear_mxfp8_prepared_ex")
     return y
+
+
+def _prepared_call_args(x, prepared, sel, p, shared, out):
+    dev = x.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    _need(shared, "shared", torch.bfloat16, 2, dev)
+    if not isinstance(prepared, PreparedMx) or prepared.buf.device != dev:
+        raise ValueError("prepared must come from prepare_mx on x's device")
+    T, I = x.shape
+    E, O, G = prepared.E, prepared.O, prepared.G
+    K = sel.shape[1]
+    if I != 32 * G:
+        raise ValueError(f"x has {I} inputs; the prepared weights have 32 * {G}")
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K) or tuple(shared.shape) != (T, O):
+        raise ValueError("sel and p must be [T, K] and shared [T, O]")
+    y = torch.empty_like(shared) if out is None else out
+    _need(y, "out", torch.bfloat16, 2, dev)
+    if tuple(y.shape) != (T, O):
+        raise ValueError("out must be [T, O]")
+    return dev, T, E, O, G, K, y
+
+
+def moe_linear_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.Tensor, p: torch.Tensor,
+                        shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The bf16 routed linear (prefill-shaped path) on weights repacked by
+    ``prepare_mx``: bucketing, the register-decode grouped GEMM, combine."""
+    dev, T, E, O, G, K, y = _prepared_call_args(x, prepared, sel, p, shared, out)
+    need = workspace_size(T, E, O, G, K, DTYPE_BF16, FLAG_FORCE_GEMM)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_linear_prepared_ex(
+            _ptr(x), _ptr(prepared.buf), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, O, G, K, flags,
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_linear_prepared_ex")
+    return y
+
+
+def gemm_stage_prepared(x: torch.Tensor, prepared: PreparedMx, K: int, workspace: torch.Tensor) -> None:
+    """Re-run only the grouped GEMM of ``moe_linear_prepared`` on the bucketing
+    its last call with this workspace (same sizes) left there. For timing."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    T = x.shape[0]
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_gemm_stage_prepared(_ptr(x), _ptr(prepared.buf), T, prepared.E, prepared.O,
+                                                      prepared.G, K, _ptr(workspace), workspace.numel(),
+                                                      _stream(dev))
+    _abi.check(st, "mxfp4_moe_gemm_stage_prepared")
 
 
 def mxfp4_expert_linear(latent_tokens: torch.Tensor, packed_weights: torch.Tensor, scale_bytes: torch.Tensor,

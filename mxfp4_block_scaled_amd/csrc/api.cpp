@@ -477,6 +477,76 @@ int mxfp4_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, in
   return hip_status(launch_prepare_mx(packed, scales, E, (int)O, (int)G, static_cast<uint8_t*>(prepared), stream));
 }
 
+int mxfp4_moe_linear_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,
+                                  const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O, int64_t G,
+                                  int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~MXFP4_FLAG_CHECK) return MXFP4_ERR_INVALID_ARG;
+  if (!gemm_mx_supported(T, O, G) || !gemm_regdec_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  const uint8_t* pp = static_cast<const uint8_t*>(prepared);
+  const size_t pbytes = mx_prepared_bytes(E, O, G);
+  const uint8_t* ps = pp ? pp + pbytes / 17 * 16 : nullptr;
+  st = check_linear_args(x, pp, ps, sel, p, shared, y, d, MXFP4_DTYPE_BF16);
+  if (st != MXFP4_OK) return st;
+  if (d.T == 0) return MXFP4_OK;
+  if (overlap(y, (size_t)T * O * 2, pp, pbytes)) return MXFP4_ERR_INVALID_ARG;
+  const Layout L = layout(d, MXFP4_PATH_GEMM);
+  if (workspace_bytes < L.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  BucketOut b;
+  b.count = reinterpret_cast<int32_t*>(base + L.count);
+  b.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  b.perm = reinterpret_cast<int32_t*>(base + L.perm);
+  b.slot_of_pair = reinterpret_cast<int32_t*>(base + L.slot);
+  b.n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
+  b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
+  b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+  float* part = reinterpret_cast<float*>(base + L.part);
+  hipError_t err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
+  if (err == hipSuccess)
+    err = launch_gemm_regdec(x, pp, ps, b.perm, b.tiles, b.n_tiles, gemm_max_tiles(d.P, d.E), part, (int)d.T, (int)d.K,
+                             (int)d.O, (int)d.G, stream);
+  if (err == hipSuccess)
+    err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.T, (int)d.K, (int)d.O, MXFP4_DTYPE_BF16, stream);
+  if (err != hipSuccess) return MXFP4_ERR_HIP;
+  if (flags & MXFP4_FLAG_CHECK) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+    int32_t inv = 0;
+    if (hipMemcpy(&inv, b.n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
+    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
+  }
+  return MXFP4_OK;
+}
+
+int mxfp4_moe_gemm_stage_prepared(const uint16_t* x, const void* prepared, int64_t T, int64_t E, int64_t O,
+                                  int64_t G, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (d.T == 0) return MXFP4_OK;
+  if (!x || !prepared) return MXFP4_ERR_INVALID_ARG;
+  if (!gemm_mx_supported(T, O, G) || !gemm_regdec_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  const Layout L = layout(d, MXFP4_PATH_GEMM);
+  if (workspace_bytes < L.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  const uint8_t* pp = static_cast<const uint8_t*>(prepared);
+  const size_t pbytes = mx_prepared_bytes(E, O, G);
+  return hip_status(launch_gemm_regdec(x, pp, pp + pbytes / 17 * 16, reinterpret_cast<const int32_t*>(base + L.perm),
+                                       reinterpret_cast<const GemmTile*>(base + L.tiles),
+                                       reinterpret_cast<const int32_t*>(base + L.n_tiles), gemm_max_tiles(d.P, d.E),
+                                       reinterpret_cast<float*>(base + L.part), (int)d.T, (int)d.K, (int)d.O, (int)d.G,
+                                       stream));
+}
+
 int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,
                                        const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
                                        int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,

@@ -1,0 +1,302 @@
+// Prefill-shaped grouped GEMM on prepared weights, decoded in registers:
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation, the same
+// results contract as the LDS-staged kernel of gemm.hip (page "MXFP4 Routed
+// Expert Linear", "Reconstruct the matrix in the right orientation": each
+// output coordinate is a row of W_e dotted with the token; page "MXFP4
+// Dequant", "How it works": code n of byte j, low nibble first, times
+// 2^(s-127)).
+//
+// The weights come in the prepared layout of prepare_mx_kernel (a load-time
+// byte permutation: per expert, 128-row tile, chunk of 4 groups and 16-row
+// fragment, the 64 group slots in MFMA lane order - slot l = row l & 15,
+// group 4q + (l >> 4) - 1 KB contiguous; and the slots' scale bytes, four
+// fragments to a dword per lane).
+//
+// Work: the M-tiles of the bucketing (<= 128 pairs of one expert) x N-tiles
+// of 512 weight rows. Eight waves per workgroup, 2 (pairs) x 4 (rows): wave
+// (wm, wn) owns pairs 64 wm .. +63 and the 128 rows of prepared tile
+// 4 nt + wn, 8 x 4 MFMA tiles of 16 x 16. Inputs go in chunks of 128 (4
+// groups). Per chunk the workgroup brings into LDS, by DMA (buffer loads that
+// write LDS directly, no registers): the 128 gathered activation rows (row =
+// perm / K; 32 KB; two-slot ring, one chunk ahead - they come from L2,
+// shared by the N-tiles of the M-tile) and the 32 fragment blocks of its
+// weights (32 KB; three-slot ring, two chunks ahead - they come from HBM).
+// Each weight byte is fetched once per workgroup; each activation row once
+// per 512 weight rows. The scale dwords go straight to registers (two per
+// wave and chunk, a three-slot ring).
+//
+// Operand A = weights: for MFMA k-step s (0..3) lane (r, c) reads dword s of
+// its slot of each fragment from LDS and turns those 8 codes into
+// 8 bf16 with gfx950's scaled FP4 convert, scale applied (exact: E2M1 times
+// a power of two is a bf16 value, or +-inf where it overflows). No decoded
+// weight is stored anywhere. Operand B = activations: lane (p, c) of k-step s
+// takes the 8 bf16 inputs 128q + 32c + 8s .. +7 of pair p - the inputs of the
+// weight lane (r, c) of that k-step, so every product pairs x_i with w_i. The
+// 16-byte pieces of activation row m sit at position piece ^ (m & 7) of its
+// LDS row, so the fragment reads are conflict-free. Every chunk issues the
+// same number of requests, so one counted wait (this wave's activation DMA
+// of the next chunk, which also covers the older weight DMA) and a bare
+// barrier per chunk replace a full fence. Rows past the tile, inputs past I
+// and prepared tiles past O read through an offset beyond their buffer
+// resource: zeros, no memory traffic.
+//
+// A scale byte of 255 (2^128) would make the convert return NaN: such a
+// lane's codes are rewritten (under a wave-uniform branch that ordinary
+// data never takes) to twice their magnitude at scale 254, which gives the
+// same bf16 values - E2M1 x 2^128 is 2^127 for 0.5 and +-inf from 1 up.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxfp4 {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kRsrcFlags = 0x00020000;
+constexpr uint32_t kOob = 0x80000000u;
+constexpr int MT = kGemmTileM;    // 128 pairs
+constexpr int kWaves = 8;         // 2 (pairs) x 4 (rows)
+constexpr int PT = 128;           // rows of a prepared weight tile (one per wave column)
+constexpr int kWI = PT / 16;      // 16-row weight fragments per wave
+constexpr int kWJ = 4;            // 16-pair activation fragments per wave
+constexpr int NW = 4 * PT;        // weight rows per workgroup
+constexpr int KC = 128;           // inputs per chunk (4 groups)
+constexpr int ROWB = 2 * KC;      // LDS bytes of one activation row and chunk
+constexpr int kXBytes = MT * ROWB;        // activation slot (32 KB)
+constexpr int kWBytes = NW / 16 * 1024;   // weight slot: 32 fragment blocks of 1 KB
+constexpr int kXDma = kXBytes / (1024 * kWaves);  // 1 KB requests per wave and chunk
+constexpr int kWDma = kWBytes / (1024 * kWaves);
+constexpr int kScLoads = 2;                        // scale dwords per wave and chunk
+
+// codes of a lane whose scale byte is 255: magnitude m -> the code of 2 m at
+// scale 254 (0 -> 0, 0.5 -> 1, 1 -> 2, 1.5 -> 3, 2 -> 4, 3 and up -> 6, which
+// overflows to inf like every value from 2^128 up)
+__device__ __forceinline__ uint32_t double_codes(uint32_t w) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int n = 0; n < 8; n++) {
+    const uint32_t c = (w >> (4 * n)) & 15u;
+    r |= (((0x77765420u >> (4 * (c & 7u))) & 7u) | (c & 8u)) << (4 * n);
+  }
+  return r;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __restrict__ x,
+                                                             const uint8_t* __restrict__ pcodes,
+                                                             const uint8_t* __restrict__ pscales,
+                                                             const int32_t* __restrict__ perm,
+                                                             const GemmTile* __restrict__ tiles,
+                                                             const int32_t* __restrict__ n_tiles,
+                                                             float* __restrict__ part, int K, int O, int G, int n_wg,
+                                                             int n_ptiles, uint32_t x_bytes) {
+  // Workgroup i runs on XCD i mod 8: XCD x takes M-tiles x, x + 8, ... with
+  // all their N-tiles back to back, so the N-tiles of an M-tile share its
+  // gathered activation rows in one L2.
+  const int xcd_step = blockIdx.x >> 3;
+  const int ti = (blockIdx.x & 7) + 8 * (xcd_step / n_wg);
+  const int nt = xcd_step % n_wg;
+  if (ti >= n_tiles[0]) return;
+  const GemmTile tl = tiles[ti];
+
+  __shared__ __attribute__((aligned(16))) uint8_t X0[kXBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t X1[kXBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t W0[kWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t W1[kWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t W2[kWBytes];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lc = lane >> 4;
+  const int wm = w >> 2, wn = w & 3;
+  const int nq = (G + 3) / 4;  // chunks
+
+  // ---- activation DMA: request j of wave w fills rows 16 w + 4 j .. +3 of a
+  // slot (1 KB); lane l lands at row 16 w + 4 j + (l >> 4), position l & 15,
+  // so it fetches piece (l & 15) ^ (row & 7) of that row.
+  const int xld = 32 * G;  // bf16 inputs per activation row
+  uint32_t x_off[kXDma], x_in[kXDma];  // byte offset of the piece in chunk 0; its first input
+#pragma unroll
+  for (int j = 0; j < kXDma; j++) {
+    const int m = 16 * w + 4 * j + (lane >> 4);
+    const int piece = (lane & 15) ^ (m & 7);
+    const int row = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
+    x_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)(2 * xld) + 16u * (uint32_t)piece : kOob;
+    x_in[j] = 8u * (uint32_t)piece;
+  }
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRsrcFlags);
+
+  // ---- weight DMA: request j of wave w fetches fragment block 4 w + j of the
+  // workgroup (prepared tile 4 nt + (w >> 1), fragment 4 (w & 1) + j) into the
+  // same 1 KB of a slot
+  const int64_t ebase = (int64_t)tl.e * n_ptiles * nq * 512;  // group slots before expert e
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(pcodes + ebase * 16), (short)0, n_ptiles * nq * 8192, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(pscales + ebase), (short)0, n_ptiles * nq * 512, kRsrcFlags);
+  const int dpt = 4 * nt + (w >> 1);
+  // byte offset of this lane's slot of the first fragment block, chunk 0 (chunk q: + 8192 q)
+  const uint32_t w_off = dpt < n_ptiles ? (uint32_t)(((dpt * nq * 8 + 4 * (w & 1)) * 64 + lane) * 16) : kOob;
+  // scale dwords of this wave's own tile (fragments 0..3 and 4..7), chunk 0 (chunk q: + 512 q)
+  const int pt = 4 * nt + wn;
+  const uint32_t s_off = pt < n_ptiles ? (uint32_t)((pt * nq * 2 * 64 + lane) * 4) : kOob;
+
+  uint32_t wsp[3][kScLoads];
+  auto dma_x = [&](int q, uint8_t* dst) {
+#pragma unroll
+    for (int j = 0; j < kXDma; j++) {
+      // an input past I moves the offset past the resource
+      const uint32_t past = (uint32_t)(xld - 1 - (int)(128u * q + x_in[j])) >> 31 << 31;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(dst + (16 * w + 4 * j) * ROWB), 16,
+                                               (int)((x_off[j] + 256u * q) | past), 0, 0, 0);
+    }
+  };
+  auto dma_w = [&](int q, uint8_t* dst, int slot) {
+#pragma unroll
+    for (int j = 0; j < kWDma; j++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + (4 * w + j) * 1024), 16,
+                                               (int)((w_off + 8192u * q + 1024u * j) | (w_off & kOob)), 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < kScLoads; h++)
+      wsp[slot][h] =
+          __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)((s_off + 512u * q + 256u * h) | (s_off & kOob)), 0, 0);
+  };
+  // wait until this wave's activation DMA of the next chunk has landed: it
+  // was followed by one chunk's weight and scale requests
+  auto wait_next_x = [&]() {
+    constexpr int n = kWDma + kScLoads;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+  };
+
+  // whether this wave multiplies anything: pairs left in the tile, rows left in O
+  const bool live = 64 * wm < tl.mlen && NW * nt + PT * wn < O;
+
+  v4f acc[kWI][kWJ];
+#pragma unroll
+  for (int i = 0; i < kWI; i++)
+#pragma unroll
+    for (int j = 0; j < kWJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // One chunk q, activation slot q mod 2 and weight slot q mod 3 (both
+  // compile-time): request the activations of chunk q + 1 (into the slot read
+  // last during chunk q - 1) and the weights of chunk q + 2 (likewise),
+  // multiply chunk q, wait for this wave's activation DMA of chunk q + 1,
+  // barrier. Past the last chunk the requests repeat the last chunk into
+  // slots nobody reads again, so the number of requests per chunk - and every
+  // wait count - is fixed.
+  auto step = [&](int q, auto xs, auto ws) {
+    constexpr int RX = decltype(xs)::value, RW = decltype(ws)::value, RWN = (RW + 2) % 3;
+    const uint8_t* xc = RX == 0 ? X0 : X1;
+    uint8_t* xn = RX == 0 ? X1 : X0;
+    const uint8_t* wc = RW == 0 ? W0 : (RW == 1 ? W1 : W2);
+    uint8_t* wnx = RWN == 0 ? W0 : (RWN == 1 ? W1 : W2);
+    dma_x(min(q + 1, nq - 1), xn);
+    dma_w(min(q + 2, nq - 1), wnx, RWN);
+    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
+    if (live) {
+      uint32_t sb[kWI];
+      bool s255 = false;
+#pragma unroll
+      for (int i = 0; i < kWI; i++) {
+        sb[i] = (wsp[RW][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        s255 |= sb[i] == 255u;
+      }
+      const bool slow = __ballot(s255) != 0;
+      float sc[kWI];
+#pragma unroll
+      for (int i = 0; i < kWI; i++) sc[i] = e8m0_operand(sb[i] == 255u ? 254u : sb[i]);
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        bf16x8 b[kWJ];
+#pragma unroll
+        for (int j = 0; j < kWJ; j++) {
+          const int p = 64 * wm + 16 * j + lr;  // rows past the tile hold zeros (their DMA read past the resource)
+          b[j] = __builtin_bit_cast(bf16x8,
+                                    *reinterpret_cast<const u32x4*>(&xc[p * ROWB + 16 * ((4 * lc + s) ^ (p & 7))]));
+        }
+        uint32_t raw[kWI];  // dword s of this lane's slot of each fragment: 8 codes
+#pragma unroll
+        for (int i = 0; i < kWI; i++)
+          raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(wn * kWI + i) * 1024 + 16 * lane + 4 * s]);
+        if (__builtin_expect(slow, 0)) {
+#pragma unroll
+          for (int i = 0; i < kWI; i++)
+            if (sb[i] == 255u) raw[i] = double_codes(raw[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kWI; i++) {
+          const bf16x8 a = decode8_bf16x8(raw[i], sc[i]);
+#pragma unroll
+          for (int j = 0; j < kWJ; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+    wait_next_x();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  dma_x(0, X0);
+  dma_w(0, W0, 0);
+  dma_w(min(1, nq - 1), W1, 1);
+  wait_next_x();  // chunk 0's activations and weights: followed by chunk 1's weight requests
+  __builtin_amdgcn_s_barrier();
+  int q = 0;
+  for (; q + 5 < nq; q += 6) {  // activation slots cycle by 2, weight slots by 3
+    step(q, C0{}, C0{});
+    step(q + 1, C1{}, C1{});
+    step(q + 2, C0{}, C2{});
+    step(q + 3, C1{}, C0{});
+    step(q + 4, C0{}, C1{});
+    step(q + 5, C1{}, C2{});
+  }
+  if (q < nq) step(q, C0{}, C0{});
+  if (q + 1 < nq) step(q + 1, C1{}, C1{});
+  if (q + 2 < nq) step(q + 2, C0{}, C2{});
+  if (q + 3 < nq) step(q + 3, C1{}, C0{});
+  if (q + 4 < nq) step(q + 4, C0{}, C1{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
+
+  // lane (lr, lc) of MFMA tile (i, j): pair 64 wm + 16 j + lr, rows 4 lc .. 4 lc + 3 of fragment i
+#pragma unroll
+  for (int j = 0; j < kWJ; j++) {
+    const int p = 64 * wm + 16 * j + lr;
+    if (p >= tl.mlen) continue;
+    float* row = part + (int64_t)(tl.row0 + p) * O;
+#pragma unroll
+    for (int i = 0; i < kWI; i++) {
+      const int r = NW * nt + PT * wn + 16 * i + 4 * lc;  // O % 4 == 0: all four or none
+      if (r < O) *reinterpret_cast<v4f*>(row + r) = acc[i][j];
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_regdec_supported(int64_t T, int64_t O, int64_t G) {
+  // 32-bit byte offsets into the activations and into one expert's prepared
+  // codes, whole 16-byte output stores
+  const int64_t nq = (G + 3) / 4, prepared = (O + PT - 1) / PT * nq * 8192;
+  return O % 4 == 0 && T * 64 * G < ((int64_t)1 << 31) && prepared < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_regdec(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* perm,
+                              const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T,
+                              int K, int O, int G, hipStream_t stream) {
+  if (!gemm_regdec_supported(T, O, G)) return hipErrorInvalidValue;
+  const int n_wg = (O + NW - 1) / NW, n_ptiles = (O + PT - 1) / PT;
+  // 8 XCDs x ceil(max_tiles / 8) M-tiles x the N-tiles
+  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_wg;
+  if (nblk <= 0) return hipSuccess;
+  const uint32_t x_bytes = (uint32_t)((int64_t)T * 64 * G);
+  hipLaunchKernelGGL(gemm_regdec_kernel, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, x, pcodes, pscales, perm,
+                     tiles, n_tiles, part, K, O, G, n_wg, n_ptiles, x_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4

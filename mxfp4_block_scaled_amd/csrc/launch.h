@@ -110,6 +110,14 @@ bool gemm_supported(int64_t T, int64_t O, int64_t G);
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                             const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
                             int O, int G, hipStream_t stream);
+// The same on weights in the prepared layout of launch_prepare_mx (pcodes:
+// its code slots, pscales: its scale array), decoded in registers (8-wave
+// workgroups over 128 pairs x 512 rows); needs gemm_regdec_supported:
+// O % 4 == 0 and 32-bit offsets into the activations and one expert's codes.
+bool gemm_regdec_supported(int64_t T, int64_t O, int64_t G);
+hipError_t launch_gemm_regdec(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* perm,
+                              const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T,
+                              int K, int O, int G, hipStream_t stream);
 // SwiGLU expert block, gate/up stage: weights (E, 2F, G, 16) with gate rows
 // [0, F) over up rows [F, 2F); writes h[sorted position, f] = bf16 of
 // silu(gate) * up, h being (P, F).

@@ -110,6 +110,18 @@ def test_graph_block_scaled_variant(prepared):
     _replays_match(call, out, disturb)
 
 
+def test_graph_prepared_bf16():
+    say("graph: moe_linear_prepared")
+    x, packed, scales, sel, p, shared = _case(4, 300, 8, 4, 9, 1040)
+    prep = mx.prepare_mx(packed, scales)
+    ws = torch.empty(mx.workspace_size(300, 8, 1040, 9, 4, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty_like(shared)
+    other = torch.empty_like(shared)
+    _replays_match(lambda: mx.moe_linear_prepared(x, prep, sel, p, shared, out=out, workspace=ws), out,
+                   lambda: mx.moe_linear_prepared(x, prep, sel.flip(1).contiguous(), p, shared, out=other))
+
+
 def test_graph_router():
     say("graph: route")
     logits, bias = workloads.router_logits(700, 96, seed=5, bias_std=0.1)

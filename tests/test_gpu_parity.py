@@ -301,6 +301,8 @@ EDGE_CASES = [
     (20, 4, 2, 33, 40, True),    # odd G over three 16-group scale chunks
     (17, 3, 3, 47, 129, True),   # odd G, ragged N-tile, scale rows at every byte offset
     (6, 5, 2, 32, 36, True),     # G an exact multiple of the scale chunk
+    (150, 2, 2, 6, 516, True),   # M-tiles of 128 and 22 pairs, a 4-row last N-tile
+    (70, 1, 1, 90, 260, True),   # one expert, 70 pairs, the prefill input width
 ]
 
 

@@ -1,0 +1,209 @@
+"""GPU parity of the bf16 routed linear on prepared weights
+(mxfp4_moe_linear_prepared_ex and mxfp4_moe_gemm_stage_prepared, through
+their C ABI) against the float64 oracle.
+
+Bar (written in each check): relative L2 <= 1e-2 against oracle.expert_linear
+on the same bf16 inputs - the bf16 bar; what remains is the bf16 output
+rounding (the decoded weights are exact in bf16, the products exact in fp32,
+the sums fp32).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only machines, never run there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import mxfp4_block_scaled_amd as mx  # noqa: E402
+from mxfp4_block_scaled_amd import _abi  # noqa: E402
+
+DEV = torch.device("cuda:0")
+BF16_REL_L2 = 1e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rel_l2(y, ref):
+    return float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def bf16_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+
+
+def host64(y):
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def case(seed, T, E, K, G, O, scale_lo=118, scale_hi=130, distinct=True, empty_experts=()):
+    rng = np.random.default_rng(seed)
+    x = workloads.round_to_bf16(rng.standard_normal((T, 32 * G)).astype(np.float32))
+    shared = workloads.round_to_bf16(rng.standard_normal((T, O)).astype(np.float32))
+    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, (E, O, G), dtype=np.uint8)
+    pool = [e for e in range(E) if e not in empty_experts]
+    if distinct:
+        sel = np.stack([rng.permutation(pool)[:K] for _ in range(T)]).astype(np.int32)
+    else:
+        sel = rng.choice(pool, (T, K)).astype(np.int32)
+    p = rng.random((T, K)).astype(np.float32)
+    return x, packed, scales, sel, p, shared
+
+
+def run_case(x, packed, scales, sel, p, shared, out=None):
+    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    y = mx.moe_linear_prepared(bf16_dev(x), prep, torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV),
+                               bf16_dev(shared), out=out)
+    torch.cuda.synchronize()
+    return y
+
+
+def check(y, ref, what):
+    yh = host64(y)
+    r = rel_l2(yh, ref)
+    say(f"  {what}: rel L2 {r:.3e}")
+    assert r <= BF16_REL_L2, f"{what}: relative L2 {r:.3e}"
+    assert np.all(np.isfinite(yh))
+
+
+CASES = [  # seed, T, E, K, G, O
+    (1, 1, 4, 2, 4, 128),       # one chunk of 128 inputs, one 128-row tile
+    (2, 5, 3, 2, 1, 40),        # G = 1, O not a multiple of 16 or 128
+    (3, 37, 8, 3, 6, 256),      # a 2-group last chunk
+    (4, 130, 4, 2, 9, 132),     # M-tiles past 128 rows, a 4-row last tile
+    (5, 300, 16, 4, 90, 200),   # the prefill input width (a half chunk at the end)
+    (6, 150, 2, 2, 7, 1028),    # three 512-row N-tiles, the last with 4 rows; tiles of 128 and 22 pairs
+    (7, 70, 1, 1, 5, 520),      # 70 pairs: the second half of the waves holds 6
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"T{c[1]}E{c[2]}K{c[3]}G{c[4]}O{c[5]}" for c in CASES])
+def test_prepared_against_oracle(c):
+    args = case(*c)
+    say(f"prepared bf16 case {c}")
+    check(run_case(*args), oracle.expert_linear(*args), f"case {c}")
+
+
+def test_prepared_edges():
+    # duplicate experts in a token, experts nobody picks, K = 1
+    args = case(8, 50, 6, 3, 3, 64, distinct=False, empty_experts=(1, 4))
+    check(run_case(*args), oracle.expert_linear(*args), "duplicates and empty experts")
+    args = case(9, 9, 5, 1, 5, 36)
+    check(run_case(*args), oracle.expert_linear(*args), "K = 1")
+    # every token on one expert: 5 full M-tiles and a ragged one
+    x, packed, scales, sel, p, shared = case(10, 700, 3, 1, 4, 64)
+    sel[:] = 2
+    args = (x, packed, scales, sel, p, shared)
+    check(run_case(*args), oracle.expert_linear(*args), "one hot expert")
+    # in place: out = shared
+    x, packed, scales, sel, p, shared = case(11, 12, 4, 2, 2, 48)
+    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    sh = bf16_dev(shared)
+    y = mx.moe_linear_prepared(bf16_dev(x), prep, torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV), sh,
+                               out=sh)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == sh.data_ptr()
+    check(y, oracle.expert_linear(x, packed, scales, sel, p, shared), "in place")
+
+
+def test_prepared_largest_scales_with_finite_weights():
+    """Scale bytes 253..255 with codes small enough that every decoded weight
+    is a finite bf16 value (|E2M1| <= 1.5 at 253/254, <= 0.5 at 255): the
+    scale-255 rewrite of the codes is checked against the float64 oracle."""
+    T, E, K, G, O = 20, 3, 2, 37, 72
+    x, packed, scales, sel, p, shared = case(12, T, E, K, G, O)
+    x = workloads.round_to_bf16((x * np.float32(2.0 ** -110)).astype(np.float32))
+    rng = np.random.default_rng(13)
+    scales = rng.integers(253, 256, scales.shape).astype(np.uint8)
+    small = np.array([0, 1, 8, 9], np.uint8)              # 0, 0.5, -0, -0.5
+    mid = np.array([0, 1, 2, 3, 8, 9, 10, 11], np.uint8)  # |E2M1| <= 1.5
+    lo255, hi255 = rng.choice(small, packed.shape), rng.choice(small, packed.shape)
+    lo, hi = rng.choice(mid, packed.shape), rng.choice(mid, packed.shape)
+    is255 = (scales == 255)[..., None]
+    packed = np.where(is255, lo255 | (hi255 << 4), lo | (hi << 4)).astype(np.uint8)
+    ref = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    assert np.all(np.isfinite(ref))
+    check(run_case(x, packed, scales, sel, p, shared), ref, "scales 253..255, finite weights")
+
+
+def test_prepared_scale_255_overflows_like_the_canonical_path():
+    """At scale byte 255 every code of magnitude >= 1 overflows bf16 (the
+    reading of the grouped GEMM's bf16 weights): both GEMM paths give the same
+    non-finite pattern on a row whose weights do, and agree elsewhere."""
+    T, E, K, G, O = 4, 2, 1, 2, 16
+    x, packed, scales, sel, p, shared = case(14, T, E, K, G, O)
+    scales[:, 3, :] = 255   # row 3 of both experts: weights 2^127 (code 1) or inf
+    args = (x, packed, scales, sel, p, shared)
+    y_prep = host64(run_case(*args))
+    d = [torch.from_numpy(a).to(DEV) for a in (packed, scales, sel, p)]
+    y_can = host64(mx.moe_linear(bf16_dev(x), d[0], d[1], d[2], d[3], bf16_dev(shared), flags=_abi.FLAG_FORCE_GEMM))
+    fin = np.isfinite(y_can)
+    assert not fin[:, 3].any() and fin[:, [c for c in range(O) if c != 3]].all()
+    assert np.array_equal(np.isfinite(y_prep), fin)
+    assert np.array_equal(np.isnan(y_prep), np.isnan(y_can))
+    assert np.array_equal(np.sign(y_prep[~fin & ~np.isnan(y_prep)]), np.sign(y_can[~fin & ~np.isnan(y_can)]))
+    rest = [c for c in range(O) if c != 3]
+    ref = oracle.expert_linear(*args)[:, rest]
+    assert rel_l2(y_prep[:, rest], ref) <= BF16_REL_L2
+
+
+def test_prepared_deterministic_and_gemm_stage():
+    args = case(15, 64, 8, 4, 8, 96)
+    x, packed, scales, sel, p, shared = args
+    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    xd, seld, pd, shd = bf16_dev(x), torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV), bf16_dev(shared)
+    ws = torch.empty(mx.workspace_size(64, 8, 96, 8, 4, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM), dtype=torch.uint8,
+                     device=DEV)
+    y1 = mx.moe_linear_prepared(xd, prep, seld, pd, shd, workspace=ws)
+    torch.cuda.synchronize()
+    part = ws.clone()
+    mx.gemm_stage_prepared(xd, prep, 4, ws)  # the GEMM alone, again, on the same bucketing
+    torch.cuda.synchronize()
+    assert torch.equal(ws, part)
+    y2 = mx.moe_linear_prepared(xd, prep, seld, pd, shd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    check(y1, oracle.expert_linear(*args), "deterministic")
+
+
+@pytest.mark.parametrize("name,nrows", [("prefill", 48), ("skewed", 40)])
+def test_prepared_full_workloads_sampled_rows(name, nrows):
+    inp = workloads.make_inputs(name, n_routing_sets=1)
+    w = inp.workload
+    say(f"prepared bf16 at {name}: T={w.T} E={w.E} K={w.K} G={w.G} O={w.O}")
+    pk = torch.empty(inp.packed.shape, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(inp.scales.shape, dtype=torch.uint8, device=DEV)
+    for e in range(w.E):  # the expert tensors are drawn expert by expert
+        pk[e].copy_(torch.from_numpy(np.ascontiguousarray(inp.packed[e])))
+        sc[e].copy_(torch.from_numpy(np.ascontiguousarray(inp.scales[e])))
+    prep = mx.prepare_mx(pk, sc)
+    del pk, sc
+    y = mx.moe_linear_prepared(bf16_dev(inp.x), prep, torch.from_numpy(inp.sel).to(DEV),
+                               torch.from_numpy(inp.p).to(DEV), bf16_dev(inp.shared))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.array(sorted(set(rng.choice(w.O, nrows, replace=False).tolist()) | {0, 127, 128, 511, 512, w.O - 1}))
+    ref = oracle.expert_linear_rows(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
+    check(y[:, torch.from_numpy(rows).to(DEV)], ref, name)
+    assert torch.isfinite(y.float()).all()
+
+
+def test_prepared_rejects_unsupported_and_empty():
+    x, packed, scales, sel, p, shared = case(16, 3, 2, 1, 2, 34)  # O % 4 != 0: no prepared layout
+    with pytest.raises(mx.Mxfp4Error):
+        mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    x, packed, scales, sel, p, shared = case(17, 3, 2, 1, 2, 32)
+    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    y = mx.moe_linear_prepared(bf16_dev(x[:0]), prep, torch.from_numpy(sel[:0]).to(DEV),
+                               torch.from_numpy(p[:0]).to(DEV), bf16_dev(shared[:0]))
+    assert tuple(y.shape) == (0, 32)
