@@ -32,8 +32,9 @@
 // weight is stored anywhere. Operand B = activations: lane (p, c) of k-step s
 // takes the 8 bf16 inputs 128q + 32c + 8s .. +7 of pair p - the inputs of the
 // weight lane (r, c) of that k-step, so every product pairs x_i with w_i. The
-// 16-byte pieces of activation row m sit at position piece ^ (m & 7) of its
-// LDS row, so the fragment reads are conflict-free. Every chunk issues the
+// 16-byte pieces of activation row m sit at position piece ^ (m & 15) of its
+// LDS row: the 16 lanes that LDS serves together (16 bytes each across its 64
+// banks) read 16 rows at 16 distinct positions. Every chunk issues the
 // same number of requests, so one counted wait (this wave's activation DMA
 // of the next chunk, which also covers the older weight DMA) and a bare
 // barrier per chunk replace a full fence. Rows past the tile, inputs past I
@@ -115,16 +116,15 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
 
   // ---- activation DMA: request j of wave w fills rows 16 w + 4 j .. +3 of a
   // slot (1 KB); lane l lands at row 16 w + 4 j + (l >> 4), position l & 15,
-  // so it fetches piece (l & 15) ^ (row & 7) of that row.
+  // so it fetches piece (l & 15) ^ (row & 15) of that row.
   const int xld = 32 * G;  // bf16 inputs per activation row
-  uint32_t x_off[kXDma], x_in[kXDma];  // byte offset of the piece in chunk 0; its first input
+  uint32_t x_off[kXDma];  // byte offset of the piece in chunk 0
 #pragma unroll
   for (int j = 0; j < kXDma; j++) {
     const int m = 16 * w + 4 * j + (lane >> 4);
-    const int piece = (lane & 15) ^ (m & 7);
+    const int piece = (lane & 15) ^ (m & 15);
     const int row = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
     x_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)(2 * xld) + 16u * (uint32_t)piece : kOob;
-    x_in[j] = 8u * (uint32_t)piece;
   }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRsrcFlags);
 
@@ -147,8 +147,10 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   auto dma_x = [&](int q, uint8_t* dst) {
 #pragma unroll
     for (int j = 0; j < kXDma; j++) {
-      // an input past I moves the offset past the resource
-      const uint32_t past = (uint32_t)(xld - 1 - (int)(128u * q + x_in[j])) >> 31 << 31;
+      // an input past I moves the offset past the resource (the piece's first
+      // input is 8 ((l & 15) ^ (row & 15)), row & 15 = 4 j + (l >> 4))
+      const int first = 128 * q + 8 * ((lane & 15) ^ ((4 * j + lc) & 15));
+      const uint32_t past = (uint32_t)(xld - 1 - first) >> 31 << 31;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(dst + (16 * w + 4 * j) * ROWB), 16,
                                                (int)((x_off[j] + 256u * q) | past), 0, 0, 0);
     }
@@ -212,9 +214,9 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
         bf16x8 b[kWJ];
 #pragma unroll
         for (int j = 0; j < kWJ; j++) {
-          const int p = 64 * wm + 16 * j + lr;  // rows past the tile hold zeros (their DMA read past the resource)
-          b[j] = __builtin_bit_cast(bf16x8,
-                                    *reinterpret_cast<const u32x4*>(&xc[p * ROWB + 16 * ((4 * lc + s) ^ (p & 7))]));
+          // row p = 64 wm + 16 j + lr (p & 15 = lr); rows past the tile hold zeros (their DMA read past the resource)
+          b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                &xc[(64 * wm + 16 * j + lr) * ROWB + 16 * ((4 * lc + s) ^ lr)]));
         }
         uint32_t raw[kWI];  // dword s of this lane's slot of each fragment: 8 codes
 #pragma unroll
