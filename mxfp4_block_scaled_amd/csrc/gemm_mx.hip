@@ -142,8 +142,10 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   const int f0 = nt * NW;
 
   // Activation ring: three chunk slots, each 128 rows x 128 bytes with the
-  // 16-byte pieces of row m stored at position piece ^ (m & 7) (conflict-free
-  // 16-byte reads without padding), and 4 x 64 scale dwords (wave w's dword
+  // 16-byte pieces of row m stored at position piece ^ ((m >> 1) & 7): LDS
+  // serves a 16-byte read for 16 lanes at a time over 64 banks (256 bytes, two
+  // rows), and the 16 rows of a fragment read then land on 16 distinct bank
+  // groups without padding; and 4 x 64 scale dwords (wave w's dword
   // l < 32 is row 32 w + l). Three separate arrays, so that the compiler can
   // tell a slot being read from the slots the DMA is filling.
   __shared__ __attribute__((aligned(16))) uint8_t X0[MT * KC];
@@ -157,8 +159,8 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   const int lr = lane & 15, lc = lane >> 4;
 
   // activation DMA: wave w, request j fills rows 16 w + 8 j .. +7 of a slot
-  // (1 KB); lane l lands at row l >> 3, position l & 7 and so fetches piece
-  // (l & 7) ^ (l >> 3) of its row. Scale DMA: lane l < 16 fetches the dword of
+  // (1 KB); lane l lands at row m = 16 w + 8 j + (l >> 3), position l & 7 and
+  // so fetches piece (l & 7) ^ ((m >> 1) & 7) of its row. Scale DMA: lane l < 16 fetches the dword of
   // row 16 w + l (blocks 4q .. 4q+3); lanes 16 .. 63 read past the resource
   // and write zeros into the unused part of the wave's 64 dwords.
   uint32_t x_off[2];
@@ -166,7 +168,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   for (int j = 0; j < 2; j++) {
     const int m = 16 * w + 8 * j + (lane >> 3);
     const int tok = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
-    x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 16u * (uint32_t)((lane & 7) ^ (lane >> 3)) : kOob;
+    x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 16u * (uint32_t)((lane & 7) ^ ((m >> 1) & 7)) : kOob;
   }
   uint32_t s_off;
   {
@@ -262,8 +264,8 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
 #pragma unroll
     for (int j = 0; j < kWJ; j++) {
       const int p = 16 * j + lr;  // rows past the tile's end hold zeros (their DMA read past the resource)
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * (lc ^ (p & 7))]);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * ((4 + lc) ^ (p & 7))]);
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * (lc ^ (lr >> 1))]);  // (p >> 1) & 7 = lr >> 1
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * ((4 + lc) ^ (lr >> 1))]);
       const v8i bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       const int bs = (int)((sc[(p >> 4) * 64 + (p & 15)] >> (8 * lc)) & 0xFFu);
 #pragma unroll
