@@ -156,9 +156,7 @@ def _kind(w, variant=None, prepared=False) -> str:
             raise SystemExit("the MXFP8 variant runs the bf16 routed linear workloads only")
         return "mx"
     if w.F:
-        if prepared:
-            raise SystemExit("--prepared runs the routed linear workloads only")
-        return "swiglu"
+        return "swiglup" if prepared else "swiglu"
     if w.name in DECODE_WORKLOADS:
         if prepared:
             raise SystemExit("--prepared runs the prefill-shaped workloads only")
@@ -176,7 +174,7 @@ def cpu_baseline(inp, kind, sample_seconds):
     except Exception:  # threadpoolctl missing: numpy's BLAS threads unknown
         threads = os.cpu_count() or 1
     w = inp.workload
-    if kind == "swiglu":
+    if kind in ("swiglu", "swiglup"):
         # one token's full SwiGLU (all K pairs) on a sample of output rows
         rows_per_call = 16
         done_flops, calls, t0 = 0.0, 0, time.perf_counter()
@@ -232,6 +230,8 @@ def _path_name(mx, w, kind) -> str:
         return "GEMM on prepared weights (bucketing, register-decode grouped GEMM, combine)"
     if kind == "swiglu":
         return "SwiGLU block (bucketing, gate/up GEMM, down GEMM, combine)"
+    if kind == "swiglup":
+        return "SwiGLU block on prepared weights (bucketing, register-decode gate/up and down GEMMs, combine)"
     return "GEMV" if mx.select_path(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1) == 1 else "GEMM"
 
 
@@ -393,7 +393,7 @@ def main():
         packed[e].copy_(torch.from_numpy(inp.packed[e]))
         scales[e].copy_(torch.from_numpy(inp.scales[e]))
     dn_packed = dn_scales = None
-    if kind == "swiglu":
+    if kind in ("swiglu", "swiglup"):
         dn_packed = torch.empty(inp.dn_packed.shape, dtype=torch.uint8, device=dev)
         dn_scales = torch.empty(inp.dn_scales.shape, dtype=torch.uint8, device=dev)
         for e in range(w.E):
@@ -404,7 +404,7 @@ def main():
     sels = torch.from_numpy(np.stack([s for s, _ in inp.routing_sets])).to(dev)
     ps = torch.from_numpy(np.stack([p for _, p in inp.routing_sets])).to(dev)
     y = torch.empty_like(shared)
-    if kind == "swiglu":
+    if kind in ("swiglu", "swiglup"):
         ws_bytes = mx.swiglu_workspace_size(w.T, w.E, w.F, w.G, w.O, w.K)
     elif kind == "mx":
         ws_bytes = mx.mxfp8_workspace_size(w.T, w.E, w.O, w.G, w.K)
@@ -415,7 +415,8 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     prepared = None
     if args.prepared:
-        prepared = mx.prepare_mx(packed, scales)
+        prepared = (mx.prepare_swiglu(packed, scales, dn_packed, dn_scales) if kind == "swiglup"
+                    else mx.prepare_mx(packed, scales))
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs drawn and resident in {time.perf_counter() - t_gen:.1f} s; "
         f"packed {packed.numel() / 1e9:.2f} GB, workspace {ws.numel() / 1e6:.1f} MB, "
@@ -425,6 +426,8 @@ def main():
         r = i % N_ROUTING_SETS
         if kind == "swiglu":
             mx.moe_swiglu(x, packed, scales, dn_packed, dn_scales, sels[r], ps[r], shared, out=y, workspace=ws)
+        elif kind == "swiglup":
+            mx.moe_swiglu_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "mx" and prepared is not None:
             mx.moe_linear_mxfp8_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "mx":
@@ -517,7 +520,7 @@ def main():
     uniq = [len(np.unique(inp.routing_sets[i % N_ROUTING_SETS][0])) for i in range(args.steps)]
     bytes_per_step = float(np.mean(uniq)) * w.O * w.G * 17
     flops_per_step = 2.0 * w.P * w.O * w.I
-    if kind == "swiglu":
+    if kind in ("swiglu", "swiglup"):
         flops_per_step = 2.0 * w.P * (2 * w.F * w.I + w.O * w.F)
     if kind == "mx":
         # the variant's grouped GEMM on the scaled MFMA is its work; timed as
@@ -528,14 +531,15 @@ def main():
                 "frac": round(value / MFMA_FP8_PEAK_TFLOPS, 4)}
         roof["kernel"] = "gemm_mx_kernel<%s> (whole call)" % ("true" if prepared is not None else "false")
         roof["launch_ms"] = round(ms_step, 6)
-    elif kind == "swiglu":
+    elif kind in ("swiglu", "swiglup"):
         # the block's two grouped GEMMs are its work; timed here as the whole
         # call (bucketing and combine included), a lower bound on the GEMMs
         value = flops_per_step / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4)}
-        roof["kernel"] = "gemm_bf16_kernel<1> + gemm_bf16_kernel<2> (whole call)"
+        roof["kernel"] = ("gemm_regdec_kernel<1> + gemm_regdec_kernel<2> (whole call)" if kind == "swiglup"
+                          else "gemm_bf16_kernel<1> + gemm_bf16_kernel<2> (whole call)")
         roof["launch_ms"] = round(ms_step, 6)
     elif kind == "gemv":
         # one launch per step: the fused kernel is the whole call
@@ -554,7 +558,7 @@ def main():
         roof["kernel"] = KERNEL_NAMES[kind]
         roof["launch_ms"] = round(gemm_ms, 6)
     roof["per_launch"] = ({"bytes": bytes_per_step} if kind == "gemv" else {"flops": flops_per_step})
-    if kind in ("swiglu", "mx"):
+    if kind in ("swiglu", "swiglup", "mx"):
         roof["traffic"] = None
     else:
         roof["traffic"] = committed_traffic(w.name + ("-prepared" if kind == "gemmp" else ""), kind)

@@ -331,6 +331,30 @@ int mxfp4_moe_gemm_stage_prepared(const uint16_t* x, const void* prepared, int64
                                   int64_t G, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The SwiGLU expert block on prepared weights (page "MoE Expert Kernels:
+ * Grouped Prefill and Mixed-Quant Compact Experts", section 1; the weights
+ * repacked once at load time, nothing decoded).
+ *   mxfp4_prepare_swiglu: gate/up packed (E, 2F, G, 16) and scales (E, 2F, G)
+ *     (gate rows [0, F) over up rows [F, 2F)) -> the prepared layout of
+ *     mxfp4_prepare_mx with the rows reordered so that each 128-row tile holds
+ *     the gate rows of 64 features followed by their up rows. Size:
+ *     mxfp4_mx_prepared_size(E, 2F, G). Alignment, overlap and errors as
+ *     mxfp4_prepare_mx; F a multiple of 32.
+ *   mxfp4_moe_swiglu_prepared_ex: mxfp4_moe_swiglu_ex with gu_prepared from
+ *     mxfp4_prepare_swiglu and dn_prepared from mxfp4_prepare_mx(dn_packed,
+ *     dn_scales, E, O, F / 32, ...); the same workspace size, flags, errors
+ *     and bar (both GEMMs on the register-decode kernel). Also
+ *     MXFP4_ERR_UNSUPPORTED unless O % 4 == 0 and one expert's prepared codes
+ *     stay below 2^31 bytes. Allocates nothing; may be captured in a graph.
+ */
+int mxfp4_prepare_swiglu(const uint8_t* gu_packed, const uint8_t* gu_scales, int64_t E, int64_t F, int64_t G,
+                         void* prepared, size_t bytes, hipStream_t stream);
+int mxfp4_moe_swiglu_prepared_ex(const uint16_t* x, const void* gu_prepared, const void* dn_prepared,
+                                 const int32_t* sel, const float* p, const uint16_t* shared, uint16_t* y, int64_t T,
+                                 int64_t E, int64_t F, int64_t G, int64_t O, int64_t K, uint32_t flags,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * mxfp4_moe_route - the router that produces sel and p from router logits
  * (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
  * Experts", section 1, for both router kinds and the floor on the selected

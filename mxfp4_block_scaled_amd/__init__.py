@@ -29,6 +29,7 @@ __all__ = [
     "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
     "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared", "moe_linear_prepared", "gemm_stage_prepared",
+    "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
     "Mxfp4Error", "library_path",
 ]
 
@@ -330,6 +331,72 @@ def gemm_stage_prepared(x: torch.Tensor, prepared: PreparedMx, K: int, workspace
                                                       prepared.G, K, _ptr(workspace), workspace.numel(),
                                                       _stream(dev))
     _abi.check(st, "mxfp4_moe_gemm_stage_prepared")
+
+
+class PreparedSwiGLU:
+    """SwiGLU expert weights repacked once (``prepare_swiglu``): the gate/up
+    buffer, the down buffer and the (E, F, G, O) they were made from."""
+
+    def __init__(self, gu: torch.Tensor, dn: PreparedMx, E: int, F: int, G: int, O: int):
+        self.gu, self.dn, self.E, self.F, self.G, self.O = gu, dn, E, F, G, O
+
+
+def prepare_swiglu(gu_packed: torch.Tensor, gu_scales: torch.Tensor, dn_packed: torch.Tensor,
+                   dn_scales: torch.Tensor) -> PreparedSwiGLU:
+    """Load-time repack of a SwiGLU block's weights: gate/up [E, 2F, G, 16]
+    (gate rows first) in the row order that puts 64 features' gate and up
+    rows in one tile, and the down projection [E, O, F/32, 16] as
+    ``prepare_mx``. A byte permutation plus zero padding."""
+    dev = gu_packed.device
+    _need(gu_packed, "gu_packed", torch.uint8, 4, dev)
+    _need(gu_scales, "gu_scales", torch.uint8, 3, dev)
+    E, F2, G, B = gu_packed.shape
+    if B != 16 or F2 % 64 != 0 or tuple(gu_scales.shape) != (E, F2, G):
+        raise ValueError("gu_packed must be [E, 2F, G, 16] with F a multiple of 32, gu_scales [E, 2F, G]")
+    F = F2 // 2
+    dn = prepare_mx(dn_packed, dn_scales)
+    if dn.E != E or dn.G != F // 32:
+        raise ValueError("dn_packed must be [E, O, F/32, 16]")
+    n = _abi.mx_prepared_size(E, F2, G)
+    gu = torch.empty(n, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_prepare_swiglu(_ptr(gu_packed), _ptr(gu_scales), E, F, G, _ptr(gu), n, _stream(dev))
+    _abi.check(st, "mxfp4_prepare_swiglu")
+    return PreparedSwiGLU(gu, dn, E, F, G, dn.O)
+
+
+def moe_swiglu_prepared(x: torch.Tensor, prepared: PreparedSwiGLU, sel: torch.Tensor, p: torch.Tensor,
+                        shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``moe_swiglu`` on weights repacked by ``prepare_swiglu`` (both GEMMs on
+    the register-decode kernel)."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    _need(shared, "shared", torch.bfloat16, 2, dev)
+    if not isinstance(prepared, PreparedSwiGLU) or prepared.gu.device != dev:
+        raise ValueError("prepared must come from prepare_swiglu on x's device")
+    T, I = x.shape
+    E, F, G, O = prepared.E, prepared.F, prepared.G, prepared.O
+    K = sel.shape[1]
+    if I != 32 * G:
+        raise ValueError(f"x has {I} inputs; the prepared weights have 32 * {G}")
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K) or tuple(shared.shape) != (T, O):
+        raise ValueError("sel and p must be [T, K] and shared [T, O]")
+    y = torch.empty_like(shared) if out is None else out
+    _need(y, "out", torch.bfloat16, 2, dev)
+    if tuple(y.shape) != (T, O):
+        raise ValueError("out must be [T, O]")
+    need = _abi.swiglu_workspace_size(T, E, F, G, O, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_swiglu_prepared_ex(
+            _ptr(x), _ptr(prepared.gu), _ptr(prepared.dn.buf), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, F, G,
+            O, K, flags, _ptr(workspace), workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_swiglu_prepared_ex")
+    return y
 
 
 def mxfp4_expert_linear(latent_tokens: torch.Tensor, packed_weights: torch.Tensor, scale_bytes: torch.Tensor,

@@ -420,6 +420,86 @@ int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8
   return MXFP4_OK;
 }
 
+int mxfp4_prepare_swiglu(const uint8_t* gu_packed, const uint8_t* gu_scales, int64_t E, int64_t F, int64_t G,
+                         void* prepared, size_t bytes, hipStream_t stream) {
+  if (F < 32 || F % 32 != 0 || F > (int64_t(1) << 29)) return MXFP4_ERR_INVALID_ARG;
+  Dims d;
+  int st = check_dims(1, E, 2 * F, G, 1, &d);
+  if (st != MXFP4_OK) return st;
+  if (!gemm_mx_supported(1, 2 * F, G)) return MXFP4_ERR_UNSUPPORTED;
+  const size_t need = mx_prepared_bytes(E, 2 * F, G);
+  if (bytes < need) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!gu_packed || !gu_scales || !prepared || !aligned(gu_packed, 16) || !aligned(prepared, 16))
+    return MXFP4_ERR_INVALID_ARG;
+  if (overlap(prepared, need, gu_packed, (size_t)E * 2 * F * G * 16) ||
+      overlap(prepared, need, gu_scales, (size_t)E * 2 * F * G))
+    return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  return hip_status(launch_prepare_mx(gu_packed, gu_scales, E, (int)(2 * F), (int)G, static_cast<uint8_t*>(prepared),
+                                      stream, (int)F));
+}
+
+int mxfp4_moe_swiglu_prepared_ex(const uint16_t* x, const void* gu_prepared, const void* dn_prepared,
+                                 const int32_t* sel, const float* p, const uint16_t* shared, uint16_t* y, int64_t T,
+                                 int64_t E, int64_t F, int64_t G, int64_t O, int64_t K, uint32_t flags,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  SwDims d;
+  int st = check_swiglu_dims(T, E, F, G, O, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~MXFP4_FLAG_CHECK) return MXFP4_ERR_INVALID_ARG;
+  if (!swiglu_supported(d) || !gemm_mx_supported(d.gu.T, d.gu.O, d.gu.G) ||
+      !gemm_regdec_supported(d.gu.T, d.gu.O, d.gu.G) || !gemm_mx_supported(d.dn.P, d.dn.O, d.dn.G) ||
+      !gemm_regdec_supported(d.dn.P, d.dn.O, d.dn.G))
+    return MXFP4_ERR_UNSUPPORTED;
+  const uint8_t* gp = static_cast<const uint8_t*>(gu_prepared);
+  const uint8_t* dp = static_cast<const uint8_t*>(dn_prepared);
+  const size_t gbytes = mx_prepared_bytes(E, 2 * F, G), dbytes = mx_prepared_bytes(E, O, F / 32);
+  st = check_swiglu_args(x, gp, gp ? gp + gbytes / 17 * 16 : nullptr, dp, dp ? dp + dbytes / 17 * 16 : nullptr, sel,
+                         p, shared, y, d);
+  if (st != MXFP4_OK) return st;
+  if (d.gu.T == 0) return MXFP4_OK;
+  if (overlap(y, (size_t)T * O * 2, gp, gbytes) || overlap(y, (size_t)T * O * 2, dp, dbytes))
+    return MXFP4_ERR_INVALID_ARG;
+  const SwLayout S = swiglu_layout(d);
+  if (workspace_bytes < S.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  const Layout& L = S.L;
+  BucketOut b;
+  b.count = reinterpret_cast<int32_t*>(base + L.count);
+  b.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  b.perm = reinterpret_cast<int32_t*>(base + L.perm);
+  b.slot_of_pair = reinterpret_cast<int32_t*>(base + L.slot);
+  b.n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
+  b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
+  b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + S.h);
+  float* part = reinterpret_cast<float*>(base + L.part);
+  const int64_t max_tiles = gemm_max_tiles(d.gu.P, d.gu.E);
+  hipError_t err = launch_bucket_multi(sel, (int)d.gu.P, (int)d.gu.E, reinterpret_cast<int32_t*>(base + L.bcount), b,
+                                       stream);
+  if (err == hipSuccess)
+    err = launch_gemm_regdec_swiglu(x, gp, gp + gbytes / 17 * 16, b.perm, b.tiles, b.n_tiles, max_tiles, h,
+                                    (int)d.gu.T, (int)d.gu.K, (int)d.F, (int)d.gu.G, stream);
+  if (err == hipSuccess)
+    err = launch_gemm_regdec_direct(h, dp, dp + dbytes / 17 * 16, b.tiles, b.n_tiles, max_tiles, part, d.dn.P,
+                                    (int)d.dn.O, (int)d.dn.G, stream);
+  if (err == hipSuccess)
+    err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.dn.T, (int)d.dn.K, (int)d.dn.O, MXFP4_DTYPE_BF16,
+                         stream);
+  if (err != hipSuccess) return MXFP4_ERR_HIP;
+  if (flags & MXFP4_FLAG_CHECK) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+    int32_t inv = 0;
+    if (hipMemcpy(&inv, b.n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
+    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
+  }
+  return MXFP4_OK;
+}
+
 int mxfp4_quantize_mxfp8(const uint16_t* x, int64_t T, int64_t I, int64_t ld, uint8_t* codes, uint8_t* scale_bytes,
                          hipStream_t stream) {
   if (T < 0 || I < 32 || I % 32 || ld < I || ld % 32 || T * ld >= (int64_t(1) << 31)) return MXFP4_ERR_INVALID_ARG;

@@ -324,10 +324,14 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
 // of the tile, group 4 q + (l >> 4): exactly what lane l of the MFMA's A
 // operand takes) and, in a second array, their 64 scale bytes in the same
 // order. Rows past O and groups past G are zero. One thread per group slot.
+// F > 0 (SwiGLU order): the source stacks gate rows [0, F) over up rows
+// [F, 2F) (O = 2F), and prepared tile n holds gate rows 64 n .. 64 n + 63
+// followed by the up rows of the same features, so that one 128-row tile
+// carries both halves of 64 features; rows of features past F are zero.
 __global__ void __launch_bounds__(256) prepare_mx_kernel(const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ scales, int64_t n_slots, int O,
                                                          int G, int n_ntiles, int nq, uint8_t* __restrict__ pp,
-                                                         uint8_t* __restrict__ ps) {
+                                                         uint8_t* __restrict__ ps, int F) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n_slots) return;
   const int l = (int)(idx & 63), fr = (int)((idx >> 6) & 7);
@@ -336,7 +340,12 @@ __global__ void __launch_bounds__(256) prepare_mx_kernel(const uint8_t* __restri
   const int64_t en = rest / nq;
   const int n = (int)(en % n_ntiles);
   const int64_t e = en / n_ntiles;
-  const int row = 128 * n + 16 * fr + (l & 15), g = 4 * q + (l >> 4);
+  const int k = 16 * fr + (l & 15), g = 4 * q + (l >> 4);
+  int row = 128 * n + k;
+  if (F > 0) {
+    const int f = 64 * n + (k & 63);
+    row = f < F ? (k < 64 ? f : F + f) : O;
+  }
   u32x4 v = u32x4{0u, 0u, 0u, 0u};
   uint8_t sc = 0;
   if (row < O && g < G) {
@@ -358,12 +367,12 @@ size_t mx_prepared_bytes(int64_t E, int64_t O, int64_t G) {
 }
 
 hipError_t launch_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int O, int G, uint8_t* prepared,
-                             hipStream_t stream) {
+                             hipStream_t stream, int swiglu_F) {
   const int n_ntiles = (O + NT - 1) / NT, nq = mx_row_bytes(32 * (int64_t)G) / KC;
   const int64_t slots = E * n_ntiles * nq * 512;
   if (slots == 0) return hipSuccess;
   hipLaunchKernelGGL(prepare_mx_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream, packed, scales,
-                     slots, O, G, n_ntiles, nq, prepared, prepared + slots * 16);
+                     slots, O, G, n_ntiles, nq, prepared, prepared + slots * 16, swiglu_F);
   return hipGetLastError();
 }
 

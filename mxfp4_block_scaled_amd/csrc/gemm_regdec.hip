@@ -13,7 +13,8 @@
 // fragments to a dword per lane).
 //
 // Work: the M-tiles of the bucketing (<= 128 pairs of one expert) x N-tiles
-// of 512 weight rows. Eight waves per workgroup, 2 (pairs) x 4 (rows): wave
+// of 512 weight rows (modes below: the routed linear, and the two stages of
+// the SwiGLU expert block). Eight waves per workgroup, 2 (pairs) x 4 (rows): wave
 // (wm, wn) owns pairs 64 wm .. +63 and the 128 rows of prepared tile
 // 4 nt + wn, 8 x 4 MFMA tiles of 16 x 16. Inputs go in chunks of 128 (4
 // groups). Per chunk the workgroup brings into LDS, by DMA (buffer loads that
@@ -54,6 +55,7 @@ namespace mxfp4 {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOob = 0x80000000u;
@@ -86,14 +88,29 @@ __device__ __forceinline__ uint32_t double_codes(uint32_t w) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// What the rows and columns are:
+//  kGather: activation rows are the tokens of the tile's pairs (perm / K);
+//           output fp32 rows of `part` at the sorted positions.
+//  kSwiGLU: activation rows as kGather; the weights are the stacked gate and
+//           up matrices prepared with prepare_mx_kernel's SwiGLU row order
+//           (prepared tile n: gate rows 64 n .. +63, then the up rows of the
+//           same features), so a wave's fragments 0..3 hold the gate rows and
+//           4..7 the up rows of 64 features; the epilogue writes bf16
+//           h[position, f] = silu(gate) * up (page "MoE Expert Kernels:
+//           Grouped Prefill and Mixed-Quant Compact Experts", section 1).
+//  kDirect: activation rows are the sorted positions themselves (rows of h);
+//           output fp32 rows of `part`.
+enum Mode { kGather = 0, kSwiGLU = 1, kDirect = 2 };
+
+template <int MODE>
 __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __restrict__ x,
                                                              const uint8_t* __restrict__ pcodes,
                                                              const uint8_t* __restrict__ pscales,
                                                              const int32_t* __restrict__ perm,
                                                              const GemmTile* __restrict__ tiles,
                                                              const int32_t* __restrict__ n_tiles,
-                                                             float* __restrict__ part, int K, int O, int G, int n_wg,
-                                                             int n_ptiles, uint32_t x_bytes) {
+                                                             void* __restrict__ out, int K, int O, int G, int F,
+                                                             int n_wg, int n_ptiles, uint32_t x_bytes) {
   // Workgroup i runs on XCD i mod 8: XCD x takes M-tiles x, x + 8, ... with
   // all their N-tiles back to back, so the N-tiles of an M-tile share its
   // gathered activation rows in one L2.
@@ -123,7 +140,8 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   for (int j = 0; j < kXDma; j++) {
     const int m = 16 * w + 4 * j + (lane >> 4);
     const int piece = (lane & 15) ^ (m & 15);
-    const int row = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
+    int row = -1;
+    if (m < tl.mlen) row = MODE == kDirect ? tl.row0 + m : perm[tl.row0 + m] / K;
     x_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)(2 * xld) + 16u * (uint32_t)piece : kOob;
   }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRsrcFlags);
@@ -173,7 +191,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   };
 
   // whether this wave multiplies anything: pairs left in the tile, rows left in O
-  const bool live = 64 * wm < tl.mlen && NW * nt + PT * wn < O;
+  const bool live = 64 * wm < tl.mlen && (MODE == kSwiGLU ? 64 * pt < F : NW * nt + PT * wn < O);
 
   v4f acc[kWI][kWJ];
 #pragma unroll
@@ -265,17 +283,56 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
 
   // lane (lr, lc) of MFMA tile (i, j): pair 64 wm + 16 j + lr, rows 4 lc .. 4 lc + 3 of fragment i
+  if constexpr (MODE == kSwiGLU) {
+    uint16_t* h = static_cast<uint16_t*>(out);
 #pragma unroll
-  for (int j = 0; j < kWJ; j++) {
-    const int p = 64 * wm + 16 * j + lr;
-    if (p >= tl.mlen) continue;
-    float* row = part + (int64_t)(tl.row0 + p) * O;
+    for (int j = 0; j < kWJ; j++) {
+      const int p = 64 * wm + 16 * j + lr;
+      if (p >= tl.mlen) continue;
 #pragma unroll
-    for (int i = 0; i < kWI; i++) {
-      const int r = NW * nt + PT * wn + 16 * i + 4 * lc;  // O % 4 == 0: all four or none
-      if (r < O) *reinterpret_cast<v4f*>(row + r) = acc[i][j];
+      for (int i = 0; i < kWI / 2; i++) {
+        const int f = 64 * pt + 16 * i + 4 * lc;  // F % 4 == 0: all four or none
+        if (f >= F) continue;
+        // silu(g) * u = g / (1 + e^-g) * u, with the hardware reciprocal (1 ulp), rounded to bf16
+        // (round to nearest even by the conversion instruction)
+        bf16x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const float g = acc[i][j][t], u = acc[i + kWI / 2][j][t];
+          v[t] = (__bf16)(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);
+        }
+        *reinterpret_cast<bf16x4*>(h + (int64_t)(tl.row0 + p) * F + f) = v;
+      }
+    }
+  } else {
+    float* part = static_cast<float*>(out);
+#pragma unroll
+    for (int j = 0; j < kWJ; j++) {
+      const int p = 64 * wm + 16 * j + lr;
+      if (p >= tl.mlen) continue;
+      float* row = part + (int64_t)(tl.row0 + p) * O;
+#pragma unroll
+      for (int i = 0; i < kWI; i++) {
+        const int r = NW * nt + PT * wn + 16 * i + 4 * lc;  // O % 4 == 0: all four or none
+        if (r < O) *reinterpret_cast<v4f*>(row + r) = acc[i][j];
+      }
     }
   }
+}
+
+template <int MODE>
+hipError_t launch_mode(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* perm,
+                       const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, void* out, int64_t x_rows,
+                       int K, int O, int G, int F, hipStream_t stream) {
+  // O: rows of the prepared matrix (2F for kSwiGLU)
+  const int n_wg = (O + NW - 1) / NW, n_ptiles = (O + PT - 1) / PT;
+  // 8 XCDs x ceil(max_tiles / 8) M-tiles x the N-tiles
+  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_wg;
+  if (nblk <= 0) return hipSuccess;
+  const uint32_t x_bytes = (uint32_t)(x_rows * 64 * G);
+  hipLaunchKernelGGL(gemm_regdec_kernel<MODE>, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, x, pcodes, pscales,
+                     perm, tiles, n_tiles, out, K, O, G, F, n_wg, n_ptiles, x_bytes);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -291,14 +348,21 @@ hipError_t launch_gemm_regdec(const uint16_t* x, const uint8_t* pcodes, const ui
                               const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T,
                               int K, int O, int G, hipStream_t stream) {
   if (!gemm_regdec_supported(T, O, G)) return hipErrorInvalidValue;
-  const int n_wg = (O + NW - 1) / NW, n_ptiles = (O + PT - 1) / PT;
-  // 8 XCDs x ceil(max_tiles / 8) M-tiles x the N-tiles
-  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_wg;
-  if (nblk <= 0) return hipSuccess;
-  const uint32_t x_bytes = (uint32_t)((int64_t)T * 64 * G);
-  hipLaunchKernelGGL(gemm_regdec_kernel, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, x, pcodes, pscales, perm,
-                     tiles, n_tiles, part, K, O, G, n_wg, n_ptiles, x_bytes);
-  return hipGetLastError();
+  return launch_mode<kGather>(x, pcodes, pscales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0, stream);
+}
+
+hipError_t launch_gemm_regdec_swiglu(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales,
+                                     const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
+                                     int64_t max_tiles, uint16_t* h, int T, int K, int F, int G, hipStream_t stream) {
+  if (F % 4 || !gemm_regdec_supported(T, 2 * (int64_t)F, G)) return hipErrorInvalidValue;
+  return launch_mode<kSwiGLU>(x, pcodes, pscales, perm, tiles, n_tiles, max_tiles, h, T, K, 2 * F, G, F, stream);
+}
+
+hipError_t launch_gemm_regdec_direct(const uint16_t* h, const uint8_t* pcodes, const uint8_t* pscales,
+                                     const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part,
+                                     int64_t P, int O, int G, hipStream_t stream) {
+  if (!gemm_regdec_supported(P, O, G)) return hipErrorInvalidValue;
+  return launch_mode<kDirect>(h, pcodes, pscales, nullptr, tiles, n_tiles, max_tiles, part, P, 1, O, G, 0, stream);
 }
 
 }  // namespace mxfp4

@@ -90,8 +90,10 @@ hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* p
 // the prepared weight layout of the block-scaled variant: 16 bytes of codes and
 // one scale byte per group slot, slots = E * ceil(O / 128) * (Kp / 128) * 512
 size_t mx_prepared_bytes(int64_t E, int64_t O, int64_t G);
+// swiglu_F > 0: the SwiGLU row order (O = 2F stacked gate/up rows; prepared
+// tile n = gate rows 64 n .. +63, then the up rows of the same features).
 hipError_t launch_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int O, int G, uint8_t* prepared,
-                             hipStream_t stream);
+                             hipStream_t stream, int swiglu_F = 0);
 
 // ---- router: logits (T, E) fp32 -> sel (T, K) int32, p (T, K) fp32.
 // mode 0 softmax, 1 sigmoid with a selection-only bias (may be null).
@@ -118,6 +120,15 @@ bool gemm_regdec_supported(int64_t T, int64_t O, int64_t G);
 hipError_t launch_gemm_regdec(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* perm,
                               const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T,
                               int K, int O, int G, hipStream_t stream);
+// SwiGLU block on prepared weights: gate/up stage (weights prepared in the
+// SwiGLU row order, O = 2F; writes bf16 h (P, F)) and down stage (A rows =
+// rows of h; writes fp32 part rows).
+hipError_t launch_gemm_regdec_swiglu(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales,
+                                     const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
+                                     int64_t max_tiles, uint16_t* h, int T, int K, int F, int G, hipStream_t stream);
+hipError_t launch_gemm_regdec_direct(const uint16_t* h, const uint8_t* pcodes, const uint8_t* pscales,
+                                     const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part,
+                                     int64_t P, int O, int G, hipStream_t stream);
 // SwiGLU expert block, gate/up stage: weights (E, 2F, G, 16) with gate rows
 // [0, F) over up rows [F, 2F); writes h[sorted position, f] = bf16 of
 // silu(gate) * up, h being (P, F).

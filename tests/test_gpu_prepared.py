@@ -207,3 +207,83 @@ def test_prepared_rejects_unsupported_and_empty():
     y = mx.moe_linear_prepared(bf16_dev(x[:0]), prep, torch.from_numpy(sel[:0]).to(DEV),
                                torch.from_numpy(p[:0]).to(DEV), bf16_dev(shared[:0]))
     assert tuple(y.shape) == (0, 32)
+
+
+# ------------------------------------------------------------------ SwiGLU block on prepared weights
+
+def swiglu_case(seed, T, E, K, G, F, O, scale_lo=118, scale_hi=126, distinct=True):
+    rng = np.random.default_rng(seed)
+    x = workloads.round_to_bf16(rng.standard_normal((T, 32 * G)).astype(np.float32))
+    shared = workloads.round_to_bf16(rng.standard_normal((T, O)).astype(np.float32))
+    gu_p = rng.integers(0, 256, (E, 2 * F, G, 16), dtype=np.uint8)
+    gu_s = rng.integers(scale_lo, scale_hi + 1, (E, 2 * F, G), dtype=np.uint8)
+    dn_p = rng.integers(0, 256, (E, O, F // 32, 16), dtype=np.uint8)
+    dn_s = rng.integers(scale_lo, scale_hi + 1, (E, O, F // 32), dtype=np.uint8)
+    if distinct:
+        sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    else:
+        sel = rng.integers(0, E, (T, K)).astype(np.int32)
+    p = rng.random((T, K)).astype(np.float32)
+    return x, gu_p, gu_s, dn_p, dn_s, sel, p, shared
+
+
+def run_swiglu_prepared(x, gu_p, gu_s, dn_p, dn_s, sel, p, shared):
+    dv = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    prep = mx.prepare_swiglu(dv(gu_p), dv(gu_s), dv(dn_p), dv(dn_s))
+    y = mx.moe_swiglu_prepared(bf16_dev(x), prep, dv(sel), dv(p), bf16_dev(shared))
+    torch.cuda.synchronize()
+    return y
+
+
+SWIGLU_CASES = [  # T, E, K, G, F, O, distinct
+    (1, 3, 1, 1, 32, 8, True),         # F = 32: half of one prepared gate/up tile
+    (5, 4, 2, 2, 64, 40, True),
+    (33, 6, 3, 3, 96, 132, True),      # F = 1.5 prepared tiles, a 4-row last down tile
+    (70, 16, 4, 5, 160, 72, True),     # several M-tiles, odd G
+    (40, 3, 2, 17, 64, 36, False),     # duplicates within a token
+    (300, 8, 4, 4, 544, 520, True),    # three 512-row gate/up N-tiles (2F = 1088), two down N-tiles
+]
+
+
+@pytest.mark.parametrize("c", SWIGLU_CASES, ids=lambda c: "T{}E{}K{}G{}F{}O{}{}".format(*c[:6], "" if c[6] else "dup"))
+def test_swiglu_prepared_against_oracle(c):
+    T, E, K, G, F, O, distinct = c
+    say(f"swiglu prepared {c}")
+    host = swiglu_case(sum(c[:6]), T, E, K, G, F, O, distinct=distinct)
+    check(run_swiglu_prepared(*host), oracle.expert_swiglu(*host), f"swiglu prepared {c}")
+
+
+def test_swiglu_prepared_matches_canonical_and_ignores_unselected():
+    host = list(swiglu_case(21, 48, 10, 3, 3, 96, 64))
+    x, gu_p, gu_s, dn_p, dn_s, sel, p, shared = host
+    y = run_swiglu_prepared(*host)
+    assert torch.equal(y, run_swiglu_prepared(*host)), "not deterministic"
+    dv = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    y_can = mx.moe_swiglu(bf16_dev(x), dv(gu_p), dv(gu_s), dv(dn_p), dv(dn_s), dv(sel), dv(p), bf16_dev(shared))
+    torch.cuda.synchronize()
+    assert rel_l2(host64(y), host64(y_can)) <= BF16_REL_L2
+    rng = np.random.default_rng(22)
+    gu2, dn2, gs2, ds2 = gu_p.copy(), dn_p.copy(), gu_s.copy(), dn_s.copy()
+    for e in set(range(10)) - set(np.unique(sel).tolist()):
+        gu2[e] = rng.integers(0, 256, gu2[e].shape)
+        dn2[e] = rng.integers(0, 256, dn2[e].shape)
+        gs2[e] = 255
+        ds2[e] = 255
+    assert torch.equal(run_swiglu_prepared(x, gu2, gs2, dn2, ds2, sel, p, shared), y)
+
+
+def test_swiglu_prepared_large_shape_sampled():
+    """The gate/up shape of the SwiGLU workload (I = 7168, 2F = 4096, O = 7168)
+    with 16 experts and 512 tokens (128 pairs per expert, several M-tiles);
+    the oracle checks two tokens on a sample of output rows."""
+    T, E, K, G, F, O = 512, 16, 4, 224, 2048, 7168
+    host = swiglu_case(2027, T, E, K, G, F, O)
+    x, gu_p, gu_s, dn_p, dn_s, sel, p, shared = host
+    y = host64(run_swiglu_prepared(*host))
+    toks = np.array([0, 311])
+    rows = np.sort(np.random.default_rng(3).choice(O, 64, replace=False))
+    ref = oracle.expert_swiglu_rows(x[toks], gu_p, gu_s, dn_p, dn_s, sel[toks], p[toks], shared[toks], rows)
+    r = rel_l2(y[np.ix_(toks, rows)], ref)
+    say(f"  swiglu prepared large: rel L2 {r:.3e}")
+    assert r <= BF16_REL_L2
+    assert np.all(np.isfinite(y))
