@@ -352,7 +352,7 @@ def main():
     ap.add_argument("--variant", choices=["mxfp8"],
                     help="time the block-scaled variant (MXFP8 activations on the scaled MFMA) instead of the layer")
     ap.add_argument("--prepared", action="store_true",
-                    help="weights repacked once (outside the timed region) by prepare_mx: the bf16 GEMM on "
+                    help="weights repacked once (outside the timed region) by prepare_bf16: the bf16 GEMM on "
                          "prepared weights, or with --variant mxfp8 the variant's")
     ap.add_argument("--router", choices=["softmax", "sigmoid"],
                     help="time the router alone at the workload's T, E and K instead of the layer")
@@ -416,7 +416,7 @@ def main():
     prepared = None
     if args.prepared:
         prepared = (mx.prepare_swiglu(packed, scales, dn_packed, dn_scales) if kind == "swiglup"
-                    else mx.prepare_mx(packed, scales))
+                    else mx.prepare_bf16(packed, scales) if kind == "gemmp" else mx.prepare_mx(packed, scales))
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs drawn and resident in {time.perf_counter() - t_gen:.1f} s; "
         f"packed {packed.numel() / 1e9:.2f} GB, workspace {ws.numel() / 1e6:.1f} MB, "

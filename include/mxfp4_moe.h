@@ -303,14 +303,20 @@ int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, 
                                        hipStream_t stream);
 
 /*
- * The bf16 routed linear on prepared weights (the buffer of mxfp4_prepare_mx,
- * a load-time byte permutation of packed and scales; page "MXFP4 Routed
+ * The bf16 routed linear on prepared weights (page "MXFP4 Routed
  * Expert Linear", "Reconstruct the matrix in the right orientation", for the
  * product): the prefill-shaped path - bucketing, a grouped GEMM that brings
  * each 1 KB block of prepared codes into LDS with one request, decodes it in
  * registers and multiplies on bf16 MFMA with fp32 accumulation, and the
  * combine.
- *   mxfp4_moe_linear_prepared_ex: x (T, 32G), shared and y (T, O) bf16 as
+ *   mxfp4_prepare_bf16: the repack of mxfp4_prepare_mx (same slots, scale
+ *     array, size, arguments and errors) with the code blocks of each tile
+ *     and chunk in dword-interleaved order: block 4 h + s holds, at bytes
+ *     16 l + 4 (f mod 4) .. +3, bytes 4 s .. 4 s + 3 of slot l of fragment f
+ *     (f = 4 h .. 4 h + 3), so that one 16-byte read gives a lane one MFMA
+ *     step's codes of four fragments.
+ *   mxfp4_moe_linear_prepared_ex: reads a buffer of mxfp4_prepare_bf16;
+ *     x (T, 32G), shared and y (T, O) bf16 as
  *     mxfp4_moe_linear_ex with MXFP4_DTYPE_BF16; the workspace is
  *     mxfp4_moe_workspace_size(T, E, O, G, K, MXFP4_DTYPE_BF16,
  *     MXFP4_FLAG_FORCE_GEMM, ...) bytes; flags 0 or MXFP4_FLAG_CHECK; errors
@@ -323,6 +329,8 @@ int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, 
  * prepared codes stay below 2^31 bytes. Allocates nothing; may be captured
  * in a graph.
  */
+int mxfp4_prepare_bf16(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, void* prepared,
+                       size_t bytes, hipStream_t stream);
 int mxfp4_moe_linear_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,
                                   const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O, int64_t G,
                                   int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
@@ -336,12 +344,12 @@ int mxfp4_moe_gemm_stage_prepared(const uint16_t* x, const void* prepared, int64
  * repacked once at load time, nothing decoded).
  *   mxfp4_prepare_swiglu: gate/up packed (E, 2F, G, 16) and scales (E, 2F, G)
  *     (gate rows [0, F) over up rows [F, 2F)) -> the prepared layout of
- *     mxfp4_prepare_mx with the rows reordered so that each 128-row tile holds
+ *     mxfp4_prepare_bf16 with the rows reordered so that each 128-row tile holds
  *     the gate rows of 64 features followed by their up rows. Size:
  *     mxfp4_mx_prepared_size(E, 2F, G). Alignment, overlap and errors as
  *     mxfp4_prepare_mx; F a multiple of 32.
  *   mxfp4_moe_swiglu_prepared_ex: mxfp4_moe_swiglu_ex with gu_prepared from
- *     mxfp4_prepare_swiglu and dn_prepared from mxfp4_prepare_mx(dn_packed,
+ *     mxfp4_prepare_swiglu and dn_prepared from mxfp4_prepare_bf16(dn_packed,
  *     dn_scales, E, O, F / 32, ...); the same workspace size, flags, errors
  *     and bar (both GEMMs on the register-decode kernel). Also
  *     MXFP4_ERR_UNSUPPORTED unless O % 4 == 0 and one expert's prepared codes

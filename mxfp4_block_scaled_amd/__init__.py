@@ -29,7 +29,7 @@ __all__ = [
     "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
     "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared", "moe_linear_prepared", "gemm_stage_prepared",
-    "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
+    "prepare_bf16", "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
     "Mxfp4Error", "library_path",
 ]
 
@@ -225,14 +225,15 @@ class PreparedMx:
     and by the bf16 prepared path): a uint8 device buffer and the (E, O, G)
     it was made from."""
 
-    def __init__(self, buf: torch.Tensor, E: int, O: int, G: int):
-        self.buf, self.E, self.O, self.G = buf, E, O, G
+    def __init__(self, buf: torch.Tensor, E: int, O: int, G: int, interleaved: bool = False):
+        self.buf, self.E, self.O, self.G, self.interleaved = buf, E, O, G, interleaved
 
 
-def prepare_mx(packed: torch.Tensor, scales: torch.Tensor) -> PreparedMx:
+def prepare_mx(packed: torch.Tensor, scales: torch.Tensor, *, interleaved: bool = False) -> PreparedMx:
     """Load-time repack of [E, O, G, 16] codes and [E, O, G] scale bytes into
     the fragment-major layout the block-scaled variant streams (a byte
-    permutation plus zero padding)."""
+    permutation plus zero padding); ``interleaved``: the dword-interleaved
+    code order of ``prepare_bf16``."""
     dev = packed.device
     _need(packed, "packed", torch.uint8, 4, dev)
     _need(scales, "scales", torch.uint8, 3, dev)
@@ -242,9 +243,17 @@ def prepare_mx(packed: torch.Tensor, scales: torch.Tensor) -> PreparedMx:
     n = _abi.mx_prepared_size(E, O, G)
     buf = torch.empty(n, dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        st = _abi.lib().mxfp4_prepare_mx(_ptr(packed), _ptr(scales), E, O, G, _ptr(buf), n, _stream(dev))
-    _abi.check(st, "mxfp4_prepare_mx")
-    return PreparedMx(buf, E, O, G)
+        fn = _abi.lib().mxfp4_prepare_bf16 if interleaved else _abi.lib().mxfp4_prepare_mx
+        st = fn(_ptr(packed), _ptr(scales), E, O, G, _ptr(buf), n, _stream(dev))
+    _abi.check(st, "mxfp4_prepare_bf16" if interleaved else "mxfp4_prepare_mx")
+    return PreparedMx(buf, E, O, G, interleaved)
+
+
+def prepare_bf16(packed: torch.Tensor, scales: torch.Tensor) -> PreparedMx:
+    """Load-time repack for the bf16 prepared paths (``moe_linear_prepared``,
+    the SwiGLU block's down projection): ``prepare_mx``'s slots with the code
+    blocks in dword-interleaved order."""
+    return prepare_mx(packed, scales, interleaved=True)
 
 
 def moe_linear_mxfp8_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.Tensor, p: torch.Tensor,
@@ -257,7 +266,7 @@ def moe_linear_mxfp8_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.
     _need(sel, "sel", torch.int32, 2, dev)
     _need(p, "p", torch.float32, 2, dev)
     _need(shared, "shared", torch.bfloat16, 2, dev)
-    if not isinstance(prepared, PreparedMx) or prepared.buf.device != dev:
+    if not isinstance(prepared, PreparedMx) or prepared.buf.device != dev or prepared.interleaved:
         raise ValueError("prepared must come from prepare_mx on x's device")
     T, I = x.shape
     E, O, G = prepared.E, prepared.O, prepared.G
@@ -287,8 +296,8 @@ def _prepared_call_args(x, prepared, sel, p, shared, out):
     _need(sel, "sel", torch.int32, 2, dev)
     _need(p, "p", torch.float32, 2, dev)
     _need(shared, "shared", torch.bfloat16, 2, dev)
-    if not isinstance(prepared, PreparedMx) or prepared.buf.device != dev:
-        raise ValueError("prepared must come from prepare_mx on x's device")
+    if not isinstance(prepared, PreparedMx) or prepared.buf.device != dev or not prepared.interleaved:
+        raise ValueError("prepared must come from prepare_bf16 on x's device")
     T, I = x.shape
     E, O, G = prepared.E, prepared.O, prepared.G
     K = sel.shape[1]
@@ -307,7 +316,7 @@ def moe_linear_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.Tensor
                         shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
                         workspace: torch.Tensor | None = None) -> torch.Tensor:
     """The bf16 routed linear (prefill-shaped path) on weights repacked by
-    ``prepare_mx``: bucketing, the register-decode grouped GEMM, combine."""
+    ``prepare_bf16``: bucketing, the register-decode grouped GEMM, combine."""
     dev, T, E, O, G, K, y = _prepared_call_args(x, prepared, sel, p, shared, out)
     need = workspace_size(T, E, O, G, K, DTYPE_BF16, FLAG_FORCE_GEMM)
     if workspace is None:
@@ -354,7 +363,7 @@ def prepare_swiglu(gu_packed: torch.Tensor, gu_scales: torch.Tensor, dn_packed: 
     if B != 16 or F2 % 64 != 0 or tuple(gu_scales.shape) != (E, F2, G):
         raise ValueError("gu_packed must be [E, 2F, G, 16] with F a multiple of 32, gu_scales [E, 2F, G]")
     F = F2 // 2
-    dn = prepare_mx(dn_packed, dn_scales)
+    dn = prepare_bf16(dn_packed, dn_scales)
     if dn.E != E or dn.G != F // 32:
         raise ValueError("dn_packed must be [E, O, F/32, 16]")
     n = _abi.mx_prepared_size(E, F2, G)

@@ -437,7 +437,7 @@ int mxfp4_prepare_swiglu(const uint8_t* gu_packed, const uint8_t* gu_scales, int
   st = check_device();
   if (st != MXFP4_OK) return st;
   return hip_status(launch_prepare_mx(gu_packed, gu_scales, E, (int)(2 * F), (int)G, static_cast<uint8_t*>(prepared),
-                                      stream, (int)F));
+                                      stream, (int)F, true));
 }
 
 int mxfp4_moe_swiglu_prepared_ex(const uint16_t* x, const void* gu_prepared, const void* dn_prepared,
@@ -541,8 +541,9 @@ int mxfp4_mx_prepared_size(int64_t E, int64_t O, int64_t G, size_t* bytes) {
   return MXFP4_OK;
 }
 
-int mxfp4_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, void* prepared,
-                     size_t bytes, hipStream_t stream) {
+namespace {
+int prepare(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, void* prepared,
+            size_t bytes, hipStream_t stream, bool interleaved) {
   Dims d;
   int st = check_dims(1, E, O, G, 1, &d);
   if (st != MXFP4_OK) return st;
@@ -554,7 +555,19 @@ int mxfp4_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, in
     return MXFP4_ERR_INVALID_ARG;
   st = check_device();
   if (st != MXFP4_OK) return st;
-  return hip_status(launch_prepare_mx(packed, scales, E, (int)O, (int)G, static_cast<uint8_t*>(prepared), stream));
+  return hip_status(launch_prepare_mx(packed, scales, E, (int)O, (int)G, static_cast<uint8_t*>(prepared), stream, 0,
+                                      interleaved));
+}
+}  // namespace
+
+int mxfp4_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, void* prepared,
+                     size_t bytes, hipStream_t stream) {
+  return prepare(packed, scales, E, O, G, prepared, bytes, stream, false);
+}
+
+int mxfp4_prepare_bf16(const uint8_t* packed, const uint8_t* scales, int64_t E, int64_t O, int64_t G, void* prepared,
+                       size_t bytes, hipStream_t stream) {
+  return prepare(packed, scales, E, O, G, prepared, bytes, stream, true);
 }
 
 int mxfp4_moe_linear_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,

@@ -117,9 +117,10 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
 
 // ---- grouped GEMM
 
-// PREP: the weights come in the prepared layout of prepare_mx_kernel (one
-// contiguous 1 KB block per 16-row fragment and chunk, and a 64-byte block of
-// its scales) instead of the canonical [E, O, G, 16] / [E, O, G].
+// PREP: the weights come in the fragment-major prepared layout of
+// prepare_mx_kernel (one contiguous 1 KB block per 16-row fragment and chunk,
+// and one scale dword per lane for four fragments) instead of the canonical
+// [E, O, G, 16] / [E, O, G].
 template <bool PREP>
 __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                          const uint8_t* __restrict__ packed,
@@ -319,11 +320,16 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   }
 }
 
-// Prepared layout, per expert e, N-tile n (128 rows), chunk q (4 groups) and
-// 16-row fragment f: 64 group slots of 16 bytes (slot l = row 16 f + (l & 15)
-// of the tile, group 4 q + (l >> 4): exactly what lane l of the MFMA's A
-// operand takes) and, in a second array, their 64 scale bytes in the same
-// order. Rows past O and groups past G are zero. One thread per group slot.
+// Prepared layout, per expert e, N-tile n (128 rows) and chunk q (4 groups):
+// group slot (f, l) = row 16 f + (l & 15) of the tile, group 4 q + (l >> 4)
+// (exactly what lane l of the MFMA's A operand for 16-row fragment f takes).
+// The codes form 8 blocks of 1 KB: fragment-major (block f = the 16-byte
+// slots of fragment f in lane order; the block-scaled variant loads one slot
+// per lane) or, with `interleaved`, dword-interleaved (block 4 h + s holds at
+// bytes 16 l + 4 (f & 3) dword s of slot (f, l) for the fragments f of half h;
+// one 16-byte read then gives a lane one bf16 MFMA step's codes of four
+// fragments). In a second array, the slots' scale bytes (four fragments to a
+// lane's dword). Rows past O and groups past G are zero. One thread per slot.
 // F > 0 (SwiGLU order): the source stacks gate rows [0, F) over up rows
 // [F, 2F) (O = 2F), and prepared tile n holds gate rows 64 n .. 64 n + 63
 // followed by the up rows of the same features, so that one 128-row tile
@@ -331,7 +337,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
 __global__ void __launch_bounds__(256) prepare_mx_kernel(const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ scales, int64_t n_slots, int O,
                                                          int G, int n_ntiles, int nq, uint8_t* __restrict__ pp,
-                                                         uint8_t* __restrict__ ps, int F) {
+                                                         uint8_t* __restrict__ ps, int F, bool interleaved) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n_slots) return;
   const int l = (int)(idx & 63), fr = (int)((idx >> 6) & 7);
@@ -353,7 +359,14 @@ __global__ void __launch_bounds__(256) prepare_mx_kernel(const uint8_t* __restri
     v = *reinterpret_cast<const u32x4*>(packed + src * 16);
     sc = scales[src];
   }
-  *reinterpret_cast<u32x4*>(pp + idx * 16) = v;
+  if (interleaved) {
+    // dword s of slot (fr, l) goes to block 4 (fr >> 2) + s of the (tile, chunk), lane l, position fr & 3
+#pragma unroll
+    for (int sd = 0; sd < 4; sd++)
+      *reinterpret_cast<uint32_t*>(pp + ((((rest * 2 + (fr >> 2)) * 4 + sd) * 64 + l) * 16 + 4 * (fr & 3))) = v[sd];
+  } else {
+    *reinterpret_cast<u32x4*>(pp + idx * 16) = v;
+  }
   // scales: per (tile, chunk, half of the 8 fragments) 64 lanes x 4 bytes,
   // byte 4 l + (fr & 3): one dword per lane holds its four fragments' scales
   ps[((rest * 2 + (fr >> 2)) * 64 + l) * 4 + (fr & 3)] = sc;
@@ -367,12 +380,12 @@ size_t mx_prepared_bytes(int64_t E, int64_t O, int64_t G) {
 }
 
 hipError_t launch_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int O, int G, uint8_t* prepared,
-                             hipStream_t stream, int swiglu_F) {
+                             hipStream_t stream, int swiglu_F, bool interleaved) {
   const int n_ntiles = (O + NT - 1) / NT, nq = mx_row_bytes(32 * (int64_t)G) / KC;
   const int64_t slots = E * n_ntiles * nq * 512;
   if (slots == 0) return hipSuccess;
   hipLaunchKernelGGL(prepare_mx_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream, packed, scales,
-                     slots, O, G, n_ntiles, nq, prepared, prepared + slots * 16, swiglu_F);
+                     slots, O, G, n_ntiles, nq, prepared, prepared + slots * 16, swiglu_F, interleaved);
   return hipGetLastError();
 }
 

@@ -7,10 +7,11 @@
 // 2^(s-127)).
 //
 // The weights come in the prepared layout of prepare_mx_kernel (a load-time
-// byte permutation: per expert, 128-row tile, chunk of 4 groups and 16-row
-// fragment, the 64 group slots in MFMA lane order - slot l = row l & 15,
-// group 4q + (l >> 4) - 1 KB contiguous; and the slots' scale bytes, four
-// fragments to a dword per lane).
+// byte permutation: per expert, 128-row tile and chunk of 4 groups, the group
+// slots of the 8 16-row fragments in MFMA lane order - slot l of fragment f =
+// row 16 f + (l & 15), group 4q + (l >> 4) - as 8 blocks of 1 KB, block
+// 4 h + s holding for lane l dword s of fragments 4 h .. 4 h + 3; and the
+// slots' scale bytes, four fragments to a dword per lane).
 //
 // Work: the M-tiles of the bucketing (<= 128 pairs of one expert) x N-tiles
 // of 512 weight rows (modes below: the routed linear, and the two stages of
@@ -26,8 +27,9 @@
 // per 512 weight rows. The scale dwords go straight to registers (two per
 // wave and chunk, a three-slot ring).
 //
-// Operand A = weights: for MFMA k-step s (0..3) lane (r, c) reads dword s of
-// its slot of each fragment from LDS and turns those 8 codes into
+// Operand A = weights: for MFMA k-step s (0..3) lane (r, c) reads, with two
+// conflict-free 16-byte LDS reads, dword s of its slot of all 8 fragments and
+// turns each dword's 8 codes into
 // 8 bf16 with gfx950's scaled FP4 convert, scale applied (exact: E2M1 times
 // a power of two is a bf16 value, or +-inf where it overflows). No decoded
 // weight is stored anywhere. Operand B = activations: lane (p, c) of k-step s
@@ -146,9 +148,9 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRsrcFlags);
 
-  // ---- weight DMA: request j of wave w fetches fragment block 4 w + j of the
-  // workgroup (prepared tile 4 nt + (w >> 1), fragment 4 (w & 1) + j) into the
-  // same 1 KB of a slot
+  // ---- weight DMA: request j of wave w fetches code block 4 w + j of the
+  // workgroup (prepared tile 4 nt + (w >> 1), block 4 (w & 1) + j: dword j of
+  // fragments 4 (w & 1) .. +3) into the same 1 KB of a slot
   const int64_t ebase = (int64_t)tl.e * n_ptiles * nq * 512;  // group slots before expert e
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc((void*)(pcodes + ebase * 16), (short)0, n_ptiles * nq * 8192, kRsrcFlags);
@@ -236,10 +238,10 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
           b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                 &xc[(64 * wm + 16 * j + lr) * ROWB + 16 * ((4 * lc + s) ^ lr)]));
         }
-        uint32_t raw[kWI];  // dword s of this lane's slot of each fragment: 8 codes
-#pragma unroll
-        for (int i = 0; i < kWI; i++)
-          raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(wn * kWI + i) * 1024 + 16 * lane + 4 * s]);
+        // dword s of this lane's slot of each fragment (8 codes each): blocks s and 4 + s of tile wn
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + s) * 1024 + 16 * lane]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + 4 + s) * 1024 + 16 * lane]);
+        uint32_t raw[kWI] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if (__builtin_expect(slow, 0)) {
 #pragma unroll
           for (int i = 0; i < kWI; i++)

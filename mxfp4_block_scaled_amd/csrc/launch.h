@@ -92,8 +92,10 @@ hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* p
 size_t mx_prepared_bytes(int64_t E, int64_t O, int64_t G);
 // swiglu_F > 0: the SwiGLU row order (O = 2F stacked gate/up rows; prepared
 // tile n = gate rows 64 n .. +63, then the up rows of the same features).
+// interleaved: the dword-interleaved code blocks the bf16 register-decode
+// GEMM reads (else fragment-major, for the block-scaled variant).
 hipError_t launch_prepare_mx(const uint8_t* packed, const uint8_t* scales, int64_t E, int O, int G, uint8_t* prepared,
-                             hipStream_t stream, int swiglu_F = 0);
+                             hipStream_t stream, int swiglu_F = 0, bool interleaved = false);
 
 // ---- router: logits (T, E) fp32 -> sel (T, K) int32, p (T, K) fp32.
 // mode 0 softmax, 1 sigmoid with a selection-only bias (may be null).

@@ -113,7 +113,7 @@ def test_graph_block_scaled_variant(prepared):
 def test_graph_prepared_bf16():
     say("graph: moe_linear_prepared")
     x, packed, scales, sel, p, shared = _case(4, 300, 8, 4, 9, 1040)
-    prep = mx.prepare_mx(packed, scales)
+    prep = mx.prepare_bf16(packed, scales)
     ws = torch.empty(mx.workspace_size(300, 8, 1040, 9, 4, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM), dtype=torch.uint8,
                      device=DEV)
     out = torch.empty_like(shared)

@@ -61,7 +61,7 @@ def case(seed, T, E, K, G, O, scale_lo=118, scale_hi=130, distinct=True, empty_e
 
 
 def run_case(x, packed, scales, sel, p, shared, out=None):
-    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    prep = mx.prepare_bf16(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
     y = mx.moe_linear_prepared(bf16_dev(x), prep, torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV),
                                bf16_dev(shared), out=out)
     torch.cuda.synchronize()
@@ -107,7 +107,7 @@ def test_prepared_edges():
     check(run_case(*args), oracle.expert_linear(*args), "one hot expert")
     # in place: out = shared
     x, packed, scales, sel, p, shared = case(11, 12, 4, 2, 2, 48)
-    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    prep = mx.prepare_bf16(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
     sh = bf16_dev(shared)
     y = mx.moe_linear_prepared(bf16_dev(x), prep, torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV), sh,
                                out=sh)
@@ -160,7 +160,7 @@ def test_prepared_scale_255_overflows_like_the_canonical_path():
 def test_prepared_deterministic_and_gemm_stage():
     args = case(15, 64, 8, 4, 8, 96)
     x, packed, scales, sel, p, shared = args
-    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    prep = mx.prepare_bf16(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
     xd, seld, pd, shd = bf16_dev(x), torch.from_numpy(sel).to(DEV), torch.from_numpy(p).to(DEV), bf16_dev(shared)
     ws = torch.empty(mx.workspace_size(64, 8, 96, 8, 4, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM), dtype=torch.uint8,
                      device=DEV)
@@ -186,7 +186,7 @@ def test_prepared_full_workloads_sampled_rows(name, nrows):
     for e in range(w.E):  # the expert tensors are drawn expert by expert
         pk[e].copy_(torch.from_numpy(np.ascontiguousarray(inp.packed[e])))
         sc[e].copy_(torch.from_numpy(np.ascontiguousarray(inp.scales[e])))
-    prep = mx.prepare_mx(pk, sc)
+    prep = mx.prepare_bf16(pk, sc)
     del pk, sc
     y = mx.moe_linear_prepared(bf16_dev(inp.x), prep, torch.from_numpy(inp.sel).to(DEV),
                                torch.from_numpy(inp.p).to(DEV), bf16_dev(inp.shared))
@@ -201,9 +201,9 @@ def test_prepared_full_workloads_sampled_rows(name, nrows):
 def test_prepared_rejects_unsupported_and_empty():
     x, packed, scales, sel, p, shared = case(16, 3, 2, 1, 2, 34)  # O % 4 != 0: no prepared layout
     with pytest.raises(mx.Mxfp4Error):
-        mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+        mx.prepare_bf16(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
     x, packed, scales, sel, p, shared = case(17, 3, 2, 1, 2, 32)
-    prep = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    prep = mx.prepare_bf16(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
     y = mx.moe_linear_prepared(bf16_dev(x[:0]), prep, torch.from_numpy(sel[:0]).to(DEV),
                                torch.from_numpy(p[:0]).to(DEV), bf16_dev(shared[:0]))
     assert tuple(y.shape) == (0, 32)
@@ -287,3 +287,43 @@ def test_swiglu_prepared_large_shape_sampled():
     say(f"  swiglu prepared large: rel L2 {r:.3e}")
     assert r <= BF16_REL_L2
     assert np.all(np.isfinite(y))
+
+
+def _interleaved_layout_numpy(packed, scales):
+    """prepare_bf16's documented layout, built with numpy: slot (e, n, q, f, l)
+    holds group 4q + l // 16 of row 128n + 16f + l % 16 (zeros past O / G);
+    its dword s sits at byte ((((e, n, q) * 2 + f // 4) * 4 + s) * 64 + l) * 16
+    + 4 (f % 4) of the codes, its scale byte at (((e, n, q) * 2 + f // 4) * 64
+    + l) * 4 + f % 4 of the scale array that follows."""
+    E, O, G, _ = packed.shape
+    NT, NQ = -(-O // 128), -(-(32 * G) // 128)
+    e, n, q, f, l = np.meshgrid(np.arange(E), np.arange(NT), np.arange(NQ), np.arange(8), np.arange(64), indexing="ij")
+    row = 128 * n + 16 * f + l % 16
+    g = 4 * q + l // 16
+    ok = (row < O) & (g < G)
+    codes = np.zeros(e.shape + (16,), np.uint8)
+    sc = np.zeros(e.shape, np.uint8)
+    codes[ok] = packed[e[ok], row[ok], g[ok]]
+    sc[ok] = scales[e[ok], row[ok], g[ok]]
+    # (e, n, q, half, f % 4, l, s, byte) -> (e, n, q, half, s, l, f % 4, byte)
+    codes = codes.reshape(E, NT, NQ, 2, 4, 64, 4, 4).transpose(0, 1, 2, 3, 6, 5, 4, 7)
+    sc = sc.reshape(E, NT, NQ, 2, 4, 64).transpose(0, 1, 2, 3, 5, 4)
+    return np.concatenate([codes.reshape(-1), sc.reshape(-1)])
+
+
+@pytest.mark.parametrize("E,O,G", [(2, 40, 1), (3, 132, 9), (2, 256, 6)])
+def test_prepare_bf16_layout_bytes(E, O, G):
+    rng = np.random.default_rng(E * O + G + 1)
+    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
+    scales = rng.integers(0, 255, (E, O, G), dtype=np.uint8)
+    prep = mx.prepare_bf16(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(prep.buf.cpu().numpy(), _interleaved_layout_numpy(packed, scales))
+    # the two orders are different permutations of the same slots
+    other = mx.prepare_mx(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    torch.cuda.synchronize()
+    a, b = prep.buf.cpu().numpy(), other.buf.cpu().numpy()
+    assert np.array_equal(np.sort(a), np.sort(b)) and (G * O < 16 or not np.array_equal(a, b))
+    with pytest.raises(ValueError):  # the fragment-major order is refused by the bf16 path
+        mx.moe_linear_prepared(bf16_dev(np.zeros((1, 32 * G))), other, torch.zeros((1, 1), dtype=torch.int32, device=DEV),
+                               torch.ones((1, 1), dtype=torch.float32, device=DEV), bf16_dev(np.zeros((1, O))))
