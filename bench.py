@@ -158,9 +158,7 @@ def _kind(w, variant=None, prepared=False) -> str:
     if w.F:
         return "swiglup" if prepared else "swiglu"
     if w.name in DECODE_WORKLOADS:
-        if prepared:
-            raise SystemExit("--prepared runs the prefill-shaped workloads only")
-        return "gemv"
+        return "gemvp" if prepared else "gemv"
     return "gemmp" if prepared else "gemm"
 
 
@@ -192,7 +190,7 @@ def cpu_baseline(inp, kind, sample_seconds):
         return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                 "sample": f"{calls} tokens (all {w.K} pairs each) x {rows_per_call} output rows of the {w.name} "
                           "workload", "seconds": round(dt, 2)}
-    if kind == "gemv":
+    if kind in ("gemv", "gemvp"):
         done_bytes, calls, t0 = 0.0, 0, time.perf_counter()
         while True:
             sel, p = inp.routing_sets[calls % len(inp.routing_sets)]
@@ -226,6 +224,8 @@ def cpu_baseline(inp, kind, sample_seconds):
 def _path_name(mx, w, kind) -> str:
     if kind == "mx":
         return "MXFP8 variant (bucketing, quantisation, scaled-MFMA grouped GEMM, combine)"
+    if kind == "gemvp":
+        return "decode-shaped MFMA kernel on prepared weights (routing, dequant-GEMV, combine in one launch)"
     if kind == "gemmp":
         return "GEMM on prepared weights (bucketing, register-decode grouped GEMM, combine)"
     if kind == "swiglu":
@@ -410,6 +410,8 @@ def main():
         ws_bytes = mx.mxfp8_workspace_size(w.T, w.E, w.O, w.G, w.K)
     elif kind == "gemmp":
         ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM)
+    elif kind == "gemvp":
+        ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1, mx.FLAG_FORCE_GEMV)
     else:
         ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -434,6 +436,8 @@ def main():
             mx.moe_linear_mxfp8(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "gemmp":
             mx.moe_linear_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
+        elif kind == "gemvp":
+            mx.moe_decode_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         else:
             mx.moe_linear(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
 
@@ -541,13 +545,13 @@ def main():
         roof["kernel"] = ("gemm_regdec_kernel<1> + gemm_regdec_kernel<2> (whole call)" if kind == "swiglup"
                           else "gemm_bf16_kernel<1> + gemm_bf16_kernel<2> (whole call)")
         roof["launch_ms"] = round(ms_step, 6)
-    elif kind == "gemv":
+    elif kind in ("gemv", "gemvp"):
         # one launch per step: the fused kernel is the whole call
         value = bytes_per_step / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
         roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4)}
-        roof["kernel"] = "gemv_rows_kernel"
+        roof["kernel"] = "decode_fused_kernel<prepared>" if kind == "gemvp" else "gemv_rows_kernel"
         roof["launch_ms"] = round(ms_step, 6)
     else:
         value = flops_per_step / (ms_step * 1e-3) / 1e12
@@ -557,8 +561,8 @@ def main():
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
         roof["kernel"] = KERNEL_NAMES[kind]
         roof["launch_ms"] = round(gemm_ms, 6)
-    roof["per_launch"] = ({"bytes": bytes_per_step} if kind == "gemv" else {"flops": flops_per_step})
-    if kind in ("swiglu", "swiglup", "mx"):
+    roof["per_launch"] = ({"bytes": bytes_per_step} if kind in ("gemv", "gemvp") else {"flops": flops_per_step})
+    if kind in ("swiglu", "swiglup", "mx", "gemvp"):
         roof["traffic"] = None
     else:
         roof["traffic"] = committed_traffic(w.name + ("-prepared" if kind == "gemmp" else ""), kind)

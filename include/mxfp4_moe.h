@@ -303,6 +303,24 @@ int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, 
                                        hipStream_t stream);
 
 /*
+ * The decode-shaped path (routing, dequant-GEMV and combine in one launch per
+ * token chunk; page "MXFP4 Routed Expert Linear", "Route, weight, and add the
+ * shared path") on weights repacked by mxfp4_prepare_mx: the MFMA decode
+ * kernel, each workgroup's 16 rows being one prepared fragment whose 1 KB
+ * blocks are loaded straight into the MFMA operand.
+ *   mxfp4_moe_decode_prepared_ex: arguments, dtypes (MXFP4_DTYPE_F32 or
+ *     MXFP4_DTYPE_BF16), results, bars and errors as mxfp4_moe_linear_ex with
+ *     MXFP4_FLAG_FORCE_GEMV | MXFP4_FLAG_GEMV_MFMA, with `prepared` in place
+ *     of packed and scales; the workspace is mxfp4_moe_workspace_size(T, E,
+ *     O, G, K, dtype, MXFP4_FLAG_FORCE_GEMV, ...) bytes; flags 0 or
+ *     MXFP4_FLAG_CHECK. Allocates nothing; may be captured in a graph.
+ */
+int mxfp4_moe_decode_prepared_ex(const void* x, const void* prepared, const int32_t* sel, const float* p,
+                                 const void* shared, void* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,
+                                 int dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
  * The bf16 routed linear on prepared weights (page "MXFP4 Routed
  * Expert Linear", "Reconstruct the matrix in the right orientation", for the
  * product): the prefill-shaped path - bucketing, a grouped GEMM that brings

@@ -29,7 +29,7 @@ __all__ = [
     "mxfp4_expert_linear", "moe_linear", "moe_swiglu", "decode_rows", "bucket", "gemm_stage", "workspace_size",
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
     "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared", "moe_linear_prepared", "gemm_stage_prepared",
-    "prepare_bf16", "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
+    "prepare_bf16", "moe_decode_prepared", "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
     "Mxfp4Error", "library_path",
 ]
 
@@ -405,6 +405,45 @@ def moe_swiglu_prepared(x: torch.Tensor, prepared: PreparedSwiGLU, sel: torch.Te
             _ptr(x), _ptr(prepared.gu), _ptr(prepared.dn.buf), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, F, G,
             O, K, flags, _ptr(workspace), workspace.numel(), _stream(dev))
     _abi.check(st, "mxfp4_moe_swiglu_prepared_ex")
+    return y
+
+
+def moe_decode_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.Tensor, p: torch.Tensor,
+                        shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The decode-shaped path (fp32 or bf16 x) on weights repacked by
+    ``prepare_mx``: routing, the MFMA dequant-GEMV and the combine in one
+    launch per token chunk."""
+    dev = x.device
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be float32 or bfloat16")
+    td = x.dtype
+    _need(x, "x", td, 2, dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    _need(shared, "shared", td, 2, dev)
+    if not isinstance(prepared, PreparedMx) or prepared.buf.device != dev or prepared.interleaved:
+        raise ValueError("prepared must come from prepare_mx on x's device")
+    T, I = x.shape
+    E, O, G = prepared.E, prepared.O, prepared.G
+    K = sel.shape[1]
+    if I != 32 * G:
+        raise ValueError(f"x has {I} inputs; the prepared weights have 32 * {G}")
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K) or tuple(shared.shape) != (T, O):
+        raise ValueError("sel and p must be [T, K] and shared [T, O]")
+    y = torch.empty_like(shared) if out is None else out
+    _need(y, "out", td, 2, dev)
+    if tuple(y.shape) != (T, O):
+        raise ValueError("out must be [T, O]")
+    dt = _DTYPES[td]
+    need = workspace_size(T, E, O, G, K, dt, FLAG_FORCE_GEMV)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_decode_prepared_ex(
+            _ptr(x), _ptr(prepared.buf), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, O, G, K, dt, flags,
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    _abi.check(st, "mxfp4_moe_decode_prepared_ex")
     return y
 
 

@@ -69,6 +69,7 @@ SIGNATURES = {
     "mxfp4_moe_linear_mxfp8_prepared_ex": (_int, [_vp] * 6 + [_i64] * 5 + [_u32, _vp, _sz, _vp]),
     "mxfp4_moe_linear_prepared_ex": (_int, [_vp] * 6 + [_i64] * 5 + [_u32, _vp, _sz, _vp]),
     "mxfp4_moe_gemm_stage_prepared": (_int, [_vp] * 2 + [_i64] * 5 + [_vp, _sz, _vp]),
+    "mxfp4_moe_decode_prepared_ex": (_int, [_vp] * 6 + [_i64] * 5 + [_int, _u32, _vp, _sz, _vp]),
     "mxfp4_prepare_bf16": (_int, [_vp] * 2 + [_i64] * 3 + [_vp, _sz, _vp]),
     "mxfp4_prepare_swiglu": (_int, [_vp] * 2 + [_i64] * 3 + [_vp, _sz, _vp]),
     "mxfp4_moe_swiglu_prepared_ex": (_int, [_vp] * 7 + [_i64] * 6 + [_u32, _vp, _sz, _vp]),

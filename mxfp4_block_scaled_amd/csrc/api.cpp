@@ -640,6 +640,50 @@ int mxfp4_moe_gemm_stage_prepared(const uint16_t* x, const void* prepared, int64
                                        stream));
 }
 
+int mxfp4_moe_decode_prepared_ex(const void* x, const void* prepared, const int32_t* sel, const float* p,
+                                 const void* shared, void* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,
+                                 int dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  Dims d;
+  int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (flags & ~MXFP4_FLAG_CHECK) return MXFP4_ERR_INVALID_ARG;
+  if (dtype_size(dtype) == 0) return MXFP4_ERR_INVALID_ARG;
+  if (!gemm_mx_supported(1, O, G) || !gemv_rows_supported((int)O, (int)G)) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t tc = decode_tokens_per_launch((int)K, (int)E, (int)G, dtype);
+  if (tc < 1) return MXFP4_ERR_UNSUPPORTED;
+  const uint8_t* pp = static_cast<const uint8_t*>(prepared);
+  const size_t pbytes = mx_prepared_bytes(E, O, G);
+  const uint8_t* ps = pp ? pp + pbytes / 17 * 16 : nullptr;
+  st = check_linear_args(x, pp, ps, sel, p, shared, y, d, dtype);
+  if (st != MXFP4_OK) return st;
+  if (d.T == 0) return MXFP4_OK;
+  const int es = dtype_size(dtype);
+  if (overlap(y, (size_t)T * O * es, pp, pbytes)) return MXFP4_ERR_INVALID_ARG;
+  const Layout L = layout(d, MXFP4_PATH_GEMV);
+  if (workspace_bytes < L.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != MXFP4_OK) return st;
+  int32_t* n_invalid = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.n_invalid);
+  hipError_t err = hipSuccess;
+  int chunk = 0;
+  for (int64_t t0 = 0; t0 < d.T && err == hipSuccess; t0 += tc, chunk++) {
+    const int64_t tn = (d.T - t0 < tc) ? d.T - t0 : tc;
+    err = launch_decode_prepared(static_cast<const char*>(x) + t0 * d.I * es, pp, ps, sel + t0 * d.K, p + t0 * d.K,
+                                 static_cast<const char*>(shared) + t0 * d.O * es, static_cast<char*>(y) + t0 * d.O * es,
+                                 (int)tn, (int)d.E, (int)d.O, (int)d.G, (int)d.K, dtype, n_invalid, chunk, stream);
+  }
+  if (err != hipSuccess) return MXFP4_ERR_HIP;
+  if (flags & MXFP4_FLAG_CHECK) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+    int32_t inv = 0;
+    if (hipMemcpy(&inv, n_invalid, 4, hipMemcpyDeviceToHost) != hipSuccess) return MXFP4_ERR_HIP;
+    if (inv != 0) return MXFP4_ERR_INVALID_INDEX;
+  }
+  return MXFP4_OK;
+}
+
 int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel, const float* p,
                                        const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
                                        int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,

@@ -26,6 +26,14 @@
 // holds group 4i+q of row r and feeds its dword j to MFMA j; the B operand
 // uses the same permutation of k, so each MFMA sums matching products.
 //
+// Prepared weights (PREP, the fragment-major layout of prepare_mx_kernel):
+// a workgroup's 16 rows are one fragment, and each 1 KB block (one chunk of 4
+// groups) is exactly the MFMA operand, lane (r, q) holding group 4i + q of
+// row r: an iteration is two 16-byte loads per lane straight into the
+// operand registers plus one scale byte each, no transpose. Workgroups are
+// ordered so that the four fragments that share a lane's scale dword run on
+// the same XCD (one L2).
+//
 // Memory: an iteration covers 8 groups of the 16 rows. Lane (lr, lg) loads
 // group lg of rows lr and 8 + lr (8 whole 128-byte row segments per load)
 // and the matching scale bytes; a per-wave LDS buffer with padded rows
@@ -48,6 +56,7 @@ constexpr int kRows = 16;  // output rows per workgroup (one MFMA tile)
 constexpr int kTrRow = 8 * 16 + 16;           // bytes per row of a wave's transpose buffer (padded)
 constexpr int kTrBytes = kRows * kTrRow + kRows * 8;  // weights then scale bytes
 constexpr uint32_t kOobGroup = 0x08000000u;   // group offset beyond any expert's resource
+constexpr uint32_t kOob32 = 0x80000000u;      // byte offset beyond any resource
 constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
 
 // fp32 -> three bf16 (bit patterns) with f = x0 + x1 + x2 exactly: each
@@ -63,7 +72,7 @@ __device__ __forceinline__ void split3(float f, uint32_t& b0, uint32_t& b1, uint
   b2 = __float_as_uint(r2) >> 16;
 }
 
-template <bool XF32>
+template <bool XF32, bool PREP>
 __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const int32_t* __restrict__ sel, const float* __restrict__ p, const void* shared, void* y, int T, int E, int O,
@@ -75,7 +84,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, kept in a scalar register
   const int r = lane & 15, q = lane >> 4;
   const int P = T * K, I = 32 * G, IL = I + 40;  // IL: a zero group 32G..32G+31, then 8 of padding
-  const int o0 = blockIdx.x * kRows;
+  // PREP: row blocks 32 c + 4 x .. 32 c + 4 x + 3 (x = XCD) for block indices 32 c + x + 8 k, k < 4
+  int rb = blockIdx.x;
+  if (PREP && (rb | 31) < (int)gridDim.x) rb = (rb & ~31) + ((rb & 7) << 2) + ((rb >> 3) & 3);
+  const int o0 = rb * kRows;
   uint16_t* xs = reinterpret_cast<uint16_t*>(dyn);  // [T][NP][IL] bf16
   const size_t xs_bytes = ((size_t)T * NP * IL * 2 + 15) & ~(size_t)15;
   float* part = reinterpret_cast<float*>(dyn + xs_bytes);  // [S][P*NP][16]
@@ -159,7 +171,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
   // the resource and read zeros without memory traffic, so every slot issues
   // the same loads and the waits pipeline.
   const int lr = lane >> 3, lg = lane & 7;
-  const int nrec_w = O * G * 16, nrec_s = O * G;
+  // prepared layout: tile n = o0 / 128, fragment f of the tile, nq chunks of 4 groups
+  const int nq = (G + 3) / 4, n_pt = (O + 127) / 128, pf = (o0 >> 4) & 7, pn = o0 >> 7;
+  const int nrec_w = PREP ? n_pt * nq * 8192 : O * G * 16, nrec_s = PREP ? n_pt * nq * 512 : O * G;
   int l_j = 0, l_it = 0, l_nit = 1;
   bool l_done = n_mine == 0;
   const uint8_t* l_wb = packed;
@@ -170,10 +184,16 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     l_nit = it.nit;
     l_wb = packed + (int64_t)it.e * nrec_w;
     l_sb = scales + (int64_t)it.e * nrec_s;
+    if constexpr (PREP) {
+      // slot of chunk gbeg / 4 (+ 2 per iteration, + 1 for the second load)
+      l_off[0] = (uint32_t)(((pn * nq + it.gbeg / 4) * 8 + pf) * 64 + lane);
+      l_off[1] = l_off[0] + 512u;
+    } else {
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-      const int o = o0 + 8 * t + lr;
-      l_off[t] = o < O ? (uint32_t)(o * G + it.gbeg + lg) : kOobGroup;
+      for (int t = 0; t < 2; t++) {
+        const int o = o0 + 8 * t + lr;
+        l_off[t] = o < O ? (uint32_t)(o * G + it.gbeg + lg) : kOobGroup;
+      }
     }
   };
   if (!l_done) l_refresh();
@@ -184,12 +204,25 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)l_sb, (short)0, nrec_s, kRsrcFlags);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      // a lane past its split reads the following group (the next row at the
-      // end of a row; beyond the resource at the end of the expert); it
-      // meets the zero activation group, so it adds nothing
-      const uint32_t gi = l_done ? kOobGroup : l_off[t] + (uint32_t)(8 * l_it);
-      rw[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, 0));
-      rs[s][t] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)gi, 0, 0);
+      if constexpr (PREP) {
+        // chunk gbeg / 4 + 2 it + t; one past the expert's last chunk reads the
+        // next tile's codes (or beyond the resource: zeros) and meets the zero
+        // activation group; the scale byte: dword of fragments 4 (f / 4) ..,
+        // byte f % 4
+        const uint32_t si = l_off[t] + 1024u * (uint32_t)l_it;  // slot index
+        const uint32_t ck = si >> 9;                             // (tile, chunk) of the slot
+        const uint32_t so = ((ck * 2u + (uint32_t)(pf >> 2)) * 64u + (uint32_t)lane) * 4u + (uint32_t)(pf & 3);
+        rw[s][t] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(l_done ? kOob32 : si * 16u), 0, 0));
+        rs[s][t] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)(l_done ? kOob32 : so), 0, 0);
+      } else {
+        // a lane past its split reads the following group (the next row at the
+        // end of a row; beyond the resource at the end of the expert); it
+        // meets the zero activation group, so it adds nothing
+        const uint32_t gi = l_done ? kOobGroup : l_off[t] + (uint32_t)(8 * l_it);
+        rw[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, 0));
+        rs[s][t] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)gi, 0, 0);
+      }
     }
     if (!l_done && ++l_it == l_nit) {
       l_it = 0;
@@ -264,18 +297,21 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
       // must wait for slot s's loads only
       __builtin_amdgcn_sched_barrier(0);
       if (base + s < total) {
-        // transpose through this wave's LDS buffer: rows as loaded (8 groups
-        // each, padded rows: conflict-free both ways), then lane (r, q) takes
-        // group 4i + q of row r for MFMA step i
+        // canonical: transpose through this wave's LDS buffer (rows as loaded,
+        // 8 groups each, padded rows: conflict-free both ways), then lane (r, q)
+        // takes group 4i + q of row r for MFMA step i; prepared: the loads are
+        // already that
+        if constexpr (!PREP) {
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-          *reinterpret_cast<u32x4*>(tr + (8 * t + lr) * kTrRow + lg * 16) = rw[s][t];
-          tr[kRows * kTrRow + (8 * t + lr) * 8 + lg] = rs[s][t];
+          for (int t = 0; t < 2; t++) {
+            *reinterpret_cast<u32x4*>(tr + (8 * t + lr) * kTrRow + lg * 16) = rw[s][t];
+            tr[kRows * kTrRow + (8 * t + lr) * 8 + lg] = rs[s][t];
+          }
         }
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-          const u32x4 wq = *reinterpret_cast<const u32x4*>(tr + r * kTrRow + (4 * i + q) * 16);
-          const uint32_t sv = tr[kRows * kTrRow + r * 8 + 4 * i + q];
+          const u32x4 wq = PREP ? rw[s][i] : *reinterpret_cast<const u32x4*>(tr + r * kTrRow + (4 * i + q) * 16);
+          const uint32_t sv = PREP ? (uint32_t)rs[s][i] : (uint32_t)tr[kRows * kTrRow + r * 8 + 4 * i + q];
           uint32_t wd[4][4];
           // scale bytes >= 253 can make E2M1 * 2^(s-127) overflow bf16: such a
           // lane's group is decoded at 2^(s-135) into a second accumulator,
@@ -385,9 +421,11 @@ int decode_tokens_per_launch(int K, int E, int G, int dtype) {
   return tc;
 }
 
-hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
-                               const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
-                               int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream) {
+namespace {
+template <bool PREP>
+hipError_t launch_decode(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                         const float* p, const void* shared, void* y, int T, int E, int O, int G, int K, int dtype,
+                         int32_t* n_invalid, int chunk_index, hipStream_t stream) {
   if (T * K > kMaxFusedPairs || !gemv_rows_supported(O, G)) return hipErrorInvalidValue;
   const int S = decode_splits(T, K, E, G);
   const size_t lds = decode_lds_bytes(T, K, G, dtype, S);
@@ -397,23 +435,38 @@ hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8
   if (dtype == 0) {
     static bool attr = false;  // large LDS needs the opt-in once per kernel
     if (!attr) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<true>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<true, PREP>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
       attr = true;
     }
-    hipLaunchKernelGGL(decode_fused_kernel<true>, grid, dim3(kDecThreads), lds, stream, x, packed, scales, sel, p,
-                       shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
+    hipLaunchKernelGGL((decode_fused_kernel<true, PREP>), grid, dim3(kDecThreads), lds, stream, x, packed, scales, sel,
+                       p, shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
   } else {
     static bool attr = false;
     if (!attr) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<false>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<false, PREP>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
       attr = true;
     }
-    hipLaunchKernelGGL(decode_fused_kernel<false>, grid, dim3(kDecThreads), lds, stream, x, packed, scales, sel, p,
-                       shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
+    hipLaunchKernelGGL((decode_fused_kernel<false, PREP>), grid, dim3(kDecThreads), lds, stream, x, packed, scales,
+                       sel, p, shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                               const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
+                               int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream) {
+  return launch_decode<false>(x, packed, scales, sel, p, shared, y, T, E, O, G, K, dtype, n_invalid, chunk_index,
+                              stream);
+}
+
+hipError_t launch_decode_prepared(const void* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* sel,
+                                  const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
+                                  int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream) {
+  return launch_decode<true>(x, pcodes, pscales, sel, p, shared, y, T, E, O, G, K, dtype, n_invalid, chunk_index,
+                             stream);
 }
 
 }  // namespace mxfp4

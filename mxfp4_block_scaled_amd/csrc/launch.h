@@ -65,6 +65,12 @@ hipError_t launch_bucket_one_block(const int32_t* sel, int P, int E, BucketOut o
 hipError_t launch_decode_fused(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
                                const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
                                int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream);
+// The same MFMA decode kernel on weights in the fragment-major prepared
+// layout of launch_prepare_mx (pcodes: its code slots, pscales: its scale
+// array); needs gemm_mx_supported's per-expert size bound.
+hipError_t launch_decode_prepared(const void* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* sel,
+                                  const float* p, const void* shared, void* y, int T, int E, int O, int G, int K,
+                                  int dtype, int32_t* n_invalid, int chunk_index, hipStream_t stream);
 // Most tokens one decode-shaped launch takes for these sizes (0: none fits).
 int decode_tokens_per_launch(int K, int E, int G, int dtype);
 

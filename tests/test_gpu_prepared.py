@@ -327,3 +327,94 @@ def test_prepare_bf16_layout_bytes(E, O, G):
     with pytest.raises(ValueError):  # the fragment-major order is refused by the bf16 path
         mx.moe_linear_prepared(bf16_dev(np.zeros((1, 32 * G))), other, torch.zeros((1, 1), dtype=torch.int32, device=DEV),
                                torch.ones((1, 1), dtype=torch.float32, device=DEV), bf16_dev(np.zeros((1, O))))
+
+
+# ------------------------------------------------------------------ decode-shaped path on prepared weights
+
+F32_TOL = 1e-4
+
+
+def _decode_both(x, packed, scales, sel, p, shared, dtype):
+    """(prepared, canonical MFMA decode kernel) results on the same inputs."""
+    td = torch.float32 if dtype == "fp32" else torch.bfloat16
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    xd = dv(x.astype(np.float32)).to(td)
+    shd = dv(shared.astype(np.float32)).to(td)
+    pk, sc = dv(packed), dv(scales)
+    prep = mx.prepare_mx(pk, sc)
+    y_p = mx.moe_decode_prepared(xd, prep, dv(sel), dv(p), shd)
+    y_c = mx.moe_linear(xd, pk, sc, dv(sel), dv(p), shd, flags=_abi.FLAG_FORCE_GEMV | _abi.FLAG_GEMV_MFMA)
+    torch.cuda.synchronize()
+    return y_p, y_c
+
+
+def _check_decode(y, ref, dtype, what):
+    yh = host64(y)
+    if dtype == "fp32":
+        err = np.abs(yh - ref)
+        bound = F32_TOL * (1.0 + np.abs(ref))
+        say(f"  {what}: max err/bound {np.max(err / bound):.3g}")
+        assert np.all(err <= bound), what
+    else:
+        check(y, ref, what)
+
+
+DECODE_CASES = [  # seed, T, E, K, G, O, dtype, distinct
+    (1, 4, 4, 2, 2, 32, "fp32", True),      # the tiny workload's shape
+    (2, 1, 128, 4, 90, 5760, "fp32", True),  # the decode workload's shape (fewer experts drawn)
+    (3, 8, 24, 8, 37, 264, "bf16", True),   # odd G, a partial last 128-row tile
+    (4, 5, 6, 4, 2, 16, "bf16", False),     # duplicates within a token
+    (5, 40, 9, 3, 5, 132, "fp32", True),    # 120 pairs: several token chunks
+    (6, 3, 3, 3, 9, 1028, "bf16", True),    # every expert in every token, 65 row blocks (a remapped group of 32 and a tail)
+]
+
+
+@pytest.mark.parametrize("c", DECODE_CASES, ids=lambda c: "T{}E{}K{}G{}O{}{}{}".format(*c[1:7], "" if c[7] else "dup"))
+def test_decode_prepared_against_oracle_and_canonical(c):
+    seed, T, E, K, G, O, dtype, distinct = c
+    say(f"decode prepared {c}")
+    x, packed, scales, sel, p, shared = case(seed, T, E, K, G, O, distinct=distinct)
+    if dtype == "fp32":
+        rng = np.random.default_rng(seed + 100)
+        x = rng.standard_normal(x.shape).astype(np.float32)
+        shared = rng.standard_normal(shared.shape).astype(np.float32)
+    y_p, y_c = _decode_both(x, packed, scales, sel, p, shared, dtype)
+    # the same MFMA sequence on the same operands: bit for bit the canonical kernel's result
+    assert torch.equal(y_p, y_c), "differs from the canonical MFMA decode kernel"
+    _check_decode(y_p, oracle.expert_linear(x, packed, scales, sel, p, shared), dtype, f"decode prepared {c}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_prepared_largest_scales(dtype):
+    """Scale bytes 253..255 (the kernels' 2^-8 second accumulator) with
+    tiny activations: finite results equal to the float64 oracle's."""
+    T, E, K, G, O = 3, 4, 2, 9, 72
+    x, packed, scales, sel, p, shared = case(31, T, E, K, G, O)
+    # small but well inside the normal range, so that the three-piece bf16 split of fp32 x stays exact
+    x = (np.random.default_rng(32).standard_normal(x.shape) * 2.0 ** -100).astype(np.float32)
+    if dtype == "bf16":
+        x = workloads.round_to_bf16(x)
+    scales = np.random.default_rng(33).integers(253, 256, scales.shape).astype(np.uint8)
+    y_p, y_c = _decode_both(x, packed, scales, sel, p, shared, dtype)
+    assert torch.equal(y_p, y_c)
+    ref = oracle.expert_linear(x, packed, scales, sel, p, shared)
+    assert np.all(np.isfinite(ref)) and np.all(np.isfinite(host64(y_p)))
+    _check_decode(y_p, ref, dtype, f"decode prepared scales 253..255 {dtype}")
+
+
+def test_decode_prepared_decode8_workload_sampled():
+    inp = workloads.make_inputs("decode8", n_routing_sets=1)
+    w = inp.workload
+    say(f"decode prepared at decode8: T={w.T} E={w.E} K={w.K} G={w.G} O={w.O}")
+    pk = torch.empty(inp.packed.shape, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(inp.scales.shape, dtype=torch.uint8, device=DEV)
+    for e in range(w.E):
+        pk[e].copy_(torch.from_numpy(np.ascontiguousarray(inp.packed[e])))
+        sc[e].copy_(torch.from_numpy(np.ascontiguousarray(inp.scales[e])))
+    prep = mx.prepare_mx(pk, sc)
+    y = mx.moe_decode_prepared(bf16_dev(inp.x), prep, torch.from_numpy(inp.sel).to(DEV),
+                               torch.from_numpy(inp.p).to(DEV), bf16_dev(inp.shared))
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(np.random.default_rng(8).choice(w.O, 96, replace=False).tolist()) | {0, w.O - 1}))
+    ref = oracle.expert_linear_rows(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
+    check(y[:, torch.from_numpy(rows).to(DEV)], ref, "decode8 prepared")
