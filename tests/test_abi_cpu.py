@@ -301,3 +301,43 @@ def test_mx_prepared_size_and_host_checks():
     assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(A, B, C + 0x10000, C + 0x20000, C + 0x30000, B + 32, 2, 2, 8,
                                                   2, 2, 0, ws, 1 << 24, None) == _abi.ERR_INVALID_ARG
     assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(0, 0, 0, 0, 0, 0, 0, 2, 8, 2, 2, 0, 0, 0, None) == _abi.OK
+
+
+# ------------------------------------------------------------------ prepared-weight entry points (host checks)
+
+M28 = 1 << 28  # far-apart fake device addresses: no buffer overlaps another
+
+
+def _prep_ex(fn, x=1 * M28, prep=2 * M28, sel=4 * M28, p=5 * M28, shared=6 * M28, y=7 * M28, T=64, E=4, O=64, G=2,
+             K=2, flags=0, ws=8 * M28, ws_bytes=1 << 30, dtype=None):
+    lib = _abi.lib()
+    if fn == "decode":
+        return lib.mxfp4_moe_decode_prepared_ex(x, prep, sel, p, shared, y, T, E, O, G, K,
+                                                _abi.DTYPE_F32 if dtype is None else dtype, flags, ws, ws_bytes, None)
+    return lib.mxfp4_moe_linear_prepared_ex(x, prep, sel, p, shared, y, T, E, O, G, K, flags, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["linear", "decode"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), "ERR_INVALID_ARG"), (dict(E=0), "ERR_INVALID_ARG"), (dict(x=0), "ERR_INVALID_ARG"),
+    (dict(prep=0), "ERR_INVALID_ARG"), (dict(sel=0), "ERR_INVALID_ARG"), (dict(y=2 * M28), "ERR_INVALID_ARG"),
+    (dict(flags=_abi.FLAG_FORCE_GEMM), "ERR_INVALID_ARG"), (dict(O=34), "ERR_UNSUPPORTED"),
+    (dict(ws_bytes=16), "ERR_WORKSPACE_TOO_SMALL"), (dict(T=0, x=0, prep=0, sel=0, p=0, shared=0, y=0), "OK"),
+])
+def test_prepared_entry_points_validate_on_the_host(fn, kw, status):
+    assert _prep_ex(fn, **kw) == getattr(_abi, status)
+
+
+def test_prepare_entry_points_validate_on_the_host():
+    lib = _abi.lib()
+    n = _abi.mx_prepared_size(4, 64, 2)
+    assert n == 4 * 1 * 1 * 512 * 17  # one 128-row tile, one 128-input chunk per expert
+    for fn in (lib.mxfp4_prepare_mx, lib.mxfp4_prepare_bf16):
+        assert fn(1 * M28, 2 * M28, 4, 64, 2, 3 * M28, n - 1, None) == _abi.ERR_WORKSPACE_TOO_SMALL
+        assert fn(1 * M28, 2 * M28, 4, 66, 2, 3 * M28, 1 << 30, None) == _abi.ERR_UNSUPPORTED  # O % 4
+        assert fn(1 * M28 + 8, 2 * M28, 4, 64, 2, 3 * M28, n, None) == _abi.ERR_INVALID_ARG    # alignment
+        assert fn(1 * M28, 2 * M28, 4, 64, 2, 1 * M28, n, None) == _abi.ERR_INVALID_ARG        # overlap
+    # SwiGLU gate/up: F a multiple of 32, the size of a (E, 2F, G) repack
+    assert lib.mxfp4_prepare_swiglu(1 * M28, 2 * M28, 4, 48, 2, 3 * M28, 1 << 30, None) == _abi.ERR_INVALID_ARG
+    assert lib.mxfp4_prepare_swiglu(1 * M28, 2 * M28, 4, 64, 2, 3 * M28, _abi.mx_prepared_size(4, 128, 2) - 1,
+                                    None) == _abi.ERR_WORKSPACE_TOO_SMALL
