@@ -122,6 +122,45 @@ def test_graph_prepared_bf16():
                    lambda: mx.moe_linear_prepared(x, prep, sel.flip(1).contiguous(), p, shared, out=other))
 
 
+def test_graph_decode_prepared():
+    say("graph: moe_decode_prepared (fp32)")
+    rng = np.random.default_rng(6)
+    T, E, K, G, O = 3, 16, 4, 9, 264
+    x = torch.from_numpy(rng.standard_normal((T, 32 * G)).astype(np.float32)).to(DEV)
+    shared = torch.from_numpy(rng.standard_normal((T, O)).astype(np.float32)).to(DEV)
+    packed = torch.from_numpy(rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)).to(DEV)
+    scales = torch.from_numpy(rng.integers(118, 131, (E, O, G), dtype=np.uint8)).to(DEV)
+    sel = torch.from_numpy(np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)).to(DEV)
+    p = torch.from_numpy(rng.random((T, K)).astype(np.float32)).to(DEV)
+    prep = mx.prepare_mx(packed, scales)
+    ws = torch.empty(mx.workspace_size(T, E, O, G, K, mx.DTYPE_F32, mx.FLAG_FORCE_GEMV), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty_like(shared)
+    other = torch.empty_like(shared)
+    _replays_match(lambda: mx.moe_decode_prepared(x, prep, sel, p, shared, out=out, workspace=ws), out,
+                   lambda: mx.moe_decode_prepared(x, prep, sel.flip(1).contiguous(), p, shared, out=other))
+
+
+def test_graph_swiglu_prepared():
+    say("graph: moe_swiglu_prepared")
+    rng = np.random.default_rng(7)
+    T, E, K, G, F, O = 70, 6, 2, 4, 64, 96
+    x = bf16(workloads.round_to_bf16(rng.standard_normal((T, 32 * G)).astype(np.float32)))
+    shared = bf16(workloads.round_to_bf16(rng.standard_normal((T, O)).astype(np.float32)))
+    dv = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    prep = mx.prepare_swiglu(dv(rng.integers(0, 256, (E, 2 * F, G, 16), dtype=np.uint8)),
+                             dv(rng.integers(118, 127, (E, 2 * F, G), dtype=np.uint8)),
+                             dv(rng.integers(0, 256, (E, O, F // 32, 16), dtype=np.uint8)),
+                             dv(rng.integers(118, 127, (E, O, F // 32), dtype=np.uint8)))
+    sel = dv(np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32))
+    p = dv(rng.random((T, K)).astype(np.float32))
+    ws = torch.empty(mx.swiglu_workspace_size(T, E, F, G, O, K), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(shared)
+    other = torch.empty_like(shared)
+    _replays_match(lambda: mx.moe_swiglu_prepared(x, prep, sel, p, shared, out=out, workspace=ws), out,
+                   lambda: mx.moe_swiglu_prepared(x, prep, sel, p * 2, shared, out=other))
+
+
 def test_graph_router():
     say("graph: route")
     logits, bias = workloads.router_logits(700, 96, seed=5, bias_std=0.1)
