@@ -132,8 +132,10 @@ __global__ void __launch_bounds__(kScanThreads) bucket_scan_kernel(int32_t* __re
   int* tmp = sh + E;          // [E]
   int* wave_tot = sh + 2 * E; // [17]
   __shared__ int inv_red[kScanThreads / 64];
+  // the chunk loops are unrolled so that many of their (independent) loads are in flight at once
   for (int e = threadIdx.x; e < E; e += kScanThreads) {
     int total = 0;
+#pragma unroll 16
     for (int c = 0; c < nchunks; c++) total += bcount[(size_t)c * E + e];
     cnt[e] = total;
     tmp[e] = total;
@@ -149,6 +151,7 @@ __global__ void __launch_bounds__(kScanThreads) bucket_scan_kernel(int32_t* __re
   for (int e = threadIdx.x; e < E; e += kScanThreads) {
     out.offsets[e] = tmp[e];
     int run = tmp[e];
+#pragma unroll 16
     for (int c = 0; c < nchunks; c++) {  // chunk c's first position for expert e
       const int v = bcount[(size_t)c * E + e];
       bcount[(size_t)c * E + e] = run;
