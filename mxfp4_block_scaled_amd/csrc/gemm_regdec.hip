@@ -117,7 +117,11 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   // all their N-tiles back to back, so the N-tiles of an M-tile share its
   // gathered activation rows in one L2.
   const int xcd_step = blockIdx.x >> 3;
-  const int ti = (blockIdx.x & 7) + 8 * (xcd_step / n_wg);
+  // tiles in pairs: XCD x takes tiles 2x, 2x + 1, 2x + 16, 2x + 17, ..., so that
+  // the partial second M-tile of an expert usually follows its first on the
+  // same XCD and finds the expert's weights in that L2
+  const int jx = xcd_step / n_wg;
+  const int ti = 2 * ((blockIdx.x & 7) + 8 * (jx >> 1)) + (jx & 1);
   const int nt = xcd_step % n_wg;
   if (ti >= n_tiles[0]) return;
   const GemmTile tl = tiles[ti];
@@ -329,7 +333,7 @@ hipError_t launch_mode(const uint16_t* x, const uint8_t* pcodes, const uint8_t* 
   // O: rows of the prepared matrix (2F for kSwiGLU)
   const int n_wg = (O + NW - 1) / NW, n_ptiles = (O + PT - 1) / PT;
   // 8 XCDs x ceil(max_tiles / 8) M-tiles x the N-tiles
-  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_wg;
+  const int64_t nblk = (max_tiles + 15) / 16 * 16 * n_wg;  // an even number of tiles per XCD
   if (nblk <= 0) return hipSuccess;
   const uint32_t x_bytes = (uint32_t)(x_rows * 64 * G);
   hipLaunchKernelGGL(gemm_regdec_kernel<MODE>, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, x, pcodes, pscales,
