@@ -130,13 +130,15 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
                                                          const int32_t* __restrict__ n_tiles, float* __restrict__ part,
                                                          int K, int O, int G, int Kp, int n_ntiles, int n_wg, uint32_t xq_bytes,
                                                          uint32_t xs_bytes) {
-  // Workgroup i runs on XCD i mod 8. XCD x takes M-tiles x, x + 8, ... with
+  // Workgroup i runs on XCD i mod 8. Each XCD takes its M-tiles (below) with
   // all their N-tiles back to back, so the N-tiles of an M-tile share its
   // gathered activation rows in one L2 instead of every XCD fetching them,
-  // while neighbouring M-tiles (full and partial ones) still spread over all
-  // XCDs.
+  // while the pairs of neighbouring M-tiles still spread over all XCDs.
   const int xcd_step = blockIdx.x >> 3;
-  const int ti = (blockIdx.x & 7) + 8 * (xcd_step / n_wg);
+  // tiles in pairs (2x, 2x + 1, 2x + 16, ...): an expert's partial second
+  // M-tile usually runs on the same XCD as its first and finds the weights in L2
+  const int jx = xcd_step / n_wg;
+  const int ti = 2 * ((blockIdx.x & 7) + 8 * (jx >> 1)) + (jx & 1);
   const int nt = xcd_step % n_wg;  // feature tile of NW features
   if (ti >= n_tiles[0]) return;
   const GemmTile tl = tiles[ti];
@@ -413,8 +415,8 @@ hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* p
                           float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared) {
   const int Kp = mx_row_bytes(32 * (int64_t)G);
   const int n_ntiles = (O + NT - 1) / NT, n_wg = (O + NW - 1) / NW;
-  // 8 XCDs x ceil(max_tiles / 8) M-tiles x the feature tiles
-  const int64_t nblk = (max_tiles + 7) / 8 * 8 * n_wg;
+  // 8 XCDs x an even number of M-tiles each x the feature tiles
+  const int64_t nblk = (max_tiles + 15) / 16 * 16 * n_wg;  // an even number of tiles per XCD
   if (nblk == 0) return hipSuccess;
   const uint32_t xq_bytes = (uint32_t)((int64_t)T * Kp), xs_bytes = (uint32_t)((int64_t)T * Kp / 32);
   if (prepared)

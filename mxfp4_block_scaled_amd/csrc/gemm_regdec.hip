@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ n_tiles,
                                                              void* __restrict__ out, int K, int O, int G, int F,
                                                              int n_wg, int n_ptiles, uint32_t x_bytes) {
-  // Workgroup i runs on XCD i mod 8: XCD x takes M-tiles x, x + 8, ... with
+  // Workgroup i runs on XCD i mod 8: each XCD takes its M-tiles (below) with
   // all their N-tiles back to back, so the N-tiles of an M-tile share its
   // gathered activation rows in one L2.
   const int xcd_step = blockIdx.x >> 3;
