@@ -272,7 +272,8 @@ int mxfp4_moe_linear_mxfp8_ex(const uint16_t* x, const uint8_t* packed, const ui
                               hipStream_t stream);
 
 /*
- * Load-time weight repack for the block-scaled variant. The prepared buffer
+ * Load-time weight repack for the block-scaled variant and the prepared
+ * decode-shaped path (mxfp4_moe_decode_prepared_ex). The prepared buffer
  * holds, per expert, per N-tile of 128 output rows, per chunk of 128 inputs
  * (4 groups) and per 16-row fragment, 64 group slots of 16 code bytes in the
  * order the scaled MFMA's weight operand takes them (slot l: row 16 f + (l mod
