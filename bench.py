@@ -1,17 +1,25 @@
 """Benchmark of the MXFP4 routed-expert linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-    python bench.py --router softmax|sigmoid --workload NAME   (the router alone)
+    python bench.py [--gpus 1] [--steps K] [--warmup W]          (the full suite)
+    python bench.py --workload NAME [--steps K] [--warmup W]     (one workload)
+    python bench.py --router softmax|sigmoid --workload NAME      (the router alone)
 
 A step is one call of the whole layer (bucketing, dequant-GEMV or grouped
 GEMM, combine) on one batch of the workload's synthetic inputs, all resident
 in HBM before the timed region. Step i uses routing draw i mod R (R = 64
-distinct (sel, p) draws), so consecutive calls read different experts and
-the Infinity Cache cannot serve the weights from the previous call.
+distinct (sel, p) draws for the decode-shaped workloads, 4 for the
+prefill-shaped ones, which read every expert in every call), so consecutive
+calls read different experts and the Infinity Cache cannot serve the weights
+from the previous call.
 
 The K timed steps are captured once in a HIP graph and replayed; the timed
 region is bracketed by device synchronisation, and HIP events on the replay
 stream give its duration. One JSON line goes to stdout; details to stderr.
+
+Without --workload the line is the decode workload's (T1 E128 K4 G90 O5760,
+fp32) and carries a "suite" object with one record per other workload
+(tiny, decode8, prefill, skewed; each with its own roofline and oracle
+baseline) and the plain streaming-read ceiling of the same bytes.
 
 value:
   decode-shaped workloads: algorithmic weight bytes per second, where a call
@@ -46,8 +54,8 @@ MFMA_FP8_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 MFMA, published (the fp4 x fp
 N_ROUTING_SETS = 64
 DECODE_WORKLOADS = ("tiny", "decode", "decode8")
 KERNEL_SOURCES = {
-    "gemv": ["mxfp4_block_scaled_amd/csrc/gemv_rows.hip", "mxfp4_block_scaled_amd/csrc/device_common.h",
-             "mxfp4_block_scaled_amd/csrc/wave_routing.h"],
+    "gemv": ["mxfp4_block_scaled_amd/csrc/gemv_rows.hip", "mxfp4_block_scaled_amd/csrc/gemv_one.hip",
+             "mxfp4_block_scaled_amd/csrc/device_common.h", "mxfp4_block_scaled_amd/csrc/wave_routing.h"],
     "gemm": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "swiglu": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "mx": ["mxfp4_block_scaled_amd/csrc/gemm_mx.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
@@ -122,7 +130,7 @@ def record_traffic(args):
     the kernel's sources; prints a summary."""
     w = workloads.WORKLOADS[args.workload]
     kind = "gemv" if args.workload in DECODE_WORKLOADS else ("gemmp" if args.prepared else "gemm")
-    kname = KERNEL_NAMES[kind]
+    kname = "gemv_one_kernel" if (kind == "gemv" and w.T == 1) else KERNEL_NAMES[kind]
     fdir, wdir, cfdir, cwdir = args.record_traffic
     copy_kib = args.copy_mib * 1024.0
     k_fetch, n_f = _counter_means(fdir, "FETCH_SIZE", kname)
@@ -335,75 +343,81 @@ def bench_router(args, w):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph replay")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work for the oracle baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="run only the copy calibration kernel of this size (for the byte counters)")
-    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="host only: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload and of "
-                         "the copy calibration (--copy-mib) into profiles/traffic.json")
-    ap.add_argument("--variant", choices=["mxfp8"],
-                    help="time the block-scaled variant (MXFP8 activations on the scaled MFMA) instead of the layer")
-    ap.add_argument("--prepared", action="store_true",
-                    help="weights repacked once (outside the timed region) by prepare_bf16: the bf16 GEMM on "
-                         "prepared weights, or with --variant mxfp8 the variant's")
-    ap.add_argument("--router", choices=["softmax", "sigmoid"],
-                    help="time the router alone at the workload's T, E and K instead of the layer")
-    args = ap.parse_args()
-    if args.record_traffic:
-        if args.copy_mib <= 0:
-            raise SystemExit("--record-traffic needs the --copy-mib size the calibration ran with")
-        record_traffic(args)
-        return
+def host_info():
+    """The host the oracle baseline runs on: cores this process may use, CPU
+    model, the BLAS NumPy calls and its thread count."""
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", cores
+    try:
+        from threadpoolctl import threadpool_info
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
-        sys.exit(2)
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+            threads = int(libs[0].get("num_threads", cores))
+    except Exception:  # threadpoolctl missing: BLAS unknown
+        pass
+    return {"host_cores": cores, "cpu_model": model, "blas": blas, "blas_threads": threads}
 
-    if args.copy_mib > 0:
-        copy_calibration(args.copy_mib)
-        return
-    if args.router:
-        bench_router(args, workloads.WORKLOADS[args.workload])
-        return
 
+def device_info():
+    import torch
+
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", "?"), "compute_units": pr.multi_processor_count}
+    clk = getattr(pr, "clock_rate", None)
+    if clk:
+        info["clock_mhz"] = round(clk / 1000.0)
+    return info
+
+
+def _upload_experts(t, arr, E):
+    for e in range(E):  # the expert tensors are drawn expert by expert
+        t[e].copy_(torch_from(arr[e]))
+
+
+def torch_from(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a))
+
+
+def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
+    """Time `steps` graph-replayed calls of workload w on the path `kind`;
+    returns the JSON record (without the top-level contract keys)."""
     import torch
 
     import mxfp4_block_scaled_amd as mx
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = workloads.WORKLOADS[args.workload]
-    kind = _kind(w, args.variant, args.prepared)
     td = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     t_gen = time.perf_counter()
-    inp = workloads.make_inputs(w, n_routing_sets=N_ROUTING_SETS)
+    inp = workloads.make_inputs(w, n_routing_sets=n_sets)
     packed = torch.empty(inp.packed.shape, dtype=torch.uint8, device=dev)
     scales = torch.empty(inp.scales.shape, dtype=torch.uint8, device=dev)
-    for e in range(w.E):
-        packed[e].copy_(torch.from_numpy(inp.packed[e]))
-        scales[e].copy_(torch.from_numpy(inp.scales[e]))
+    _upload_experts(packed, inp.packed, w.E)
+    _upload_experts(scales, inp.scales, w.E)
     dn_packed = dn_scales = None
     if kind in ("swiglu", "swiglup"):
         dn_packed = torch.empty(inp.dn_packed.shape, dtype=torch.uint8, device=dev)
         dn_scales = torch.empty(inp.dn_scales.shape, dtype=torch.uint8, device=dev)
-        for e in range(w.E):
-            dn_packed[e].copy_(torch.from_numpy(inp.dn_packed[e]))
-            dn_scales[e].copy_(torch.from_numpy(inp.dn_scales[e]))
+        _upload_experts(dn_packed, inp.dn_packed, w.E)
+        _upload_experts(dn_scales, inp.dn_scales, w.E)
     x = torch.from_numpy(inp.x).to(dev).to(td)
     shared = torch.from_numpy(inp.shared).to(dev).to(td)
     sels = torch.from_numpy(np.stack([s for s, _ in inp.routing_sets])).to(dev)
     ps = torch.from_numpy(np.stack([p for _, p in inp.routing_sets])).to(dev)
     y = torch.empty_like(shared)
+    dt = 0 if w.dtype == "fp32" else 1
     if kind in ("swiglu", "swiglup"):
         ws_bytes = mx.swiglu_workspace_size(w.T, w.E, w.F, w.G, w.O, w.K)
     elif kind == "mx":
@@ -411,9 +425,9 @@ def main():
     elif kind == "gemmp":
         ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM)
     elif kind == "gemvp":
-        ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1, mx.FLAG_FORCE_GEMV)
+        ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, dt, mx.FLAG_FORCE_GEMV)
     else:
-        ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, 0 if w.dtype == "fp32" else 1)
+        ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, dt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     prepared = None
     if args.prepared:
@@ -425,7 +439,7 @@ def main():
         f"path {_path_name(mx, w, kind)}")
 
     def step(i):
-        r = i % N_ROUTING_SETS
+        r = i % n_sets
         if kind == "swiglu":
             mx.moe_swiglu(x, packed, scales, dn_packed, dn_scales, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "swiglup":
@@ -442,11 +456,11 @@ def main():
             mx.moe_linear(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
 
     # eager reference of the last timed step, for the graph replay check
-    last = (args.steps - 1) % N_ROUTING_SETS
+    last = (steps - 1) % n_sets
     step(last)
     torch.cuda.synchronize()
     y_eager = y.clone()
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
@@ -459,15 +473,15 @@ def main():
             step(0)  # the binding allocates nothing here; this call only settles the stream
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=stream):
-            for i in range(args.steps):
+            for i in range(steps):
                 step(i)
         graph.replay()
         torch.cuda.synchronize()
         if not torch.equal(y, y_eager):
-            raise SystemExit("graph replay result differs from the eager call")
-        log("[bench] graph replay matches the eager call bit for bit")
+            raise SystemExit(f"{w.name}: graph replay result differs from the eager call")
+        log(f"[bench] {w.name}: graph replay matches the eager call bit for bit")
 
-    # timed region
+    # timed region: HIP events recorded on the stream the kernels run on
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -476,14 +490,14 @@ def main():
         if graph is not None:
             graph.replay()
         else:
-            for i in range(args.steps):
+            for i in range(steps):
                 step(i)
         ev1.record(stream)
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step = ms_total / steps
     if not torch.equal(y, y_eager):
-        raise SystemExit("timed steps ended with a result that differs from the eager call")
+        raise SystemExit(f"{w.name}: timed steps ended with a result that differs from the eager call")
 
     gemm_ms = None
     if kind in ("gemm", "gemmp"):
@@ -494,8 +508,7 @@ def main():
                 mx.gemm_stage(x, packed, scales, w.K, ws)
 
         # the grouped GEMM alone, on the bucketing the last timed step left in
-        # the workspace: K launches captured in a graph, timed like the steps
-        r_last = (args.steps - 1) % N_ROUTING_SETS
+        # the workspace: `steps` launches captured in a graph, timed like the steps
         with torch.cuda.stream(stream):
             gemm_alone()
         torch.cuda.synchronize()
@@ -503,7 +516,7 @@ def main():
         if graph is not None:
             g2 = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g2, stream=stream):
-                for _ in range(args.steps):
+                for _ in range(steps):
                     gemm_alone()
             g2.replay()
             torch.cuda.synchronize()
@@ -514,18 +527,19 @@ def main():
             if g2 is not None:
                 g2.replay()
             else:
-                for _ in range(args.steps):
+                for _ in range(steps):
                     gemm_alone()
             e2b.record(stream)
         torch.cuda.synchronize()
-        gemm_ms = e2a.elapsed_time(e2b) / args.steps
-        log(f"[bench] grouped GEMM alone (routing draw {r_last}): {gemm_ms * 1e3:.1f} us per launch")
+        gemm_ms = e2a.elapsed_time(e2b) / steps
+        log(f"[bench] {w.name}: grouped GEMM alone (routing draw {last}): {gemm_ms * 1e3:.1f} us per launch")
 
-    uniq = [len(np.unique(inp.routing_sets[i % N_ROUTING_SETS][0])) for i in range(args.steps)]
+    uniq = [len(np.unique(inp.routing_sets[i % n_sets][0])) for i in range(steps)]
     bytes_per_step = float(np.mean(uniq)) * w.O * w.G * 17
     flops_per_step = 2.0 * w.P * w.O * w.I
     if kind in ("swiglu", "swiglup"):
         flops_per_step = 2.0 * w.P * (2 * w.F * w.I + w.O * w.F)
+    extra = {}
     if kind == "mx":
         # the variant's grouped GEMM on the scaled MFMA is its work; timed as
         # the whole call (bucketing, quantisation and combine included)
@@ -551,8 +565,11 @@ def main():
         unit = "GB/s"
         roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4)}
-        roof["kernel"] = "decode_fused_kernel<prepared>" if kind == "gemvp" else "gemv_rows_kernel"
+        roof["kernel"] = ("decode_fused_kernel<prepared>" if kind == "gemvp"
+                          else "gemv_one_kernel" if w.T == 1 else KERNEL_NAMES["gemv"])
         roof["launch_ms"] = round(ms_step, 6)
+        packed_only = float(np.mean(uniq)) * w.O * w.G * 16 / (ms_step * 1e-3) / 1e9
+        extra["packed_only_GBs"] = round(packed_only, 1)
     else:
         value = flops_per_step / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -561,30 +578,178 @@ def main():
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
         roof["kernel"] = KERNEL_NAMES[kind]
         roof["launch_ms"] = round(gemm_ms, 6)
+        extra["whole_call_frac"] = round(value / MFMA_BF16_PEAK_TFLOPS, 4)
+        extra["weight_GBs_whole_call"] = round(w.E * w.O * w.G * 17 / (ms_step * 1e-3) / 1e9, 1) \
+            if len(np.unique(inp.sel)) == w.E else None
     roof["per_launch"] = ({"bytes": bytes_per_step} if kind in ("gemv", "gemvp") else {"flops": flops_per_step})
     if kind in ("swiglu", "swiglup", "mx", "gemvp"):
         roof["traffic"] = None
     else:
         roof["traffic"] = committed_traffic(w.name + ("-prepared" if kind == "gemmp" else ""), kind)
-    log(f"[bench] {args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, "
-        f"{value:.1f} {unit} ({100 * roof['frac']:.1f}% of peak); mean distinct experts {np.mean(uniq):.1f}")
-
-    out = {
-        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp4xfp8" if kind == "mx" else ("f32" if w.dtype == "fp32" else "bf16"),
-        "data": "synthetic",
+    log(f"[bench] {w.name}: {steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, "
+        f"{value:.1f} {unit} ({100 * roof['frac']:.1f}% of peak for the timed kernel); "
+        f"mean distinct experts {np.mean(uniq):.1f}")
+    rec = {
+        "value": round(value, 2), "unit": unit, "ms_per_step": round(ms_step, 6), "steps": steps,
+        "dtype": "fp4xfp8" if kind == "mx" else ("f32" if w.dtype == "fp32" else "bf16"),
         "config": {"workload": w.name + ("-mxfp8" if kind == "mx" else "") + ("-prepared" if prepared is not None else ""),
                    "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
                    **({"F": w.F} if w.F else {}),
                    "x_dtype": w.dtype, "routing": w.routing if w.routing == "uniform" else f"zipf({w.zipf_s})",
-                   "routing_draws": N_ROUTING_SETS, "graph": graph is not None},
-        "roofline": roof,
+                   "routing_draws": n_sets, "graph": graph is not None},
+        "path": _path_name(mx, w, kind),
+        "roofline": roof, **extra,
     }
-    if not args.no_cpu_baseline:
-        cb = cpu_baseline(inp, kind, args.cpu_seconds)
-        out["cpu_baseline"] = cb
-        log(f"[bench] oracle on the host: {cb['value']:.4g} {cb['unit']} with {cb['cores']} threads ({cb['sample']})")
+    if cpu_seconds > 0:
+        cb = cpu_baseline(inp, kind, cpu_seconds)
+        cb.update(host_info())
+        rec["cpu_baseline"] = cb
+        log(f"[bench] {w.name}: oracle on the host: {cb['value']:.4g} {cb['unit']} with {cb['cores']} threads "
+            f"({cb['sample']})")
+    del packed, scales, dn_packed, dn_scales, x, shared, sels, ps, y, ws, prepared, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def stream_ceiling(window_bytes, steps, warmup):
+    """The plain streaming-read kernel (mxfp4_stream_read) on windows of
+    window_bytes taken in turn from a buffer of 64 such windows (larger than
+    the Infinity Cache), in a graph of `steps` launches; and on one 1 GiB
+    read. The practical read ceiling of the bytes a decode call moves."""
+    import torch
+
+    import mxfp4_block_scaled_amd as mx
+
+    dev = torch.device("cuda:0")
+    win = (int(window_bytes) + 4095) // 4096 * 4096
+    n_win = 64
+    buf = torch.randint(0, 255, (n_win * win,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    out = {}
+    for label, nbytes, views in (("decode_call_bytes", win, [buf[i * win:(i + 1) * win] for i in range(n_win)]),
+                                 ("one_GiB", 1 << 30, [buf[:1 << 30]])):
+        def step(i):
+            mx.stream_read(views[i % len(views)], sink)
+
+        for i in range(warmup):
+            step(i)
+        stream = torch.cuda.Stream(device=dev)
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            step(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[label] = {"bytes": nbytes, "ms_per_launch": round(ms, 6), "GBs": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"[bench] streaming read of {nbytes / 1e6:.1f} MB: {ms * 1e3:.2f} us, {gbs:.0f} GB/s "
+            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+        del g
+    del buf, sink
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_read_kernel", **out}
+
+
+SUITE = ("tiny", "decode8", "prefill", "skewed")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(workloads.WORKLOADS),
+                    help="time one workload (default: the decode workload, with the whole suite as sub-records)")
+    ap.add_argument("--no-suite", action="store_true", help="without --workload: the decode workload only")
+    ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work for the oracle baseline")
+    ap.add_argument("--suite-cpu-seconds", type=float, default=4.0, help="CPU work per suite workload's baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run only the copy calibration kernel of this size (for the byte counters)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="host only: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload and of "
+                         "the copy calibration (--copy-mib) into profiles/traffic.json")
+    ap.add_argument("--variant", choices=["mxfp8"],
+                    help="time the block-scaled variant (MXFP8 activations on the scaled MFMA) instead of the layer")
+    ap.add_argument("--prepared", action="store_true",
+                    help="weights repacked once (outside the timed region) by prepare_bf16: the bf16 GEMM on "
+                         "prepared weights, or with --variant mxfp8 the variant's")
+    ap.add_argument("--router", choices=["softmax", "sigmoid"],
+                    help="time the router alone at the workload's T, E and K instead of the layer")
+    ap.add_argument("--stream", action="store_true", help="time only the plain streaming-read ceiling")
+    args = ap.parse_args()
+    if args.record_traffic:
+        if args.copy_mib <= 0:
+            raise SystemExit("--record-traffic needs the --copy-mib size the calibration ran with")
+        if not args.workload:
+            raise SystemExit("--record-traffic needs --workload")
+        record_traffic(args)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib)
+        return
+    if args.router:
+        bench_router(args, workloads.WORKLOADS[args.workload or "decode"])
+        return
+
+    import torch
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    dec = workloads.WORKLOADS["decode"]
+    if args.stream:
+        st = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup)
+        print(json.dumps({"stream_ceiling": st}), flush=True)
+        return
+    suite = not args.workload and not args.no_suite
+    w = workloads.WORKLOADS[args.workload or "decode"]
+    kind = _kind(w, args.variant, args.prepared)
+    n_sets = N_ROUTING_SETS if kind in ("gemv", "gemvp") else 4
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    rec = measure(args, w, kind, args.steps, args.warmup, cpu_s, n_sets)
+    out = {
+        "metric": METRIC, "value": rec["value"], "unit": rec["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": rec["dtype"], "data": "synthetic", "config": rec["config"],
+        "roofline": rec["roofline"],
+    }
+    for key in ("packed_only_GBs", "whole_call_frac", "weight_GBs_whole_call", "cpu_baseline"):
+        if key in rec:
+            out[key] = rec[key]
+    out["device"] = device_info()
+    if suite:
+        sub = {}
+        sargs = argparse.Namespace(**{**vars(args), "prepared": False, "variant": None})
+        for name in SUITE:
+            sw = workloads.WORKLOADS[name]
+            skind = _kind(sw)
+            s_sets = N_ROUTING_SETS if skind == "gemv" else 4
+            sub[name] = measure(sargs, sw, skind, args.steps, args.warmup,
+                                0.0 if args.no_cpu_baseline else args.suite_cpu_seconds, s_sets)
+        sub["stream_ceiling"] = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup)
+        out["suite"] = sub
     print(json.dumps(out), flush=True)
 
 

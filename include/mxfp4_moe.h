@@ -53,7 +53,18 @@
  *             valid and enqueues nothing. A device that is not gfx950 gets
  *             MXFP4_ERR_UNSUPPORTED_DEVICE: there is no fallback path.
  * Threads.    All entry points are reentrant; the only shared state is a
- *             per-device cache of the architecture check.
+ *             per-device cache of the architecture check and, per kernel and
+ *             device, the one-time opt-in to large dynamic LDS (taken once,
+ *             under std::call_once).
+ * Large scale bytes. Every path returns the layer's value up to fp32
+ *             rounding for every scale byte 0..255 (2^(s-127)), also where a
+ *             decoded weight E2M1 * 2^(s-127) itself would overflow fp32 or
+ *             bf16 (s >= 253): the decode-shaped kernels scale each group's
+ *             dot product by 2^(s-127) after it is taken, the grouped GEMMs
+ *             decode a tile that holds such a byte at 2^(s-130) and scale the
+ *             tile's sums by 2^3 (the block-scaled MXFP8 variant excepted:
+ *             see its entry point). A value whose magnitude exceeds the output
+ *             type's range is +-inf there, as a rounding of the exact value.
  */
 #ifndef MXFP4_MOE_H
 #define MXFP4_MOE_H
@@ -74,10 +85,11 @@ typedef enum mxfp4_status {
   MXFP4_ERR_HIP = -3,                /* a HIP runtime call or a launch failed */
   MXFP4_ERR_WORKSPACE_TOO_SMALL = -4,
   MXFP4_ERR_INVALID_INDEX = -5,      /* with MXFP4_FLAG_CHECK: some sel entry outside [0, E) */
-  MXFP4_ERR_UNSUPPORTED = -6         /* a forced path that does not exist for these sizes or dtype:
+  MXFP4_ERR_UNSUPPORTED = -6         /* a forced path that does not exist for these sizes:
                                         the decode-shaped path needs one expert's packed bytes
                                         O*G*16 < 2^31 and one token's rows in LDS; the
-                                        prefill-shaped path is bf16-only */
+                                        prefill-shaped path needs O*G*16 < 2^31 and
+                                        T*32G*2 (bf16) or 3*T*32G*2 (fp32) below 2^31 */
 } mxfp4_status;
 
 typedef enum mxfp4_dtype {
@@ -135,6 +147,14 @@ int mxfp4_moe_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t
  * mxfp4_moe_workspace_size bytes (256-byte aligned). It allocates nothing
  * and does not synchronise unless MXFP4_FLAG_CHECK is set, so it may be
  * captured in a HIP graph. Calls that share one workspace must not overlap.
+ * Paths (page "MoE Expert Kernels: Grouped Prefill and Mixed-Quant Compact
+ * Experts", section 5: the schedule changes, the contract does not): the
+ * decode-shaped path (routing, dequant-GEMV and combine in one launch) when
+ * one launch takes every pair (at most 64 pairs, activations in LDS);
+ * otherwise bucketing, the grouped GEMM on bf16 MFMA (fp32 activations as
+ * their exact split into three bf16 pieces, every piece multiplied by the
+ * same decoded weights into one fp32 sum) and the combine. Both paths meet
+ * the same bars.
  */
 int mxfp4_moe_linear_ex(const void* x, const uint8_t* packed, const uint8_t* scales,
                         const int32_t* sel, const float* p, const void* shared, void* y,
@@ -412,6 +432,18 @@ int mxfp4_moe_swiglu_prepared_ex(const uint16_t* x, const void* gu_prepared, con
 #define MXFP4_ROUTE_MAX_K 64
 int mxfp4_moe_route(const float* logits, const float* bias, int64_t T, int64_t E, int64_t K, int mode, float scale,
                     int32_t* sel, float* p, hipStream_t stream);
+
+/*
+ * mxfp4_stream_read - a measurement helper, not a step of the layer: read
+ * `bytes` bytes of the device buffer `buf` once, in 16-byte pieces spread
+ * over `blocks` workgroups of 256 threads (0: min(bytes / 4096, 2048)), and
+ * write nothing except, with a chance of about 2^-32, one word of `sink`
+ * (a device array of at least `blocks` (or 2048) uint32). Its time is the
+ * practical read ceiling the decode-shaped path is compared with (the
+ * benchmark's stream workload). buf 16-byte aligned, bytes a multiple of 16
+ * below 2^40; MXFP4_ERR_INVALID_ARG otherwise. Enqueued on `stream`.
+ */
+int mxfp4_stream_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t stream);
 
 /* A static, human-readable name of a status code. */
 const char* mxfp4_status_string(int status);

@@ -30,7 +30,7 @@ __all__ = [
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
     "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared", "moe_linear_prepared", "gemm_stage_prepared",
     "prepare_bf16", "moe_decode_prepared", "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
-    "Mxfp4Error", "library_path",
+    "stream_read", "Mxfp4Error", "library_path",
 ]
 
 _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
@@ -495,6 +495,22 @@ def gemm_stage(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: i
         st = _abi.lib().mxfp4_moe_gemm_stage(_ptr(x), _ptr(packed), _ptr(scales), T, E, O, G, K, _ptr(workspace),
                                              workspace.numel(), _stream(dev))
     _abi.check(st, "mxfp4_moe_gemm_stage")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0) -> None:
+    """Read every byte of the device tensor ``buf`` once with the plain
+    streaming-read kernel (a measurement helper, not a step of the layer);
+    ``sink`` is an int32/uint32 device tensor of at least ``blocks`` (or 2048)
+    elements that is practically never written."""
+    dev = buf.device
+    if not buf.is_contiguous() or sink.device != dev or sink.element_size() != 4:
+        raise ValueError("buf must be contiguous and sink a 4-byte tensor on the same device")
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < (blocks or 2048):
+        raise ValueError("sink too small")
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_stream_read(_ptr(buf), nbytes, blocks, _ptr(sink), _stream(dev))
+    _abi.check(st, "mxfp4_stream_read")
 
 
 def route(logits: torch.Tensor, K: int, mode: str = "softmax", bias: torch.Tensor | None = None,

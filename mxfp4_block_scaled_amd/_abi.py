@@ -73,6 +73,7 @@ SIGNATURES = {
     "mxfp4_prepare_bf16": (_int, [_vp] * 2 + [_i64] * 3 + [_vp, _sz, _vp]),
     "mxfp4_prepare_swiglu": (_int, [_vp] * 2 + [_i64] * 3 + [_vp, _sz, _vp]),
     "mxfp4_moe_swiglu_prepared_ex": (_int, [_vp] * 7 + [_i64] * 6 + [_u32, _vp, _sz, _vp]),
+    "mxfp4_stream_read": (_int, [_vp, _sz, _int, _vp, _vp]),
     "mxfp4_status_string": (ctypes.c_char_p, [_int]),
 }
 

@@ -17,10 +17,6 @@ namespace {
 
 using namespace mxfp4;
 
-// Decode-shaped path up to this many tokens (bf16): every expert's pairs
-// then fit one 16-column MFMA tile when a token lists distinct experts, so
-// each selected expert's bytes are streamed exactly once.
-constexpr int64_t kGemvMaxTokens = 16;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -65,30 +61,37 @@ int64_t gemv_tokens_per_launch(const Dims& d, int dtype, uint32_t flags) {
                                 : decode_tokens_per_launch((int)d.K, (int)d.E, (int)d.G, dtype);
 }
 
+// Activation planes the grouped GEMM reads: bf16 x as is, fp32 x as its
+// exact three-piece bf16 split.
+int gemm_planes(int dtype) { return dtype == MXFP4_DTYPE_F32 ? 3 : 1; }
+
 int select_path(const Dims& d, int dtype, uint32_t flags) {
   if (dtype_size(dtype) == 0) return MXFP4_ERR_INVALID_ARG;
   const bool fv = flags & MXFP4_FLAG_FORCE_GEMV, fm = flags & MXFP4_FLAG_FORCE_GEMM;
   if (fv && fm) return MXFP4_ERR_INVALID_ARG;
-  // the decode-shaped kernels need one token's activations and partial rows in LDS
-  const bool gemv_ok = gemv_tokens_per_launch(d, dtype, flags) >= 1;
-  if (dtype == MXFP4_DTYPE_F32) {
-    if (fm || !gemv_ok) return MXFP4_ERR_UNSUPPORTED;  // the MFMA grouped GEMM is bf16-only
-    return MXFP4_PATH_GEMV;
-  }
-  const bool gemm_ok = gemm_supported(d.T, d.O, d.G);
+  // tokens one fused decode-shaped launch takes: at most 64 pairs, and the
+  // tokens' activations and partial rows must fit LDS
+  const int64_t tpl = gemv_tokens_per_launch(d, dtype, flags);
+  const bool gemv_ok = tpl >= 1;
+  const bool gemm_ok = gemm_supported(d.T, d.O, d.G, gemm_planes(dtype));
   if (fv) return gemv_ok ? MXFP4_PATH_GEMV : MXFP4_ERR_UNSUPPORTED;
   if (fm) return gemm_ok ? MXFP4_PATH_GEMM : MXFP4_ERR_UNSUPPORTED;
-  if (gemv_ok && (d.T <= kGemvMaxTokens || !gemm_ok)) return MXFP4_PATH_GEMV;
+  // The decode-shaped path when one launch takes every pair: each selected
+  // expert's bytes are then read once. Past that, successive launches would
+  // read a selected expert once per launch, while the grouped GEMM reads it
+  // once per 128 of its pairs.
+  if (gemv_ok && (d.T <= tpl || !gemm_ok)) return MXFP4_PATH_GEMV;
   return gemm_ok ? MXFP4_PATH_GEMM : MXFP4_ERR_UNSUPPORTED;
 }
 
 // Workspace layout. GEMV: n_invalid only. GEMM: bucketing arrays, the M-tile
-// list and the fp32 partial rows [P, O].
+// list, the fp32 partial rows [P, O] and, for fp32 activations, their
+// three bf16 planes [3, T, I].
 struct Layout {
-  size_t n_invalid, count, offsets, perm, slot, bcount, tiles, n_tiles, part, total;
+  size_t n_invalid, count, offsets, perm, slot, bcount, tiles, n_tiles, part, xs, total;
 };
 
-Layout layout(const Dims& d, int path) {
+Layout layout(const Dims& d, int path, int dtype = MXFP4_DTYPE_BF16) {
   Layout L{};
   size_t off = 0;
   L.n_invalid = off;
@@ -111,12 +114,17 @@ Layout layout(const Dims& d, int path) {
     off += kAlign;
     L.part = off;
     off = align_up(off + (size_t)d.P * d.O * 4);
+    if (dtype == MXFP4_DTYPE_F32) {
+      L.xs = off;
+      off = align_up(off + (size_t)3 * d.T * d.I * 2);
+    }
   }
   L.total = off;
   return L;
 }
 
 std::atomic<int> g_arch[64];  // 0 unknown, 1 gfx950, -1 another device
+std::atomic<int> g_cus[64];   // compute units of the device (0 unknown)
 
 int check_device() {
   int dev = 0;
@@ -128,9 +136,20 @@ int check_device() {
     v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':'))
             ? 1
             : -1;
-    if (dev >= 0 && dev < 64) g_arch[dev].store(v, std::memory_order_relaxed);
+    if (dev >= 0 && dev < 64) {
+      g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1, std::memory_order_relaxed);
+      g_arch[dev].store(v, std::memory_order_relaxed);
+    }
   }
   return v == 1 ? MXFP4_OK : MXFP4_ERR_UNSUPPORTED_DEVICE;
+}
+
+// compute units of the current device (after check_device)
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  const int n = g_cus[dev].load(std::memory_order_relaxed);
+  return n > 0 ? n : 256;
 }
 
 int check_linear_args(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
@@ -160,7 +179,7 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
                hipStream_t stream) {
   const int path = select_path(d, dtype, flags);
   if (path < 0) return path;
-  const Layout L = layout(d, path);
+  const Layout L = layout(d, path, dtype);
   if (ws_bytes < L.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
   if (!ws || !aligned(ws, kAlign)) return MXFP4_ERR_INVALID_ARG;
   int st = check_device();
@@ -169,7 +188,11 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
   int32_t* n_invalid = reinterpret_cast<int32_t*>(base + L.n_invalid);
   hipError_t err = hipSuccess;
   const int es = dtype_size(dtype);
-  if (path == MXFP4_PATH_GEMV) {
+  if (path == MXFP4_PATH_GEMV && d.T == 1 && use_rows_kernel(flags) && gemv_one_supported((int)d.O, (int)d.G, (int)d.K)) {
+    // one token: its activations stay in registers for the whole call
+    err = launch_gemv_one(x, packed, scales, sel, p, shared, y, (int)d.E, (int)d.O, (int)d.G, (int)d.K, dtype, n_invalid,
+                          device_cus(), stream);
+  } else if (path == MXFP4_PATH_GEMV) {
     // token chunks whose pairs and activations fit one fused launch
     const int64_t tc = gemv_tokens_per_launch(d, dtype, flags);
     if (tc < 1) return MXFP4_ERR_UNSUPPORTED;
@@ -192,10 +215,17 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
     b.tiles = reinterpret_cast<GemmTile*>(base + L.tiles);
     b.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
     err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
-    if (err == hipSuccess)
+    float* part = reinterpret_cast<float*>(base + L.part);
+    if (dtype == MXFP4_DTYPE_F32) {
+      uint16_t* xs = reinterpret_cast<uint16_t*>(base + L.xs);
+      if (err == hipSuccess) err = launch_split3(static_cast<const float*>(x), d.T * d.I, xs, stream);
+      if (err == hipSuccess)
+        err = launch_gemm_f32(xs, packed, scales, b.perm, b.tiles, b.n_tiles, gemm_max_tiles(d.P, d.E), part,
+                              (int)d.T, (int)d.K, (int)d.O, (int)d.G, stream);
+    } else if (err == hipSuccess) {
       err = launch_gemm_bf16(static_cast<const uint16_t*>(x), packed, scales, b.perm, b.tiles, b.n_tiles,
-                             gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.T, (int)d.K,
-                             (int)d.O, (int)d.G, stream);
+                             gemm_max_tiles(d.P, d.E), part, (int)d.T, (int)d.K, (int)d.O, (int)d.G, stream);
+    }
     if (err == hipSuccess)
       err = launch_combine(reinterpret_cast<const float*>(base + L.part), b.slot_of_pair, p, shared, y, (int)d.T,
                            (int)d.K, (int)d.O, dtype, stream);
@@ -220,7 +250,7 @@ int linear_alloc(const void* x, const uint8_t* packed, const uint8_t* scales, co
   if (st != MXFP4_OK || d.T == 0) return st;
   const int path = select_path(d, dtype, 0);
   if (path < 0) return path;
-  const size_t bytes = layout(d, path).total;
+  const size_t bytes = layout(d, path, dtype).total;
   st = check_device();
   if (st != MXFP4_OK) return st;
   void* ws = nullptr;
@@ -739,7 +769,7 @@ int mxfp4_moe_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t
   if (st != MXFP4_OK) return st;
   const int path = select_path(d, dtype, flags);
   if (path < 0) return path;
-  *bytes = (T == 0) ? 0 : layout(d, path).total;
+  *bytes = (T == 0) ? 0 : layout(d, path, dtype).total;
   return MXFP4_OK;
 }
 
@@ -832,6 +862,16 @@ int mxfp4_decode_rows(const uint8_t* packed, const uint8_t* scales, int64_t E, i
   if (st != MXFP4_OK) return st;
   const int64_t row = e * O + row0;
   return hip_status(launch_decode_rows(packed + row * G * 16, scales + row * G, nrows, G, dtype, out, stream));
+}
+
+int mxfp4_stream_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t stream) {
+  if (bytes == 0) return MXFP4_OK;
+  if (!buf || !sink || !aligned(buf, 16) || bytes % 16 != 0 || blocks < 0 || blocks > 65536 ||
+      bytes > ((size_t)1 << 40))
+    return MXFP4_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != MXFP4_OK) return st;
+  return hip_status(launch_stream_read(buf, (int64_t)bytes, blocks, sink, stream));
 }
 
 const char* mxfp4_status_string(int status) {

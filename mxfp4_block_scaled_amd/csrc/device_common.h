@@ -149,6 +149,19 @@ __device__ __forceinline__ void decode8_f32_unscaled(uint32_t w, float out[8]) {
   out[4] = c.x; out[5] = c.y; out[6] = d.x; out[7] = d.y;
 }
 
+// fp32 -> three bf16 (bit patterns) with f = x0 + x1 + x2 exactly: each
+// piece keeps the top 8 significant bits of what is left, and the
+// subtractions are exact (both operands share sign and exponent range).
+__device__ __forceinline__ void split3(float f, uint32_t& b0, uint32_t& b1, uint32_t& b2) {
+  const uint32_t u = __float_as_uint(f);
+  const float r1 = f - __uint_as_float(u & 0xffff0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+  b0 = u >> 16;
+  b1 = u1 >> 16;
+  b2 = __float_as_uint(r2) >> 16;
+}
+
 // Sum over the 64 lanes of a wave in a fixed butterfly order. Every lane
 // gets the same bits, so the result is deterministic.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -24,6 +24,30 @@
 // Waves are 2 x 2 over the 128 x 128 tile; each owns 64 x 64 = 2 x 2 MFMA
 // tiles (a 32-row sub-tile past the segment's end is skipped). Loads of the
 // next stage overlap the MFMAs of the current one.
+//
+// fp32 activations (NP = 3): the host splits every value exactly into three
+// bf16 pieces, x = x0 + x1 + x2 (each piece the top 8 significant bits of
+// what is left), stored as three planes of the activation array. The kernel
+// stages all three and multiplies each decoded weight fragment by each piece
+// into one fp32 accumulator: every product is exact. To keep the fp32 sum
+// of I = 32G products within the fp32 bar for outputs near zero, the MFMA
+// accumulator holds only the sum of one chunk of 128 inputs (two stages) and
+// is then added into a running (hi, lo) pair with an error-free TwoSum
+// (Knuth: s = hi + a, e = (hi - (s - (s - hi))) + (a - (s - hi))), so the
+// error is that of the short chunk sums.
+//
+// Large scale bytes. E2M1 * 2^(s-127) exceeds the bf16 range for s >= 253
+// (|code value| >= 4 at 253, >= 2 at 254, >= 1 at 255), while the layer's
+// value stays finite. A wave that meets such a scale byte (a wave-uniform
+// test, never true on ordinary data) switches for the rest of its tile to
+// decoding every group at scale byte s - 3 (0 for s < 3) and multiplies its
+// accumulators by 2^-3 once; at the end it multiplies them by 2^3. Power of
+// two scaling commutes with the exact products and the fp32 sums, so the
+// result is the exact layer's up to fp32 rounding, as on the decode-shaped
+// path; the only approximation is in a tile that mixes such bytes with scale
+// bytes 0..2, whose weights (below 2^-121 in magnitude) are read at 2^-124.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,6 +64,8 @@ constexpr int kScGroups = 16;                   // scale bytes per row and chunk
 constexpr int kScStages = kScGroups / 2;        // stages per chunk
 constexpr int kScPitch = 5;                     // dwords per LDS row of a chunk (16 bytes at offset 0..3)
 constexpr int kScSlots = (kGemmTileN * kScPitch + 255) / 256;
+constexpr uint32_t kShiftFrom = 253;  // scale bytes whose decoded weights may overflow bf16
+constexpr uint32_t kShift = 3;        // scale-byte shift of a wave that met one
 static_assert(kGemmTileN * kScPitch <= 1020, "q / 5 by multiply-shift");
 
 // What the kernel's rows and columns are:
@@ -56,14 +82,15 @@ static_assert(kGemmTileN * kScPitch <= 1020, "q / 5 by multiply-shift");
 //           fp32 part rows.
 enum GemmMode { kGather = 0, kSwiGLU = 1, kDirect = 2 };
 
-template <int MODE>
-__global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __restrict__ x,
+template <int MODE, int NP>
+__global__ void __launch_bounds__(256, NP == 1 ? 3 : 1) gemm_bf16_kernel(const uint16_t* __restrict__ x,
                                                            const uint8_t* __restrict__ packed,
                                                            const uint8_t* __restrict__ scales,
                                                            const int32_t* __restrict__ perm,
                                                            const GemmTile* __restrict__ tiles,
                                                            const int32_t* __restrict__ n_tiles, void* __restrict__ out,
-                                                           int K, int O, int G, int n_ntiles, uint32_t x_bytes, int F) {
+                                                           int K, int O, int G, int n_ntiles, uint32_t x_bytes, int F,
+                                                           uint32_t plane_bytes) {
   const int ti = blockIdx.x / n_ntiles;
   const int nt = blockIdx.x - ti * n_ntiles;
   if (ti >= n_tiles[0]) return;
@@ -80,7 +107,7 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
     }
   };
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * A_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NP][MT * A_LD];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][NT * B_LD];
   __shared__ __attribute__((aligned(16))) uint32_t Sc[NT * kScPitch];  // scale chunk: row r at dword kScPitch r
 
@@ -147,30 +174,58 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
   }
   const uint8_t* scb = reinterpret_cast<const uint8_t*>(Sc);
 
-  u32x4 ra[4], rb;
+  u32x4 ra[NP][4], rb;
   auto gload = [&](int st) {
     const int g0 = 2 * st;
     // past G: the sign bit of G - 1 - group moves the offset past the resource
     const uint32_t past = (uint32_t)(G - 1 - (g0 + ((tid & 7) >> 2))) >> 31 << 31;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((a_off[i] + 128u * st) | past), 0, 0));
+    for (int pc = 0; pc < NP; pc++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        ra[pc][i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((a_off[i] + plane_bytes * pc + 128u * st) | past), 0, 0));
     const uint32_t bpast = (uint32_t)(G - 1 - (g0 + (tid & 1))) >> 31 << 31;
     rb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((b_off + 32u * st) | bpast), 0, 0));
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      *reinterpret_cast<u32x4*>(&As[buf][((tid >> 3) + 32 * i) * A_LD + (tid & 7) * 8]) = ra[i];
+    for (int pc = 0; pc < NP; pc++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        *reinterpret_cast<u32x4*>(&As[buf][pc][((tid >> 3) + 32 * i) * A_LD + (tid & 7) * 8]) = ra[pc][i];
     *reinterpret_cast<u32x4*>(&Bs[buf][(tid >> 1) * B_LD + (tid & 1) * 16]) = rb;
   };
 
   f32x16 acc[2][2];
+  f32x16 hi[NP == 3 ? 2 : 1][2], lo[NP == 3 ? 2 : 1][2];  // fp32 activations: the compensated total
 #pragma unroll
   for (int a = 0; a < 2; a++)
 #pragma unroll
     for (int b = 0; b < 2; b++) acc[a][b] = f32x16{};
+  if constexpr (NP == 3) {
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int b = 0; b < 2; b++) hi[a][b] = lo[a][b] = f32x16{};
+  }
+  // fp32 activations: add the chunk sums to (hi, lo) without rounding error, restart the chunk
+  auto fold = [&]() {
+    if constexpr (NP == 3) {
+#pragma unroll
+      for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+          const f32x16 sum = hi[a][b] + acc[a][b];
+          const f32x16 bp = sum - hi[a][b];
+          lo[a][b] += (hi[a][b] - (sum - bp)) + (acc[a][b] - bp);
+          hi[a][b] = sum;
+          acc[a][b] = f32x16{};
+        }
+    }
+  };
 
+  bool shifted = false;  // wave-uniform: decoding at scale byte s - kShift
   const int nst = (G + 1) / 2;
   gload(0);
   sc_load(0);
@@ -183,48 +238,70 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
     if (st + 1 < nst) gload(st + 1);
     if (sst == 0 && st / kScStages + 1 < nchunk) sc_load(st / kScStages + 1);
     u32x4 wv[2];
-    float sc[2];
-    bool s255[2];
+    uint32_t sb[2];
 #pragma unroll
     for (int nj = 0; nj < 2; nj++) {
       const int nl = 64 * wn + 32 * nj + lm;
       wv[nj] = *reinterpret_cast<const u32x4*>(&Bs[buf][nl * B_LD + lq * 16]);
       // a group past G (odd G, last stage) has zero weights; its byte is unused
-      const uint32_t sb = scb[s_row[nj] + 2 * sst + lq];
-      sc[nj] = e8m0_operand(sb);
-      s255[nj] = sb == 255;
+      sb[nj] = scb[s_row[nj] + 2 * sst + lq];
     }
-    // a scale byte of 255 anywhere in the wave (never on ordinary data): those lanes decode exactly
-    const bool slow = __ballot(s255[0] | s255[1]) != 0;
+    // a scale byte from kShiftFrom up anywhere in the wave (never on ordinary data)
+    if (!shifted && __ballot(sb[0] >= kShiftFrom || sb[1] >= kShiftFrom) != 0) {
+      shifted = true;
+#pragma unroll
+      for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+          acc[a][b] *= 0.125f;
+          if constexpr (NP == 3) {
+            hi[a][b] *= 0.125f;
+            lo[a][b] *= 0.125f;
+          }
+        }
+    }
+    float sc[2];
+#pragma unroll
+    for (int nj = 0; nj < 2; nj++)
+      sc[nj] = e8m0_operand(!shifted ? sb[nj] : (sb[nj] > kShift ? sb[nj] - kShift : 0u));
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       bf16x8 bw[2];
 #pragma unroll
-      for (int nj = 0; nj < 2; nj++) {
-        bw[nj] = decode8_bf16x8(wv[nj][j], sc[nj]);
-        if (__builtin_expect(slow, 0) && s255[nj]) {
-          uint32_t t[4];
-          decode8_bf16_slow(wv[nj][j], 255u, t);
-          bw[nj] = __builtin_bit_cast(bf16x8, (u32x4{t[0], t[1], t[2], t[3]}));
-        }
-      }
+      for (int nj = 0; nj < 2; nj++) bw[nj] = decode8_bf16x8(wv[nj][j], sc[nj]);
 #pragma unroll
       for (int mi = 0; mi < 2; mi++) {
         if (64 * wm + 32 * mi >= tl.mlen) continue;  // a 32-row sub-tile past the segment
         const int ml = 64 * wm + 32 * mi + lm;
-        const u32x4 av = *reinterpret_cast<const u32x4*>(&As[buf][ml * A_LD + lq * 32 + j * 8]);
 #pragma unroll
-        for (int nj = 0; nj < 2; nj++)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bw[nj], acc[mi][nj],
-                                                                0, 0, 0);
+        for (int pc = 0; pc < NP; pc++) {
+          const u32x4 av = *reinterpret_cast<const u32x4*>(&As[buf][pc][ml * A_LD + lq * 32 + j * 8]);
+#pragma unroll
+          for (int nj = 0; nj < 2; nj++)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bw[nj],
+                                                                  acc[mi][nj], 0, 0, 0);
+        }
       }
     }
+    if (NP == 3 && ((st & 1) || st + 1 == nst)) fold();
     if (st + 1 < nst) sstore(buf ^ 1);
     __syncthreads();
     if (sst == kScStages - 1 && st + 1 < nst) {  // every wave is past the chunk's last stage
       sc_store();
       __syncthreads();
     }
+  }
+  if constexpr (NP == 3) {
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int b = 0; b < 2; b++) acc[a][b] = hi[a][b] + lo[a][b];
+  }
+  if (shifted) {
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int b = 0; b < 2; b++) acc[a][b] *= 8.0f;
   }
   // D layout of the 32x32 MFMA: element i of lane l is row 8(i/4) + 4(l/32) + i%4, column l%32.
   if constexpr (MODE == kSwiGLU) {
@@ -265,45 +342,80 @@ __global__ void __launch_bounds__(256, 3) gemm_bf16_kernel(const uint16_t* __res
 
 }  // namespace
 
-bool gemm_supported(int64_t T, int64_t O, int64_t G) {
-  // 32-bit byte offsets into the activations and into one expert's packed bytes
-  return T * 64 * G < ((int64_t)1 << 31) && O * G * 16 < ((int64_t)1 << 31);
+bool gemm_supported(int64_t T, int64_t O, int64_t G, int np) {
+  // 32-bit byte offsets into the activations (np planes) and into one expert's packed bytes
+  return np * T * 64 * G < ((int64_t)1 << 31) && O * G * 16 < ((int64_t)1 << 31);
 }
 
 namespace {
-template <int MODE>
+template <int MODE, int NP>
 hipError_t launch_mode(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                        const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, void* out, int64_t x_rows,
                        int K, int O, int G, int F, int n_ntiles, hipStream_t stream) {
-  if (!gemm_supported(x_rows, O, G)) return hipErrorInvalidValue;
+  if (!gemm_supported(x_rows, O, G, NP)) return hipErrorInvalidValue;
   const int64_t nblk = max_tiles * n_ntiles;
   if (nblk <= 0) return hipSuccess;
-  const uint32_t x_bytes = (uint32_t)(x_rows * 64 * G);
-  hipLaunchKernelGGL(gemm_bf16_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, stream, x, packed, scales, perm, tiles,
-                     n_tiles, out, K, O, G, n_ntiles, x_bytes, F);
+  const uint32_t plane = (uint32_t)(x_rows * 64 * G);
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, NP>), dim3((unsigned)nblk), dim3(256), 0, stream, x, packed, scales, perm,
+                     tiles, n_tiles, out, K, O, G, n_ntiles, NP * plane, F, plane);
   return hipGetLastError();
+}
+
+// fp32 activations -> three bf16 planes (plane j holds piece j of every
+// value), four values per thread
+__global__ void __launch_bounds__(256) split3_kernel(const u32x4* __restrict__ x, uint32_t* __restrict__ xs,
+                                                     int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const u32x4 v = x[i];
+    uint32_t b[3][4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) split3(__uint_as_float(v[c]), b[0][c], b[1][c], b[2][c]);
+#pragma unroll
+    for (int pc = 0; pc < 3; pc++) {
+      uint32_t* dst = xs + 2 * (pc * n4 + i);
+      dst[0] = b[pc][0] | (b[pc][1] << 16);
+      dst[1] = b[pc][2] | (b[pc][3] << 16);
+    }
+  }
 }
 }  // namespace
 
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                             const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
                             int O, int G, hipStream_t stream) {
-  return launch_mode<kGather>(x, packed, scales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0,
-                              (O + NT - 1) / NT, stream);
+  return launch_mode<kGather, 1>(x, packed, scales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0,
+                                 (O + NT - 1) / NT, stream);
+}
+
+hipError_t launch_split3(const float* x, int64_t n, uint16_t* xs, hipStream_t stream) {
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(split3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(x),
+                     reinterpret_cast<uint32_t*>(xs), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const uint16_t* xs, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
+                           const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
+                           int O, int G, hipStream_t stream) {
+  return launch_mode<kGather, 3>(xs, packed, scales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0,
+                                 (O + NT - 1) / NT, stream);
 }
 
 hipError_t launch_gemm_swiglu(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales,
                               const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
                               uint16_t* h, int T, int K, int F, int G, hipStream_t stream) {
-  return launch_mode<kSwiGLU>(x, gu_packed, gu_scales, perm, tiles, n_tiles, max_tiles, h, T, K, 2 * F, G, F,
-                              (F + NT / 2 - 1) / (NT / 2), stream);
+  return launch_mode<kSwiGLU, 1>(x, gu_packed, gu_scales, perm, tiles, n_tiles, max_tiles, h, T, K, 2 * F, G, F,
+                                 (F + NT / 2 - 1) / (NT / 2), stream);
 }
 
 hipError_t launch_gemm_direct(const uint16_t* h, const uint8_t* packed, const uint8_t* scales, const GemmTile* tiles,
                               const int32_t* n_tiles, int64_t max_tiles, float* part, int64_t P, int O, int G,
                               hipStream_t stream) {
-  return launch_mode<kDirect>(h, packed, scales, nullptr, tiles, n_tiles, max_tiles, part, P, 1, O, G, 0,
-                              (O + NT - 1) / NT, stream);
+  return launch_mode<kDirect, 1>(h, packed, scales, nullptr, tiles, n_tiles, max_tiles, part, P, 1, O, G, 0,
+                                 (O + NT - 1) / NT, stream);
 }
 
 }  // namespace mxfp4

@@ -44,10 +44,15 @@
 // and prepared tiles past O read through an offset beyond their buffer
 // resource: zeros, no memory traffic.
 //
-// A scale byte of 255 (2^128) would make the convert return NaN: such a
-// lane's codes are rewritten (under a wave-uniform branch that ordinary
-// data never takes) to twice their magnitude at scale 254, which gives the
-// same bf16 values - E2M1 x 2^128 is 2^127 for 0.5 and +-inf from 1 up.
+// Large scale bytes: E2M1 * 2^(s-127) leaves the bf16 range for s >= 253
+// while the layer's value stays finite. A wave that meets such a byte (a
+// wave-uniform test that ordinary data never passes) decodes from then on
+// at scale byte s - 3 (0 for s < 3), having multiplied its accumulators by
+// 2^-3, and multiplies them by 2^3 at the end: power-of-two scaling commutes
+// with the exact products and the fp32 sums, so the result is the exact
+// layer's up to fp32 rounding (weights with scale bytes 0..2 in such a tile,
+// below 2^-121 in magnitude, are read at 2^-124). This also keeps scale byte
+// 255, which the convert reads as NaN, away from the convert.
 #include <type_traits>
 
 #include "device_common.h"
@@ -75,18 +80,8 @@ constexpr int kXDma = kXBytes / (1024 * kWaves);  // 1 KB requests per wave and 
 constexpr int kWDma = kWBytes / (1024 * kWaves);
 constexpr int kScLoads = 2;                        // scale dwords per wave and chunk
 
-// codes of a lane whose scale byte is 255: magnitude m -> the code of 2 m at
-// scale 254 (0 -> 0, 0.5 -> 1, 1 -> 2, 1.5 -> 3, 2 -> 4, 3 and up -> 6, which
-// overflows to inf like every value from 2^128 up)
-__device__ __forceinline__ uint32_t double_codes(uint32_t w) {
-  uint32_t r = 0;
-#pragma unroll
-  for (int n = 0; n < 8; n++) {
-    const uint32_t c = (w >> (4 * n)) & 15u;
-    r |= (((0x77765420u >> (4 * (c & 7u))) & 7u) | (c & 8u)) << (4 * n);
-  }
-  return r;
-}
+constexpr uint32_t kShiftFrom = 253;  // scale bytes whose decoded weights may overflow bf16
+constexpr uint32_t kShift = 3;        // scale-byte shift of a wave that met one
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -204,6 +199,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   for (int i = 0; i < kWI; i++)
 #pragma unroll
     for (int j = 0; j < kWJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  bool shifted = false;  // wave-uniform: decoding at scale byte s - kShift
 
   // One chunk q, activation slot q mod 2 and weight slot q mod 3 (both
   // compile-time): request the activations of chunk q + 1 (into the slot read
@@ -223,16 +219,23 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
     if (live) {
       uint32_t sb[kWI];
-      bool s255 = false;
+      bool big = false;
 #pragma unroll
       for (int i = 0; i < kWI; i++) {
         sb[i] = (wsp[RW][i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        s255 |= sb[i] == 255u;
+        big |= sb[i] >= kShiftFrom;
       }
-      const bool slow = __ballot(s255) != 0;
+      if (!shifted && __ballot(big) != 0) {
+        shifted = true;
+#pragma unroll
+        for (int i = 0; i < kWI; i++)
+#pragma unroll
+          for (int j = 0; j < kWJ; j++) acc[i][j] *= 0.125f;
+      }
       float sc[kWI];
 #pragma unroll
-      for (int i = 0; i < kWI; i++) sc[i] = e8m0_operand(sb[i] == 255u ? 254u : sb[i]);
+      for (int i = 0; i < kWI; i++)
+        sc[i] = e8m0_operand(!shifted ? sb[i] : (sb[i] > kShift ? sb[i] - kShift : 0u));
 #pragma unroll
       for (int s = 0; s < 4; s++) {
         bf16x8 b[kWJ];
@@ -245,12 +248,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
         // dword s of this lane's slot of each fragment (8 codes each): blocks s and 4 + s of tile wn
         const u32x4 lo = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + s) * 1024 + 16 * lane]);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + 4 + s) * 1024 + 16 * lane]);
-        uint32_t raw[kWI] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (__builtin_expect(slow, 0)) {
-#pragma unroll
-          for (int i = 0; i < kWI; i++)
-            if (sb[i] == 255u) raw[i] = double_codes(raw[i]);
-        }
+        const uint32_t raw[kWI] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int i = 0; i < kWI; i++) {
           const bf16x8 a = decode8_bf16x8(raw[i], sc[i]);
@@ -287,6 +285,12 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   if (q + 3 < nq) step(q + 3, C1{}, C0{});
   if (q + 4 < nq) step(q + 4, C0{}, C1{});
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
+  if (shifted) {
+#pragma unroll
+    for (int i = 0; i < kWI; i++)
+#pragma unroll
+      for (int j = 0; j < kWJ; j++) acc[i][j] *= 8.0f;
+  }
 
   // lane (lr, lc) of MFMA tile (i, j): pair 64 wm + 16 j + lr, rows 4 lc .. 4 lc + 3 of fragment i
   if constexpr (MODE == kSwiGLU) {

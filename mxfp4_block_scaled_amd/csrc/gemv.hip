@@ -59,19 +59,6 @@ constexpr uint32_t kOobGroup = 0x08000000u;   // group offset beyond any expert'
 constexpr uint32_t kOob32 = 0x80000000u;      // byte offset beyond any resource
 constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
 
-// fp32 -> three bf16 (bit patterns) with f = x0 + x1 + x2 exactly: each
-// piece keeps the top 8 significant bits of what is left, and the
-// subtractions are exact (both operands share sign and exponent range).
-__device__ __forceinline__ void split3(float f, uint32_t& b0, uint32_t& b1, uint32_t& b2) {
-  const uint32_t u = __float_as_uint(f);
-  const float r1 = f - __uint_as_float(u & 0xffff0000u);
-  const uint32_t u1 = __float_as_uint(r1);
-  const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
-  b0 = u >> 16;
-  b1 = u1 >> 16;
-  b2 = __float_as_uint(r2) >> 16;
-}
-
 template <bool XF32, bool PREP>
 __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
@@ -433,21 +420,13 @@ hipError_t launch_decode(const void* x, const uint8_t* packed, const uint8_t* sc
   const int nb = bits_for_experts(E);
   const dim3 grid((O + kRows - 1) / kRows);
   if (dtype == 0) {
-    static bool attr = false;  // large LDS needs the opt-in once per kernel
-    if (!attr) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<true, PREP>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
-      attr = true;
-    }
+    const hipError_t attr = allow_dynamic_lds<&decode_fused_kernel<true, PREP>>(kDecodeMaxLds);
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((decode_fused_kernel<true, PREP>), grid, dim3(kDecThreads), lds, stream, x, packed, scales, sel,
                        p, shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
   } else {
-    static bool attr = false;
-    if (!attr) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused_kernel<false, PREP>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
-      attr = true;
-    }
+    const hipError_t attr = allow_dynamic_lds<&decode_fused_kernel<false, PREP>>(kDecodeMaxLds);
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((decode_fused_kernel<false, PREP>), grid, dim3(kDecThreads), lds, stream, x, packed, scales,
                        sel, p, shared, y, T, E, O, G, K, S, nb, n_invalid, chunk_index);
   }

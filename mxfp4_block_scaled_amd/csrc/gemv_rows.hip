@@ -442,12 +442,8 @@ template <bool XF32, int L, int NW>
 hipError_t launch_rows_nw(const RowsPlan& pl, size_t lds, const void* x, const uint8_t* packed, const uint8_t* scales,
                        const int32_t* sel, const float* p, const void* shared, void* y, int T, int E, int O, int G,
                        int K, int32_t* n_invalid, int chunk_index, hipStream_t stream) {
-  static bool attr = false;  // large LDS needs the opt-in once per kernel
-  if (!attr) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_rows_kernel<XF32, L, NW>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
-    attr = true;
-  }
+  const hipError_t attr = allow_dynamic_lds<&gemv_rows_kernel<XF32, L, NW>>(kDecodeMaxLds);
+  if (attr != hipSuccess) return attr;
   const dim3 grid((O + pl.R - 1) / pl.R);
   hipLaunchKernelGGL((gemv_rows_kernel<XF32, L, NW>), grid, dim3(NW * 64), lds, stream, x, packed, scales, sel, p,
                      shared, y, T, E, O, G, K, pl.S, pl.gs, bits_for(E), n_invalid, chunk_index);

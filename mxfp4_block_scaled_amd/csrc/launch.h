@@ -6,7 +6,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace mxfp4 {
+
+// Let KERNEL use `bytes` of dynamic LDS (beyond the default limit): the
+// attribute is set once per device, from whichever host thread gets there
+// first, and every later call returns that call's status.
+constexpr int kMaxDevices = 64;
+template <auto* KERNEL>
+hipError_t allow_dynamic_lds(int bytes) {
+  static std::once_flag once[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    status[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(KERNEL),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  });
+  return status[dev];
+}
 
 // Largest number of pairs (T*K) one fused decode-shaped launch handles
 // (one per lane of a wave).
@@ -82,6 +101,15 @@ hipError_t launch_gemv_rows(const void* x, const uint8_t* packed, const uint8_t*
                             const float* p, const void* shared, void* y, int T, int E, int O, int G, int K, int dtype,
                             int32_t* n_invalid, int chunk_index, hipStream_t stream);
 
+// One-token decode-shaped kernel (activations in registers): T = 1, any K
+// up to kMaxFusedPairs, G <= 256, O * G * 16 < 2^31; n_cu = the device's
+// compute units (the grid is sized from it). n_invalid (may be null)
+// receives the number of out-of-range indices.
+bool gemv_one_supported(int O, int G, int K);
+hipError_t launch_gemv_one(const void* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                           const float* p, const void* shared, void* y, int E, int O, int G, int K, int dtype,
+                           int32_t* n_invalid, int n_cu, hipStream_t stream);
+
 // ---- block-scaled variant: MXFP8 activations x MXFP4 weights on the scaled MFMA.
 // Activation rows are padded to mx_row_bytes(I) = 128 * ceil(I / 128) codes.
 int mx_row_bytes(int64_t I);
@@ -114,12 +142,21 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
                         int32_t* sel, float* p, hipStream_t stream, int lanes = 0);
 
 // ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
-// The grouped GEMM addresses the activations and one expert's packed bytes
-// with 32-bit byte offsets: T * 32G * 2 < 2^31 and O * G * 16 < 2^31.
-bool gemm_supported(int64_t T, int64_t O, int64_t G);
+// The grouped GEMM addresses the activations (np bf16 planes of T x 32G) and
+// one expert's packed bytes with 32-bit byte offsets: np * T * 32G * 2 < 2^31
+// and O * G * 16 < 2^31.
+bool gemm_supported(int64_t T, int64_t O, int64_t G, int np = 1);
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
                             const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
                             int O, int G, hipStream_t stream);
+// fp32 activations: launch_split3 writes the exact three-piece bf16 split of
+// the n (a multiple of 4) values of x as three planes of n (xs: 3n bf16);
+// launch_gemm_f32 is launch_gemm_bf16 on those planes (every weight fragment
+// multiplied by all three pieces into one fp32 accumulator).
+hipError_t launch_split3(const float* x, int64_t n, uint16_t* xs, hipStream_t stream);
+hipError_t launch_gemm_f32(const uint16_t* xs, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
+                           const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T, int K,
+                           int O, int G, hipStream_t stream);
 // The same on weights in the prepared layout of launch_prepare_mx (pcodes:
 // its code slots, pscales: its scale array), decoded in registers (8-wave
 // workgroups over 128 pairs x 512 rows); needs gemm_regdec_supported:
@@ -151,6 +188,11 @@ hipError_t launch_gemm_direct(const uint16_t* h, const uint8_t* packed, const ui
 hipError_t launch_combine(const float* part, const int32_t* slot_of_pair, const float* p,
                           const void* shared, void* y, int T, int K, int O, int dtype,
                           hipStream_t stream);
+
+// ---- plain streaming read of `bytes` (a multiple of 16) from a 16-byte
+// aligned buffer; `blocks` workgroups of 256 threads (0: up to 2048); sink
+// holds one uint32 per workgroup and is written only by a 2^-32 chance.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int blocks, uint32_t* sink, hipStream_t stream);
 
 // ---- exported decode (test and inspection)
 hipError_t launch_decode_rows(const uint8_t* packed_rows, const uint8_t* scales_rows, int64_t nrows,

@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES)
@@ -70,15 +70,25 @@ def test_workspace_sizes_host_only():
 def test_path_selection():
     f32, bf16 = _abi.DTYPE_F32, _abi.DTYPE_BF16
     assert _abi.select_path(1, 128, 5760, 90, 4, f32) == _abi.PATH_GEMV
+    # the decode-shaped path while one fused launch takes every pair (at most
+    # 64 pairs, activations in LDS), the grouped GEMM past that
     assert _abi.select_path(8, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMV
-    assert _abi.select_path(16, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMV
-    assert _abi.select_path(17, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMM
+    assert _abi.select_path(9, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMM
+    assert _abi.select_path(16, 384, 4096, 224, 8, bf16) == _abi.PATH_GEMM
+    assert _abi.select_path(16, 128, 5760, 90, 4, bf16) == _abi.PATH_GEMV
+    assert _abi.select_path(17, 128, 5760, 90, 4, bf16) == _abi.PATH_GEMM
+    assert _abi.select_path(64, 128, 5760, 2, 1, bf16) == _abi.PATH_GEMV
+    assert _abi.select_path(65, 128, 5760, 2, 1, bf16) == _abi.PATH_GEMM
     assert _abi.select_path(4096, 128, 5760, 90, 4, bf16) == _abi.PATH_GEMM
-    assert _abi.select_path(4096, 128, 5760, 90, 4, f32) == _abi.PATH_GEMV
+    assert _abi.select_path(4096, 128, 5760, 90, 4, f32) == _abi.PATH_GEMM
     assert _abi.select_path(8, 384, 4096, 224, 8, bf16, _abi.FLAG_FORCE_GEMM) == _abi.PATH_GEMM
     assert _abi.select_path(4096, 128, 5760, 90, 4, bf16, _abi.FLAG_FORCE_GEMV) == _abi.PATH_GEMV
+    assert _abi.select_path(4096, 128, 5760, 90, 4, f32, _abi.FLAG_FORCE_GEMV) == _abi.PATH_GEMV
+    assert _abi.select_path(4, 4, 32, 2, 2, f32, _abi.FLAG_FORCE_GEMM) == _abi.PATH_GEMM
+    # fp32 activations: the grouped GEMM reads three bf16 planes of them
+    assert _abi.select_path(5000, 8, 64, 1 << 11, 1, bf16, _abi.FLAG_FORCE_GEMM) == _abi.PATH_GEMM
     with pytest.raises(_abi.Mxfp4Error) as e:
-        _abi.select_path(4, 4, 32, 2, 2, f32, _abi.FLAG_FORCE_GEMM)
+        _abi.select_path(5500, 8, 64, 1 << 11, 1, f32, _abi.FLAG_FORCE_GEMM)
     assert e.value.status == _abi.ERR_UNSUPPORTED
     with pytest.raises(_abi.Mxfp4Error) as e:
         _abi.select_path(4, 4, 32, 2, 2, bf16, _abi.FLAG_FORCE_GEMM | _abi.FLAG_FORCE_GEMV)
@@ -126,8 +136,17 @@ def test_workspace_too_small_rejected():
     assert _ex(T=4096, E=128, O=64, G=2, K=4, dtype=1, ws_bytes=1024, **kw) == _abi.ERR_WORKSPACE_TOO_SMALL
 
 
-def test_fp32_forced_gemm_unsupported():
-    assert _ex(flags=_abi.FLAG_FORCE_GEMM) == _abi.ERR_UNSUPPORTED
+def test_fp32_forced_gemm_workspace_holds_the_activation_planes():
+    # fp32 activations on the grouped GEMM: the workspace also holds their
+    # three bf16 planes (3 * T * I * 2 bytes) beside what the bf16 call needs
+    T, E, O, G, K = 300, 8, 64, 4, 2
+    f32 = _abi.workspace_size(T, E, O, G, K, _abi.DTYPE_F32, _abi.FLAG_FORCE_GEMM)
+    bf16 = _abi.workspace_size(T, E, O, G, K, _abi.DTYPE_BF16, _abi.FLAG_FORCE_GEMM)
+    assert f32 >= bf16 + 3 * T * 32 * G * 2
+    M = 1 << 28
+    kw = dict(x=1 * M, packed=2 * M, scales=3 * M, sel=4 * M, p=5 * M, shared=6 * M, y=7 * M, ws=8 * M)
+    assert _ex(T=T, E=E, O=O, G=G, K=K, dtype=0, flags=_abi.FLAG_FORCE_GEMM, ws_bytes=f32 - 1,
+               **kw) == _abi.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_empty_batch_is_a_no_op():
