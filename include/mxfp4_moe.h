@@ -162,6 +162,27 @@ int mxfp4_moe_linear_ex(const void* x, const uint8_t* packed, const uint8_t* sca
                         uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mxfp4_moe_linear_noalloc - mxfp4_moe_linear_ex (same arguments, dtype,
+ * flags, results and errors) without a workspace argument and without any
+ * allocation, for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). It works in
+ * a scratch array the library holds in device memory, one copy per device
+ * (MXFP4_NOALLOC_SCRATCH_BYTES, kept until the process ends); its address is
+ * looked up once per device on the first call there. Calls whose workspace
+ * (mxfp4_moe_workspace_size) exceeds the array return
+ * MXFP4_ERR_WORKSPACE_TOO_SMALL before anything is enqueued: every
+ * decode-shaped call fits, prefill-shaped calls up to about
+ * T * K * O * 4 = 30 MB of partial rows. All calls on one device share its
+ * array, so calls that overlap on one device (two streams, two host threads)
+ * race; order them, or use mxfp4_moe_linear_ex with workspaces of their own.
+ */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mxfp4_moe_linear_noalloc(const void* x, const uint8_t* packed, const uint8_t* scales,
+                             const int32_t* sel, const float* p, const void* shared, void* y,
+                             int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, int dtype,
+                             uint32_t flags, hipStream_t stream);
+
+/*
  * mxfp4_moe_select_path - which path the _ex call takes for these sizes,
  * dtype and flags: MXFP4_PATH_GEMV or MXFP4_PATH_GEMM, or a negative
  * mxfp4_status. Host-only.

@@ -30,6 +30,8 @@ FLAG_GEMV_MFMA = 0x8
 FLAG_BUCKET_ONE_BLOCK = 0x10
 FLAG_BUCKET_MULTI_BLOCK = 0x20
 
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
 MAX_EXPERTS = 8192
 MAX_PAIRS = 1 << 26
 
@@ -53,6 +55,7 @@ SIGNATURES = {
     "mxfp4_moe_linear_bf16": (_int, [_vp] * 7 + [_i64] * 5 + [_vp]),
     "mxfp4_moe_workspace_size": (_int, [_i64] * 5 + [_int, _u32, ctypes.POINTER(_sz)]),
     "mxfp4_moe_linear_ex": (_int, [_vp] * 7 + [_i64] * 5 + [_int, _u32, _vp, _sz, _vp]),
+    "mxfp4_moe_linear_noalloc": (_int, [_vp] * 7 + [_i64] * 5 + [_int, _u32, _vp]),
     "mxfp4_moe_select_path": (_int, [_i64] * 5 + [_int, _u32]),
     "mxfp4_moe_bucket_workspace_size": (_int, [_i64] * 3 + [_u32, ctypes.POINTER(_sz)]),
     "mxfp4_moe_bucket": (_int, [_vp] + [_i64] * 3 + [_vp] * 5 + [_u32, _vp, _sz, _vp]),

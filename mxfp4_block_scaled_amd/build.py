@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmxfp4_moe.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-HIP_SOURCES = ["bucket.hip", "gemv.hip", "gemv_rows.hip", "gemv_one.hip", "gemm.hip", "combine.hip", "route.hip", "gemm_mx.hip", "gemm_regdec.hip", "stream.hip"]
+HIP_SOURCES = ["bucket.hip", "gemv.hip", "gemv_rows.hip", "gemv_one.hip", "gemm.hip", "combine.hip", "route.hip", "gemm_mx.hip", "gemm_regdec.hip", "stream.hip", "noalloc.hip"]
 HOST_SOURCES = ["api.cpp"]
 ARCH = "gfx950"
 
