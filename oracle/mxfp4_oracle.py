@@ -473,6 +473,56 @@ def route_sigmoid(logits, bias, K: int, scale: float = 1.0):
     return sel.astype(np.int32), route_weights(l, sel, "sigmoid", scale)
 
 
+def _group_scores(keys: np.ndarray, n_group: int) -> np.ndarray:
+    """(T, n_group): the sum of the two largest keys of each group of
+    E / n_group consecutive experts."""
+    T, E = keys.shape
+    two = -np.sort(-keys.reshape(T, n_group, E // n_group), axis=2)[:, :, :2]
+    return two[:, :, 0] + two[:, :, 1]
+
+
+def route_sigmoid_grouped(logits, bias, K: int, n_group: int, topk_group: int, scale: float = 1.0,
+                          renormalize: bool = True):
+    """Group-limited sigmoid router (the CPU kernels page, section 1, its
+    first router): the choice score of expert e is sigmoid(logit) + bias[e];
+    the E experts form n_group groups of E / n_group consecutive experts; a
+    group's score is the sum of its two largest choice scores; the topk_group
+    groups with the largest scores are kept (ties to the lower group index);
+    the K experts with the largest choice scores inside the kept groups are
+    chosen (descending, ties to the lower expert index); their weights are
+    gathered from the unbiased scores sigmoid(logit). Readings, the page
+    being silent: a NaN choice score counts as -inf everywhere (also in its
+    group's sum); with renormalize the gathered scores are divided by their
+    left-to-right sum + 1e-20 as the ungrouped sigmoid router does (the page
+    stops at the gather: renormalize=False), then times ``scale``. Needs
+    n_group | E, E / n_group >= 2, 1 <= topk_group <= n_group and
+    K <= topk_group * E / n_group. Returns (sel int32 [T, K], p float64)."""
+    l = _logits2d(logits, K)
+    T, E = l.shape
+    if n_group < 1 or E % n_group or E // n_group < 2 or not 1 <= topk_group <= n_group:
+        raise ValueError("need n_group | E, E / n_group >= 2 and 1 <= topk_group <= n_group")
+    eg = E // n_group
+    if K > topk_group * eg:
+        raise ValueError("K exceeds the experts of the kept groups")
+    keys = route_keys(l, bias, "sigmoid")
+    keys = np.where(np.isnan(keys), -np.inf, keys)
+    groups = _topk_desc(_group_scores(keys, n_group), topk_group)
+    kept = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(kept, groups, True, axis=1)
+    masked = np.where(np.repeat(kept, eg, axis=1), keys, -np.inf)
+    sel = np.empty((T, K), dtype=np.int64)
+    for t in range(T):  # the largest K of the kept experts; an -inf key may be chosen only inside a kept group
+        order = [e for e in np.argsort(-masked[t], kind="stable") if kept[t, e // eg]]
+        sel[t] = order[:K]
+    chosen = np.take_along_axis(_sigmoid(l), sel, axis=1)
+    if renormalize:
+        total = np.zeros((T, 1))
+        for k in range(K):  # left to right
+            total += chosen[:, k:k + 1]
+        chosen = chosen / (total + SIGMOID_EPS)
+    return sel.astype(np.int32), chosen * scale
+
+
 def route_scalar(logits, bias, K: int, mode: str, scale: float = 1.0):
     """Brute force with plain Python numbers (tiny shapes): repeated
     selection of the largest remaining key, lower index on ties."""
@@ -503,6 +553,56 @@ def route_scalar(logits, bias, K: int, mode: str, scale: float = 1.0):
         den = max(mass, SOFTMAX_MASS_FLOOR) if mode == "softmax" else mass + SIGMOID_EPS
         out_sel.append(sel)
         out_p.append([prob[e] / den * scale for e in sel])
+    return out_sel, out_p
+
+
+def route_grouped_scalar(logits, bias, K: int, n_group: int, topk_group: int, scale: float = 1.0,
+                         renormalize: bool = True):
+    """Brute force of route_sigmoid_grouped with plain Python numbers (tiny
+    shapes): group scores by scanning each group for its two largest scores,
+    then repeated selection of the largest remaining group and expert."""
+    import math
+    out_sel, out_p = [], []
+    for row in logits:
+        E = len(row)
+        eg = E // n_group
+        raw = [1.0 / (1.0 + math.exp(-float(v))) for v in row]
+        keys = [raw[e] + (0.0 if bias is None else float(bias[e])) for e in range(E)]
+        keys = [-math.inf if k != k else k for k in keys]
+        gscore = []
+        for g in range(n_group):
+            a = b = -math.inf
+            for e in range(g * eg, (g + 1) * eg):
+                if keys[e] > a:
+                    a, b = keys[e], a
+                elif keys[e] > b:
+                    b = keys[e]
+            gscore.append(a + b)
+        gleft, kept = list(range(n_group)), []
+        for _ in range(topk_group):
+            best = gleft[0]
+            for g in gleft[1:]:
+                if gscore[g] > gscore[best]:
+                    best = g
+            kept.append(best)
+            gleft.remove(best)
+        left = [e for e in range(E) if e // eg in kept]
+        sel = []
+        for _ in range(K):
+            best = left[0]
+            for e in left[1:]:
+                if keys[e] > keys[best]:
+                    best = e
+            sel.append(best)
+            left.remove(best)
+        w = [raw[e] for e in sel]
+        if renormalize:
+            mass = 0.0
+            for v in w:
+                mass += v
+            w = [v / (mass + SIGMOID_EPS) for v in w]
+        out_sel.append(sel)
+        out_p.append([v * scale for v in w])
     return out_sel, out_p
 
 

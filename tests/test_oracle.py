@@ -604,6 +604,82 @@ def test_router_planted_mistakes_are_caught(monkeypatch):
     assert not np.allclose(biased / biased.sum(1, keepdims=True), np.array(want_p2), rtol=1e-6)
 
 
+def test_grouped_router_worked_example():
+    """Eight experts in four pairs, all logits 0 (every unbiased score 1/2),
+    the bias alone ranks: choice scores 0.9 0.1 | 0.8 0.8 | 0.5 0.5 | 0 0.95.
+    Group scores (sum of the two best) 1.0, 1.6, 1.0, 0.95: the two kept
+    groups are 1 and then 0 (tied with 2, the lower index wins), so the best
+    expert overall (7, 0.95) is out; inside the kept groups the best two are
+    0 (0.9) and 2 (0.8, tied with 3). The weights are the unbiased scores
+    (1/2 each) over their sum: 1/2 each, times the scale."""
+    logits = np.zeros((1, 8))
+    bias = np.array([0.4, -0.4, 0.3, 0.3, 0.0, 0.0, -0.5, 0.45])
+    sel, p = oracle.route_sigmoid_grouped(logits, bias, 2, n_group=4, topk_group=2, scale=3.0)
+    assert sel.tolist() == [[0, 2]]
+    np.testing.assert_allclose(p, [[1.5, 1.5]], rtol=1e-15)
+    sel_raw, p_raw = oracle.route_sigmoid_grouped(logits, bias, 2, 4, 2, scale=3.0, renormalize=False)
+    assert sel_raw.tolist() == [[0, 2]]
+    np.testing.assert_allclose(p_raw, [[1.5, 1.5]], rtol=1e-15)  # the gathered scores 1/2, times 3
+    # scoring a group by its single best expert instead would keep groups 3 and 0
+    assert oracle.route_sigmoid(logits, bias, 2)[0].tolist() == [[7, 0]]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_grouped_router_brute_force_matches(seed):
+    rng = _rng(40 + seed)
+    E, n_group = [(16, 4), (24, 6), (12, 2), (32, 8)][seed]
+    logits = rng.standard_normal((7, E)) * 2
+    bias = rng.standard_normal(E) * 0.2
+    for topk_group, K, renorm in ((1, 2, True), (2, 3, False), (n_group, 4, True)):
+        sel, p = oracle.route_sigmoid_grouped(logits, bias, K, n_group, topk_group, 1.25, renorm)
+        s2, p2 = oracle.route_grouped_scalar(logits.tolist(), bias.tolist(), K, n_group, topk_group, 1.25, renorm)
+        assert sel.tolist() == s2
+        np.testing.assert_allclose(p, np.array(p2), rtol=1e-14)
+
+
+def test_grouped_router_special_cases():
+    rng = _rng(45)
+    logits = rng.standard_normal((9, 20)) * 1.5
+    bias = rng.standard_normal(20) * 0.1
+    # every group kept: the ungrouped sigmoid router
+    s_all, p_all = oracle.route_sigmoid_grouped(logits, bias, 5, n_group=5, topk_group=5, scale=2.0)
+    s_ref, p_ref = oracle.route_sigmoid(logits, bias, 5, scale=2.0)
+    assert np.array_equal(s_all, s_ref)
+    np.testing.assert_allclose(p_all, p_ref, rtol=1e-15)
+    # one group kept: every chosen expert lies in the group with the best two-score sum
+    sel, _ = oracle.route_sigmoid_grouped(logits, bias, 3, n_group=5, topk_group=1)
+    keys = 1.0 / (1.0 + np.exp(-logits)) + bias
+    two = -np.sort(-keys.reshape(9, 5, 4), axis=2)[:, :, :2].sum(2)
+    assert np.array_equal(sel // 4, np.repeat(two.argmax(1)[:, None], 3, axis=1))
+    # NaN logits read as -inf: never chosen while finite experts remain
+    bad = logits.copy()
+    bad[:, 0] = np.nan
+    sel, _ = oracle.route_sigmoid_grouped(bad, bias, 3, n_group=5, topk_group=2)
+    assert not np.any(sel == 0)
+
+
+def test_grouped_router_planted_mistakes_are_caught(monkeypatch):
+    rng = _rng(46)
+    logits = rng.standard_normal((12, 32)) * 2
+    bias = rng.standard_normal(32) * 0.3
+    want_s, want_p = oracle.route_grouped_scalar(logits.tolist(), bias.tolist(), 4, 8, 3, 1.0, True)
+    orig_keys = om.route_keys
+    mistakes = {
+        "group score = best expert only": lambda mp: mp.setattr(
+            om, "_group_scores", lambda k, n: k.reshape(k.shape[0], n, -1).max(axis=2)),
+        "unbiased ranking": lambda mp: mp.setattr(om, "route_keys", lambda l, b, m: orig_keys(l, None, m)),
+    }
+    for name, plant in mistakes.items():
+        with monkeypatch.context() as mp:
+            plant(mp)
+            s, _ = oracle.route_sigmoid_grouped(logits, bias, 4, 8, 3)
+            assert s.tolist() != want_s, f"planted mistake not caught: {name}"
+    # weights from the biased scores would differ from the brute force
+    keys = 1.0 / (1.0 + np.exp(-logits)) + bias
+    biased = np.take_along_axis(keys, np.array(want_s), 1)
+    assert not np.allclose(biased / biased.sum(1, keepdims=True), np.array(want_p), rtol=1e-6)
+
+
 @pytest.mark.parametrize("mode", ["softmax", "sigmoid"])
 def test_router_weights_of_any_selection_brute_force(mode):
     """route_weights on a selection that is not the top k (the GPU may pick
