@@ -466,6 +466,35 @@ int mxfp4_moe_route(const float* logits, const float* bias, int64_t T, int64_t E
  */
 int mxfp4_stream_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t stream);
 
+/*
+ * mxfp4_moe_route_grouped - the group-limited sigmoid router (page "MoE
+ * Expert Kernels: Grouped Prefill and Mixed-Quant Compact Experts", section
+ * 1, the first of its two routers):
+ *   choice score c_e = sigmoid(logits[t, e]) + bias[e] (bias NULL reads as
+ *     zeros; a NaN score counts as -inf);
+ *   the E experts form n_group groups of E / n_group consecutive experts; a
+ *     group's score is the sum of its two largest choice scores;
+ *   the topk_group groups with the largest scores are kept (equal scores:
+ *     the lower group first);
+ *   sel[t] = the K experts of the kept groups with the largest choice
+ *     scores, in descending order (equal scores: the lower index first);
+ *   p[t, k] = sigmoid(logits[t, sel[t, k]]) (the bias steers the choice
+ *     only), divided by (the chosen scores summed left to right + 1e-20) when
+ *     renormalize is 1 (as mxfp4_moe_route's sigmoid mode; 0 keeps the
+ *     gathered scores), times scale.
+ * Arithmetic is fp32 (the sigmoid with the hardware reciprocal). Shapes,
+ * alignment, overlap rules and errors as mxfp4_moe_route, and: 2 <= E <=
+ * MXFP4_ROUTE_MAX_EXPERTS, 1 <= n_group <= MXFP4_ROUTE_MAX_GROUPS dividing E
+ * with E / n_group >= 2, 1 <= topk_group <= n_group, 1 <= K <=
+ * min(MXFP4_ROUTE_MAX_K, topk_group * E / n_group), renormalize 0 or 1;
+ * anything else is MXFP4_ERR_INVALID_ARG. Enqueued on `stream`, no
+ * synchronisation, no allocation; may be captured in a graph.
+ */
+#define MXFP4_ROUTE_MAX_GROUPS 64
+int mxfp4_moe_route_grouped(const float* logits, const float* bias, int64_t T, int64_t E, int64_t K,
+                            int64_t n_group, int64_t topk_group, int renormalize, float scale, int32_t* sel,
+                            float* p, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* mxfp4_status_string(int status);
 

@@ -30,7 +30,7 @@ __all__ = [
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
     "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared", "moe_linear_prepared", "gemm_stage_prepared",
     "prepare_bf16", "moe_decode_prepared", "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
-    "stream_read", "Mxfp4Error", "library_path",
+    "route_grouped", "stream_read", "Mxfp4Error", "library_path",
 ]
 
 _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
@@ -541,6 +541,34 @@ def route(logits: torch.Tensor, K: int, mode: str = "softmax", bias: torch.Tenso
         st = _abi.lib().mxfp4_moe_route(_ptr(logits), _ptr(bias), T, logits.shape[1], K, modes[mode],
                                         float(scale), _ptr(sel), _ptr(p), _stream(dev))
     _abi.check(st, "mxfp4_moe_route")
+    return sel, p
+
+
+def route_grouped(logits: torch.Tensor, K: int, n_group: int, topk_group: int, bias: torch.Tensor | None = None,
+                  scale: float = 1.0, renormalize: bool = True, *, sel: torch.Tensor | None = None,
+                  p: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Group-limited sigmoid router (mxfp4_moe_route_grouped): fp32 logits
+    (T, E) -> (sel int32 (T, K), p fp32 (T, K)); bias (E,) fp32 or None."""
+    dev = logits.device
+    _need(logits, "logits", torch.float32, 2, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1, dev)
+        if bias.shape[0] != logits.shape[1]:
+            raise ValueError(f"bias has {bias.shape[0]} entries, logits have {logits.shape[1]} experts")
+    T = logits.shape[0]
+    if sel is None:
+        sel = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if p is None:
+        p = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _need(sel, "sel", torch.int32, 2, dev)
+    _need(p, "p", torch.float32, 2, dev)
+    if tuple(sel.shape) != (T, K) or tuple(p.shape) != (T, K):
+        raise ValueError(f"sel and p must be ({T}, {K})")
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_moe_route_grouped(_ptr(logits), _ptr(bias), T, logits.shape[1], K, n_group, topk_group,
+                                                int(bool(renormalize)), float(scale), _ptr(sel), _ptr(p),
+                                                _stream(dev))
+    _abi.check(st, "mxfp4_moe_route_grouped")
     return sel, p
 
 

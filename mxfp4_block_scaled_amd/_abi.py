@@ -42,6 +42,7 @@ ROUTE_SOFTMAX = 0
 ROUTE_SIGMOID = 1
 ROUTE_MAX_EXPERTS = 1024
 ROUTE_MAX_K = 64
+ROUTE_MAX_GROUPS = 64
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -76,6 +77,7 @@ SIGNATURES = {
     "mxfp4_prepare_bf16": (_int, [_vp] * 2 + [_i64] * 3 + [_vp, _sz, _vp]),
     "mxfp4_prepare_swiglu": (_int, [_vp] * 2 + [_i64] * 3 + [_vp, _sz, _vp]),
     "mxfp4_moe_swiglu_prepared_ex": (_int, [_vp] * 7 + [_i64] * 6 + [_u32, _vp, _sz, _vp]),
+    "mxfp4_moe_route_grouped": (_int, [_vp] * 2 + [_i64] * 5 + [_int, ctypes.c_float, _vp, _vp, _vp]),
     "mxfp4_stream_read": (_int, [_vp, _sz, _int, _vp, _vp]),
     "mxfp4_status_string": (ctypes.c_char_p, [_int]),
 }

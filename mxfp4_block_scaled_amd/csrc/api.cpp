@@ -749,6 +749,28 @@ int mxfp4_moe_route(const float* logits, const float* bias, int64_t T, int64_t E
   return hip_status(launch_route(logits, bias, (int)T, (int)E, (int)K, mode, scale, sel, p, stream));
 }
 
+int mxfp4_moe_route_grouped(const float* logits, const float* bias, int64_t T, int64_t E, int64_t K, int64_t n_group,
+                            int64_t topk_group, int renormalize, float scale, int32_t* sel, float* p,
+                            hipStream_t stream) {
+  if (T < 0 || T > (int64_t(1) << 30) || E < 2 || E > MXFP4_ROUTE_MAX_EXPERTS || n_group < 1 ||
+      n_group > MXFP4_ROUTE_MAX_GROUPS || E % n_group != 0 || E / n_group < 2 || topk_group < 1 ||
+      topk_group > n_group || K < 1 || K > MXFP4_ROUTE_MAX_K || K > topk_group * (E / n_group))
+    return MXFP4_ERR_INVALID_ARG;
+  if (renormalize != 0 && renormalize != 1) return MXFP4_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MXFP4_ERR_INVALID_ARG;
+  if (T == 0) return MXFP4_OK;
+  if (!logits || !sel || !p) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(sel, 4) || !aligned(p, 4) || (bias && !aligned(bias, 4)))
+    return MXFP4_ERR_INVALID_ARG;
+  const size_t nl = size_t(T) * size_t(E) * 4, no = size_t(T) * size_t(K) * 4, nb = size_t(E) * 4;
+  if (overlap(sel, no, p, no) || overlap(sel, no, logits, nl) || overlap(p, no, logits, nl)) return MXFP4_ERR_INVALID_ARG;
+  if (bias && (overlap(sel, no, bias, nb) || overlap(p, no, bias, nb))) return MXFP4_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != MXFP4_OK) return st;
+  return hip_status(launch_route_grouped(logits, bias, (int)T, (int)E, (int)K, (int)n_group, (int)topk_group,
+                                         renormalize, scale, sel, p, stream));
+}
+
 int mxfp4_moe_linear(const float* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel, const float* p,
                      const float* shared, float* y, int64_t T, int64_t E, int64_t O, int64_t G, int64_t K,
                      hipStream_t stream) {

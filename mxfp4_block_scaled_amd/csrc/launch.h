@@ -140,6 +140,11 @@ int route_values_per_lane(int E, int lanes);
 int route_lanes(int64_t T, int E, int K);
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, int mode, float scale,
                         int32_t* sel, float* p, hipStream_t stream, int lanes = 0);
+// Group-limited sigmoid router: E <= 1024, n_group | E with E / n_group >= 2
+// and n_group <= 64, 1 <= topk_group <= n_group, 1 <= K <= min(64,
+// topk_group * E / n_group); renorm: divide by the chosen scores' sum + 1e-20.
+hipError_t launch_route_grouped(const float* logits, const float* bias, int T, int E, int K, int n_group,
+                               int topk_group, int renorm, float scale, int32_t* sel, float* p, hipStream_t stream);
 
 // ---- prefill-shaped path: grouped GEMM over the tiles, then the combine.
 // The grouped GEMM addresses the activations (np bf16 planes of T x 32G) and

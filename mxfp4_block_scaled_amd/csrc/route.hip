@@ -203,6 +203,94 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
   }
 }
 
+// Group-limited sigmoid router (the CPU kernels page, section 1, its first
+// router): choice score c_e = sigmoid(logit_e) + bias_e (NaN read as -inf);
+// groups of eg = E / n_group consecutive experts, scored by the sum of
+// their two largest choice scores; the topk_group best groups are kept
+// (ties to the lower group); the K best choice scores inside them are
+// chosen (ties to the lower expert); the weights are the unbiased sigmoid
+// scores of the chosen, divided by their left-to-right sum + 1e-20 when
+// renorm is set, times scale. One wave per token: lane j holds experts
+// j, j + 64, ...; the choice scores also go to LDS, where lane g < n_group
+// scans group g for its two best; the groups are then chosen by
+// topk_group rounds of the wave-wide arg-max, and the experts of the
+// dropped groups get the sentinel key 0 before the K rounds.
+constexpr int kGroupedWaves = 4;
+
+template <int VPL>
+__global__ void __launch_bounds__(64 * kGroupedWaves) route_grouped_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int K, int n_group,
+    int topk_group, int renorm, float scale, int32_t* __restrict__ sel, float* __restrict__ p) {
+  __shared__ float cs[kGroupedWaves][64 * VPL];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kGroupedWaves + w;
+  const bool live = t0 < T;
+  const int t = live ? t0 : T - 1;  // a wave past the batch repeats the last token and stores nothing
+  const float* row = logits + (int64_t)t * E;
+  const int eg = E / n_group;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  uint32_t key[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; v++) {
+    const int e = lane + 64 * v;
+    const int ec = e < E ? e : E - 1;
+    const float b = bias ? bias[ec] : 0.f;
+    const float c = fmaxf(sigmoid(row[ec]) + b, kNegInf);  // NaN -> -inf
+    if (e < E) cs[w][e] = c;
+    key[v] = e < E ? order_key(c) : 0u;
+  }
+  __syncthreads();
+  // group scores: lane g scans its group for the two largest choice scores
+  uint32_t gk = 0;
+  if (lane < n_group) {
+    float a = kNegInf, b = kNegInf;
+    for (int i = 0; i < eg; i++) {
+      const float c = cs[w][lane * eg + i];
+      const bool first = c > a, second = c > b;
+      b = first ? a : (second ? c : b);
+      a = first ? c : a;
+    }
+    gk = order_key(a + b);
+  }
+  uint64_t kept = 0;
+  for (int r = 0; r < topk_group; r++) {
+    uint32_t hi = gk, lo = ~static_cast<uint32_t>(lane);
+    group_max_pair<64>(hi, lo);
+    const uint32_t g = ~lo;
+    kept |= uint64_t(1) << g;
+    gk = (static_cast<uint32_t>(lane) == g) ? 0u : gk;
+  }
+#pragma unroll
+  for (int v = 0; v < VPL; v++) {
+    const int e = lane + 64 * v;
+    const bool in = e < E && ((kept >> (e / eg)) & 1);
+    key[v] = in ? key[v] : 0u;
+  }
+  uint32_t taken = 0;
+  uint32_t h0, i0, h1, i1;
+  local_top2<VPL>(key, taken, h0, i0, h1, i1);
+  int my_sel = 0;
+  for (int k = 0; k < K; k++) {
+    uint32_t hi = h0, lo = ~static_cast<uint32_t>(lane + 64 * i0);
+    group_max_pair<64>(hi, lo);
+    const uint32_t win = ~lo;
+    const bool own = (win & 63u) == static_cast<uint32_t>(lane);
+    if (lane == k) my_sel = static_cast<int>(win);
+    taken |= own ? (1u << i0) : 0u;
+    h0 = own ? h1 : h0;
+    i0 = own ? i1 : i0;
+    h1 = own ? 0u : h1;
+    if (own && h0 == 0) local_top2<VPL>(key, taken, h0, i0, h1, i1);
+  }
+  const float sc = lane < K ? sigmoid(row[my_sel]) : 0.f;
+  float mass = 0.f;
+  for (int k = 0; k < K; k++) mass += __shfl(sc, k, 64);  // left to right
+  if (live && lane < K) {
+    sel[(int64_t)t * K + lane] = my_sel;
+    p[(int64_t)t * K + lane] = (renorm ? sc / (mass + kSigmoidEps) : sc) * scale;
+  }
+}
+
 constexpr int kVplChoices[] = {1, 2, 4, 8, 12, 16, 24, 32};  // E <= 1024 at 32 lanes
 
 template <int L, int VPL>
@@ -248,6 +336,31 @@ int route_lanes(int64_t T, int E, int K) {
   // whenever K > 32
   const int lanes = (T >= 512 && K <= 32) ? 32 : 64;
   return route_values_per_lane(E, lanes) ? lanes : 0;
+}
+
+hipError_t launch_route_grouped(const float* logits, const float* bias, int T, int E, int K, int n_group,
+                               int topk_group, int renorm, float scale, int32_t* sel, float* p, hipStream_t stream) {
+  const int vpl = (E + 63) / 64;
+  if (E < 2 || E > 1024 || n_group < 1 || n_group > 64 || E % n_group || E / n_group < 2 || topk_group < 1 ||
+      topk_group > n_group || K < 1 || K > 64 || K > topk_group * (E / n_group))
+    return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  const dim3 grid((T + kGroupedWaves - 1) / kGroupedWaves), block(64 * kGroupedWaves);
+#define MXFP4_ROUTE_GROUPED_CASE(V)                                                                             \
+  case V:                                                                                                      \
+    hipLaunchKernelGGL((route_grouped_kernel<V>), grid, block, 0, stream, logits, bias, T, E, K, n_group,     \
+                       topk_group, renorm, scale, sel, p);                                                     \
+    break;
+  switch (vpl <= 2 ? vpl : (vpl <= 4 ? 4 : (vpl <= 8 ? 8 : 16))) {
+    MXFP4_ROUTE_GROUPED_CASE(1)
+    MXFP4_ROUTE_GROUPED_CASE(2)
+    MXFP4_ROUTE_GROUPED_CASE(4)
+    MXFP4_ROUTE_GROUPED_CASE(8)
+    MXFP4_ROUTE_GROUPED_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MXFP4_ROUTE_GROUPED_CASE
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, int mode, float scale,

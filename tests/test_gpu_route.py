@@ -189,3 +189,112 @@ def test_router_rejects_bad_arguments():
         mx.route(lg, 2, "softmax", torch.zeros(8, dtype=torch.float32, device=DEV))
     with pytest.raises(ValueError):
         mx.route(lg, 2, "tanh")
+
+
+# ------------------------------------------------------------- group-limited sigmoid router
+
+EPS_GROUP = 2e-6  # a group score is a sum of two keys: twice their EPS_KEY
+
+
+def run_grouped(logits, K, n_group, topk_group, bias=None, scale=1.0, renorm=True):
+    dl = torch.from_numpy(logits).to(DEV)
+    db = None if bias is None else torch.from_numpy(bias).to(DEV)
+    sel, p = mx.route_grouped(dl, K, n_group, topk_group, db, scale, renorm)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), p.cpu().numpy()
+
+
+def check_grouped(sel, p, logits, bias, K, n_group, topk_group, scale, renorm):
+    """Exact agreement with the oracle on tokens whose group scores around the
+    topk_group cut and whose kept keys around the K cut are more than the
+    fp32 margins apart; a valid choice within those margins elsewhere."""
+    T, E = logits.shape
+    eg = E // n_group
+    want_sel, want_p = oracle.route_sigmoid_grouped(logits, bias, K, n_group, topk_group, scale, renorm)
+    keys = oracle.route_keys(logits, bias, "sigmoid")
+    keys = np.where(np.isnan(keys), -np.inf, keys)
+    gsc = -np.sort(-keys.reshape(T, n_group, eg), axis=2)[:, :, :2].sum(2)
+    gsorted = -np.sort(-gsc, axis=1)
+    cut = gsorted[:, topk_group - 1]
+    g_clear = (topk_group == n_group) | (np.abs(gsorted[:, topk_group - 1] - gsorted[:, min(topk_group, n_group - 1)])
+                                         > EPS_GROUP)
+    kept = gsc >= cut[:, None]
+    masked = np.where(np.repeat(kept, eg, axis=1), keys, -np.inf)
+    ks = -np.sort(-masked, axis=1)[:, :K + 1]
+    k_clear = np.all(np.abs(np.diff(ks, axis=1)) > EPS_KEY, axis=1)
+    clear = g_clear & k_clear
+    assert sel.shape == (T, K) and sel.min() >= 0 and sel.max() < E
+    for t in range(T):
+        assert len(set(sel[t].tolist())) == K, f"token {t}: repeated expert"
+        # every chosen expert's group is within the margin of the kept set
+        assert np.all(gsc[t, sel[t] // eg] >= cut[t] - EPS_GROUP), f"token {t}: a group below the cut"
+        ck = keys[t, sel[t]]
+        assert np.all(np.diff(ck) <= EPS_KEY), f"token {t}: not descending"
+    bad = np.nonzero(clear & np.any(sel != want_sel, axis=1))[0]
+    assert bad.size == 0, f"tokens {bad[:5]} differ from the oracle with no near tie"
+    same = np.all(sel == want_sel, axis=1)
+    err = np.abs(p[same].astype(np.float64) - want_p[same])
+    assert np.all(err <= P_RTOL * np.abs(want_p[same]) + P_ATOL), f"weights: max err {err.max():.3g}"
+    return int(clear.sum())
+
+
+GROUPED_SHAPES = [  # T, E, K, n_group, topk_group
+    (1, 8, 2, 4, 2), (33, 64, 4, 8, 2), (100, 256, 8, 8, 4), (129, 128, 6, 4, 1), (50, 1000, 16, 8, 3),
+    (17, 384, 8, 12, 4), (40, 1024, 64, 64, 32), (3, 2, 1, 1, 1), (64, 160, 6, 10, 10),
+]
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("T,E,K,n_group,topk_group", GROUPED_SHAPES)
+def test_grouped_router_against_oracle(T, E, K, n_group, topk_group, renorm):
+    say(f"grouped router T={T} E={E} K={K} groups {n_group} keep {topk_group} renorm={renorm}")
+    logits, bias = workloads.router_logits(T, E, seed=3 * E + K + n_group, std=1.5, bias_std=0.1)
+    sel, p = run_grouped(logits, K, n_group, topk_group, bias, 1.75, renorm)
+    n = check_grouped(sel, p, logits, bias, K, n_group, topk_group, 1.75, renorm)
+    assert n >= 0.85 * T, f"only {n} of {T} tokens clear of near ties: the case proves little"
+
+
+def test_grouped_router_worked_example():
+    # biases on a 1/8 grid and logits 0: every score exact on both sides;
+    # group scores 1.0, 1.5, 1.0, 0.9375 keep groups 1 and 0 (tie with 2 to
+    # the lower index), so the best expert overall (7) is dropped
+    logits = np.zeros((3, 8), np.float32)
+    bias = np.array([0.375, -0.375, 0.25, 0.25, 0.0, 0.0, -0.5, 0.4375], np.float32)
+    sel, p = run_grouped(logits, 2, 4, 2, bias, 3.0)
+    assert sel.tolist() == [[0, 2]] * 3
+    assert np.all(p == 1.5)
+    sel1, _ = run_grouped(logits, 2, 4, 1, bias)  # one group kept: group 1 (1.5)
+    assert sel1.tolist() == [[2, 3]] * 3
+
+
+def test_grouped_router_every_group_kept_is_the_sigmoid_router():
+    T, E, K = 300, 256, 8
+    logits, bias = workloads.router_logits(T, E, seed=31, std=1.5, bias_std=0.1)
+    sel_g, p_g = run_grouped(logits, K, 8, 8, bias, 2.0)
+    sel_s, p_s = run(logits, K, "sigmoid", bias, scale=2.0)
+    assert np.array_equal(sel_g, sel_s)
+    assert np.array_equal(p_g, p_s)
+
+
+def test_grouped_router_full_batch_and_nan():
+    # 4096 tokens over 256 experts in 8 groups, 4 kept, top 8 (the shape of
+    # the large group-limited routers), then NaN logits that never win
+    T, E, K = 4096, 256, 8
+    logits, bias = workloads.router_logits(T, E, seed=32, std=2.0, bias_std=0.1)
+    sel, p = run_grouped(logits, K, 8, 4, bias)
+    n = check_grouped(sel, p, logits, bias, K, 8, 4, 1.0, True)
+    assert n >= 0.9 * T
+    bad = logits[:64].copy()
+    bad[:, 3] = np.nan
+    sel, p = run_grouped(bad, K, 8, 4, bias)
+    assert not np.any(sel == 3)
+    check_grouped(sel, p, bad, bias, K, 8, 4, 1.0, True)
+
+
+def test_grouped_router_rejects_bad_arguments():
+    lg = torch.zeros((4, 12), dtype=torch.float32, device=DEV)
+    for args in ((2, 5, 1), (2, 4, 5), (2, 12, 1), (7, 4, 1), (0, 4, 1)):  # 5 does not divide 12; one per group; K too big
+        with pytest.raises(mx.Mxfp4Error):
+            mx.route_grouped(lg, *args)
+    sel, p = mx.route_grouped(torch.empty((0, 12), dtype=torch.float32, device=DEV), 2, 4, 2)
+    assert sel.shape == (0, 2)
