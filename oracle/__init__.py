@@ -5,6 +5,5 @@ from .mxfp4_oracle import (  # noqa: F401
     expert_linear_scalar, silu, swiglu_hidden, expert_swiglu, expert_swiglu_rows, expert_swiglu_scalar,
     route_softmax, route_sigmoid, route_sigmoid_grouped, route_scalar, route_grouped_scalar, route_keys, route_weights, SOFTMAX_MASS_FLOOR, SIGMOID_EPS,
     E4M3_MAX, E4M3_TABLE, e4m3_value, mxfp8_block_exponent, quantize_e4m3, quantize_mxfp8, dequantize_mxfp8,
-    expert_linear_mxfp8, expert_linear_mxfp8_rows, quantize_mxfp8_split, dequantize_mxfp8_split,
-    expert_linear_mxfp8_split, expert_linear_mxfp8_split_rows,
+    expert_linear_mxfp8, expert_linear_mxfp8_rows,
 )

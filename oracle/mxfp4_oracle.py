@@ -716,39 +716,3 @@ def expert_linear_mxfp8_rows(x, packed, scales, sel, p, shared, rows) -> np.ndar
     """expert_linear_mxfp8 restricted to the output rows ``rows``."""
     xh = dequantize_mxfp8(*quantize_mxfp8(x))
     return expert_linear_rows(xh, packed, scales, sel, p, shared, rows)
-
-
-# ------------------------------- two-piece MXFP8 split of bf16 activations
-#
-# A second reading of the block-scaled variant that keeps the bf16 path's
-# accuracy: each activation is written as hi + lo, hi the MXFP8 quantisation
-# above and lo the MXFP8 quantisation (with its own block scales) of the
-# residual x - hi. A bf16 value has 8 significant bits and an E4M3 code 4, so
-# the residual of a rounded hi has at most 4 and hi + lo reproduces x exactly
-# unless the residual block's scale pushes a small residual into the E4M3
-# subnormals. The defining result is the routed linear of hi + lo, exact in
-# float64; it equals the exact layer wherever the split is exact.
-
-def quantize_mxfp8_split(x) -> tuple:
-    """Activations (T, I) -> (hi codes, hi scale bytes, lo codes, lo scale
-    bytes), lo quantising the residual x - dequantize(hi)."""
-    x = np.asarray(x, dtype=np.float64)
-    c_hi, s_hi = quantize_mxfp8(x)
-    c_lo, s_lo = quantize_mxfp8(x - dequantize_mxfp8(c_hi, s_hi))
-    return c_hi, s_hi, c_lo, s_lo
-
-
-def dequantize_mxfp8_split(c_hi, s_hi, c_lo, s_lo) -> np.ndarray:
-    """float64 hi + lo of a two-piece split."""
-    return dequantize_mxfp8(c_hi, s_hi) + dequantize_mxfp8(c_lo, s_lo)
-
-
-def expert_linear_mxfp8_split(x, packed, scales, sel, p, shared) -> np.ndarray:
-    """The routed linear of the two-piece MXFP8 split of the activations."""
-    return expert_linear(dequantize_mxfp8_split(*quantize_mxfp8_split(x)), packed, scales, sel, p, shared)
-
-
-def expert_linear_mxfp8_split_rows(x, packed, scales, sel, p, shared, rows) -> np.ndarray:
-    """expert_linear_mxfp8_split restricted to the output rows ``rows``."""
-    xh = dequantize_mxfp8_split(*quantize_mxfp8_split(x))
-    return expert_linear_rows(xh, packed, scales, sel, p, shared, rows)

@@ -842,60 +842,3 @@ def test_mxfp8_planted_mistakes_are_caught(monkeypatch):
     amax = np.array([300.0, 448.0, 500.0, 1.0])
     floor_rule = np.floor(np.log2(amax)).astype(np.int64) - 8
     assert not np.array_equal(floor_rule, oracle.mxfp8_block_exponent(amax))
-
-
-def test_mxfp8_split_is_exact_on_bf16_values():
-    """hi + lo reproduces bf16 activations: every value of a block whose
-    elements share a binade (no subnormal residuals), and all but a tiny
-    fraction of normal activations; the layer of the split then equals the
-    exact layer up to float64 rounding."""
-    rng = _rng(12)
-    # a block per binade: 32 bf16 values with the same exponent
-    e = rng.integers(-20, 20, (40, 1))
-    x = np.ldexp(rng.integers(128, 256, (40, 32)) / 128.0, e) * rng.choice([-1, 1], (40, 32))
-    x = workloads.round_to_bf16(x.astype(np.float32)).astype(np.float64)
-    xh = oracle.dequantize_mxfp8_split(*oracle.quantize_mxfp8_split(x))
-    np.testing.assert_array_equal(xh, x)
-    # normal activations: nearly every value exact, the rest off by far less than bf16 rounding
-    xn = workloads.round_to_bf16(rng.standard_normal((32, 2880)).astype(np.float32)).astype(np.float64)
-    xh = oracle.dequantize_mxfp8_split(*oracle.quantize_mxfp8_split(xn))
-    exact = np.mean(xh == xn)
-    assert exact > 0.999, exact
-    # the error left is lo's own E4M3 rounding of the residual r = x - hi:
-    # at most 2^-4 |r| (3 mantissa bits) or half lo's subnormal quantum 2^(Y - 9)
-    c1, s1, c2, s2 = oracle.quantize_mxfp8_split(xn)
-    r = xn - oracle.dequantize_mxfp8(c1, s1)
-    y_lo = np.repeat(s2.astype(np.int64) - 127, 32, axis=1)
-    assert np.all(np.abs(xh - xn) <= np.maximum(np.abs(r) * 2.0 ** -4, np.ldexp(1.0, y_lo - 10)))
-    # one piece alone is E4M3 rounding (a few percent); the split is a lossless re-encoding
-    assert np.linalg.norm(oracle.dequantize_mxfp8(c1, s1) - xn) / np.linalg.norm(xn) > 1e-2
-    T, E, K, G, O = 5, 4, 2, 2, 16
-    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
-    scales = rng.integers(120, 131, (E, O, G), dtype=np.uint8)
-    sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
-    p = rng.uniform(0.1, 1.0, (T, K))
-    xs = x[:T, :].repeat(2, axis=1)
-    sh = rng.standard_normal((T, O))
-    np.testing.assert_allclose(oracle.expert_linear_mxfp8_split(xs, packed, scales, sel, p, sh),
-                               oracle.expert_linear(xs, packed, scales, sel, p, sh), rtol=1e-13, atol=1e-13)
-    rows = np.array([1, 15])
-    np.testing.assert_array_equal(oracle.expert_linear_mxfp8_split_rows(xs, packed, scales, sel, p, sh, rows),
-                                  oracle.expert_linear_mxfp8_split(xs, packed, scales, sel, p, sh)[:, rows])
-
-
-def test_mxfp8_split_pieces():
-    """The pieces themselves: hi is the one-piece quantisation, lo quantises
-    the residual with its own scales; a residual that is zero gives a zero
-    block (scale byte 0)."""
-    rng = _rng(13)
-    x = workloads.round_to_bf16(rng.standard_normal((3, 64)).astype(np.float32)).astype(np.float64)
-    x[1, :32] = 448.0 * np.ldexp(1.0, rng.integers(-4, 4, 32)) / 8  # on the hi grid: zero residual
-    c1, s1, c2, s2 = oracle.quantize_mxfp8_split(x)
-    h1, hs = oracle.quantize_mxfp8(x)
-    np.testing.assert_array_equal(c1, h1)
-    np.testing.assert_array_equal(s1, hs)
-    r = x - oracle.dequantize_mxfp8(c1, s1)
-    l1, ls = oracle.quantize_mxfp8(r)
-    np.testing.assert_array_equal(c2, l1)
-    np.testing.assert_array_equal(s2, ls)
-    assert s2[1, 0] == 0 and np.all((c2[1, :32] & 0x7F) == 0)
