@@ -84,21 +84,54 @@ __host__ __device__ inline int bits_for(int E) {
 }
 
 // Writes the M-tile list of the grouped GEMM from count/offsets (LDS copy
-// of count in `tmp`, clobbered). Tiles are expert-major: the full tiles of
-// expert e, then its partial tile.
+// of count in `count_lds`; `tmp` is clobbered). The work is ordered longest
+// first by expert: experts with more pairs come first (equal counts: the
+// lower index first), each expert's tiles stay together - its full tiles of
+// kGemmTileM pairs, then its partial tile - so that the partial tile runs
+// right after the full ones and finds the expert's weights in L2. (The order
+// is a permutation of experts by rank = number of experts with more pairs,
+// or as many and a lower index; up to kSortMaxE experts, beyond that the
+// experts keep their index order.) Each tile's height is its expert's pairs
+// left (at most kGemmTileM); the kernels skip the 32-row MFMA sub-tiles past it.
+constexpr int kSortMaxE = 1024;
+
 template <int NT>
 __device__ void write_tiles(const int* count_lds, int* tmp, int E, const int32_t* offsets, GemmTile* tiles,
                             int32_t* n_tiles, int* wave_tot) {
-  for (int e = threadIdx.x; e < E; e += NT) tmp[e] = (count_lds[e] + kGemmTileM - 1) / kGemmTileM;
+  __shared__ int order[kSortMaxE];  // position -> expert
+  const bool ranked = E <= kSortMaxE;
+  if (ranked) {
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int c = count_lds[e];
+      int r = 0;
+      // every lane reads the same counts (an LDS broadcast), eight at a time
+      int f = 0;
+      for (; f + 8 <= E; f += 8) {
+        int cf[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) cf[i] = count_lds[f + i];
+#pragma unroll
+        for (int i = 0; i < 8; i++) r += (cf[i] > c) || (cf[i] == c && f + i < e);
+      }
+      for (; f < E; f++) {
+        const int cf = count_lds[f];
+        r += (cf > c) || (cf == c && f < e);
+      }
+      order[r] = e;
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < E; i += NT) tmp[i] = (count_lds[ranked ? order[i] : i] + kGemmTileM - 1) / kGemmTileM;
   __syncthreads();
   const int total = block_exclusive_scan<NT>(tmp, E, wave_tot);
-  for (int e = threadIdx.x; e < E; e += NT) {
+  for (int i = threadIdx.x; i < E; i += NT) {
+    const int e = ranked ? order[i] : i;
     const int c = count_lds[e], base = offsets[e];
-    for (int i = 0, t = tmp[e]; i * kGemmTileM < c; i++, t++) {
+    for (int j = 0, t = tmp[i]; j * kGemmTileM < c; j++, t++) {
       GemmTile tl;
       tl.e = e;
-      tl.row0 = base + i * kGemmTileM;
-      tl.mlen = min(kGemmTileM, c - i * kGemmTileM);
+      tl.row0 = base + j * kGemmTileM;
+      tl.mlen = min(kGemmTileM, c - j * kGemmTileM);
       tl.pad = 0;
       tiles[t] = tl;
     }

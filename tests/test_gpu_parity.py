@@ -316,7 +316,7 @@ def test_large_workloads_full_rows_of_some_tokens(name):
 def test_prefill_fp32_activations_sampled():
     # the prefill shape with genuine fp32 activations: the grouped GEMM on the
     # three-piece bf16 split, at the fp32 bar
-    w = workloads.WORKLOADS["prefill"].with_(name="prefill-fp32", dtype="fp32")
+    w = workloads.WORKLOADS["prefill_fp32"]
     inp = workloads.make_inputs(w)
     assert mx.select_path(w.T, w.E, w.O, w.G, w.K, _abi.DTYPE_F32) == _abi.PATH_GEMM
     d = upload(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, "fp32")

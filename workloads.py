@@ -87,6 +87,10 @@ WORKLOADS = {
     "skewed": Workload("skewed", 4, T=8192, E=384, K=8, G=64, O=7168, dtype="bf16",
                        scale_lo=110, scale_hi=135, routing="zipf", zipf_s=1.2,
                        logit_std=math.sqrt(2.0)),
+    # the prefill shape with fp32 activations (the prefill workload's seeds):
+    # the grouped GEMM on the three-piece bf16 split
+    "prefill_fp32": Workload("prefill_fp32", 3, T=4096, E=128, K=4, G=90, O=5760, dtype="fp32",
+                             scale_lo=118, scale_hi=128),
     # SwiGLU expert block: decode8's gate/up shape (I = 7168, 2F = 4096)
     # feeding the skewed workload's down shape (F = 2048 -> O = 7168), with
     # the skewed workload's tokens and routing
