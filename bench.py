@@ -632,36 +632,41 @@ def stream_ceiling(window_bytes, steps, warmup):
     out = {}
     for label, nbytes, views in (("decode_call_bytes", win, [buf[i * win:(i + 1) * win] for i in range(n_win)]),
                                  ("one_GiB", 1 << 30, [buf[:1 << 30]])):
-        def step(i):
-            mx.stream_read(views[i % len(views)], sink)
+        best = None
+        for blocks in STREAM_BLOCKS:  # the best of a few grid sizes is the ceiling
+            def step(i):
+                mx.stream_read(views[i % len(views)], sink, blocks)
 
-        for i in range(warmup):
-            step(i)
-        stream = torch.cuda.Stream(device=dev)
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            step(0)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(steps):
+            for i in range(warmup):
                 step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
+            stream = torch.cuda.Stream(device=dev)
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                step(0)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    step(i)
             g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            if best is None or ms < best[0]:
+                best = (ms, blocks)
+            del g
+        ms, blocks = best
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[label] = {"bytes": nbytes, "ms_per_launch": round(ms, 6), "GBs": round(gbs, 1),
-                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "workgroups": blocks}
         log(f"[bench] streaming read of {nbytes / 1e6:.1f} MB: {ms * 1e3:.2f} us, {gbs:.0f} GB/s "
-            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
-        del g
+            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s; best of {len(STREAM_BLOCKS)} grids: {blocks} workgroups)")
     del buf, sink
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -669,6 +674,7 @@ def stream_ceiling(window_bytes, steps, warmup):
 
 
 SUITE = ("tiny", "decode8", "prefill", "skewed")
+STREAM_BLOCKS = (512, 2048, 8192)
 
 
 def main():
