@@ -39,9 +39,19 @@
 namespace mxfp4 {
 namespace {
 
-constexpr int kRing = 2;  // slots whose loads a wave keeps in flight
+#ifndef MXFP4_ROWS_RING
+#define MXFP4_ROWS_RING 2  // slots whose loads a wave keeps in flight
+#endif
+// waves of a large-activation workgroup (16 rows either way)
+#ifndef MXFP4_ROWS_BIG_WAVES
+#define MXFP4_ROWS_BIG_WAVES 16
+#endif
+#ifndef MXFP4_ROWS_TMAX
+#define MXFP4_ROWS_TMAX 4
+#endif
+constexpr int kRing = MXFP4_ROWS_RING;
 constexpr int kRpl = 2;   // weight rows per lane in a slot
-constexpr int kTmax = 2;  // pairs per work item (an expert with more pairs gets more items)
+constexpr int kTmax = MXFP4_ROWS_TMAX;  // pairs per work item (an expert with more pairs gets more items)
 constexpr int kXPre = 4;   // 16-byte chunks of x per thread loaded with the routing input
 // group offset beyond any expert's resource (O * G < 2^27): loads return zero
 constexpr uint32_t kOobGroup = 0x08000000u;
@@ -62,7 +72,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
     int G, int K, int S, int gs, int nbits, int32_t* __restrict__ n_invalid, int chunk_index) {
   constexpr int RI = 64 / L;        // rows per wave-wide load
   constexpr int RW = RI * kRpl;     // rows per work item
-  constexpr int R = 2 * NW;         // rows per workgroup
+  constexpr int R = NW == 4 ? 8 : 16;  // rows per workgroup
   constexpr int NRG = R / RW;       // row groups per workgroup (a power of two)
   constexpr int CH = XF32 ? 8 : 4;  // 16-byte activation chunks per group
   constexpr int kThreads = NW * 64, kWaves = NW;
@@ -415,13 +425,14 @@ struct RowsPlan {
 // k-splits: enough work items for the workgroup's waves when few experts
 // are selected, every split non-empty.
 // Small activations: 4-wave workgroups of 8 rows (many workgroups, all
-// resident at once). Large activations: 8-wave workgroups of 16 rows, so
-// that fewer workgroups copy x into LDS.
+// resident at once). Large activations: 16-wave workgroups of 16 rows: the
+// staged x limits a CU to one workgroup, whose 16 waves (4 per SIMD) keep
+// enough loads in flight and hide the arithmetic.
 RowsPlan rows_plan(int T, int K, int E, int G, int dtype) {
   const int P = T * K, uexp = P < E ? P : E;
   const int64_t xbytes = (int64_t)T * G * 32 * (dtype == 0 ? 4 : 2);
   const bool big = xbytes > 32 * 1024;
-  const int NW = big ? 8 : 4, R = 2 * NW;
+  const int NW = big ? MXFP4_ROWS_BIG_WAVES : 4, R = big ? 16 : 8;
   RowsPlan pl{R, NW, 64, 1, G};
   for (int S = 1; S <= G; S++) {
     const int gs = (G + S - 1) / S;
@@ -457,8 +468,8 @@ hipError_t launch_rows(const RowsPlan& pl, size_t lds, const void* x, const uint
   if (pl.NW == 4)
     return launch_rows_nw<XF32, L, 4>(pl, lds, x, packed, scales, sel, p, shared, y, T, E, O, G, K, n_invalid,
                                       chunk_index, stream);
-  return launch_rows_nw<XF32, L, 8>(pl, lds, x, packed, scales, sel, p, shared, y, T, E, O, G, K, n_invalid,
-                                    chunk_index, stream);
+  return launch_rows_nw<XF32, L, MXFP4_ROWS_BIG_WAVES>(pl, lds, x, packed, scales, sel, p, shared, y, T, E, O, G,
+                                                      K, n_invalid, chunk_index, stream);
 }
 
 }  // namespace
