@@ -298,6 +298,15 @@ def bench_router(args, w):
         torch.cuda.synchronize()
         if not (torch.equal(sel, sel_eager) and torch.equal(p, p_eager)):
             raise SystemExit("graph replay result differs from the eager call")
+
+    def one_pass():
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(i)
+
+    settle_passes(one_pass, stream, args.steps, args.settle_ms)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -391,6 +400,25 @@ def torch_from(a):
     return torch.from_numpy(np.ascontiguousarray(a))
 
 
+def settle_passes(one_pass, stream, steps, settle_ms):
+    """Untimed passes over the timed steps until about settle_ms have gone by,
+    so that the timed region does not start on GPU clocks that are still
+    ramping up after host-side work. Returns each pass's ms per step."""
+    import torch
+
+    per_step = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_ms * 1e-3:
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e_a.record(stream)
+            one_pass()
+            e_b.record(stream)
+        torch.cuda.synchronize()
+        per_step.append(e_a.elapsed_time(e_b) / steps)
+    return per_step
+
+
 def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
     """Time `steps` graph-replayed calls of workload w on the path `kind`;
     returns the JSON record (without the top-level contract keys)."""
@@ -480,6 +508,18 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
         if not torch.equal(y, y_eager):
             raise SystemExit(f"{w.name}: graph replay result differs from the eager call")
         log(f"[bench] {w.name}: graph replay matches the eager call bit for bit")
+
+    def one_pass():
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(steps):
+                step(i)
+
+    settle = settle_passes(one_pass, stream, steps, args.settle_ms)
+    if settle:
+        log(f"[bench] {w.name}: settle: {len(settle)} untimed passes, {settle[0] * 1e3:.2f} us/step first, "
+            f"{settle[-1] * 1e3:.2f} us/step last")
 
     # timed region: HIP events recorded on the stream the kernels run on
     torch.cuda.synchronize()
@@ -615,7 +655,7 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
     return rec
 
 
-def stream_ceiling(window_bytes, steps, warmup):
+def stream_ceiling(window_bytes, steps, warmup, settle_ms):
     """The plain streaming-read kernel (mxfp4_stream_read) on windows of
     window_bytes taken in turn from a buffer of 64 such windows (larger than
     the Infinity Cache), in a graph of `steps` launches; and on one 1 GiB
@@ -650,6 +690,7 @@ def stream_ceiling(window_bytes, steps, warmup):
                     step(i)
             g.replay()
             torch.cuda.synchronize()
+            settle_passes(g.replay, stream, steps, settle_ms)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
@@ -686,6 +727,8 @@ def main():
                     help="time one workload (default: the decode workload, with the whole suite as sub-records)")
     ap.add_argument("--no-suite", action="store_true", help="without --workload: the decode workload only")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a graph replay")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="untimed passes over the timed steps before the timed one, for about this long")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work for the oracle baseline")
     ap.add_argument("--suite-cpu-seconds", type=float, default=4.0, help="CPU work per suite workload's baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -729,7 +772,7 @@ def main():
     torch.cuda.set_device(torch.device("cuda:0"))
     dec = workloads.WORKLOADS["decode"]
     if args.stream:
-        st = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup)
+        st = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup, args.settle_ms)
         print(json.dumps({"stream_ceiling": st}), flush=True)
         return
     suite = not args.workload and not args.no_suite
@@ -757,7 +800,7 @@ def main():
             s_sets = N_ROUTING_SETS if skind == "gemv" else 4
             sub[name] = measure(sargs, sw, skind, args.steps, args.warmup,
                                 0.0 if args.no_cpu_baseline else args.suite_cpu_seconds, s_sets)
-        sub["stream_ceiling"] = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup)
+        sub["stream_ceiling"] = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup, args.settle_ms)
         out["suite"] = sub
     print(json.dumps(out), flush=True)
 
