@@ -22,7 +22,9 @@
 // for both operands; this permutes the order of k inside the stage, which
 // leaves every product x_i * w_i paired correctly.
 // Waves are 2 x 2 over the 128 x 128 tile; each owns 64 x 64 = 2 x 2 MFMA
-// tiles (a 32-row sub-tile past the segment's end is skipped). Loads of the
+// tiles. A wave whose 64 rows hold no pair skips its MFMAs; otherwise both
+// of its 32-row sub-tiles run, so the stage body has no branch and its LDS
+// reads (one k-step ahead), converts and MFMAs interleave. Loads of the
 // next stage overlap the MFMAs of the current one.
 //
 // fp32 activations (NP = 3): the host splits every value exactly into three
@@ -111,7 +113,7 @@ __global__ void __launch_bounds__(256, NP == 1 ? 3 : 1) gemm_bf16_kernel(const u
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][NT * B_LD];
   __shared__ __attribute__((aligned(16))) uint32_t Sc[NT * kScPitch];  // scale chunk: row r at dword kScPitch r
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lm = lane & 31, lq = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
 
@@ -264,23 +266,43 @@ __global__ void __launch_bounds__(256, NP == 1 ? 3 : 1) gemm_bf16_kernel(const u
 #pragma unroll
     for (int nj = 0; nj < 2; nj++)
       sc[nj] = e8m0_operand(!shifted ? sb[nj] : (sb[nj] > kShift ? sb[nj] - kShift : 0u));
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      bf16x8 bw[2];
-#pragma unroll
-      for (int nj = 0; nj < 2; nj++) bw[nj] = decode8_bf16x8(wv[nj][j], sc[nj]);
-#pragma unroll
-      for (int mi = 0; mi < 2; mi++) {
-        if (64 * wm + 32 * mi >= tl.mlen) continue;  // a 32-row sub-tile past the segment
+    // A wave whose rows hold no pair skips the MFMAs; otherwise both of its
+    // 32-row sub-tiles run (rows past the segment hold zeros), so the body
+    // has no branch and its LDS reads, converts and MFMAs interleave: the A
+    // fragments are read one k-step ahead, and a scheduling barrier between
+    // k-steps keeps the compiler from hoisting the whole stage's reads.
+    if (64 * wm < tl.mlen) {
+      auto aload = [&](int j, int mi, int pc) {
         const int ml = 64 * wm + 32 * mi + lm;
+        return *reinterpret_cast<const u32x4*>(&As[buf][pc][ml * A_LD + lq * 32 + j * 8]);
+      };
+      u32x4 av[2][2][NP];
 #pragma unroll
-        for (int pc = 0; pc < NP; pc++) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(&As[buf][pc][ml * A_LD + lq * 32 + j * 8]);
+      for (int mi = 0; mi < 2; mi++)
 #pragma unroll
-          for (int nj = 0; nj < 2; nj++)
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bw[nj],
-                                                                  acc[mi][nj], 0, 0, 0);
+        for (int pc = 0; pc < NP; pc++) av[0][mi][pc] = aload(0, mi, pc);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (j + 1 < 4) {
+#pragma unroll
+          for (int mi = 0; mi < 2; mi++)
+#pragma unroll
+            for (int pc = 0; pc < NP; pc++) av[(j + 1) & 1][mi][pc] = aload(j + 1, mi, pc);
         }
+        bf16x8 bw[2];
+#pragma unroll
+        for (int nj = 0; nj < 2; nj++) bw[nj] = decode8_bf16x8(wv[nj][j], sc[nj]);
+#pragma unroll
+        for (int mi = 0; mi < 2; mi++)
+#pragma unroll
+          for (int pc = 0; pc < NP; pc++)
+#pragma unroll
+            for (int nj = 0; nj < 2; nj++)
+              acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j & 1][mi][pc]),
+                                                                    bw[nj], acc[mi][nj], 0, 0, 0);
+#ifndef MXFP4_GEMM_NO_SCHED_BARRIER
+        __builtin_amdgcn_sched_barrier(0);
+#endif
       }
     }
     if (NP == 3 && ((st & 1) || st + 1 == nst)) fold();
