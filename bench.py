@@ -56,12 +56,15 @@ DECODE_WORKLOADS = ("tiny", "decode", "decode8")
 KERNEL_SOURCES = {
     "gemv": ["mxfp4_block_scaled_amd/csrc/gemv_rows.hip", "mxfp4_block_scaled_amd/csrc/gemv_one.hip",
              "mxfp4_block_scaled_amd/csrc/device_common.h", "mxfp4_block_scaled_amd/csrc/wave_routing.h"],
-    "gemm": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
-    "swiglu": ["mxfp4_block_scaled_amd/csrc/gemm.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+    "gemm": ["mxfp4_block_scaled_amd/csrc/gemm_regdec.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+    "swiglu": ["mxfp4_block_scaled_amd/csrc/gemm_regdec.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "mx": ["mxfp4_block_scaled_amd/csrc/gemm_mx.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "gemmp": ["mxfp4_block_scaled_amd/csrc/gemm_regdec.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
 }
-KERNEL_NAMES = {"gemv": "gemv_rows_kernel", "gemm": "gemm_bf16_kernel", "gemmp": "gemm_regdec_kernel"}
+# the dominant kernel per path: bf16 prefill-shaped calls on canonical weights
+# run the register-decode GEMM's canonical-layout instantiation
+KERNEL_NAMES = {"gemv": "gemv_rows_kernel", "gemm": "gemm_regdec_kernel<0, true>",
+                "gemmp": "gemm_regdec_kernel<0, false>"}
 
 
 def log(*a):
@@ -598,8 +601,9 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
         unit = "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4)}
-        roof["kernel"] = ("gemm_regdec_kernel<1> + gemm_regdec_kernel<2> (whole call)" if kind == "swiglup"
-                          else "gemm_bf16_kernel<1> + gemm_bf16_kernel<2> (whole call)")
+        roof["kernel"] = ("gemm_regdec_kernel<1, false> + gemm_regdec_kernel<2, false> (whole call)"
+                          if kind == "swiglup"
+                          else "gemm_regdec_kernel<1, true> + gemm_regdec_kernel<2, true> (whole call)")
         roof["launch_ms"] = round(ms_step, 6)
     elif kind in ("gemv", "gemvp"):
         # one launch per step: the fused kernel is the whole call

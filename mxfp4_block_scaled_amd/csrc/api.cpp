@@ -50,6 +50,22 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Prefill-shaped grouped GEMM on canonical weights with bf16 activations: the
+// register-decode kernel (weights brought into LDS by DMA, 8-wave workgroups
+// over 128 pairs x 512 rows) where it applies (O % 4 == 0), else the
+// LDS-staged kernel of gemm.hip. Both give the same results contract.
+bool regdec_canon_ok(int64_t T, int64_t O, int64_t G) { return gemm_regdec_canon_supported(T, O, G); }
+
+hipError_t launch_canonical_gemm(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* perm,
+                                 const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part,
+                                 int64_t T, int64_t K, int64_t O, int64_t G, hipStream_t stream) {
+  if (regdec_canon_ok(T, O, G))
+    return launch_gemm_regdec_canon(x, packed, scales, perm, tiles, n_tiles, max_tiles, part, (int)T, (int)K, (int)O,
+                                    (int)G, stream);
+  return launch_gemm_bf16(x, packed, scales, perm, tiles, n_tiles, max_tiles, part, (int)T, (int)K, (int)O, (int)G,
+                          stream);
+}
+
 // Decode-shaped kernel: the row-contiguous one unless the MFMA one is asked
 // for. Both address an expert's packed bytes with 32-bit buffer offsets, so
 // the decode-shaped path needs O * G * 16 < 2^31.
@@ -223,8 +239,8 @@ int run_linear(const void* x, const uint8_t* packed, const uint8_t* scales, cons
         err = launch_gemm_f32(xs, packed, scales, b.perm, b.tiles, b.n_tiles, gemm_max_tiles(d.P, d.E), part,
                               (int)d.T, (int)d.K, (int)d.O, (int)d.G, stream);
     } else if (err == hipSuccess) {
-      err = launch_gemm_bf16(static_cast<const uint16_t*>(x), packed, scales, b.perm, b.tiles, b.n_tiles,
-                             gemm_max_tiles(d.P, d.E), part, (int)d.T, (int)d.K, (int)d.O, (int)d.G, stream);
+      err = launch_canonical_gemm(static_cast<const uint16_t*>(x), packed, scales, b.perm, b.tiles, b.n_tiles,
+                                  gemm_max_tiles(d.P, d.E), part, d.T, d.K, d.O, d.G, stream);
     }
     if (err == hipSuccess)
       err = launch_combine(reinterpret_cast<const float*>(base + L.part), b.slot_of_pair, p, shared, y, (int)d.T,
@@ -432,11 +448,17 @@ int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8
   hipError_t err = launch_bucket_multi(sel, (int)d.gu.P, (int)d.gu.E, reinterpret_cast<int32_t*>(base + L.bcount), b,
                                        stream);
   if (err == hipSuccess)
-    err = launch_gemm_swiglu(x, gu_packed, gu_scales, b.perm, b.tiles, b.n_tiles, max_tiles, h, (int)d.gu.T,
-                             (int)d.gu.K, (int)d.F, (int)d.gu.G, stream);
+    err = regdec_canon_ok(d.gu.T, 2 * d.F, d.gu.G) && d.F % 4 == 0
+              ? launch_gemm_regdec_canon_swiglu(x, gu_packed, gu_scales, b.perm, b.tiles, b.n_tiles, max_tiles, h,
+                                                (int)d.gu.T, (int)d.gu.K, (int)d.F, (int)d.gu.G, stream)
+              : launch_gemm_swiglu(x, gu_packed, gu_scales, b.perm, b.tiles, b.n_tiles, max_tiles, h, (int)d.gu.T,
+                                   (int)d.gu.K, (int)d.F, (int)d.gu.G, stream);
   if (err == hipSuccess)
-    err = launch_gemm_direct(h, dn_packed, dn_scales, b.tiles, b.n_tiles, max_tiles, part, d.dn.P, (int)d.dn.O,
-                             (int)d.dn.G, stream);
+    err = regdec_canon_ok(d.dn.P, d.dn.O, d.dn.G)
+              ? launch_gemm_regdec_canon_direct(h, dn_packed, dn_scales, b.tiles, b.n_tiles, max_tiles, part, d.dn.P,
+                                                (int)d.dn.O, (int)d.dn.G, stream)
+              : launch_gemm_direct(h, dn_packed, dn_scales, b.tiles, b.n_tiles, max_tiles, part, d.dn.P,
+                                   (int)d.dn.O, (int)d.dn.G, stream);
   if (err == hipSuccess)
     err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.dn.T, (int)d.dn.K, (int)d.dn.O, MXFP4_DTYPE_BF16,
                          stream);
@@ -832,11 +854,10 @@ int mxfp4_moe_gemm_stage(const void* x, const uint8_t* packed, const uint8_t* sc
   st = check_device();
   if (st != MXFP4_OK) return st;
   char* base = static_cast<char*>(workspace);
-  const hipError_t err = launch_gemm_bf16(
+  const hipError_t err = launch_canonical_gemm(
       static_cast<const uint16_t*>(x), packed, scales, reinterpret_cast<const int32_t*>(base + L.perm),
       reinterpret_cast<const GemmTile*>(base + L.tiles), reinterpret_cast<const int32_t*>(base + L.n_tiles),
-      gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), (int)d.T, (int)d.K, (int)d.O, (int)d.G,
-      stream);
+      gemm_max_tiles(d.P, d.E), reinterpret_cast<float*>(base + L.part), d.T, d.K, d.O, d.G, stream);
   return hip_status(err);
 }
 

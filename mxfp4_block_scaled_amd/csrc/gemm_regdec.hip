@@ -1,4 +1,4 @@
-// Prefill-shaped grouped GEMM on prepared weights, decoded in registers:
+// Prefill-shaped grouped GEMM, weights decoded in registers:
 // bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation, the same
 // results contract as the LDS-staged kernel of gemm.hip (page "MXFP4 Routed
 // Expert Linear", "Reconstruct the matrix in the right orientation": each
@@ -6,7 +6,15 @@
 // Dequant", "How it works": code n of byte j, low nibble first, times
 // 2^(s-127)).
 //
-// The weights come in the prepared layout of prepare_mx_kernel (a load-time
+// Two weight layouts. Canonical (CANON): packed (E, O, G, 16) and scales
+// (E, O, G) as the caller holds them; the weight DMA fetches each lane's
+// 16-byte group straight from that layout into the fragment-major slot order
+// below, and the scale bytes come into LDS in windows of 16 groups (each
+// row's bytes read as whole dwords from the dword boundary below them).
+// The weights and activations then use two-slot rings, one chunk ahead,
+// with a full wait per chunk, as the scale windows leave no room for a third
+// weight slot.
+// Prepared: the weights come in the prepared layout of prepare_mx_kernel (a load-time
 // byte permutation: per expert, 128-row tile and chunk of 4 groups, the group
 // slots of the 8 16-row fragments in MFMA lane order - slot l of fragment f =
 // row 16 f + (l & 15), group 4q + (l >> 4) - as 8 blocks of 1 KB, block
@@ -79,6 +87,13 @@ constexpr int kWBytes = NW / 16 * 1024;   // weight slot: 32 fragment blocks of 
 constexpr int kXDma = kXBytes / (1024 * kWaves);  // 1 KB requests per wave and chunk
 constexpr int kWDma = kWBytes / (1024 * kWaves);
 constexpr int kScLoads = 2;                        // scale dwords per wave and chunk
+// canonical weights: a scale window is 16 groups (4 chunks) of the
+// workgroup's 512 rows, each row's 16 bytes with the dword boundary below
+// them (5 dwords, pitch 20 bytes), 5 DMA requests per wave
+constexpr int kScPitch = 20;
+constexpr int kScWin = NW * kScPitch;
+constexpr int kScDma = kScWin / (256 * kWaves);
+static_assert(kScDma * 256 * kWaves == kScWin, "scale window DMA");
 
 constexpr uint32_t kShiftFrom = 253;  // scale bytes whose decoded weights may overflow bf16
 constexpr uint32_t kShift = 3;        // scale-byte shift of a wave that met one
@@ -99,7 +114,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 //           output fp32 rows of `part`.
 enum Mode { kGather = 0, kSwiGLU = 1, kDirect = 2 };
 
-template <int MODE>
+template <int MODE, bool CANON>
 __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __restrict__ x,
                                                              const uint8_t* __restrict__ pcodes,
                                                              const uint8_t* __restrict__ pscales,
@@ -125,9 +140,11 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   __shared__ __attribute__((aligned(16))) uint8_t X1[kXBytes];
   __shared__ __attribute__((aligned(16))) uint8_t W0[kWBytes];
   __shared__ __attribute__((aligned(16))) uint8_t W1[kWBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t W2[kWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t W2[CANON ? 16 : kWBytes];  // canonical: two weight slots
+  // canonical: scale-byte windows of 16 groups, two slots
+  __shared__ __attribute__((aligned(16))) uint8_t Sc[CANON ? 2 * kScWin : 16];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lc = lane >> 4;
   const int wm = w >> 2, wn = w & 3;
   const int nq = (G + 3) / 4;  // chunks
@@ -147,21 +164,67 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRsrcFlags);
 
-  // ---- weight DMA: request j of wave w fetches code block 4 w + j of the
-  // workgroup (prepared tile 4 nt + (w >> 1), block 4 (w & 1) + j: dword j of
-  // fragments 4 (w & 1) .. +3) into the same 1 KB of a slot
-  const int64_t ebase = (int64_t)tl.e * n_ptiles * nq * 512;  // group slots before expert e
-  const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(pcodes + ebase * 16), (short)0, n_ptiles * nq * 8192, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rsc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(pscales + ebase), (short)0, n_ptiles * nq * 512, kRsrcFlags);
+  // ---- weight DMA: request j of wave w fills LDS block 4 w + j of a slot.
+  // Prepared weights: code block 4 w + j of the workgroup (prepared tile
+  // 4 nt + (w >> 1), block 4 (w & 1) + j: dword j of fragments 4 (w & 1) .. +3).
+  // Canonical weights: fragment i = (4 w + j) & 7 of wave column
+  // t = (4 w + j) >> 3, lane l fetching the 16 bytes of (row crow(t, i, l & 15),
+  // group 4 q + (l >> 4)) - the same fragment-major slot order.
+  // crow: the matrix row of fragment i, row r of wave column t.
+  auto crow = [&](int t, int i, int r) -> int {
+    if constexpr (MODE == kSwiGLU) {
+      const int f = 64 * (4 * nt + t) + 16 * (i & 3) + r;
+      return f < F ? (i < 4 ? f : F + f) : -1;
+    } else {
+      const int row = NW * nt + PT * t + 16 * i + r;
+      return row < O ? row : -1;
+    }
+  };
+  const int64_t ebase = CANON ? (int64_t)tl.e * O * G : (int64_t)tl.e * n_ptiles * nq * 512;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(pcodes + ebase * 16), (short)0, CANON ? O * G * 16 : n_ptiles * nq * 8192, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(pscales + ebase), (short)0, CANON ? O * G : n_ptiles * nq * 512, kRsrcFlags);
   const int dpt = 4 * nt + (w >> 1);
-  // byte offset of this lane's slot of the first fragment block, chunk 0 (chunk q: + 8192 q)
+  // prepared: byte offset of this lane's slot of the first fragment block, chunk 0 (chunk q: + 8192 q)
   const uint32_t w_off = dpt < n_ptiles ? (uint32_t)(((dpt * nq * 8 + 4 * (w & 1)) * 64 + lane) * 16) : kOob;
+  // canonical: byte offset of this lane's group in chunk 0 per request (chunk q: + 64 q)
+  uint32_t wc_off[CANON ? kWDma : 1];
+  if constexpr (CANON) {
+#pragma unroll
+    for (int j = 0; j < kWDma; j++) {
+      const int row = crow((4 * w + j) >> 3, (4 * w + j) & 7, lr);
+      wc_off[j] = row >= 0 ? ((uint32_t)row * (uint32_t)G + (uint32_t)lc) * 16u : kOob;
+    }
+  }
   // scale dwords of this wave's own tile (fragments 0..3 and 4..7), chunk 0 (chunk q: + 512 q)
   const int pt = 4 * nt + wn;
   const uint32_t s_off = pt < n_ptiles ? (uint32_t)((pt * nq * 2 * 64 + lane) * 4) : kOob;
+  // canonical scales: the expert's bytes read as whole dwords from the dword
+  // boundary below them (a dword that holds a valid byte lies in a valid
+  // page); request m of wave w fills dwords d = 64 (5 w + m) + l of a window
+  // slot: LDS row R = d / 5 (row crow(R >> 7, (R >> 4) & 7, R & 15)), dword d % 5
+  const uintptr_t s_first = reinterpret_cast<uintptr_t>(pscales) + (uintptr_t)ebase;
+  const int s_mis = CANON ? (int)(s_first & 3) : 0;
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s_first & ~(uintptr_t)3), (short)0, (s_mis + O * G + 3) & ~3, kRsrcFlags);
+  uint32_t sw_off[CANON ? kScDma : 1];  // byte offset of this lane's dword, window 0 (window C: + 16 C)
+  int sc_lds[CANON ? kWI : 1];          // byte of fragment i's row in a window slot where group 16 C starts
+  if constexpr (CANON) {
+#pragma unroll
+    for (int m = 0; m < kScDma; m++) {
+      const int d = 64 * (kScDma * w + m) + lane, R = d / 5, k = d - 5 * R;
+      const int row = crow(R >> 7, (R >> 4) & 7, R & 15);
+      sw_off[m] = row >= 0 ? (uint32_t)(((s_mis + row * G) >> 2) + k) * 4u : kOob;
+    }
+#pragma unroll
+    for (int i = 0; i < kWI; i++) {
+      const int row = crow(wn, i, lr);
+      sc_lds[i] = (PT * wn + 16 * i + lr) * kScPitch + (row >= 0 ? (s_mis + row * G) & 3 : 0);
+    }
+  }
 
+  // prepared: two scale dwords per chunk (four fragments each), a three-slot ring
   uint32_t wsp[3][kScLoads];
   auto dma_x = [&](int q, uint8_t* dst) {
 #pragma unroll
@@ -175,14 +238,28 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     }
   };
   auto dma_w = [&](int q, uint8_t* dst, int slot) {
+    if constexpr (CANON) {
+      // a group past G moves the offset past the resource (zero codes)
+      const uint32_t past = (uint32_t)(G - 1 - (4 * q + lc)) >> 31 << 31;
 #pragma unroll
-    for (int j = 0; j < kWDma; j++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + (4 * w + j) * 1024), 16,
-                                               (int)((w_off + 8192u * q + 1024u * j) | (w_off & kOob)), 0, 0, 0);
+      for (int j = 0; j < kWDma; j++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + (4 * w + j) * 1024), 16,
+                                                 (int)((wc_off[j] + 64u * q) | past), 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int h = 0; h < kScLoads; h++)
-      wsp[slot][h] =
-          __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)((s_off + 512u * q + 256u * h) | (s_off & kOob)), 0, 0);
+      for (int j = 0; j < kWDma; j++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + (4 * w + j) * 1024), 16,
+                                                 (int)((w_off + 8192u * q + 1024u * j) | (w_off & kOob)), 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < kScLoads; h++)
+        wsp[slot][h] =
+            __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)((s_off + 512u * q + 256u * h) | (s_off & kOob)), 0, 0);
+    }
+  };
+  // canonical: request m of scale window C into window slot C & 1
+  auto dma_sc = [&](int C, int m) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(Sc + (C & 1) * kScWin + (kScDma * w + m) * 256), 4,
+                                             (int)(sw_off[m] + 16u * C), 0, 0, 0);
   };
   // wait until this wave's activation DMA of the next chunk has landed: it
   // was followed by one chunk's weight and scale requests
@@ -201,89 +278,161 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     for (int j = 0; j < kWJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   bool shifted = false;  // wave-uniform: decoding at scale byte s - kShift
 
-  // One chunk q, activation slot q mod 2 and weight slot q mod 3 (both
-  // compile-time): request the activations of chunk q + 1 (into the slot read
-  // last during chunk q - 1) and the weights of chunk q + 2 (likewise),
-  // multiply chunk q, wait for this wave's activation DMA of chunk q + 1,
-  // barrier. Past the last chunk the requests repeat the last chunk into
-  // slots nobody reads again, so the number of requests per chunk - and every
-  // wait count - is fixed.
-  auto step = [&](int q, auto xs, auto ws) {
-    constexpr int RX = decltype(xs)::value, RW = decltype(ws)::value, RWN = (RW + 2) % 3;
-    const uint8_t* xc = RX == 0 ? X0 : X1;
-    uint8_t* xn = RX == 0 ? X1 : X0;
-    const uint8_t* wc = RW == 0 ? W0 : (RW == 1 ? W1 : W2);
-    uint8_t* wnx = RWN == 0 ? W0 : (RWN == 1 ? W1 : W2);
-    dma_x(min(q + 1, nq - 1), xn);
-    dma_w(min(q + 2, nq - 1), wnx, RWN);
-    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
-    if (live) {
-      uint32_t sb[kWI];
-      bool big = false;
+  // the MFMAs of one chunk: activations xc, weight codes wc, the 8 scale bytes
+  auto mma_chunk = [&](const uint8_t* xc, const uint8_t* wc, const uint32_t(&sb)[kWI]) {
+    bool big = false;
 #pragma unroll
-      for (int i = 0; i < kWI; i++) {
-        sb[i] = (wsp[RW][i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        big |= sb[i] >= kShiftFrom;
-      }
-      if (!shifted && __ballot(big) != 0) {
-        shifted = true;
-#pragma unroll
-        for (int i = 0; i < kWI; i++)
-#pragma unroll
-          for (int j = 0; j < kWJ; j++) acc[i][j] *= 0.125f;
-      }
-      float sc[kWI];
+    for (int i = 0; i < kWI; i++) big |= sb[i] >= kShiftFrom;
+    if (!shifted && __ballot(big) != 0) {
+      shifted = true;
 #pragma unroll
       for (int i = 0; i < kWI; i++)
-        sc[i] = e8m0_operand(!shifted ? sb[i] : (sb[i] > kShift ? sb[i] - kShift : 0u));
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        bf16x8 b[kWJ];
+        for (int j = 0; j < kWJ; j++) acc[i][j] *= 0.125f;
+    }
+    float sc[kWI];
 #pragma unroll
-        for (int j = 0; j < kWJ; j++) {
-          // row p = 64 wm + 16 j + lr (p & 15 = lr); rows past the tile hold zeros (their DMA read past the resource)
-          b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                &xc[(64 * wm + 16 * j + lr) * ROWB + 16 * ((4 * lc + s) ^ lr)]));
-        }
+    for (int i = 0; i < kWI; i++)
+      sc[i] = e8m0_operand(!shifted ? sb[i] : (sb[i] > kShift ? sb[i] - kShift : 0u));
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      // canonical: lane group c takes dword (s + c) & 3 of its slots at k-step s,
+      // so the 64 lanes' 4-byte reads at a 16-byte stride hit 64 distinct banks;
+      // its activations follow the same order
+      const int sd = CANON ? (s + lc) & 3 : s;
+      bf16x8 b[kWJ];
+#pragma unroll
+      for (int j = 0; j < kWJ; j++) {
+        // row p = 64 wm + 16 j + lr (p & 15 = lr); rows past the tile hold zeros (their DMA read past the resource)
+        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                              &xc[(64 * wm + 16 * j + lr) * ROWB + 16 * ((4 * lc + sd) ^ lr)]));
+      }
+      uint32_t raw[kWI];
+      if constexpr (CANON) {
+        // dword sd of this lane's slot of each of the wave's fragments (blocks 8 wn .. 8 wn + 7)
+#pragma unroll
+        for (int i = 0; i < kWI; i++)
+          raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(8 * wn + i) * 1024 + 16 * lane + 4 * sd]);
+      } else {
         // dword s of this lane's slot of each fragment (8 codes each): blocks s and 4 + s of tile wn
         const u32x4 lo = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + s) * 1024 + 16 * lane]);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + 4 + s) * 1024 + 16 * lane]);
-        const uint32_t raw[kWI] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-        for (int i = 0; i < kWI; i++) {
-          const bf16x8 a = decode8_bf16x8(raw[i], sc[i]);
+        for (int t = 0; t < 4; t++) raw[t] = lo[t], raw[4 + t] = hi[t];
+      }
 #pragma unroll
-          for (int j = 0; j < kWJ; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
-        }
+      for (int i = 0; i < kWI; i++) {
+        const bf16x8 a = decode8_bf16x8(raw[i], sc[i]);
+#pragma unroll
+        for (int j = 0; j < kWJ; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
       }
     }
-    wait_next_x();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
-    __builtin_amdgcn_s_barrier();
   };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-  dma_x(0, X0);
-  dma_w(0, W0, 0);
-  dma_w(min(1, nq - 1), W1, 1);
-  wait_next_x();  // chunk 0's activations and weights: followed by chunk 1's weight requests
-  __builtin_amdgcn_s_barrier();
-  int q = 0;
-  for (; q + 5 < nq; q += 6) {  // activation slots cycle by 2, weight slots by 3
-    step(q, C0{}, C0{});
-    step(q + 1, C1{}, C1{});
-    step(q + 2, C0{}, C2{});
-    step(q + 3, C1{}, C0{});
-    step(q + 4, C0{}, C1{});
-    step(q + 5, C1{}, C2{});
+
+  if constexpr (!CANON) {
+    // One chunk q, activation slot q mod 2 and weight slot q mod 3 (both
+    // compile-time): request the activations of chunk q + 1 (into the slot read
+    // last during chunk q - 1) and the weights of chunk q + 2 (likewise),
+    // multiply chunk q, wait for this wave's activation DMA of chunk q + 1,
+    // barrier. Past the last chunk the requests repeat the last chunk into
+    // slots nobody reads again, so the number of requests per chunk - and every
+    // wait count - is fixed.
+    auto step = [&](int q, auto xs, auto ws) {
+      constexpr int RX = decltype(xs)::value, RW = decltype(ws)::value, RWN = (RW + 2) % 3;
+      const uint8_t* xc = RX == 0 ? X0 : X1;
+      uint8_t* xn = RX == 0 ? X1 : X0;
+      const uint8_t* wc = RW == 0 ? W0 : (RW == 1 ? W1 : W2);
+      uint8_t* wnx = RWN == 0 ? W0 : (RWN == 1 ? W1 : W2);
+      dma_x(min(q + 1, nq - 1), xn);
+      dma_w(min(q + 2, nq - 1), wnx, RWN);
+      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
+      if (live) {
+        uint32_t sb[kWI];
+#pragma unroll
+        for (int i = 0; i < kWI; i++) sb[i] = (wsp[RW][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        mma_chunk(xc, wc, sb);
+      }
+      wait_next_x();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+      __builtin_amdgcn_s_barrier();
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    dma_x(0, X0);
+    dma_w(0, W0, 0);
+    dma_w(min(1, nq - 1), W1, 1);
+    wait_next_x();  // chunk 0's activations and weights: followed by chunk 1's weight requests
+    __builtin_amdgcn_s_barrier();
+    int q = 0;
+    for (; q + 5 < nq; q += 6) {  // activation slots cycle by 2, weight slots by 3
+      step(q, C0{}, C0{});
+      step(q + 1, C1{}, C1{});
+      step(q + 2, C0{}, C2{});
+      step(q + 3, C1{}, C0{});
+      step(q + 4, C0{}, C1{});
+      step(q + 5, C1{}, C2{});
+    }
+    if (q < nq) step(q, C0{}, C0{});
+    if (q + 1 < nq) step(q + 1, C1{}, C1{});
+    if (q + 2 < nq) step(q + 2, C0{}, C2{});
+    if (q + 3 < nq) step(q + 3, C1{}, C0{});
+    if (q + 4 < nq) step(q + 4, C0{}, C1{});
+  } else {
+    // One chunk q, slots q mod 2 (compile-time): request the activations and
+    // weights of chunk q + 1 and a part of the next scale window (requests
+    // 0, 1 at the window's first chunk, then one per chunk), multiply chunk q,
+    // wait for all of this wave's requests, barrier: the slots written during
+    // chunk q were last read during chunk q - 1, the window slot during the
+    // window before.
+    const int nwin = (G + 15) / 16;
+    auto step = [&](int q, auto xs) {
+      constexpr int R = decltype(xs)::value;
+      const uint8_t* xc = R == 0 ? X0 : X1;
+      const uint8_t* wc = R == 0 ? W0 : W1;
+      if (q + 1 < nq) {
+        dma_x(q + 1, R == 0 ? X1 : X0);
+        dma_w(q + 1, R == 0 ? W1 : W0, 0);
+      }
+      const int C = q >> 2, qq = q & 3;
+      if (C + 1 < nwin) {
+        if (qq == 0) {
+          dma_sc(C + 1, 0);
+          dma_sc(C + 1, 1);
+        } else {
+          dma_sc(C + 1, qq + 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
+      if (live) {
+        const uint8_t* sw = Sc + (C & 1) * kScWin + 4 * qq + lc;
+        // a group past G reads another row's byte: zero instead
+        const bool in_g = 4 * q + lc < G;
+        uint32_t sb[kWI];
+#pragma unroll
+        for (int i = 0; i < kWI; i++) sb[i] = in_g ? sw[sc_lds[i]] : 0u;
+        mma_chunk(xc, wc, sb);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's requests have landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+      __builtin_amdgcn_s_barrier();
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    dma_x(0, X0);
+    dma_w(0, W0, 0);
+#pragma unroll
+    for (int m = 0; m < kScDma; m++) dma_sc(0, m);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_barrier();
+    int q = 0;
+    for (; q + 1 < nq; q += 2) {
+      step(q, C0{});
+      step(q + 1, C1{});
+    }
+    if (q < nq) step(q, C0{});
   }
-  if (q < nq) step(q, C0{}, C0{});
-  if (q + 1 < nq) step(q + 1, C1{}, C1{});
-  if (q + 2 < nq) step(q + 2, C0{}, C2{});
-  if (q + 3 < nq) step(q + 3, C1{}, C0{});
-  if (q + 4 < nq) step(q + 4, C0{}, C1{});
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
   if (shifted) {
 #pragma unroll
@@ -330,7 +479,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   }
 }
 
-template <int MODE>
+template <int MODE, bool CANON>
 hipError_t launch_mode(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* perm,
                        const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, void* out, int64_t x_rows,
                        int K, int O, int G, int F, hipStream_t stream) {
@@ -340,7 +489,7 @@ hipError_t launch_mode(const uint16_t* x, const uint8_t* pcodes, const uint8_t* 
   const int64_t nblk = (max_tiles + 15) / 16 * 16 * n_wg;  // an even number of tiles per XCD
   if (nblk <= 0) return hipSuccess;
   const uint32_t x_bytes = (uint32_t)(x_rows * 64 * G);
-  hipLaunchKernelGGL(gemm_regdec_kernel<MODE>, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, x, pcodes, pscales,
+  hipLaunchKernelGGL((gemm_regdec_kernel<MODE, CANON>), dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, x, pcodes, pscales,
                      perm, tiles, n_tiles, out, K, O, G, F, n_wg, n_ptiles, x_bytes);
   return hipGetLastError();
 }
@@ -354,25 +503,55 @@ bool gemm_regdec_supported(int64_t T, int64_t O, int64_t G) {
   return O % 4 == 0 && T * 64 * G < ((int64_t)1 << 31) && prepared < ((int64_t)1 << 31);
 }
 
+bool gemm_regdec_canon_supported(int64_t T, int64_t O, int64_t G) {
+  // 32-bit byte offsets into the activations and into one expert's packed
+  // bytes, whole 16-byte output stores
+  return O % 4 == 0 && T * 64 * G < ((int64_t)1 << 31) && O * G * 16 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_regdec_canon(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
+                                    const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
+                                    int64_t max_tiles, float* part, int T, int K, int O, int G, hipStream_t stream) {
+  if (!gemm_regdec_canon_supported(T, O, G)) return hipErrorInvalidValue;
+  return launch_mode<kGather, true>(x, packed, scales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0, stream);
+}
+
+hipError_t launch_gemm_regdec_canon_swiglu(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales,
+                                           const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
+                                           int64_t max_tiles, uint16_t* h, int T, int K, int F, int G,
+                                           hipStream_t stream) {
+  if (F % 4 || !gemm_regdec_canon_supported(T, 2 * (int64_t)F, G)) return hipErrorInvalidValue;
+  return launch_mode<kSwiGLU, true>(x, gu_packed, gu_scales, perm, tiles, n_tiles, max_tiles, h, T, K, 2 * F, G, F,
+                                    stream);
+}
+
+hipError_t launch_gemm_regdec_canon_direct(const uint16_t* h, const uint8_t* packed, const uint8_t* scales,
+                                           const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                                           float* part, int64_t P, int O, int G, hipStream_t stream) {
+  if (!gemm_regdec_canon_supported(P, O, G)) return hipErrorInvalidValue;
+  return launch_mode<kDirect, true>(h, packed, scales, nullptr, tiles, n_tiles, max_tiles, part, P, 1, O, G, 0,
+                                    stream);
+}
+
 hipError_t launch_gemm_regdec(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales, const int32_t* perm,
                               const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part, int T,
                               int K, int O, int G, hipStream_t stream) {
   if (!gemm_regdec_supported(T, O, G)) return hipErrorInvalidValue;
-  return launch_mode<kGather>(x, pcodes, pscales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0, stream);
+  return launch_mode<kGather, false>(x, pcodes, pscales, perm, tiles, n_tiles, max_tiles, part, T, K, O, G, 0, stream);
 }
 
 hipError_t launch_gemm_regdec_swiglu(const uint16_t* x, const uint8_t* pcodes, const uint8_t* pscales,
                                      const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
                                      int64_t max_tiles, uint16_t* h, int T, int K, int F, int G, hipStream_t stream) {
   if (F % 4 || !gemm_regdec_supported(T, 2 * (int64_t)F, G)) return hipErrorInvalidValue;
-  return launch_mode<kSwiGLU>(x, pcodes, pscales, perm, tiles, n_tiles, max_tiles, h, T, K, 2 * F, G, F, stream);
+  return launch_mode<kSwiGLU, false>(x, pcodes, pscales, perm, tiles, n_tiles, max_tiles, h, T, K, 2 * F, G, F, stream);
 }
 
 hipError_t launch_gemm_regdec_direct(const uint16_t* h, const uint8_t* pcodes, const uint8_t* pscales,
                                      const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part,
                                      int64_t P, int O, int G, hipStream_t stream) {
   if (!gemm_regdec_supported(P, O, G)) return hipErrorInvalidValue;
-  return launch_mode<kDirect>(h, pcodes, pscales, nullptr, tiles, n_tiles, max_tiles, part, P, 1, O, G, 0, stream);
+  return launch_mode<kDirect, false>(h, pcodes, pscales, nullptr, tiles, n_tiles, max_tiles, part, P, 1, O, G, 0, stream);
 }
 
 }  // namespace mxfp4

@@ -179,6 +179,23 @@ hipError_t launch_gemm_regdec_swiglu(const uint16_t* x, const uint8_t* pcodes, c
 hipError_t launch_gemm_regdec_direct(const uint16_t* h, const uint8_t* pcodes, const uint8_t* pscales,
                                      const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles, float* part,
                                      int64_t P, int O, int G, hipStream_t stream);
+// The register-decode GEMM on canonical weights (packed (E, O, G, 16),
+// scales (E, O, G)): the same kernel, its weight DMA fetching each lane's
+// 16-byte group straight from the canonical layout and its scale bytes
+// loaded per lane; needs gemm_regdec_canon_supported: O % 4 == 0 and 32-bit
+// offsets into the activations and one expert's packed bytes. The SwiGLU
+// gate/up stage takes (E, 2F, G, 16) with gate rows over up rows, F % 4 == 0.
+bool gemm_regdec_canon_supported(int64_t T, int64_t O, int64_t G);
+hipError_t launch_gemm_regdec_canon(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
+                                    const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
+                                    int64_t max_tiles, float* part, int T, int K, int O, int G, hipStream_t stream);
+hipError_t launch_gemm_regdec_canon_swiglu(const uint16_t* x, const uint8_t* gu_packed, const uint8_t* gu_scales,
+                                           const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles,
+                                           int64_t max_tiles, uint16_t* h, int T, int K, int F, int G,
+                                           hipStream_t stream);
+hipError_t launch_gemm_regdec_canon_direct(const uint16_t* h, const uint8_t* packed, const uint8_t* scales,
+                                           const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                                           float* part, int64_t P, int O, int G, hipStream_t stream);
 // SwiGLU expert block, gate/up stage: weights (E, 2F, G, 16) with gate rows
 // [0, F) over up rows [F, 2F); writes h[sorted position, f] = bf16 of
 // silu(gate) * up, h being (P, F).
