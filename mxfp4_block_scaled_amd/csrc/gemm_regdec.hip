@@ -87,12 +87,14 @@ constexpr int kWBytes = NW / 16 * 1024;   // weight slot: 32 fragment blocks of 
 constexpr int kXDma = kXBytes / (1024 * kWaves);  // 1 KB requests per wave and chunk
 constexpr int kWDma = kWBytes / (1024 * kWaves);
 constexpr int kScLoads = 2;                        // scale dwords per wave and chunk
-// canonical weights: a scale window is 16 groups (4 chunks) of the
-// workgroup's 512 rows, each row's 16 bytes with the dword boundary below
-// them (5 dwords, pitch 20 bytes), 5 DMA requests per wave
-constexpr int kScPitch = 20;
+// canonical weights: a scale window is 8 groups (2 chunks) of the
+// workgroup's 512 rows, each row's 8 bytes with the dword boundary below
+// them (3 dwords, pitch 12 bytes), 3 DMA requests per wave
+constexpr int kScPitch = 12;
+constexpr int kScWords = kScPitch / 4;
 constexpr int kScWin = NW * kScPitch;
 constexpr int kScDma = kScWin / (256 * kWaves);
+constexpr int kScZero = 16 * kScPitch * kWI;  // zero bytes after a window slot
 static_assert(kScDma * 256 * kWaves == kScWin, "scale window DMA");
 
 constexpr uint32_t kShiftFrom = 253;  // scale bytes whose decoded weights may overflow bf16
@@ -141,8 +143,11 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   __shared__ __attribute__((aligned(16))) uint8_t W0[kWBytes];
   __shared__ __attribute__((aligned(16))) uint8_t W1[kWBytes];
   __shared__ __attribute__((aligned(16))) uint8_t W2[CANON ? 16 : kWBytes];  // canonical: two weight slots
-  // canonical: scale-byte windows of 16 groups, two slots
-  __shared__ __attribute__((aligned(16))) uint8_t Sc[CANON ? 2 * kScWin : 16];
+  // canonical: scale-byte windows of 8 groups, two slots, each followed by
+  // zero bytes (separate arrays, and every read indexes one of them, so that
+  // a read of one is never taken to wait for a DMA into the other)
+  __shared__ __attribute__((aligned(16))) uint8_t Sc0[CANON ? kScWin + kScZero : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t Sc1[CANON ? kScWin + kScZero : 16];
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lc = lane >> 4;
@@ -202,25 +207,28 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   const uint32_t s_off = pt < n_ptiles ? (uint32_t)((pt * nq * 2 * 64 + lane) * 4) : kOob;
   // canonical scales: the expert's bytes read as whole dwords from the dword
   // boundary below them (a dword that holds a valid byte lies in a valid
-  // page); request m of wave w fills dwords d = 64 (5 w + m) + l of a window
-  // slot: LDS row R = d / 5 (row crow(R >> 7, (R >> 4) & 7, R & 15)), dword d % 5
+  // page); request m of wave w fills dwords d = 64 (3 w + m) + l of a window
+  // slot: LDS row R = d / 3 (row crow(R >> 7, (R >> 4) & 7, R & 15)), dword d % 3
   const uintptr_t s_first = reinterpret_cast<uintptr_t>(pscales) + (uintptr_t)ebase;
   const int s_mis = CANON ? (int)(s_first & 3) : 0;
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(s_first & ~(uintptr_t)3), (short)0, (s_mis + O * G + 3) & ~3, kRsrcFlags);
-  uint32_t sw_off[CANON ? kScDma : 1];  // byte offset of this lane's dword, window 0 (window C: + 16 C)
-  int sc_lds[CANON ? kWI : 1];          // byte of fragment i's row in a window slot where group 16 C starts
+  uint32_t sw_off[CANON ? kScDma : 1];  // byte offset of this lane's dword, window 0 (window C: + 8 C)
+  // byte of fragment i's row in a window slot where group 8 C starts:
+  // sc_lds[i >> 2] + 16 kScPitch i (the rows of fragments 0..3 and of 4..7
+  // share their offset within the dword: rows 16 apart, 16 G = 0 mod 4)
+  int sc_lds[2];
   if constexpr (CANON) {
 #pragma unroll
     for (int m = 0; m < kScDma; m++) {
-      const int d = 64 * (kScDma * w + m) + lane, R = d / 5, k = d - 5 * R;
+      const int d = 64 * (kScDma * w + m) + lane, R = d / kScWords, k = d - kScWords * R;
       const int row = crow(R >> 7, (R >> 4) & 7, R & 15);
       sw_off[m] = row >= 0 ? (uint32_t)(((s_mis + row * G) >> 2) + k) * 4u : kOob;
     }
 #pragma unroll
-    for (int i = 0; i < kWI; i++) {
-      const int row = crow(wn, i, lr);
-      sc_lds[i] = (PT * wn + 16 * i + lr) * kScPitch + (row >= 0 ? (s_mis + row * G) & 3 : 0);
+    for (int h = 0; h < 2; h++) {
+      const int row = crow(wn, 4 * h, lr);
+      sc_lds[h] = (PT * wn + lr) * kScPitch + (row >= 0 ? (s_mis + row * G) & 3 : 0);
     }
   }
 
@@ -256,10 +264,10 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
             __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)((s_off + 512u * q + 256u * h) | (s_off & kOob)), 0, 0);
     }
   };
-  // canonical: request m of scale window C into window slot C & 1
-  auto dma_sc = [&](int C, int m) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(Sc + (C & 1) * kScWin + (kScDma * w + m) * 256), 4,
-                                             (int)(sw_off[m] + 16u * C), 0, 0, 0);
+  // canonical: request m of scale window C into window slot dst
+  auto dma_sc = [&](int C, int m, uint8_t* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(dst + (kScDma * w + m) * 256), 4,
+                                             (int)(sw_off[m] + 8u * C), 0, 0, 0);
   };
   // wait until this wave's activation DMA of the next chunk has landed: it
   // was followed by one chunk's weight and scale requests
@@ -279,10 +287,18 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   bool shifted = false;  // wave-uniform: decoding at scale byte s - kShift
 
   // the MFMAs of one chunk: activations xc, weight codes wc, the 8 scale bytes
-  auto mma_chunk = [&](const uint8_t* xc, const uint8_t* wc, const uint32_t(&sb)[kWI]) {
+  auto mma_chunk = [&](const uint8_t* xc, const uint8_t* wc, const uint32_t(&sb_in)[kWI]) __attribute__((always_inline)) {
+    uint32_t sb[kWI];
     bool big = false;
 #pragma unroll
-    for (int i = 0; i < kWI; i++) big |= sb[i] >= kShiftFrom;
+    for (int i = 0; i < kWI; i++) {
+      sb[i] = sb_in[i];
+      // canonical: the bytes were read during the previous chunk; an empty asm
+      // keeps the compiler from moving this chunk's use of them (and so the
+      // wait for them) back to where they were read
+      if constexpr (CANON) asm volatile("" : "+v"(sb[i]));
+      big |= sb[i] >= kShiftFrom;
+    }
     if (!shifted && __ballot(big) != 0) {
       shifted = true;
 #pragma unroll
@@ -380,39 +396,48 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     if (q + 3 < nq) step(q + 3, C1{}, C0{});
     if (q + 4 < nq) step(q + 4, C0{}, C1{});
   } else {
-    // One chunk q, slots q mod 2 (compile-time): request the activations and
-    // weights of chunk q + 1 and a part of the next scale window (requests
-    // 0, 1 at the window's first chunk, then one per chunk), multiply chunk q,
-    // wait for all of this wave's requests, barrier: the slots written during
-    // chunk q were last read during chunk q - 1, the window slot during the
-    // window before.
-    const int nwin = (G + 15) / 16;
-    auto step = [&](int q, auto xs) {
-      constexpr int R = decltype(xs)::value;
+    // One chunk q, activation and weight slots q mod 2 and scale window slot
+    // (q >> 1) mod 2 (all compile-time): at a window's first chunk request
+    // the next window (into the other window slot, last read during the
+    // window before), request the activations and weights of chunk q + 1,
+    // read the scale bytes of chunk q + 1 from LDS (their latency hidden
+    // behind the MFMAs), multiply chunk q, wait for all of this wave's
+    // requests, barrier: the slots written during chunk q were last read
+    // during chunk q - 1.
+    const int nwin = (G + 7) / 8;
+    // the 8 scale bytes of chunk q from window slot sw; a group past G would
+    // read another row's byte and reads the zero bytes instead (a choice of
+    // address, so nothing waits for these reads before they are used)
+    auto read_sb = [&](int q, const uint8_t* sw, uint32_t(&sb)[kWI]) {
+      const bool in_g = 4 * q + lc < G;
+      int off[2];
+#pragma unroll
+      for (int h = 0; h < 2; h++) off[h] = in_g ? 4 * (q & 1) + lc + sc_lds[h] : kScWin;
+#pragma unroll
+      for (int i = 0; i < kWI; i++) sb[i] = sw[off[i >> 2] + 16 * kScPitch * i];
+    };
+    uint32_t sb_cur[kWI], sb_next[kWI];
+    auto step = [&](int q, auto xs, auto ws) {
+      constexpr int R = decltype(xs)::value, WS = decltype(ws)::value;
       const uint8_t* xc = R == 0 ? X0 : X1;
       const uint8_t* wc = R == 0 ? W0 : W1;
+      uint8_t* s_this = WS == 0 ? Sc0 : Sc1;
+      uint8_t* s_other = WS == 0 ? Sc1 : Sc0;
+      if (R == 0 && (q >> 1) + 1 < nwin) {
+#pragma unroll
+        for (int m = 0; m < kScDma; m++) dma_sc((q >> 1) + 1, m, s_other);
+      }
       if (q + 1 < nq) {
         dma_x(q + 1, R == 0 ? X1 : X0);
         dma_w(q + 1, R == 0 ? W1 : W0, 0);
       }
-      const int C = q >> 2, qq = q & 3;
-      if (C + 1 < nwin) {
-        if (qq == 0) {
-          dma_sc(C + 1, 0);
-          dma_sc(C + 1, 1);
-        } else {
-          dma_sc(C + 1, qq + 1);
-        }
-      }
       __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
       if (live) {
-        const uint8_t* sw = Sc + (C & 1) * kScWin + 4 * qq + lc;
-        // a group past G reads another row's byte: zero instead
-        const bool in_g = 4 * q + lc < G;
-        uint32_t sb[kWI];
+        // chunk q + 1 is in this window (q even) or the next one (q odd)
+        if (q + 1 < nq) read_sb(q + 1, R == 0 ? s_this : s_other, sb_next);
+        mma_chunk(xc, wc, sb_cur);
 #pragma unroll
-        for (int i = 0; i < kWI; i++) sb[i] = in_g ? sw[sc_lds[i]] : 0u;
-        mma_chunk(xc, wc, sb);
+        for (int i = 0; i < kWI; i++) sb_cur[i] = sb_next[i];
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's requests have landed
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
@@ -423,15 +448,24 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     dma_x(0, X0);
     dma_w(0, W0, 0);
 #pragma unroll
-    for (int m = 0; m < kScDma; m++) dma_sc(0, m);
+    for (int m = 0; m < kScDma; m++) dma_sc(0, m, Sc0);
+    if (tid < kScZero / 16) {
+      reinterpret_cast<u32x4*>(Sc0 + kScWin)[tid] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(Sc1 + kScWin)[tid] = u32x4{0u, 0u, 0u, 0u};
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __builtin_amdgcn_s_barrier();
+    if (live) read_sb(0, Sc0, sb_cur);
     int q = 0;
-    for (; q + 1 < nq; q += 2) {
-      step(q, C0{});
-      step(q + 1, C1{});
+    for (; q + 3 < nq; q += 4) {
+      step(q, C0{}, C0{});
+      step(q + 1, C1{}, C0{});
+      step(q + 2, C0{}, C1{});
+      step(q + 3, C1{}, C1{});
     }
-    if (q < nq) step(q, C0{});
+    if (q < nq) step(q, C0{}, C0{});
+    if (q + 1 < nq) step(q + 1, C1{}, C0{});
+    if (q + 2 < nq) step(q + 2, C0{}, C1{});
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
   if (shifted) {
