@@ -30,8 +30,11 @@
 // registers) into a ring of three chunk slots, two chunks ahead, each
 // wave-wide request filling eight whole 128-byte row pieces; the pieces of a
 // row sit XOR-swizzled so that the 16-byte fragment reads are conflict-free
-// without padding. Weights and their scales go to a ring of three register
-// slots, two chunks ahead. Every chunk issues the same number of requests,
+// without padding. Weights go to a ring of three register slots, two chunks
+// ahead; their scale bytes come with the activations: prepared weights as one
+// dword per lane, canonical weights by DMA into LDS (each row's bytes of the
+// chunk with the dword boundary below them), read at the chunk's start (per
+// lane byte loads had touched 16 rows' lines per instruction). Every chunk issues the same number of requests,
 // so one counted wait per chunk (this wave's DMA of the next chunk) and a
 // bare barrier replace a full fence. Groups past G and rows past O read
 // through an offset beyond the buffer resource (zeros). Output: fp32 rows of
@@ -57,12 +60,22 @@ constexpr int NW = 16 * kWI * kWaves;  // features per workgroup (each wave: all
 constexpr int KC = 128;         // inputs per chunk
 constexpr int kWJ = 8;           // activation fragments (16 pairs each) per wave: every wave covers all 128 pairs
 constexpr int kRing = 3;         // chunk slots: activations (LDS) and weights (registers), two in flight
-// vector-memory requests per wave and chunk: 2 activation + 1 scale DMA, then
-// kWI weight loads and kWI scale-byte loads (canonical) or 1 scale dword (prepared)
+// canonical weights: the chunk's weight scale bytes (4 groups of the
+// workgroup's NW rows, each row's bytes with the dword boundary below them:
+// 2 dwords, pitch 8 bytes) come into LDS by DMA with the activations, 2
+// requests per wave, followed by zero bytes read for groups past G
+constexpr int kWsPitch = 8;
+constexpr int kWsWin = NW * kWsPitch;
+constexpr int kWsDma = kWsWin / (256 * kWaves);
+constexpr int kWsZero = 16 * kWsPitch * kWI;
+static_assert(kWsDma * 256 * kWaves == kWsWin, "weight scale DMA");
+// vector-memory requests per wave and chunk: (canonical: 2 weight-scale DMA)
+// 2 activation + 1 activation-scale DMA, then kWI weight loads and
+// (prepared) 1 weight-scale dword
 template <bool PREP>
-constexpr int kWeightLoads = PREP ? kWI + 1 : 2 * kWI;
+constexpr int kWeightLoads = PREP ? kWI + 1 : kWI;
 template <bool PREP>
-constexpr int kLoadsPerChunk = 3 + kWeightLoads<PREP>;
+constexpr int kLoadsPerChunk = 3 + (PREP ? 0 : kWsDma) + kWeightLoads<PREP>;
 
 // ---- quantisation
 
@@ -157,6 +170,10 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   __shared__ __attribute__((aligned(16))) uint32_t S0[64 * kWaves];
   __shared__ __attribute__((aligned(16))) uint32_t S1[64 * kWaves];
   __shared__ __attribute__((aligned(16))) uint32_t S2[64 * kWaves];
+  // canonical: the chunk's weight scale bytes, three slots with the activations
+  __shared__ __attribute__((aligned(16))) uint8_t WS0[PREP ? 16 : kWsWin + kWsZero];
+  __shared__ __attribute__((aligned(16))) uint8_t WS1[PREP ? 16 : kWsWin + kWsZero];
+  __shared__ __attribute__((aligned(16))) uint8_t WS2[PREP ? 16 : kWsWin + kWsZero];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lc = lane >> 4;
@@ -209,11 +226,38 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
       w_grp[i] = f < O ? (uint32_t)f * (uint32_t)G + (uint32_t)lc : kOob;
   }
 
+  // canonical weight scales: request m of wave w fills dwords d = 64 (2 w + m) + l
+  // of a slot: LDS row R = d / 2 (feature f0 + R), dword d % 2 of the row's
+  // bytes from the dword boundary below group 4 q (a dword that holds a valid
+  // byte lies in a valid page)
+  const uintptr_t s_first = reinterpret_cast<uintptr_t>(scales) + (uintptr_t)ebase;
+  const int s_mis = PREP ? 0 : (int)(s_first & 3);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s_first & ~(uintptr_t)3), (short)0, (s_mis + O * G + 3) & ~3, kRsrcFlags);
+  uint32_t ws_off[PREP ? 1 : kWsDma];  // byte offset of this lane's dword in chunk 0 (chunk q: + 4 q)
+  int ws_lds = 0;  // byte of fragment 0's row in a slot where group 4 q starts (fragment i: + 16 kWsPitch i)
+  if constexpr (!PREP) {
+#pragma unroll
+    for (int m = 0; m < kWsDma; m++) {
+      const int d = 64 * (kWsDma * w + m) + lane, R = d / 2, k = d - 2 * R;
+      const int f = f0 + R;
+      ws_off[m] = f < O ? (uint32_t)(((s_mis + f * G) >> 2) + k) * 4u : kOob;
+    }
+    const int f = f0 + 16 * kWI * w + lr;  // rows 16 apart share the offset within the dword
+    ws_lds = (16 * kWI * w + lr) * kWsPitch + (f < O ? (s_mis + f * G) & 3 : 0) + lc;
+  }
+
   u32x4 wf[kRing][kWI];
-  uint32_t wsc[kRing][kWI];  // canonical: one scale byte per fragment
   uint32_t wsp[kRing];     // prepared: the four fragments' scale bytes in one dword
   // exactly kLoadsPerChunk vector-memory requests per chunk, in this order
-  auto dma_x = [&](int q, uint8_t* xdst, uint32_t* sdst) {
+  auto dma_x = [&](int q, uint8_t* xdst, uint32_t* sdst, uint8_t* wsdst) {
+    if constexpr (!PREP) {
+#pragma unroll
+      for (int m = 0; m < kWsDma; m++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsa, (__attribute__((address_space(3))) void*)(wsdst + (kWsDma * w + m) * 256), 4,
+            (int)(ws_off[m] + 4u * q), 0, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < 2; j++)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xdst + (16 * w + 8 * j) * KC),
@@ -231,7 +275,6 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
     for (int i = 0; i < kWI; i++) {
       const uint32_t g = (w_grp[i] + step_q * q) | past;  // kOob stays past the resource
       wf[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(g << 4 | (g & kOob)), 0, 0));
-      if constexpr (!PREP) wsc[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, (int)g, 0, 0);
     }
     if constexpr (PREP) wsp[slot] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)(w_sc + 512u * q), 0, 0);
   };
@@ -259,11 +302,21 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
     constexpr int R = decltype(slot)::value, RN = (R + 2) % kRing;
     uint8_t* xn = RN == 0 ? X0 : (RN == 1 ? X1 : X2);
     uint32_t* sn = RN == 0 ? S0 : (RN == 1 ? S1 : S2);
+    uint8_t* wsn = RN == 0 ? WS0 : (RN == 1 ? WS1 : WS2);
     const uint8_t* xc = R == 0 ? X0 : (R == 1 ? X1 : X2);
     const uint32_t* sc = R == 0 ? S0 : (R == 1 ? S1 : S2);
-    dma_x(min(q + 2, nq - 1), xn, sn);
+    const uint8_t* wsc = R == 0 ? WS0 : (R == 1 ? WS1 : WS2);
+    dma_x(min(q + 2, nq - 1), xn, sn, wsn);
     load_w(min(q + 2, nq - 1), RN);
     __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
+    // canonical: the fragments' scale bytes of chunk q (a group past G reads
+    // the zero bytes after the slot: another row's byte otherwise)
+    int as_c[kWI];
+    if constexpr (!PREP) {
+      const int off = 4 * q + lc < G ? ws_lds : kWsWin;
+#pragma unroll
+      for (int i = 0; i < kWI; i++) as_c[i] = wsc[off + 16 * kWsPitch * i];
+    }
 #pragma unroll
     for (int j = 0; j < kWJ; j++) {
       const int p = 16 * j + lr;  // rows past the tile's end hold zeros (their DMA read past the resource)
@@ -274,7 +327,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
 #pragma unroll
       for (int i = 0; i < kWI; i++) {
         const v8i a = v8i{(int)wf[R][i][0], (int)wf[R][i][1], (int)wf[R][i][2], (int)wf[R][i][3], 0, 0, 0, 0};
-        const int as = PREP ? (int)((wsp[R] >> (8 * i)) & 0xFFu) : (int)wsc[R][i];
+        const int as = PREP ? (int)((wsp[R] >> (8 * i)) & 0xFFu) : as_c[i];
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, 0, 0, as, 0, bs);
       }
     }
@@ -292,9 +345,16 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
-  dma_x(0, X0, S0);
+  if constexpr (!PREP) {
+    if (tid < kWsZero / 16) {
+      reinterpret_cast<u32x4*>(WS0 + kWsWin)[tid] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(WS1 + kWsWin)[tid] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(WS2 + kWsWin)[tid] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  dma_x(0, X0, S0, WS0);
   load_w(0, 0);
-  dma_x(min(1, nq - 1), X1, S1);
+  dma_x(min(1, nq - 1), X1, S1, WS1);
   load_w(min(1, nq - 1), 1);
   wait_next_x();  // chunk 0's DMA: followed by chunk 0's weights and all of chunk 1's requests
   __builtin_amdgcn_s_barrier();
