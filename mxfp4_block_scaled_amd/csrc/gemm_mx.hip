@@ -31,10 +31,11 @@
 // wave-wide request filling eight whole 128-byte row pieces; the pieces of a
 // row sit XOR-swizzled so that the 16-byte fragment reads are conflict-free
 // without padding. Weights go to a ring of three register slots, two chunks
-// ahead; their scale bytes come with the activations: prepared weights as one
-// dword per lane, canonical weights by DMA into LDS (each row's bytes of the
-// chunk with the dword boundary below them), read at the chunk's start (per
-// lane byte loads had touched 16 rows' lines per instruction). Every chunk issues the same number of requests,
+// ahead. Their scale bytes: prepared weights, one dword per lane loaded with
+// the weights; canonical weights, by DMA into LDS with the activations (each
+// row's bytes of the chunk with the dword boundary below them), read at the
+// chunk's start (per-lane byte loads had touched 16 rows' lines per
+// instruction). Every chunk issues the same number of requests,
 // so one counted wait per chunk (this wave's DMA of the next chunk) and a
 // bare barrier replace a full fence. Groups past G and rows past O read
 // through an offset beyond the buffer resource (zeros). Output: fp32 rows of
