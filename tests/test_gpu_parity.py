@@ -410,6 +410,40 @@ def test_edge_shapes(case, dtype):
         assert_close(host64(y), ref, dtype, f"{case} flags={flags}")
 
 
+# Prefill-shaped GEMM on canonical weights with O % 4 == 0 (the register-decode
+# kernel): input widths around its 4-group chunks and 8-group scale windows
+# (partial chunks, partial windows, groups past G), rows across 128-row
+# fragments and 512-row N-tiles, scale rows at every byte offset.
+GEMM_WINDOW_CASES = [
+    # T, E, K, G, O
+    (40, 3, 2, 1, 20),
+    (40, 3, 2, 3, 132),
+    (40, 3, 2, 4, 20),
+    (40, 3, 2, 5, 132),
+    (40, 3, 2, 7, 20),
+    (40, 3, 2, 8, 132),
+    (40, 3, 2, 9, 516),
+    (40, 3, 2, 12, 20),
+    (40, 3, 2, 15, 132),
+    (40, 3, 2, 16, 20),
+    (40, 3, 2, 17, 132),
+    (40, 3, 2, 23, 20),
+    (130, 2, 2, 33, 268),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("case", GEMM_WINDOW_CASES, ids=lambda c: "T{}E{}K{}G{}O{}".format(*c))
+def test_gemm_chunk_and_scale_window_edges(case, dtype):
+    T, E, K, G, O = case
+    say(f"gemm window edges {case} {dtype}")
+    host = random_case(1000 + 7 * G + O, T, E, K, G, O, dtype)
+    d = upload(*host, dtype)
+    ref = oracle.expert_linear(*host)
+    y = run(d, flags=_abi.FLAG_FORCE_GEMM)
+    assert_close(host64(y), ref, dtype, f"{case} forced GEMM")
+
+
 ONE_TOKEN_CASES = [
     # E, K, G, O, distinct: the one-token kernel's lane layouts (lanes per row
     # 64 / 32 / 16 / 2 / 1), ragged row sets, G up to its limit, many slots
