@@ -6,4 +6,6 @@ from .mxfp4_oracle import (  # noqa: F401
     route_softmax, route_sigmoid, route_sigmoid_grouped, route_scalar, route_grouped_scalar, route_keys, route_weights, SOFTMAX_MASS_FLOOR, SIGMOID_EPS,
     E4M3_MAX, E4M3_TABLE, e4m3_value, mxfp8_block_exponent, quantize_e4m3, quantize_mxfp8, dequantize_mxfp8,
     expert_linear_mxfp8, expert_linear_mxfp8_rows,
+    E2M1_MAX, mxfp4_block_exponent, quantize_e2m1, quantize_mxfp4, pack_codes, dequantize_mxfp4,
+    expert_linear_mxfp4act, expert_linear_mxfp4act_rows,
 )

@@ -716,3 +716,98 @@ def expert_linear_mxfp8_rows(x, packed, scales, sel, p, shared, rows) -> np.ndar
     """expert_linear_mxfp8 restricted to the output rows ``rows``."""
     xh = dequantize_mxfp8(*quantize_mxfp8(x))
     return expert_linear_rows(xh, packed, scales, sel, p, shared, rows)
+
+
+# ------------------------------------------- MXFP4 activations (variant)
+#
+# The same block-scaled variant with the activations in the weights' own
+# format, so that both operands of the scaled multiply are FP4: E2M1 codes
+# (the table above), blocks of 32 sharing one E8M0 scale byte (page "MXFP4
+# Dequant", "Overview": the format is defined for blocks of 32 values, not
+# for weights only). The pages say nothing of how activations would be
+# quantised to it; the readings follow the MXFP8 ones above:
+#
+# * element: E2M1, the 4-bit code sign << 3 | index of the magnitude in
+#   (0, 0.5, 1, 1.5, 2, 3, 4, 6);
+# * block: 32 consecutive inputs of one token (the same columns as weight
+#   group b);
+# * scale: the smallest power of two 2^X with max|block| <= 6 * 2^X, so no
+#   element saturates; X clamped to [-127, 127] and stored as the byte
+#   X + 127; an all-zero block takes X = -127;
+# * elements: v / 2^X rounded to the nearest E2M1 magnitude, ties to the
+#   even code, clamped to 6 (reachable only through the clamp of X); the
+#   sign kept, also when the magnitude rounds to zero (code 8);
+# * two codes per byte, low nibble first, as the weights are packed.
+#
+# The variant's defining result is the routed linear of the dequantised
+# activations, exact in float64: expert_linear(dequantize(quantize(x)), ...).
+
+E2M1_MAX = 6.0
+E2M1_MAGNITUDES = E2M1_TABLE[:8]  # 0, 0.5, 1, 1.5, 2, 3, 4, 6: codes 0..7
+
+
+def mxfp4_block_exponent(amax) -> np.ndarray:
+    """Smallest integer X with amax <= 6 * 2^X, clamped to [-127, 127];
+    -127 for amax == 0. Exact: amax = f * 2^e with f in [0.5, 1), and
+    6 = 0.75 * 2^3, so X = e - 3 when f <= 0.75 and e - 2 otherwise."""
+    a = np.asarray(amax, dtype=np.float64)
+    f, e = np.frexp(a)
+    X = np.where(f <= 0.75, e - 3, e - 2)
+    X = np.where(a == 0, -127, X)
+    return np.clip(X, -127, 127).astype(np.int64)
+
+
+def quantize_e2m1(v) -> np.ndarray:
+    """E2M1 codes of float64 values already divided by their block scale:
+    round to nearest, ties to even, clamp to +-6, keep the sign. Below 2 the
+    magnitudes are multiples of 0.5, in [2, 4) of 1, in [4, 6] of 2, and in
+    each step the even multiple has the even code."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                           # a = f * 2^e, f in [0.5, 1)
+    quantum = np.ldexp(1.0, np.maximum(e - 1, 0) - 1)
+    aq = np.minimum(np.rint(a / quantum) * quantum, E2M1_MAX)   # np.rint: ties to even
+    idx = np.searchsorted(E2M1_MAGNITUDES, aq)   # aq is one of the magnitudes
+    return (idx | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def quantize_mxfp4(x) -> tuple:
+    """Activations (T, I), I a multiple of 32 -> (codes uint8 (T, I) with
+    values 0..15, one per input, and scale bytes uint8 (T, I/32))."""
+    x = np.asarray(x, dtype=np.float64)
+    T, I = x.shape
+    if I % GROUP_VALUES:
+        raise ValueError("the input width must be a multiple of 32")
+    blocks = x.reshape(T, I // GROUP_VALUES, GROUP_VALUES)
+    X = mxfp4_block_exponent(np.abs(blocks).max(axis=2))
+    codes = quantize_e2m1(blocks / np.ldexp(1.0, X)[:, :, None])
+    return codes.reshape(T, I), (X + SCALE_BIAS).astype(np.uint8)
+
+
+def pack_codes(codes) -> np.ndarray:
+    """Four-bit codes (T, I) -> bytes (T, I/2), code 2j in the low nibble of
+    byte j (the weights' order)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def dequantize_mxfp4(codes, scale_bytes) -> np.ndarray:
+    """float64 values of MXFP4 activations: E2M1 value times 2^(s - 127)."""
+    codes = np.asarray(codes)
+    T, I = codes.shape
+    vals = E2M1_TABLE[codes].reshape(T, I // GROUP_VALUES, GROUP_VALUES)
+    f = np.ldexp(1.0, np.asarray(scale_bytes, dtype=np.int64) - SCALE_BIAS)
+    return (vals * f[:, :, None]).reshape(T, I)
+
+
+def expert_linear_mxfp4act(x, packed, scales, sel, p, shared) -> np.ndarray:
+    """The block-scaled variant with MXFP4 activations: the routed linear of
+    the quantised activations, exact in float64."""
+    xh = dequantize_mxfp4(*quantize_mxfp4(x))
+    return expert_linear(xh, packed, scales, sel, p, shared)
+
+
+def expert_linear_mxfp4act_rows(x, packed, scales, sel, p, shared, rows) -> np.ndarray:
+    """expert_linear_mxfp4act restricted to the output rows ``rows``."""
+    xh = dequantize_mxfp4(*quantize_mxfp4(x))
+    return expert_linear_rows(xh, packed, scales, sel, p, shared, rows)

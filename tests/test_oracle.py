@@ -842,3 +842,147 @@ def test_mxfp8_planted_mistakes_are_caught(monkeypatch):
     amax = np.array([300.0, 448.0, 500.0, 1.0])
     floor_rule = np.floor(np.log2(amax)).astype(np.int64) - 8
     assert not np.array_equal(floor_rule, oracle.mxfp8_block_exponent(amax))
+
+
+# ------------------------------------------- MXFP4 activations (variant)
+
+def _nearest_e2m1_brute(v):
+    """Nearest E2M1 value by search over the 8 magnitudes; ties to the even
+    code; beyond 6 the clamp; the sign kept."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    a = min(abs(v), 6.0)
+    best = None
+    for c, m in enumerate(mags):
+        d = abs(m - a)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (8 if math.copysign(1.0, v) < 0 else 0)
+
+
+def test_e2m1_quantize_grid_ties_and_clamp():
+    t = oracle.E2M1_TABLE
+    # every code's own value comes back as that code (both zeros included)
+    assert oracle.quantize_e2m1(t).tolist() == list(range(16))
+    # midpoints go to the even code
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    assert oracle.quantize_e2m1(mids).tolist() == [0, 2, 2, 4, 4, 6, 6]
+    assert oracle.quantize_e2m1([-m for m in mids]).tolist() == [8, 10, 10, 12, 12, 14, 14]
+    # just off the midpoints, the nearer one
+    assert oracle.quantize_e2m1([0.2501, 0.7499, 4.999, 5.001, 6.9, 100.0]).tolist() == [1, 1, 6, 7, 7, 7]
+    assert oracle.quantize_e2m1([-0.1, -0.0]).tolist() == [8, 8]
+
+
+def test_e2m1_quantize_brute_force():
+    rng = _rng(17)
+    vals = np.concatenate([rng.uniform(-7.0, 7.0, 600), np.ldexp(rng.uniform(0.5, 1.0, 100), rng.integers(-8, 3, 100))])
+    mags = oracle.E2M1_TABLE[:8]
+    ties = (mags[:-1] + mags[1:]) / 2
+    vals = np.concatenate([vals, ties, -ties])
+    got = oracle.quantize_e2m1(vals)
+    assert got.tolist() == [_nearest_e2m1_brute(float(v)) for v in vals]
+
+
+def test_mxfp4_block_exponent_brute_force():
+    rng = _rng(18)
+    amax = np.concatenate([np.ldexp(rng.uniform(0.5, 1.0, 300), rng.integers(-140, 130, 300)),
+                           [6.0, np.nextafter(6.0, 1e9), 3.0, np.nextafter(3.0, 1e9), 1.0, 2.0 ** -140, 0.0]])
+    got = oracle.mxfp4_block_exponent(amax)
+    for a, X in zip(amax, got):
+        if a == 0:
+            assert X == -127
+            continue
+        want = next(x for x in range(-127, 128) if a <= 6.0 * 2.0 ** x) if a <= 6.0 * 2.0 ** 127 else 127
+        assert X == want, (a, X, want)
+    assert got[-7:-1].tolist() == [0, 1, -1, 0, -2, -127]
+
+
+def test_mxfp4_quantize_blocks():
+    rng = _rng(19)
+    x = rng.standard_normal((5, 96)) * np.ldexp(1.0, rng.integers(-20, 20, (5, 1)))
+    x[2, 32:64] = 0.0                          # an all-zero block
+    x[3, 0:32] = np.linspace(-6.0, 6.0, 32)    # a block that fits at X = 0 exactly
+    codes, sb = oracle.quantize_mxfp4(x)
+    assert codes.shape == (5, 96) and sb.shape == (5, 3) and codes.max() < 16
+    assert sb[2, 1] == 0 and np.all(codes[2, 32:64] == 0)
+    assert sb[3, 0] == 127
+    xh = oracle.dequantize_mxfp4(codes, sb)
+    blocks = np.abs(x).reshape(5, 3, 32)
+    X = sb.astype(np.int64) - 127
+    nz = blocks.max(2) > 0
+    # the block max fits without clamping: within 6 * 2^X and above half of it
+    assert np.all(blocks.max(2)[nz] <= 6.0 * np.ldexp(1.0, X[nz]))
+    assert np.all(blocks.max(2)[nz] > 3.0 * np.ldexp(1.0, X[nz]))
+    # each element against the brute-force nearest value at its block's scale
+    for t in range(5):
+        for b in range(3):
+            s = 2.0 ** X[t, b]
+            for k in range(32):
+                v = x[t, 32 * b + k]
+                assert codes[t, 32 * b + k] == _nearest_e2m1_brute(v / s), (t, b, k)
+    # error: half the step of the element's range (0.25, 0.5 or 1 times 2^X)
+    err = np.abs(xh - x).reshape(5, 3, 32)
+    assert np.all(err <= np.ldexp(1.0, X)[:, :, None] * 1.0)
+    # values already on the grid come back unchanged
+    r = np.ldexp(1.0, rng.integers(-5, 5, (4, 1)))
+    ong = oracle.E2M1_TABLE[rng.integers(0, 16, (4, 64))] * r
+    ong[:, 0] = ong[:, 32] = 6.0 * r[:, 0]  # each block's maximum fixes its scale at r
+    np.testing.assert_array_equal(oracle.dequantize_mxfp4(*oracle.quantize_mxfp4(ong)), ong)
+
+
+def test_mxfp4_pack_is_the_weight_nibble_order():
+    rng = _rng(20)
+    codes = rng.integers(0, 16, (3, 64)).astype(np.uint8)
+    packed = oracle.pack_codes(codes)
+    assert packed.shape == (3, 32)
+    lo, hi = oracle.split_nibbles(packed)
+    np.testing.assert_array_equal(lo, codes[:, 0::2])
+    np.testing.assert_array_equal(hi, codes[:, 1::2])
+    # the printed example: 0x21 holds code 1 (first) and code 2 (second)
+    assert oracle.pack_codes(np.array([[1, 2]], dtype=np.uint8)).tolist() == [[0x21]]
+
+
+def test_mxfp4act_linear_composition_and_error():
+    """On grid activations the variant equals the exact layer; on normal
+    activations it differs by the E2M1 rounding of the activations (a
+    relative L2 of roughly a tenth)."""
+    rng = _rng(21)
+    T, E, K, G, O = 6, 5, 2, 3, 24
+    packed = rng.integers(0, 256, (E, O, G, 16), dtype=np.uint8)
+    scales = rng.integers(120, 131, (E, O, G), dtype=np.uint8)
+    sel = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    p = rng.uniform(0.1, 1.0, (T, K))
+    shared = rng.standard_normal((T, O))
+    r = np.ldexp(1.0, rng.integers(-3, 3, (T, 1)))
+    xg = oracle.E2M1_TABLE[rng.integers(0, 16, (T, 32 * G))] * r
+    xg[:, ::32] = 6.0 * r
+    np.testing.assert_array_equal(oracle.expert_linear_mxfp4act(xg, packed, scales, sel, p, shared),
+                                  oracle.expert_linear(xg, packed, scales, sel, p, shared))
+    x = rng.standard_normal((T, 32 * G))
+    ya = oracle.expert_linear_mxfp4act(x, packed, scales, sel, p, shared * 0)
+    ye = oracle.expert_linear(x, packed, scales, sel, p, shared * 0)
+    rel = np.linalg.norm(ya - ye) / np.linalg.norm(ye)
+    assert 3e-2 < rel < 0.3, rel
+    y8 = oracle.expert_linear_mxfp8(x, packed, scales, sel, p, shared * 0)
+    assert np.linalg.norm(y8 - ye) < np.linalg.norm(ya - ye)  # MXFP8 activations round far less
+    rows = np.array([0, 7, 23])
+    np.testing.assert_array_equal(oracle.expert_linear_mxfp4act_rows(x, packed, scales, sel, p, shared, rows),
+                                  oracle.expert_linear_mxfp4act(x, packed, scales, sel, p, shared)[:, rows])
+
+
+def test_mxfp4_planted_mistakes_are_caught(monkeypatch):
+    rng = _rng(22)
+    mags = oracle.E2M1_TABLE[:8]
+    vals = np.concatenate([(mags[:-1] + mags[1:]) / 2, rng.uniform(-7, 7, 60), [7.0, 7.5, -9.0, 100.0]])
+    want = [_nearest_e2m1_brute(float(v)) for v in vals]
+    mistakes = {
+        "ties away from zero": lambda mp: mp.setattr(om.np, "rint", lambda a: np.floor(np.asarray(a) + 0.5)),
+        "largest magnitude 8": lambda mp: mp.setattr(om, "E2M1_MAX", 8.0),
+    }
+    for name, plant in mistakes.items():
+        with monkeypatch.context() as mp:
+            plant(mp)
+            assert om.quantize_e2m1(vals).tolist() != want, f"planted mistake not caught: {name}"
+    # the standard's floor(log2 amax) - 2 scale rule instead of the fitting one
+    amax = np.array([7.0, 6.0, 3.5, 1.0])
+    floor_rule = np.floor(np.log2(amax)).astype(np.int64) - 2
+    assert not np.array_equal(floor_rule, oracle.mxfp4_block_exponent(amax))
