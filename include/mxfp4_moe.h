@@ -345,6 +345,43 @@ int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, 
                                        hipStream_t stream);
 
 /*
+ * The block-scaled variant with MXFP4 activations (both operands of the
+ * scaled MFMA in E2M1: the FP4 x FP4 form). The pages define MXFP4 for
+ * blocks of 32 values (page "MXFP4 Dequant", "Overview") without saying how
+ * activations would be quantised to it; readings as for MXFP8: per token and
+ * block of 32 inputs the smallest power of two 2^X with max|block| <= 6 * 2^X
+ * (scale byte X + 127, X clamped to [-127, 127], an all-zero block -127), each
+ * element x / 2^X rounded to the nearest E2M1 magnitude (0, .5, 1, 1.5, 2, 3,
+ * 4, 6), ties to the even code, sign kept (code sign << 3 | magnitude index).
+ *   mxfp4_quantize_mxfp4: x (T, I) bf16 raw bits, I a positive multiple of
+ *     32, 8-byte aligned -> codes (T, ld / 2) bytes, two codes per byte, the
+ *     first in the low nibble (the weights' order), and scale_bytes
+ *     (T, ld / 32); ld >= I a multiple of 32, codes 4-byte aligned; columns
+ *     [I, ld) get zero codes and scale bytes 0. T * ld < 2^31; no overlap.
+ *     MXFP4_ERR_INVALID_ARG otherwise. Enqueued on `stream`, no allocation.
+ *   mxfp4_moe_linear_mxfp4act_ex: mxfp4_moe_linear_mxfp8_ex with the
+ *     activations quantised by mxfp4_quantize_mxfp4 instead: the routed linear
+ *     of the quantised activations, an approximation of mxfp4_moe_linear_ex
+ *     (the E2M1 rounding of the activations, relative L2 around 0.1 on
+ *     normally distributed activations), reported separately. Sizes, flags,
+ *     errors, aliasing and the 255 rule as mxfp4_moe_linear_mxfp8_ex;
+ *     workspace of mxfp4_moe_mxfp4act_workspace_size bytes.
+ *   mxfp4_moe_linear_mxfp4act_prepared_ex: the same on the buffer of
+ *     mxfp4_prepare_mx; results bit for bit those of the canonical call.
+ */
+int mxfp4_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t I, int64_t ld, uint8_t* codes, uint8_t* scale_bytes,
+                         hipStream_t stream);
+int mxfp4_moe_mxfp4act_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, size_t* bytes);
+int mxfp4_moe_linear_mxfp4act_ex(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                                 const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+                                 int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+int mxfp4_moe_linear_mxfp4act_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel,
+                                          const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E,
+                                          int64_t O, int64_t G, int64_t K, uint32_t flags, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The decode-shaped path (routing, dequant-GEMV and combine in one launch per
  * token chunk; page "MXFP4 Routed Expert Linear", "Route, weight, and add the
  * shared path") on weights repacked by mxfp4_prepare_mx: the MFMA decode

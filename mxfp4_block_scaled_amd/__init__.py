@@ -21,7 +21,7 @@ from . import _abi
 from ._abi import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, FLAG_CHECK, FLAG_FORCE_GEMM, FLAG_FORCE_GEMV, FLAG_GEMV_MFMA, FLAG_BUCKET_MULTI_BLOCK,
     FLAG_BUCKET_ONE_BLOCK, PATH_GEMM, PATH_GEMV, ROUTE_SIGMOID, ROUTE_SOFTMAX, Mxfp4Error, bucket_workspace_size,
-    mxfp8_workspace_size, select_path,
+    mxfp4act_workspace_size, mxfp8_workspace_size, select_path,
     status_string, swiglu_workspace_size, workspace_size,
 )
 
@@ -30,7 +30,8 @@ __all__ = [
     "swiglu_workspace_size", "select_path", "route", "quantize_mxfp8", "moe_linear_mxfp8", "mxfp8_workspace_size",
     "prepare_mx", "PreparedMx", "moe_linear_mxfp8_prepared", "moe_linear_prepared", "gemm_stage_prepared",
     "prepare_bf16", "moe_decode_prepared", "prepare_swiglu", "PreparedSwiGLU", "moe_swiglu_prepared",
-    "route_grouped", "stream_read", "Mxfp4Error", "library_path",
+    "route_grouped", "stream_read", "quantize_mxfp4", "moe_linear_mxfp4act", "moe_linear_mxfp4act_prepared",
+    "mxfp4act_workspace_size", "Mxfp4Error", "library_path",
 ]
 
 _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
@@ -180,6 +181,23 @@ def quantize_mxfp8(x: torch.Tensor, ld: int | None = None) -> tuple[torch.Tensor
     return codes, sb
 
 
+def quantize_mxfp4(x: torch.Tensor, ld: int | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 activations [T, I] -> (E2M1 codes uint8 [T, ld/2], two per byte
+    with the first in the low nibble, and E8M0 scale bytes uint8 [T, ld/32]),
+    one scale per token and block of 32 inputs; columns past I hold zeros.
+    ld defaults to I."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    T, I = x.shape
+    ld = I if ld is None else ld
+    codes = torch.empty((T, ld // 2), dtype=torch.uint8, device=dev)
+    sb = torch.empty((T, ld // 32), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = _abi.lib().mxfp4_quantize_mxfp4(_ptr(x), T, I, ld, _ptr(codes), _ptr(sb), _stream(dev))
+    _abi.check(st, "mxfp4_quantize_mxfp4")
+    return codes, sb
+
+
 def moe_linear_mxfp8(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, sel: torch.Tensor,
                      p: torch.Tensor, shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
                      workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -187,6 +205,18 @@ def moe_linear_mxfp8(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
     quantised to MXFP8, multiplied by the packed weights as stored on the
     block-scaled MFMA. An approximation of ``moe_linear`` (activation
     rounding), reported separately. Shapes as ``moe_linear``."""
+    return _moe_linear_mx(x, packed, scales, sel, p, shared, out, flags, workspace, False)
+
+
+def moe_linear_mxfp4act(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, sel: torch.Tensor,
+                        p: torch.Tensor, shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``moe_linear_mxfp8`` with the activations quantised to MXFP4 instead
+    (both operands of the scaled MFMA in E2M1). Reported separately."""
+    return _moe_linear_mx(x, packed, scales, sel, p, shared, out, flags, workspace, True)
+
+
+def _moe_linear_mx(x, packed, scales, sel, p, shared, out, flags, workspace, act_fp4):
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("x must be on a HIP device")
@@ -207,16 +237,17 @@ def moe_linear_mxfp8(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
     _need(y, "out", torch.bfloat16, 2, dev)
     if tuple(y.shape) != (T, O):
         raise ValueError("out must be [T, O]")
-    need = _abi.mxfp8_workspace_size(T, E, O, G, K)
+    need = (_abi.mxfp4act_workspace_size if act_fp4 else _abi.mxfp8_workspace_size)(T, E, O, G, K)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     elif workspace.dtype != torch.uint8 or workspace.device != dev:
         raise ValueError("workspace must be a uint8 tensor on x's device")
+    name = "mxfp4_moe_linear_mxfp4act_ex" if act_fp4 else "mxfp4_moe_linear_mxfp8_ex"
     with torch.cuda.device(dev):
-        st = _abi.lib().mxfp4_moe_linear_mxfp8_ex(
+        st = getattr(_abi.lib(), name)(
             _ptr(x), _ptr(packed), _ptr(scales), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, O, G, K, flags,
             _ptr(workspace), workspace.numel(), _stream(dev))
-    _abi.check(st, "mxfp4_moe_linear_mxfp8_ex")
+    _abi.check(st, name)
     return y
 
 
@@ -261,6 +292,18 @@ def moe_linear_mxfp8_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.
                               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """``moe_linear_mxfp8`` on weights repacked by ``prepare_mx`` (the same
     result bit for bit)."""
+    return _moe_linear_mx_prepared(x, prepared, sel, p, shared, out, flags, workspace, False)
+
+
+def moe_linear_mxfp4act_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.Tensor, p: torch.Tensor,
+                                 shared: torch.Tensor, *, out: torch.Tensor | None = None, flags: int = 0,
+                                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``moe_linear_mxfp4act`` on weights repacked by ``prepare_mx`` (the same
+    result bit for bit)."""
+    return _moe_linear_mx_prepared(x, prepared, sel, p, shared, out, flags, workspace, True)
+
+
+def _moe_linear_mx_prepared(x, prepared, sel, p, shared, out, flags, workspace, act_fp4):
     dev = x.device
     _need(x, "x", torch.bfloat16, 2, dev)
     _need(sel, "sel", torch.int32, 2, dev)
@@ -279,14 +322,15 @@ def moe_linear_mxfp8_prepared(x: torch.Tensor, prepared: PreparedMx, sel: torch.
     _need(y, "out", torch.bfloat16, 2, dev)
     if tuple(y.shape) != (T, O):
         raise ValueError("out must be [T, O]")
-    need = _abi.mxfp8_workspace_size(T, E, O, G, K)
+    need = (_abi.mxfp4act_workspace_size if act_fp4 else _abi.mxfp8_workspace_size)(T, E, O, G, K)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    name = "mxfp4_moe_linear_mxfp4act_prepared_ex" if act_fp4 else "mxfp4_moe_linear_mxfp8_prepared_ex"
     with torch.cuda.device(dev):
-        st = _abi.lib().mxfp4_moe_linear_mxfp8_prepared_ex(
+        st = getattr(_abi.lib(), name)(
             _ptr(x), _ptr(prepared.buf), _ptr(sel), _ptr(p), _ptr(shared), _ptr(y), T, E, O, G, K, flags,
             _ptr(workspace), workspace.numel(), _stream(dev))
-    _abi.check(st, "mxfp4_moe_linear_mxfp8_prepared_ex")
+    _abi.check(st, name)
     return y
 
 

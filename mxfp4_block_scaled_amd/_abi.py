@@ -71,6 +71,10 @@ SIGNATURES = {
     "mxfp4_mx_prepared_size": (_int, [_i64] * 3 + [ctypes.POINTER(_sz)]),
     "mxfp4_prepare_mx": (_int, [_vp] * 2 + [_i64] * 3 + [_vp, _sz, _vp]),
     "mxfp4_moe_linear_mxfp8_prepared_ex": (_int, [_vp] * 6 + [_i64] * 5 + [_u32, _vp, _sz, _vp]),
+    "mxfp4_quantize_mxfp4": (_int, [_vp] + [_i64] * 3 + [_vp, _vp, _vp]),
+    "mxfp4_moe_mxfp4act_workspace_size": (_int, [_i64] * 5 + [ctypes.POINTER(_sz)]),
+    "mxfp4_moe_linear_mxfp4act_ex": (_int, [_vp] * 7 + [_i64] * 5 + [_u32, _vp, _sz, _vp]),
+    "mxfp4_moe_linear_mxfp4act_prepared_ex": (_int, [_vp] * 6 + [_i64] * 5 + [_u32, _vp, _sz, _vp]),
     "mxfp4_moe_linear_prepared_ex": (_int, [_vp] * 6 + [_i64] * 5 + [_u32, _vp, _sz, _vp]),
     "mxfp4_moe_gemm_stage_prepared": (_int, [_vp] * 2 + [_i64] * 5 + [_vp, _sz, _vp]),
     "mxfp4_moe_decode_prepared_ex": (_int, [_vp] * 6 + [_i64] * 5 + [_int, _u32, _vp, _sz, _vp]),
@@ -130,6 +134,12 @@ def swiglu_workspace_size(T, E, F, G, O, K) -> int:
 def mxfp8_workspace_size(T, E, O, G, K) -> int:
     out = _sz(0)
     check(lib().mxfp4_moe_mxfp8_workspace_size(T, E, O, G, K, ctypes.byref(out)), "mxfp8_workspace_size")
+    return out.value
+
+
+def mxfp4act_workspace_size(T, E, O, G, K) -> int:
+    out = _sz(0)
+    check(lib().mxfp4_moe_mxfp4act_workspace_size(T, E, O, G, K, ctypes.byref(out)), "mxfp4act_workspace_size")
     return out.value
 
 

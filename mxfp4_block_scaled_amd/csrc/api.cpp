@@ -344,19 +344,20 @@ struct MxLayout {
   size_t xq, xs, total;
 };
 
-MxLayout mx_layout(const Dims& d) {
+MxLayout mx_layout(const Dims& d, bool act_fp4 = false) {
   MxLayout M;
   M.L = layout(d, MXFP4_PATH_GEMM);
   M.Kp = mx_row_bytes(d.I);
   M.xq = M.L.total;
-  M.xs = align_up(M.xq + (size_t)d.T * M.Kp);
+  M.xs = align_up(M.xq + (size_t)d.T * M.Kp / (act_fp4 ? 2 : 1));
   M.total = align_up(M.xs + (size_t)d.T * M.Kp / 32);
   return M;
 }
 
-int run_mxfp8(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, bool prepared, const int32_t* sel,
-              const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O, int64_t G,
-              int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// act_fp4: activations quantised to MXFP4 instead of MXFP8
+int run_mx(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, bool prepared, bool act_fp4,
+           const int32_t* sel, const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+           int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Dims d;
   int st = check_dims(T, E, O, G, K, &d);
   if (st != MXFP4_OK) return st;
@@ -365,7 +366,7 @@ int run_mxfp8(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, b
   if (st != MXFP4_OK) return st;
   if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
   if (d.T == 0) return MXFP4_OK;
-  const MxLayout M = mx_layout(d);
+  const MxLayout M = mx_layout(d, act_fp4);
   if (workspace_bytes < M.total) return MXFP4_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, kAlign)) return MXFP4_ERR_INVALID_ARG;
   st = check_device();
@@ -384,10 +385,12 @@ int run_mxfp8(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, b
   uint8_t* xs = reinterpret_cast<uint8_t*>(base + M.xs);
   float* part = reinterpret_cast<float*>(base + L.part);
   hipError_t err = launch_bucket_multi(sel, (int)d.P, (int)d.E, reinterpret_cast<int32_t*>(base + L.bcount), b, stream);
-  if (err == hipSuccess) err = launch_quant_mxfp8(x, (int)d.T, (int)d.I, M.Kp, xq, xs, stream);
+  if (err == hipSuccess)
+    err = act_fp4 ? launch_quant_mxfp4(x, (int)d.T, (int)d.I, M.Kp, xq, xs, stream)
+                  : launch_quant_mxfp8(x, (int)d.T, (int)d.I, M.Kp, xq, xs, stream);
   if (err == hipSuccess)
     err = launch_gemm_mx(xq, xs, packed, scales, b.perm, b.tiles, b.n_tiles, gemm_max_tiles(d.P, d.E), part, (int)d.T,
-                         (int)d.K, (int)d.O, (int)d.G, stream, prepared);
+                         (int)d.K, (int)d.O, (int)d.G, stream, prepared, act_fp4);
   if (err == hipSuccess)
     err = launch_combine(part, b.slot_of_pair, p, shared, y, (int)d.T, (int)d.K, (int)d.O, MXFP4_DTYPE_BF16, stream);
   if (err != hipSuccess) return MXFP4_ERR_HIP;
@@ -579,8 +582,8 @@ int mxfp4_moe_linear_mxfp8_ex(const uint16_t* x, const uint8_t* packed, const ui
                               const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
                               int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-  return run_mxfp8(x, packed, scales, false, sel, p, shared, y, T, E, O, G, K, flags, workspace, workspace_bytes,
-                   stream);
+  return run_mx(x, packed, scales, false, false, sel, p, shared, y, T, E, O, G, K, flags, workspace, workspace_bytes,
+                stream);
 }
 
 int mxfp4_mx_prepared_size(int64_t E, int64_t O, int64_t G, size_t* bytes) {
@@ -747,8 +750,54 @@ int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, 
   const uint8_t* pp = static_cast<const uint8_t*>(prepared);
   const size_t pbytes = mx_prepared_bytes(E, O, G);
   if (T > 0 && pp && y && overlap(y, (size_t)T * O * 2, pp, pbytes)) return MXFP4_ERR_INVALID_ARG;
-  return run_mxfp8(x, pp, pp ? pp + pbytes / 17 * 16 : nullptr, true, sel, p, shared, y, T, E, O, G, K, flags,
-                   workspace, workspace_bytes, stream);
+  return run_mx(x, pp, pp ? pp + pbytes / 17 * 16 : nullptr, true, false, sel, p, shared, y, T, E, O, G, K, flags,
+                workspace, workspace_bytes, stream);
+}
+
+int mxfp4_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t I, int64_t ld, uint8_t* codes, uint8_t* scale_bytes,
+                         hipStream_t stream) {
+  if (T < 0 || I < 32 || I % 32 || ld < I || ld % 32 || T * ld >= (int64_t(1) << 31)) return MXFP4_ERR_INVALID_ARG;
+  if (T == 0) return MXFP4_OK;
+  if (!x || !codes || !scale_bytes || !aligned(x, 8) || !aligned(codes, 4)) return MXFP4_ERR_INVALID_ARG;
+  const size_t nx = size_t(T) * I * 2, nc = size_t(T) * ld / 2, ns = size_t(T) * ld / 32;
+  if (overlap(codes, nc, x, nx) || overlap(scale_bytes, ns, x, nx) || overlap(codes, nc, scale_bytes, ns))
+    return MXFP4_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != MXFP4_OK) return st;
+  return hip_status(launch_quant_mxfp4(x, (int)T, (int)I, (int)ld, codes, scale_bytes, stream));
+}
+
+int mxfp4_moe_mxfp4act_workspace_size(int64_t T, int64_t E, int64_t O, int64_t G, int64_t K, size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  Dims d;
+  const int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  *bytes = (T == 0) ? 0 : mx_layout(d, true).total;
+  return MXFP4_OK;
+}
+
+int mxfp4_moe_linear_mxfp4act_ex(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, const int32_t* sel,
+                                 const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E, int64_t O,
+                                 int64_t G, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return run_mx(x, packed, scales, false, true, sel, p, shared, y, T, E, O, G, K, flags, workspace, workspace_bytes,
+                stream);
+}
+
+int mxfp4_moe_linear_mxfp4act_prepared_ex(const uint16_t* x, const void* prepared, const int32_t* sel,
+                                          const float* p, const uint16_t* shared, uint16_t* y, int64_t T, int64_t E,
+                                          int64_t O, int64_t G, int64_t K, uint32_t flags, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  const int st = check_dims(T, E, O, G, K, &d);
+  if (st != MXFP4_OK) return st;
+  if (!gemm_mx_supported(T, O, G)) return MXFP4_ERR_UNSUPPORTED;
+  const uint8_t* pp = static_cast<const uint8_t*>(prepared);
+  const size_t pbytes = mx_prepared_bytes(E, O, G);
+  if (T > 0 && pp && y && overlap(y, (size_t)T * O * 2, pp, pbytes)) return MXFP4_ERR_INVALID_ARG;
+  return run_mx(x, pp, pp ? pp + pbytes / 17 * 16 : nullptr, true, true, sel, p, shared, y, T, E, O, G, K, flags,
+                workspace, workspace_bytes, stream);
 }
 
 int mxfp4_moe_route(const float* logits, const float* bias, int64_t T, int64_t E, int64_t K, int mode, float scale,

@@ -75,8 +75,12 @@ static_assert(kWsDma * 256 * kWaves == kWsWin, "weight scale DMA");
 // (prepared) 1 weight-scale dword
 template <bool PREP>
 constexpr int kWeightLoads = PREP ? kWI + 1 : kWI;
-template <bool PREP>
-constexpr int kLoadsPerChunk = 3 + (PREP ? 0 : kWsDma) + kWeightLoads<PREP>;
+// activation DMA requests per wave and chunk: MXFP8 rows of 128 bytes, two;
+// MXFP4 rows of 64 bytes, one
+template <bool AF4>
+constexpr int kXDma = AF4 ? 1 : 2;
+template <bool PREP, bool AF4>
+constexpr int kLoadsPerChunk = kXDma<AF4> + 1 + (PREP ? 0 : kWsDma) + kWeightLoads<PREP>;
 
 // ---- quantisation
 
@@ -129,13 +133,63 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
   if (sub == 0) sb[(int64_t)t * nb + jb] = (uint8_t)(X + 127);
 }
 
+// MXFP4 activations: the same block maximum; X is the smallest exponent with
+// amax <= 6 * 2^X (6 = 1.5 * 2^2), each element's magnitude is rounded on
+// the E2M1 grid of its range (steps 0.5 below 2, 1 in [2, 4), 2 from 4;
+// rintf: ties to the even step, which is the even code) and clamped to 6;
+// codes sign << 3 | magnitude index, two to a byte, low nibble first.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  // v = x / 2^X with |v| <= 6 by the choice of X
+  const float a = fabsf(v);
+  const int ea = (int)(__float_as_uint(a) >> 23) - 127;  // floor(log2 a); -127 for 0 and subnormals
+  const int eq = ea > 0 ? ea : 0;
+  const uint32_t n = (uint32_t)rintf(a * __uint_as_float((uint32_t)(127 + 1 - eq) << 23));  // a / 2^(eq - 1)
+  const uint32_t code = 2u * (uint32_t)eq + n;
+  return code < 7u ? code : 7u;
+}
+
+__global__ void __launch_bounds__(256) quant_mxfp4_kernel(const uint16_t* __restrict__ x, int T, int I, int Kp,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ sb) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nb = Kp / 32;                 // blocks per row
+  const int64_t blk = gid >> 3;           // (token, block)
+  const int sub = (int)(gid & 7);         // four inputs 4 sub .. 4 sub + 3 of the block
+  if (blk >= (int64_t)T * nb) return;     // whole 8-lane groups leave together
+  const int t = (int)(blk / nb), jb = (int)(blk - (int64_t)t * nb);
+  const int k0 = 32 * jb + 4 * sub;
+  uint2 raw = make_uint2(0u, 0u);
+  if (32 * jb < I) raw = *reinterpret_cast<const uint2*>(x + (int64_t)t * I + k0);  // I % 32 == 0: whole blocks
+  const uint32_t h[4] = {raw.x & 0xFFFFu, raw.x >> 16, raw.y & 0xFFFFu, raw.y >> 16};
+  uint32_t amax = 0;  // |x| as bits: bf16 magnitudes order like their bit patterns
+#pragma unroll
+  for (int i = 0; i < 4; i++) amax = max(amax, h[i] & 0x7FFFu);
+  amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
+  amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0x4E, 0xF, 0xF, false));
+  amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0x141, 0xF, 0xF, false));
+  // X: the smallest exponent with amax <= 6 * 2^X (6 = 1.5 * 2^2), clamped to [-127, 127]
+  const uint32_t ab = amax << 16;  // fp32 bits of amax
+  const int e = (int)(ab >> 23) - 127;
+  int X = (ab & 0x7FFFFFu) <= 0x400000u ? e - 2 : e - 1;
+  if ((ab >> 23) == 0) X = -127;  // zero or subnormal block
+  X = X < -127 ? -127 : (X > 127 ? 127 : X);
+  const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, X in [-127, 126] for finite bf16
+  uint32_t half = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float v = __uint_as_float(h[i] << 16) * inv;
+    half |= (e2m1_code(v) | ((h[i] >> 12) & 0x8u)) << (4 * i);
+  }
+  *reinterpret_cast<uint16_t*>(codes + (int64_t)t * (Kp / 2) + k0 / 2) = (uint16_t)half;
+  if (sub == 0) sb[(int64_t)t * nb + jb] = (uint8_t)(X + 127);
+}
+
 // ---- grouped GEMM
 
 // PREP: the weights come in the fragment-major prepared layout of
 // prepare_mx_kernel (one contiguous 1 KB block per 16-row fragment and chunk,
 // and one scale dword per lane for four fragments) instead of the canonical
 // [E, O, G, 16] / [E, O, G].
-template <bool PREP>
+template <bool PREP, bool AF4>
 __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                          const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ scales,
@@ -165,9 +219,10 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   // groups without padding; and 4 x 64 scale dwords (wave w's dword
   // l < 32 is row 32 w + l). Three separate arrays, so that the compiler can
   // tell a slot being read from the slots the DMA is filling.
-  __shared__ __attribute__((aligned(16))) uint8_t X0[MT * KC];
-  __shared__ __attribute__((aligned(16))) uint8_t X1[MT * KC];
-  __shared__ __attribute__((aligned(16))) uint8_t X2[MT * KC];
+  constexpr int XB = AF4 ? KC / 2 : KC;  // bytes of one activation row and chunk
+  __shared__ __attribute__((aligned(16))) uint8_t X0[MT * XB];
+  __shared__ __attribute__((aligned(16))) uint8_t X1[MT * XB];
+  __shared__ __attribute__((aligned(16))) uint8_t X2[MT * XB];
   __shared__ __attribute__((aligned(16))) uint32_t S0[64 * kWaves];
   __shared__ __attribute__((aligned(16))) uint32_t S1[64 * kWaves];
   __shared__ __attribute__((aligned(16))) uint32_t S2[64 * kWaves];
@@ -184,12 +239,16 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   // so fetches piece (l & 7) ^ ((m >> 1) & 7) of its row. Scale DMA: lane l < 16 fetches the dword of
   // row 16 w + l (blocks 4q .. 4q+3); lanes 16 .. 63 read past the resource
   // and write zeros into the unused part of the wave's 64 dwords.
-  uint32_t x_off[2];
+  // MXFP4 activations (rows of 64 bytes, 4 pieces): wave w's one request
+  // fills rows 16 w .. 16 w + 15; lane l lands at row m = 16 w + (l >> 2),
+  // position l & 3, and fetches piece (l & 3) ^ ((m >> 2) & 3) of its row.
+  uint32_t x_off[kXDma<AF4>];
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int m = 16 * w + 8 * j + (lane >> 3);
+  for (int j = 0; j < kXDma<AF4>; j++) {
+    const int m = AF4 ? 16 * w + (lane >> 2) : 16 * w + 8 * j + (lane >> 3);
     const int tok = m < tl.mlen ? perm[tl.row0 + m] / K : -1;
-    x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kp + 16u * (uint32_t)((lane & 7) ^ ((m >> 1) & 7)) : kOob;
+    const int piece = AF4 ? (lane & 3) ^ ((m >> 2) & 3) : (lane & 7) ^ ((m >> 1) & 7);
+    x_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)(Kp / (AF4 ? 2 : 1)) + 16u * (uint32_t)piece : kOob;
   }
   uint32_t s_off;
   {
@@ -260,9 +319,9 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
             (int)(ws_off[m] + 4u * q), 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 2; j++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xdst + (16 * w + 8 * j) * KC),
-                                               16, (int)(x_off[j] + 128u * q), 0, 0, 0);
+    for (int j = 0; j < kXDma<AF4>; j++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xdst + (16 * w + 8 * j) * XB),
+                                               16, (int)(x_off[j] + (uint32_t)XB * q), 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sdst + 64 * w), 4,
                                              (int)(s_off + 4u * q), 0, 0, 0);
   };
@@ -282,7 +341,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
   // wait until this wave's DMA of the next chunk has landed: it was followed
   // by that chunk's weight requests and by one whole chunk of requests
   auto wait_next_x = [&]() {
-    constexpr int n = kWeightLoads<PREP> + kLoadsPerChunk<PREP>;
+    constexpr int n = kWeightLoads<PREP> + kLoadsPerChunk<PREP, AF4>;
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
   };
 
@@ -321,22 +380,32 @@ __global__ void __launch_bounds__(512, 1) gemm_mx_kernel(const uint8_t* __restri
 #pragma unroll
     for (int j = 0; j < kWJ; j++) {
       const int p = 16 * j + lr;  // rows past the tile's end hold zeros (their DMA read past the resource)
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * (lc ^ (lr >> 1))]);  // (p >> 1) & 7 = lr >> 1
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * KC + 16 * ((4 + lc) ^ (lr >> 1))]);
-      const v8i bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      v8i bf;
+      if constexpr (AF4) {
+        // lane (p, c): the 16 bytes of block 4 q + c of pair p, like a weight lane's group
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * XB + 16 * (lc ^ (lr >> 2))]);  // (p >> 2) & 3 = lr >> 2
+        bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+      } else {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&xc[p * XB + 16 * (lc ^ (lr >> 1))]);  // (p >> 1) & 7 = lr >> 1
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&xc[p * XB + 16 * ((4 + lc) ^ (lr >> 1))]);
+        bf = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
       const int bs = (int)((sc[(p >> 4) * 64 + (p & 15)] >> (8 * lc)) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < kWI; i++) {
         const v8i a = v8i{(int)wf[R][i][0], (int)wf[R][i][1], (int)wf[R][i][2], (int)wf[R][i][3], 0, 0, 0, 0};
         const int as = PREP ? (int)((wsp[R] >> (8 * i)) & 0xFFu) : as_c[i];
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, 0, 0, as, 0, bs);
+        // A: E2M1 (format 4); B: E4M3 (0) or E2M1 (4)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf, acc[i][j], 4, AF4 ? 4 : 0, 0, as, 0, bs);
       }
     }
-    // interleave each fragment's three LDS reads with its MFMAs, so that only
-    // a few activation fragments are live at once (registers)
+    // interleave each fragment's LDS reads with its MFMAs, so that only a few
+    // activation fragments are live at once (registers; with MXFP4
+    // activations, groups of one read keep the canonical instantiation
+    // within its registers)
 #pragma unroll
     for (int j = 0; j < kWJ; j++) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, AF4 ? 1 : 3, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, kWI, 0);
     }
     wait_next_x();
@@ -471,21 +540,49 @@ hipError_t launch_quant_mxfp8(const uint16_t* x, int T, int I, int Kp, uint8_t* 
   return hipGetLastError();
 }
 
+namespace {
+template <bool PREP, bool AF4>
+void launch_gemm_mx_t(dim3 grid, const uint8_t* xq, const uint8_t* xs, const uint8_t* packed, const uint8_t* scales,
+                      const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, float* part, int K, int O,
+                      int G, int Kp, int n_ntiles, int n_wg, uint32_t xq_bytes, uint32_t xs_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_mx_kernel<PREP, AF4>), grid, dim3(64 * kWaves), 0, stream, xq, xs, packed, scales, perm,
+                     tiles, n_tiles, part, K, O, G, Kp, n_ntiles, n_wg, xq_bytes, xs_bytes);
+}
+}  // namespace
+
+hipError_t launch_quant_mxfp4(const uint16_t* x, int T, int I, int Kp, uint8_t* codes, uint8_t* sb,
+                              hipStream_t stream) {
+  if (I % 32 || Kp % 32 || Kp < I) return hipErrorInvalidValue;
+  const int64_t threads = (int64_t)T * (Kp / 32) * 8;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_mxfp4_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, x, T, I, Kp,
+                     codes, sb);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* packed, const uint8_t* scales,
                           const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
-                          float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared) {
+                          float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared, bool act_fp4) {
   const int Kp = mx_row_bytes(32 * (int64_t)G);
   const int n_ntiles = (O + NT - 1) / NT, n_wg = (O + NW - 1) / NW;
   // 8 XCDs x an even number of M-tiles each x the feature tiles
   const int64_t nblk = (max_tiles + 15) / 16 * 16 * n_wg;  // an even number of tiles per XCD
   if (nblk == 0) return hipSuccess;
-  const uint32_t xq_bytes = (uint32_t)((int64_t)T * Kp), xs_bytes = (uint32_t)((int64_t)T * Kp / 32);
-  if (prepared)
-    hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, xq, xs, packed, scales,
-                       perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles, n_wg, xq_bytes, xs_bytes);
+  // activation codes: Kp bytes per token (MXFP8) or Kp / 2 (MXFP4)
+  const uint32_t xq_bytes = (uint32_t)((int64_t)T * Kp / (act_fp4 ? 2 : 1)), xs_bytes = (uint32_t)((int64_t)T * Kp / 32);
+  const dim3 grid((unsigned)nblk);
+  if (prepared && act_fp4)
+    launch_gemm_mx_t<true, true>(grid, xq, xs, packed, scales, perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles,
+                                 n_wg, xq_bytes, xs_bytes, stream);
+  else if (prepared)
+    launch_gemm_mx_t<true, false>(grid, xq, xs, packed, scales, perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles,
+                                  n_wg, xq_bytes, xs_bytes, stream);
+  else if (act_fp4)
+    launch_gemm_mx_t<false, true>(grid, xq, xs, packed, scales, perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles,
+                                  n_wg, xq_bytes, xs_bytes, stream);
   else
-    hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3((unsigned)nblk), dim3(64 * kWaves), 0, stream, xq, xs, packed, scales,
-                       perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles, n_wg, xq_bytes, xs_bytes);
+    launch_gemm_mx_t<false, false>(grid, xq, xs, packed, scales, perm, tiles, n_tiles, part, K, O, G, Kp, n_ntiles,
+                                   n_wg, xq_bytes, xs_bytes, stream);
   return hipGetLastError();
 }
 

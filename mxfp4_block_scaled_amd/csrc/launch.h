@@ -116,11 +116,17 @@ int mx_row_bytes(int64_t I);
 bool gemm_mx_supported(int64_t T, int64_t O, int64_t G);  // O % 4 == 0, T * Kp and O * G * 16 below 2^31
 hipError_t launch_quant_mxfp8(const uint16_t* x, int T, int I, int Kp, uint8_t* codes, uint8_t* sb,
                               hipStream_t stream);
+// MXFP4 activations: codes (T, Kp / 2), two to a byte low nibble first, and
+// scale bytes (T, Kp / 32)
+hipError_t launch_quant_mxfp4(const uint16_t* x, int T, int I, int Kp, uint8_t* codes, uint8_t* sb,
+                              hipStream_t stream);
 // prepared = true: `packed` is a buffer written by launch_prepare_mx (its scale
 // array follows the packed slots) and `scales` points at that scale array.
+// act_fp4: xq holds MXFP4 activation codes (T, Kp / 2) instead of MXFP8 (T, Kp).
 hipError_t launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* packed, const uint8_t* scales,
                           const int32_t* perm, const GemmTile* tiles, const int32_t* n_tiles, int64_t max_tiles,
-                          float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared = false);
+                          float* part, int T, int K, int O, int G, hipStream_t stream, bool prepared = false,
+                          bool act_fp4 = false);
 // the prepared weight layout of the block-scaled variant: 16 bytes of codes and
 // one scale byte per group slot, slots = E * ceil(O / 128) * (Kp / 128) * 512
 size_t mx_prepared_bytes(int64_t E, int64_t O, int64_t G);

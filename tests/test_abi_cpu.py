@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES)
@@ -253,10 +253,12 @@ def test_route_empty_batch_is_a_no_op():
 
 # ---- the block-scaled variant
 
+MX_ENTRY = ["mxfp4_moe_linear_mxfp8_ex", "mxfp4_moe_linear_mxfp4act_ex"]
+
+
 def _mx(x=A, packed=B, scales=C, sel=C + 0x10000, p=C + 0x20000, shared=C + 0x30000, y=C + 0x40000, T=2, E=3,
-        O=8, G=2, K=2, flags=0, ws=C + 0x60000, ws_bytes=1 << 24):
-    return _abi.lib().mxfp4_moe_linear_mxfp8_ex(x, packed, scales, sel, p, shared, y, T, E, O, G, K, flags, ws,
-                                                ws_bytes, None)
+        O=8, G=2, K=2, flags=0, ws=C + 0x60000, ws_bytes=1 << 24, fn="mxfp4_moe_linear_mxfp8_ex"):
+    return getattr(_abi.lib(), fn)(x, packed, scales, sel, p, shared, y, T, E, O, G, K, flags, ws, ws_bytes, None)
 
 
 def test_mxfp8_workspace_size():
@@ -274,14 +276,28 @@ def test_mxfp8_workspace_size():
     dict(x=0), dict(packed=0), dict(scales=0), dict(sel=0), dict(p=0), dict(shared=0), dict(y=0),
     dict(x=A + 2), dict(sel=C + 0x10001), dict(y=A), dict(y=B + 16),
 ])
-def test_mxfp8_host_checks_reject(kw):
-    assert _mx(**kw) == _abi.ERR_INVALID_ARG
+@pytest.mark.parametrize("fn", MX_ENTRY)
+def test_mxfp8_host_checks_reject(kw, fn):
+    assert _mx(fn=fn, **kw) == _abi.ERR_INVALID_ARG
 
 
-def test_mxfp8_host_checks_workspace_unsupported_and_empty():
-    assert _mx(ws_bytes=16) == _abi.ERR_WORKSPACE_TOO_SMALL
-    assert _mx(O=6) == _abi.ERR_UNSUPPORTED
-    assert _mx(T=0, x=0, y=0, shared=0, sel=0, p=0) == _abi.OK
+@pytest.mark.parametrize("fn", MX_ENTRY)
+def test_mxfp8_host_checks_workspace_unsupported_and_empty(fn):
+    assert _mx(ws_bytes=16, fn=fn) == _abi.ERR_WORKSPACE_TOO_SMALL
+    assert _mx(O=6, fn=fn) == _abi.ERR_UNSUPPORTED
+    assert _mx(T=0, x=0, y=0, shared=0, sel=0, p=0, fn=fn) == _abi.OK
+
+
+def test_mxfp4act_workspace_size():
+    assert _abi.mxfp4act_workspace_size(0, 4, 8, 2, 2) == 0
+    T, E, O, G, K = 4096, 128, 5760, 90, 4
+    ws = _abi.mxfp4act_workspace_size(T, E, O, G, K)
+    # fp32 partial rows, codes (two per byte) and scales of 128-padded rows
+    assert ws >= T * K * O * 4 + T * 2944 // 2 + T * 2944 // 32
+    assert ws < _abi.mxfp8_workspace_size(T, E, O, G, K)
+    with pytest.raises(_abi.Mxfp4Error) as e:  # O % 4 != 0
+        _abi.mxfp4act_workspace_size(4, 4, 6, 2, 2)
+    assert e.value.status == _abi.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("args", [
@@ -290,13 +306,15 @@ def test_mxfp8_host_checks_workspace_unsupported_and_empty():
     (A, 2, 64, 64, B + 2, C), (A, 2, 64, 64, A + 64, C), (A, 2, 64, 64, B, A + 8),
     (A, 1 << 25, 64, 64, B, C),
 ])
-def test_quantize_mxfp8_host_checks(args):
+@pytest.mark.parametrize("fn", ["mxfp4_quantize_mxfp8", "mxfp4_quantize_mxfp4"])
+def test_quantize_mxfp8_host_checks(args, fn):
     x, T, I, ld, codes, sb = args
-    assert _abi.lib().mxfp4_quantize_mxfp8(x, T, I, ld, codes, sb, None) == _abi.ERR_INVALID_ARG
+    assert getattr(_abi.lib(), fn)(x, T, I, ld, codes, sb, None) == _abi.ERR_INVALID_ARG
 
 
-def test_quantize_mxfp8_empty():
-    assert _abi.lib().mxfp4_quantize_mxfp8(0, 0, 64, 64, 0, 0, None) == _abi.OK
+@pytest.mark.parametrize("fn", ["mxfp4_quantize_mxfp8", "mxfp4_quantize_mxfp4"])
+def test_quantize_mxfp8_empty(fn):
+    assert getattr(_abi.lib(), fn)(0, 0, 64, 64, 0, 0, None) == _abi.OK
 
 
 def test_mx_prepared_size_and_host_checks():
@@ -320,6 +338,14 @@ def test_mx_prepared_size_and_host_checks():
     assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(A, B, C + 0x10000, C + 0x20000, C + 0x30000, B + 32, 2, 2, 8,
                                                   2, 2, 0, ws, 1 << 24, None) == _abi.ERR_INVALID_ARG
     assert lib.mxfp4_moe_linear_mxfp8_prepared_ex(0, 0, 0, 0, 0, 0, 0, 2, 8, 2, 2, 0, 0, 0, None) == _abi.OK
+    for fn in (lib.mxfp4_moe_linear_mxfp4act_prepared_ex,):
+        assert fn(A, B, C + 0x10000, C + 0x20000, C + 0x30000, C + 0x40000, 2, 2, 8, 2, 2, 0, ws, 16,
+                  None) == _abi.ERR_WORKSPACE_TOO_SMALL
+        assert fn(A, 0, C + 0x10000, C + 0x20000, C + 0x30000, C + 0x40000, 2, 2, 8, 2, 2, 0, ws, 1 << 24,
+                  None) == _abi.ERR_INVALID_ARG
+        assert fn(A, B, C + 0x10000, C + 0x20000, C + 0x30000, B + 32, 2, 2, 8, 2, 2, 0, ws, 1 << 24,
+                  None) == _abi.ERR_INVALID_ARG
+        assert fn(0, 0, 0, 0, 0, 0, 0, 2, 8, 2, 2, 0, 0, 0, None) == _abi.OK
 
 
 # ------------------------------------------------------------------ prepared-weight entry points (host checks)
