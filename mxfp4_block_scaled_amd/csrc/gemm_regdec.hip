@@ -7,10 +7,11 @@
 // 2^(s-127)).
 //
 // Two weight layouts. Canonical (CANON): packed (E, O, G, 16) and scales
-// (E, O, G) as the caller holds them; the weight DMA fetches each lane's
-// 16-byte group straight from that layout into the fragment-major slot order
-// below, and the scale bytes come into LDS in windows of 16 groups (each
-// row's bytes read as whole dwords from the dword boundary below them).
+// (E, O, G) as the caller holds them; the weight DMA fetches the 16-byte
+// groups straight from that layout, four lanes to a row's 64 contiguous
+// bytes, into one 1 KB block per 16-row fragment and chunk, and the scale
+// bytes come into LDS in windows of 8 groups (each row's bytes read as whole
+// dwords from the dword boundary below them).
 // The weights and activations then use two-slot rings, one chunk ahead,
 // with a full wait per chunk, as the scale windows leave no room for a third
 // weight slot.
@@ -173,8 +174,11 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   // Prepared weights: code block 4 w + j of the workgroup (prepared tile
   // 4 nt + (w >> 1), block 4 (w & 1) + j: dword j of fragments 4 (w & 1) .. +3).
   // Canonical weights: fragment i = (4 w + j) & 7 of wave column
-  // t = (4 w + j) >> 3, lane l fetching the 16 bytes of (row crow(t, i, l & 15),
-  // group 4 q + (l >> 4)) - the same fragment-major slot order.
+  // t = (4 w + j) >> 3, lane l fetching the 16 bytes of (row crow(t, i, l >> 2),
+  // group 4 q + (((l & 3) - (l >> 4)) & 3)): each 4 lanes read the 64
+  // contiguous bytes of one row (rows are 16 G bytes apart: one lane per row
+  // would touch 16 cache lines per 16 lanes), and the slot of MFMA lane
+  // (r, c) lies at position 4 r + ((c + (r >> 2)) & 3) of the block.
   // crow: the matrix row of fragment i, row r of wave column t.
   auto crow = [&](int t, int i, int r) -> int {
     if constexpr (MODE == kSwiGLU) {
@@ -195,11 +199,12 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   const uint32_t w_off = dpt < n_ptiles ? (uint32_t)(((dpt * nq * 8 + 4 * (w & 1)) * 64 + lane) * 16) : kOob;
   // canonical: byte offset of this lane's group in chunk 0 per request (chunk q: + 64 q)
   uint32_t wc_off[CANON ? kWDma : 1];
+  const int wgrp = ((lane & 3) - (lane >> 4)) & 3;  // canonical: this lane's group in its chunk
   if constexpr (CANON) {
 #pragma unroll
     for (int j = 0; j < kWDma; j++) {
-      const int row = crow((4 * w + j) >> 3, (4 * w + j) & 7, lr);
-      wc_off[j] = row >= 0 ? ((uint32_t)row * (uint32_t)G + (uint32_t)lc) * 16u : kOob;
+      const int row = crow((4 * w + j) >> 3, (4 * w + j) & 7, lane >> 2);
+      wc_off[j] = row >= 0 ? ((uint32_t)row * (uint32_t)G + (uint32_t)wgrp) * 16u : kOob;
     }
   }
   // scale dwords of this wave's own tile (fragments 0..3 and 4..7), chunk 0 (chunk q: + 512 q)
@@ -248,7 +253,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   auto dma_w = [&](int q, uint8_t* dst, int slot) {
     if constexpr (CANON) {
       // a group past G moves the offset past the resource (zero codes)
-      const uint32_t past = (uint32_t)(G - 1 - (4 * q + lc)) >> 31 << 31;
+      const uint32_t past = (uint32_t)(G - 1 - (4 * q + wgrp)) >> 31 << 31;
 #pragma unroll
       for (int j = 0; j < kWDma; j++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + (4 * w + j) * 1024), 16,
@@ -287,6 +292,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   bool shifted = false;  // wave-uniform: decoding at scale byte s - kShift
 
   // the MFMAs of one chunk: activations xc, weight codes wc, the 8 scale bytes
+  const int wpos = 4 * lr + ((lc + (lr >> 2)) & 3);  // canonical: this lane's slot in a weight block
   auto mma_chunk = [&](const uint8_t* xc, const uint8_t* wc, const uint32_t(&sb_in)[kWI]) __attribute__((always_inline)) {
     uint32_t sb[kWI];
     bool big = false;
@@ -312,9 +318,10 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
       sc[i] = e8m0_operand(!shifted ? sb[i] : (sb[i] > kShift ? sb[i] - kShift : 0u));
 #pragma unroll
     for (int s = 0; s < 4; s++) {
-      // canonical: lane group c takes dword (s + c) & 3 of its slots at k-step s,
-      // so the 64 lanes' 4-byte reads at a 16-byte stride hit 64 distinct banks;
-      // its activations follow the same order
+      // canonical: lane group c takes dword (s + c) & 3 of its slots at k-step
+      // s (the same inputs for every row and column of the MFMA), which with
+      // the slot positions puts the 64 lanes' 4-byte reads on 64 distinct
+      // banks; its activations follow the same order
       const int sd = CANON ? (s + lc) & 3 : s;
       bf16x8 b[kWJ];
 #pragma unroll
@@ -328,7 +335,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
         // dword sd of this lane's slot of each of the wave's fragments (blocks 8 wn .. 8 wn + 7)
 #pragma unroll
         for (int i = 0; i < kWI; i++)
-          raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(8 * wn + i) * 1024 + 16 * lane + 4 * sd]);
+          raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(8 * wn + i) * 1024 + 16 * wpos + 4 * sd]);
       } else {
         // dword s of this lane's slot of each fragment (8 codes each): blocks s and 4 + s of tile wn
         const u32x4 lo = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + s) * 1024 + 16 * lane]);
