@@ -51,6 +51,7 @@ METRIC = "packed-weight GB/s (decode) & TFLOP/s (prefill), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
 MFMA_FP8_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 MFMA, published (the fp4 x fp8 scaled MFMA runs at this rate)
+MFMA_FP4_PEAK_TFLOPS = 10066.4  # MI355X dense fp4 MFMA, published (both operands of the scaled MFMA in fp4)
 N_ROUTING_SETS = 64
 DECODE_WORKLOADS = ("tiny", "decode", "decode8")
 KERNEL_SOURCES = {
@@ -59,6 +60,7 @@ KERNEL_SOURCES = {
     "gemm": ["mxfp4_block_scaled_amd/csrc/gemm_regdec.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "swiglu": ["mxfp4_block_scaled_amd/csrc/gemm_regdec.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "mx": ["mxfp4_block_scaled_amd/csrc/gemm_mx.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
+    "mx4": ["mxfp4_block_scaled_amd/csrc/gemm_mx.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
     "gemmp": ["mxfp4_block_scaled_amd/csrc/gemm_regdec.hip", "mxfp4_block_scaled_amd/csrc/device_common.h"],
 }
 # the dominant kernel per path: bf16 prefill-shaped calls on canonical weights
@@ -162,10 +164,10 @@ def record_traffic(args):
 
 
 def _kind(w, variant=None, prepared=False) -> str:
-    if variant == "mxfp8":
+    if variant in ("mxfp8", "mxfp4"):
         if w.F or w.dtype != "bf16":
-            raise SystemExit("the MXFP8 variant runs the bf16 routed linear workloads only")
-        return "mx"
+            raise SystemExit("the block-scaled variants run the bf16 routed linear workloads only")
+        return "mx" if variant == "mxfp8" else "mx4"
     if w.F:
         return "swiglup" if prepared else "swiglu"
     if w.name in DECODE_WORKLOADS:
@@ -220,7 +222,8 @@ def cpu_baseline(inp, kind, sample_seconds):
     rng = np.random.default_rng(0)
     while True:
         rows = np.sort(rng.choice(w.O, rows_per_call, replace=False))
-        rows_fn = oracle.expert_linear_mxfp8_rows if kind == "mx" else oracle.expert_linear_rows
+        rows_fn = {"mx": oracle.expert_linear_mxfp8_rows,
+                   "mx4": oracle.expert_linear_mxfp4act_rows}.get(kind, oracle.expert_linear_rows)
         rows_fn(inp.x, inp.packed, inp.scales, inp.sel, inp.p, inp.shared, rows)
         done_flops += 2.0 * w.P * rows_per_call * w.I
         calls += 1
@@ -235,6 +238,8 @@ def cpu_baseline(inp, kind, sample_seconds):
 def _path_name(mx, w, kind) -> str:
     if kind == "mx":
         return "MXFP8 variant (bucketing, quantisation, scaled-MFMA grouped GEMM, combine)"
+    if kind == "mx4":
+        return "MXFP4-activation variant (bucketing, quantisation, FP4 x FP4 scaled-MFMA grouped GEMM, combine)"
     if kind == "gemvp":
         return "decode-shaped MFMA kernel on prepared weights (routing, dequant-GEMV, combine in one launch)"
     if kind == "gemmp":
@@ -453,6 +458,8 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
         ws_bytes = mx.swiglu_workspace_size(w.T, w.E, w.F, w.G, w.O, w.K)
     elif kind == "mx":
         ws_bytes = mx.mxfp8_workspace_size(w.T, w.E, w.O, w.G, w.K)
+    elif kind == "mx4":
+        ws_bytes = mx.mxfp4act_workspace_size(w.T, w.E, w.O, w.G, w.K)
     elif kind == "gemmp":
         ws_bytes = mx.workspace_size(w.T, w.E, w.O, w.G, w.K, mx.DTYPE_BF16, mx.FLAG_FORCE_GEMM)
     elif kind == "gemvp":
@@ -479,6 +486,10 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
             mx.moe_linear_mxfp8_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "mx":
             mx.moe_linear_mxfp8(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
+        elif kind == "mx4" and prepared is not None:
+            mx.moe_linear_mxfp4act_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
+        elif kind == "mx4":
+            mx.moe_linear_mxfp4act(x, packed, scales, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "gemmp":
             mx.moe_linear_prepared(x, prepared, sels[r], ps[r], shared, out=y, workspace=ws)
         elif kind == "gemvp":
@@ -585,14 +596,16 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
     if kind in ("swiglu", "swiglup"):
         flops_per_step = 2.0 * w.P * (2 * w.F * w.I + w.O * w.F)
     extra = {}
-    if kind == "mx":
+    if kind in ("mx", "mx4"):
         # the variant's grouped GEMM on the scaled MFMA is its work; timed as
         # the whole call (bucketing, quantisation and combine included)
         value = flops_per_step / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-        roof = {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(value / MFMA_FP8_PEAK_TFLOPS, 4)}
-        roof["kernel"] = "gemm_mx_kernel<%s> (whole call)" % ("true" if prepared is not None else "false")
+        peak = MFMA_FP8_PEAK_TFLOPS if kind == "mx" else MFMA_FP4_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(value, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(value / peak, 4)}
+        roof["kernel"] = "gemm_mx_kernel<%s, %s> (whole call)" % ("true" if prepared is not None else "false",
+                                                                  "true" if kind == "mx4" else "false")
         roof["launch_ms"] = round(ms_step, 6)
     elif kind in ("swiglu", "swiglup"):
         # the block's two grouped GEMMs are its work; timed here as the whole
@@ -629,7 +642,7 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
         extra["weight_GBs_whole_call"] = round(w.E * w.O * w.G * 17 / (ms_step * 1e-3) / 1e9, 1) \
             if len(np.unique(inp.sel)) == w.E else None
     roof["per_launch"] = ({"bytes": bytes_per_step} if kind in ("gemv", "gemvp") else {"flops": flops_per_step})
-    if kind in ("swiglu", "swiglup", "mx", "gemvp"):
+    if kind in ("swiglu", "swiglup", "mx", "mx4", "gemvp"):
         roof["traffic"] = None
     else:
         roof["traffic"] = committed_traffic(w.name + ("-prepared" if kind == "gemmp" else ""), kind)
@@ -638,8 +651,9 @@ def measure(args, w, kind, steps, warmup, cpu_seconds, n_sets):
         f"mean distinct experts {np.mean(uniq):.1f}")
     rec = {
         "value": round(value, 2), "unit": unit, "ms_per_step": round(ms_step, 6), "steps": steps,
-        "dtype": "fp4xfp8" if kind == "mx" else ("f32" if w.dtype == "fp32" else "bf16"),
-        "config": {"workload": w.name + ("-mxfp8" if kind == "mx" else "") + ("-prepared" if prepared is not None else ""),
+        "dtype": {"mx": "fp4xfp8", "mx4": "fp4xfp4"}.get(kind, "f32" if w.dtype == "fp32" else "bf16"),
+        "config": {"workload": w.name + {"mx": "-mxfp8", "mx4": "-mxfp4"}.get(kind, "")
+                               + ("-prepared" if prepared is not None else ""),
                    "T": w.T, "E": w.E, "K": w.K, "G": w.G, "I": w.I, "O": w.O,
                    **({"F": w.F} if w.F else {}),
                    "x_dtype": w.dtype, "routing": w.routing if w.routing == "uniform" else f"zipf({w.zipf_s})",
@@ -718,6 +732,54 @@ def stream_ceiling(window_bytes, steps, warmup, settle_ms):
     return {"kernel": "stream_read_kernel", **out}
 
 
+def dense_gemm_ceiling(names, steps, settle_ms):
+    """The vendor library's dense bf16 GEMM (torch.matmul on hipBLASLt) at
+    each prefill workload's M = T K pairs, N = O, K = I, bf16 weights stored
+    [O, I] like the experts' rows: no gather, no decode, no expert groups.
+    A context figure for the grouped GEMM's MFMA fraction on this GPU (clock
+    and power included), not part of the layer."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    out = {}
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        M, N, K = w.T * w.K, w.O, w.I
+        a = torch.randn((M, K), generator=gen, device=dev, dtype=torch.bfloat16)
+        wt = torch.randn((N, K), generator=gen, device=dev, dtype=torch.bfloat16)
+        c = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+
+        def one_pass():
+            for _ in range(steps):
+                torch.matmul(a, wt.t(), out=c)
+
+        stream = torch.cuda.Stream(device=dev)
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            one_pass()
+        torch.cuda.synchronize()
+        settle_passes(one_pass, stream, steps, settle_ms)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            one_pass()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out[name] = {"M": M, "N": N, "K": K, "ms_per_launch": round(ms, 6), "TFLOPs": round(tf, 1),
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(f"[bench] dense bf16 GEMM {M}x{N}x{K} (library): {ms * 1e3:.1f} us, {tf:.0f} TFLOP/s "
+            f"({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}% of the bf16 MFMA peak)")
+        del a, wt, c
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"kernel": "torch.matmul (bf16, hipBLASLt)", **out}
+
+
 SUITE = ("tiny", "decode8", "prefill", "skewed")
 STREAM_BLOCKS = (512, 2048, 8192)
 
@@ -741,14 +803,17 @@ def main():
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="host only: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload and of "
                          "the copy calibration (--copy-mib) into profiles/traffic.json")
-    ap.add_argument("--variant", choices=["mxfp8"],
-                    help="time the block-scaled variant (MXFP8 activations on the scaled MFMA) instead of the layer")
+    ap.add_argument("--variant", choices=["mxfp8", "mxfp4"],
+                    help="time a block-scaled variant (activations quantised to MXFP8 or MXFP4, multiplied on "
+                         "the scaled MFMA) instead of the layer")
     ap.add_argument("--prepared", action="store_true",
                     help="weights repacked once (outside the timed region) by prepare_bf16: the bf16 GEMM on "
-                         "prepared weights, or with --variant mxfp8 the variant's")
+                         "prepared weights, or with --variant the variant's")
     ap.add_argument("--router", choices=["softmax", "sigmoid"],
                     help="time the router alone at the workload's T, E and K instead of the layer")
     ap.add_argument("--stream", action="store_true", help="time only the plain streaming-read ceiling")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time only the library's dense bf16 GEMM at the prefill workloads' sizes")
     args = ap.parse_args()
     if args.record_traffic:
         if args.copy_mib <= 0:
@@ -779,6 +844,10 @@ def main():
         st = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup, args.settle_ms)
         print(json.dumps({"stream_ceiling": st}), flush=True)
         return
+    if args.gemm_ceiling:
+        print(json.dumps({"dense_gemm_ceiling": dense_gemm_ceiling(("prefill", "skewed"), args.steps,
+                                                                   args.settle_ms)}), flush=True)
+        return
     suite = not args.workload and not args.no_suite
     w = workloads.WORKLOADS[args.workload or "decode"]
     kind = _kind(w, args.variant, args.prepared)
@@ -805,6 +874,7 @@ def main():
             sub[name] = measure(sargs, sw, skind, args.steps, args.warmup,
                                 0.0 if args.no_cpu_baseline else args.suite_cpu_seconds, s_sets)
         sub["stream_ceiling"] = stream_ceiling(dec.K * dec.O * dec.G * 17, args.steps, args.warmup, args.settle_ms)
+        sub["dense_gemm_ceiling"] = dense_gemm_ceiling(("prefill", "skewed"), args.steps, args.settle_ms)
         out["suite"] = sub
     print(json.dumps(out), flush=True)
 
