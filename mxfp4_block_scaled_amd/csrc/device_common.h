@@ -33,6 +33,14 @@ constexpr int kWave = 64;
 constexpr int kGroupBytes = 16;
 constexpr int kGroupValues = 32;
 
+// Cache-policy argument of the decode kernels' buffer loads of weight codes
+// (gfx950: 2 = nt, non-temporal). Each code byte is read once; marked so,
+// the code stream no longer evicts from the vector L1 the row's scale-byte
+// line, which the next slots of the same rows read again 32 or 64 bytes at
+// a time (unmarked, nearly every slot's scale load missed L1 and cost a
+// whole line request, and the L1's outstanding misses bound the kernel).
+constexpr int kCodeLoadPolicy = 2;
+
 // fp32 operand whose exponent field is the E8M0 byte s: the scaled converts
 // multiply by 2^(s-127).
 __device__ __forceinline__ float e8m0_operand(uint32_t s) { return __uint_as_float(s << 23); }

@@ -200,14 +200,14 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(
         const uint32_t ck = si >> 9;                             // (tile, chunk) of the slot
         const uint32_t so = ((ck * 2u + (uint32_t)(pf >> 2)) * 64u + (uint32_t)lane) * 4u + (uint32_t)(pf & 3);
         rw[s][t] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(l_done ? kOob32 : si * 16u), 0, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(l_done ? kOob32 : si * 16u), 0, kCodeLoadPolicy));
         rs[s][t] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)(l_done ? kOob32 : so), 0, 0);
       } else {
         // a lane past its split reads the following group (the next row at the
         // end of a row; beyond the resource at the end of the expert); it
         // meets the zero activation group, so it adds nothing
         const uint32_t gi = l_done ? kOobGroup : l_off[t] + (uint32_t)(8 * l_it);
-        rw[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, 0));
+        rw[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, kCodeLoadPolicy));
         rs[s][t] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)gi, 0, 0);
       }
     }

@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_rows_kernel(
     for (int i = 0; i < kRpl; i++) {
       // past the wave's last item: beyond the resource (zeros, no memory traffic)
       const uint32_t gi = l_done ? kOobGroup : l_off[i] + (uint32_t)(L * l_m);
-      rw[s][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, 0));
+      rw[s][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsw, (int)(gi * 16u), 0, kCodeLoadPolicy));
       rs[s][i] = __builtin_amdgcn_raw_buffer_load_b8(rss, (int)gi, 0, 0);
     }
     if (!l_done && ++l_m == l_nm) {
