@@ -45,7 +45,7 @@ constexpr uint32_t kOobGroup = 0x08000000u;
 constexpr uint32_t kOobByte = 0x80000000u;
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
 #ifndef MXFP4_DECODE1_RING
-#define MXFP4_DECODE1_RING 2
+#define MXFP4_DECODE1_RING 1
 #endif
 #ifndef MXFP4_DECODE1_WG_PER_CU
 #define MXFP4_DECODE1_WG_PER_CU 4
