@@ -45,6 +45,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 // K; KT = 0 takes K at run time (up to kCombMaxK).
 constexpr int kCombMaxK = 16;
 constexpr int kRsrcFlags = 0x00020000;
+// cache policy of the partial-row loads (gfx950: 2 = nt, non-temporal):
+// each partial row is read once, here
+constexpr int kPartLoadPolicy = 2;
 template <bool BF16, int KT>
 __global__ void __launch_bounds__(256) combine4_kernel(const float* __restrict__ part,
                                                        const int32_t* __restrict__ slot_of_pair,
@@ -66,7 +69,7 @@ __global__ void __launch_bounds__(256) combine4_kernel(const float* __restrict__
     for (int o4 = blockIdx.x * 256 + threadIdx.x; o4 < O4; o4 += gridDim.x * 256) {
       f32x4 v[KM];
 #pragma unroll
-      for (int k = 0; k < KM; k++) v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk[k], 16 * o4, 0, 0));
+      for (int k = 0; k < KM; k++) v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk[k], 16 * o4, 0, kPartLoadPolicy));
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KM; k++)
