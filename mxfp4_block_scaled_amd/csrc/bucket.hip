@@ -201,7 +201,10 @@ __global__ void __launch_bounds__(kScanThreads) bucket_scan_kernel(int32_t* __re
   if (out.tiles) write_tiles<kScanThreads>(cnt, tmp, E, out.offsets, out.tiles, out.n_tiles, wave_tot);
 }
 
-// One wave per chunk.
+// One wave per chunk. The expert indices of kScatterBatch steps of 64 pairs
+// are loaded before the first of them is ranked, and a step waits only for
+// its LDS reads of the cursors (the stores of earlier steps stay in flight).
+constexpr int kScatterBatch = 16;
 __global__ void __launch_bounds__(64) bucket_scatter_kernel(const int32_t* __restrict__ sel, int P, int E, int chunk,
                                                             const int32_t* __restrict__ bases, int nbits,
                                                             int32_t* __restrict__ perm, int32_t* __restrict__ slot_of_pair) {
@@ -210,22 +213,32 @@ __global__ void __launch_bounds__(64) bucket_scatter_kernel(const int32_t* __res
   for (int e = lane; e < E; e += 64) cursor[e] = bases[(size_t)c * E + e];
   __syncthreads();
   const int begin = c * chunk, end = min(P, begin + chunk);
-  for (int i0 = begin; i0 < end; i0 += 64) {
-    const int i = i0 + lane;
-    const bool in = i < end;
-    const int e = in ? sel[i] : -1;
-    const bool ok = in && e >= 0 && e < E;
-    uint64_t peers;
-    int rank;
-    match_rank(ok, ok ? e : 0, nbits, peers, rank);
-    int slot = -1;
-    if (ok) slot = cursor[e] + rank;
-    __builtin_amdgcn_s_waitcnt(0);  // all reads of cursor precede the updates below
-    __builtin_amdgcn_wave_barrier();
-    if (ok && rank == 0) cursor[e] += __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-    if (ok) perm[slot] = i;
-    if (in) slot_of_pair[i] = slot;
+  for (int i0 = begin; i0 < end; i0 += 64 * kScatterBatch) {
+    int ev[kScatterBatch];
+#pragma unroll
+    for (int b = 0; b < kScatterBatch; b++) {
+      const int i = i0 + 64 * b + lane;
+      ev[b] = i < end ? sel[i] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < kScatterBatch; b++) {
+      if (i0 + 64 * b >= end) break;  // wave-uniform
+      const int i = i0 + 64 * b + lane;
+      const bool in = i < end;
+      const int e = ev[b];
+      const bool ok = in && e >= 0 && e < E;
+      uint64_t peers;
+      int rank;
+      match_rank(ok, ok ? e : 0, nbits, peers, rank);
+      int slot = -1;
+      if (ok) slot = cursor[e] + rank;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all reads of cursor precede the updates below
+      __builtin_amdgcn_wave_barrier();
+      if (ok && rank == 0) cursor[e] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+      if (ok) perm[slot] = i;
+      if (in) slot_of_pair[i] = slot;
+    }
   }
 }
 
@@ -270,7 +283,7 @@ __global__ void __launch_bounds__(kScanThreads) bucket_one_block_kernel(const in
       match_rank(ok, ok ? e : 0, nbits, peers, rank);
       int slot = -1;
       if (ok) slot = tmp[e] + rank;
-      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all reads of the cursors precede the updates below
       __builtin_amdgcn_wave_barrier();
       if (ok && rank == 0) tmp[e] += __popcll(peers);
       __builtin_amdgcn_wave_barrier();
