@@ -280,7 +280,9 @@ int mxfp4_moe_swiglu_ex(const uint16_t* x, const uint8_t* gu_packed, const uint8
  * of two 2^X with max|block| <= 448 * 2^X (X clamped to [-127, 127]; an
  * all-zero block takes -127); each code is x / 2^X rounded to nearest, ties
  * to even, sign kept.
- *   x (T, I) bf16 raw bits, I a positive multiple of 32, 8-byte aligned;
+ *   x (T, I) bf16 raw bits, I a positive multiple of 32, 8-byte aligned,
+ *   finite (an infinite or NaN input leaves its block's codes and scale byte
+ *   unspecified; the exact layer's result is not finite either);
  *   codes (T, ld) and scale_bytes (T, ld / 32), ld >= I a multiple of 32,
  *   codes 4-byte aligned; columns [I, ld) get zero codes and scale bytes 0.
  * T * ld < 2^31; no overlap. MXFP4_ERR_INVALID_ARG otherwise. Enqueued on
@@ -354,7 +356,7 @@ int mxfp4_moe_linear_mxfp8_prepared_ex(const uint16_t* x, const void* prepared, 
  * element x / 2^X rounded to the nearest E2M1 magnitude (0, .5, 1, 1.5, 2, 3,
  * 4, 6), ties to the even code, sign kept (code sign << 3 | magnitude index).
  *   mxfp4_quantize_mxfp4: x (T, I) bf16 raw bits, I a positive multiple of
- *     32, 8-byte aligned -> codes (T, ld / 2) bytes, two codes per byte, the
+ *     32, 8-byte aligned, finite as for MXFP8 -> codes (T, ld / 2) bytes, two codes per byte, the
  *     first in the low nibble (the weights' order), and scale_bytes
  *     (T, ld / 32); ld >= I a multiple of 32, codes 4-byte aligned; columns
  *     [I, ld) get zero codes and scale bytes 0. T * ld < 2^31; no overlap.
