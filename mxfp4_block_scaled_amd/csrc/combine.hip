@@ -48,6 +48,9 @@ constexpr int kRsrcFlags = 0x00020000;
 // cache policy of the partial-row loads (gfx950: 2 = nt, non-temporal):
 // each partial row is read once, here
 constexpr int kPartLoadPolicy = 2;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// the output rows are written once and not read again by this pass, so
+// they are stored non-temporally too (global_store ... nt)
 template <bool BF16, int KT>
 __global__ void __launch_bounds__(256) combine4_kernel(const float* __restrict__ part,
                                                        const int32_t* __restrict__ slot_of_pair,
@@ -82,13 +85,14 @@ __global__ void __launch_bounds__(256) combine4_kernel(const float* __restrict__
         const uint32_t r1 = f32_to_bf16_rne(bf16_to_f32((uint16_t)(sh.x >> 16)) + a[1]);
         const uint32_t r2 = f32_to_bf16_rne(bf16_to_f32((uint16_t)sh.y) + a[2]);
         const uint32_t r3 = f32_to_bf16_rne(bf16_to_f32((uint16_t)(sh.y >> 16)) + a[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + yo) = make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+        __builtin_nontemporal_store(u32x2{r0 | (r1 << 16), r2 | (r3 << 16)},
+                                    reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + yo));
       } else {
         const f32x4 sh = *reinterpret_cast<const f32x4*>(static_cast<const float*>(shared) + yo);
         f32x4 r;
 #pragma unroll
         for (int i = 0; i < 4; i++) r[i] = sh[i] + a[i];
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + yo) = r;
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(static_cast<float*>(y) + yo));
       }
     }
   }

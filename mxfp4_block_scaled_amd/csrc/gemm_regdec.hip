@@ -96,6 +96,10 @@ constexpr int kScWords = kScPitch / 4;
 constexpr int kScWin = NW * kScPitch;
 constexpr int kScDma = kScWin / (256 * kWaves);
 constexpr int kScZero = 16 * kScPitch * kWI;  // zero bytes after a window slot
+// canonical weights: an expert's partial M-tile of at most kMergeMax pairs that
+// follows its last full tile is multiplied by the full tile's workgroup
+constexpr int kMergeMax = 16;
+constexpr int kXEBytes = kMergeMax * ROWB;  // activation slot of the merged pairs (4 KB)
 static_assert(kScDma * 256 * kWaves == kScWin, "scale window DMA");
 
 constexpr uint32_t kShiftFrom = 253;  // scale bytes whose decoded weights may overflow bf16
@@ -136,8 +140,32 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   const int jx = xcd_step / n_wg;
   const int ti = 2 * ((blockIdx.x & 7) + 8 * (jx >> 1)) + (jx & 1);
   const int nt = xcd_step % n_wg;
-  if (ti >= n_tiles[0]) return;
+  const int n_t = n_tiles[0];
+  if (ti >= n_t) return;
   const GemmTile tl = tiles[ti];
+  // Merged remainders (canonical weights; not the SwiGLU gate/up stage, whose
+  // epilogue needs a gate and an up fragment in one wave): a tile of at most
+  // kMergeMax pairs that continues the rows of its expert's full tile right
+  // before it in the list is multiplied by that tile's workgroup, which then
+  // reads the expert's weights once for both; both workgroups test the same
+  // two list entries, so every pair is multiplied exactly once.
+  constexpr bool kMerge = CANON && MODE != kSwiGLU;
+  int mtot = tl.mlen;  // pairs this workgroup multiplies: the tile's and a merged remainder's
+  if constexpr (kMerge) {
+    // the neighbours are read together with the tile (not after testing it)
+    const GemmTile pv = tiles[ti > 0 ? ti - 1 : ti];
+    const GemmTile nx = tiles[ti + 1 < n_t ? ti + 1 : ti];
+    // keeps the compiler from moving the read of nx past the return below
+    asm volatile("" ::"s"(nx.e), "s"(nx.row0), "s"(nx.mlen));
+    // (bitwise tests, both before the return: no test guards a read)
+    const bool absorbed =
+        (ti > 0) & (tl.mlen <= kMergeMax) & (pv.e == tl.e) & (pv.mlen == MT) & (pv.row0 + MT == tl.row0);
+    const bool absorbs =
+        (ti + 1 < n_t) & (tl.mlen == MT) & (nx.e == tl.e) & (nx.mlen <= kMergeMax) & (nx.row0 == tl.row0 + MT);
+    if (absorbed) return;
+    if (absorbs) mtot = MT + nx.mlen;
+  }
+  const bool extra = kMerge && mtot > MT;  // workgroup-uniform
 
   __shared__ __attribute__((aligned(16))) uint8_t X0[kXBytes];
   __shared__ __attribute__((aligned(16))) uint8_t X1[kXBytes];
@@ -149,6 +177,9 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   // a read of one is never taken to wait for a DMA into the other)
   __shared__ __attribute__((aligned(16))) uint8_t Sc0[CANON ? kScWin + kScZero : 16];
   __shared__ __attribute__((aligned(16))) uint8_t Sc1[CANON ? kScWin + kScZero : 16];
+  // the merged pairs' activation rows, two slots
+  __shared__ __attribute__((aligned(16))) uint8_t XE0[CANON && MODE != kSwiGLU ? kXEBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t XE1[CANON && MODE != kSwiGLU ? kXEBytes : 16];
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lc = lane >> 4;
@@ -167,6 +198,17 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     int row = -1;
     if (m < tl.mlen) row = MODE == kDirect ? tl.row0 + m : perm[tl.row0 + m] / K;
     x_off[j] = row >= 0 ? (uint32_t)row * (uint32_t)(2 * xld) + 16u * (uint32_t)piece : kOob;
+  }
+  // merged pairs: waves 0..3 fill rows 4 w .. 4 w + 3 of the merged slot
+  // (pairs MT + 4 w + (l >> 4)), in the same piece order
+  uint32_t xe_off = kOob;
+  if (kMerge && extra && w < 4) {
+    const int m = MT + 4 * w + (lane >> 4);
+    const int piece = (lane & 15) ^ (m & 15);
+    if (m < mtot) {
+      const int row = MODE == kDirect ? tl.row0 + m : perm[tl.row0 + m] / K;
+      xe_off = (uint32_t)row * (uint32_t)(2 * xld) + 16u * (uint32_t)piece;
+    }
   }
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRsrcFlags);
 
@@ -235,11 +277,17 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
       const int row = crow(wn, 4 * h, lr);
       sc_lds[h] = (PT * wn + lr) * kScPitch + (row >= 0 ? (s_mis + row * G) & 3 : 0);
     }
+    if (extra && wm == 1) {
+      // wave row 1 takes its fragments in the order 4..7, 0..3 (see fo below)
+      const int t0 = sc_lds[0];
+      sc_lds[0] = sc_lds[1] + 16 * kScPitch * 4;
+      sc_lds[1] = t0 - 16 * kScPitch * 4;
+    }
   }
 
   // prepared: two scale dwords per chunk (four fragments each), a three-slot ring
   uint32_t wsp[3][kScLoads];
-  auto dma_x = [&](int q, uint8_t* dst) {
+  auto dma_x = [&](int q, uint8_t* dst, uint8_t* xe_dst) {
 #pragma unroll
     for (int j = 0; j < kXDma; j++) {
       // an input past I moves the offset past the resource (the piece's first
@@ -248,6 +296,12 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
       const uint32_t past = (uint32_t)(xld - 1 - first) >> 31 << 31;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(dst + (16 * w + 4 * j) * ROWB), 16,
                                                (int)((x_off[j] + 256u * q) | past), 0, 0, 0);
+    }
+    if (kMerge && extra && w < 4) {
+      const int first = 128 * q + 8 * ((lane & 15) ^ ((4 * w + lc) & 15));
+      const uint32_t past = (uint32_t)(xld - 1 - first) >> 31 << 31;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(xe_dst + 4 * w * ROWB), 16,
+                                               (int)((xe_off + 256u * q) | past), 0, 0, 0);
     }
   };
   auto dma_w = [&](int q, uint8_t* dst, int slot) {
@@ -289,11 +343,25 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   for (int i = 0; i < kWI; i++)
 #pragma unroll
     for (int j = 0; j < kWJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // merged pairs: wave row wm multiplies them with 4 of its column's 8
+  // fragments. In a workgroup with merged pairs, wave row 1 takes its
+  // fragments in the order 4..7, 0..3 (iteration i holds fragment
+  // (i + fo) & 7), so that iterations 0..3 are, for both wave rows, the
+  // fragments whose merged products it owns: fragment 4 wm + i of the 16
+  // merged pairs goes to accx[i].
+  const int fo = extra ? 4 * wm : 0;
+  v4f accx[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) accx[i] = v4f{0.f, 0.f, 0.f, 0.f};
   bool shifted = false;  // wave-uniform: decoding at scale byte s - kShift
 
   // the MFMAs of one chunk: activations xc, weight codes wc, the 8 scale bytes
   const int wpos = 4 * lr + ((lc + (lr >> 2)) & 3);  // canonical: this lane's slot in a weight block
-  auto mma_chunk = [&](const uint8_t* xc, const uint8_t* wc, const uint32_t(&sb_in)[kWI]) __attribute__((always_inline)) {
+  // canonical: this lane's dword 0 of iteration i's weight block is at wlo + 1024 i (i < 4), whi + 1024 (i - 4)
+  const int wlo = (8 * wn + fo) * 1024 + 16 * wpos, whi = (8 * wn + 4 - fo) * 1024 + 16 * wpos;
+  auto mma_chunk = [&](auto ex, const uint8_t* xc, const uint8_t* wc, const uint8_t* xe,
+                       const uint32_t(&sb_in)[kWI]) __attribute__((always_inline)) {
+    constexpr bool EX = decltype(ex)::value;
     uint32_t sb[kWI];
     bool big = false;
 #pragma unroll
@@ -311,6 +379,8 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
       for (int i = 0; i < kWI; i++)
 #pragma unroll
         for (int j = 0; j < kWJ; j++) acc[i][j] *= 0.125f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) accx[i] *= 0.125f;
     }
     float sc[kWI];
 #pragma unroll
@@ -330,12 +400,18 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
         b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                               &xc[(64 * wm + 16 * j + lr) * ROWB + 16 * ((4 * lc + sd) ^ lr)]));
       }
+      bf16x8 bx;
+      if constexpr (EX) {
+        // merged pair MT + lr of the same k-step (row lr of the merged slot, (MT + lr) & 15 = lr)
+        bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xe[lr * ROWB + 16 * ((4 * lc + sd) ^ lr)]));
+      }
       uint32_t raw[kWI];
       if constexpr (CANON) {
-        // dword sd of this lane's slot of each of the wave's fragments (blocks 8 wn .. 8 wn + 7)
+        // dword sd of this lane's slot of each of the wave's fragments (blocks 8 wn .. 8 wn + 7,
+        // iteration i taking fragment (i + fo) & 7)
 #pragma unroll
         for (int i = 0; i < kWI; i++)
-          raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(8 * wn + i) * 1024 + 16 * wpos + 4 * sd]);
+          raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(i < 4 ? wlo + 1024 * i : whi + 1024 * (i - 4)) + 4 * sd]);
       } else {
         // dword s of this lane's slot of each fragment (8 codes each): blocks s and 4 + s of tile wn
         const u32x4 lo = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + s) * 1024 + 16 * lane]);
@@ -349,6 +425,9 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
 #pragma unroll
         for (int j = 0; j < kWJ; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
+        if constexpr (EX) {
+          if (i < 4) accx[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bx, accx[i], 0, 0, 0);
+        }
       }
     }
   };
@@ -367,14 +446,14 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
       uint8_t* xn = RX == 0 ? X1 : X0;
       const uint8_t* wc = RW == 0 ? W0 : (RW == 1 ? W1 : W2);
       uint8_t* wnx = RWN == 0 ? W0 : (RWN == 1 ? W1 : W2);
-      dma_x(min(q + 1, nq - 1), xn);
+      dma_x(min(q + 1, nq - 1), xn, nullptr);
       dma_w(min(q + 2, nq - 1), wnx, RWN);
       __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
       if (live) {
         uint32_t sb[kWI];
 #pragma unroll
         for (int i = 0; i < kWI; i++) sb[i] = (wsp[RW][i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        mma_chunk(xc, wc, sb);
+        mma_chunk(std::false_type{}, xc, wc, nullptr, sb);
       }
       wait_next_x();
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
@@ -383,7 +462,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
-    dma_x(0, X0);
+    dma_x(0, X0, nullptr);
     dma_w(0, W0, 0);
     dma_w(min(1, nq - 1), W1, 1);
     wait_next_x();  // chunk 0's activations and weights: followed by chunk 1's weight requests
@@ -415,16 +494,29 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     // the 8 scale bytes of chunk q from window slot sw; a group past G would
     // read another row's byte and reads the zero bytes instead (a choice of
     // address, so nothing waits for these reads before they are used)
-    auto read_sb = [&](int q, const uint8_t* sw, uint32_t(&sb)[kWI]) {
+    // (the loop with merged pairs keeps them four to a register: it has no
+    // registers to spare)
+    auto read_sb = [&](int q, const uint8_t* sw, auto& sb) {
+      constexpr bool PK = sizeof(sb) == 2 * sizeof(uint32_t);
       const bool in_g = 4 * q + lc < G;
       int off[2];
 #pragma unroll
       for (int h = 0; h < 2; h++) off[h] = in_g ? 4 * (q & 1) + lc + sc_lds[h] : kScWin;
+      if constexpr (PK) {
 #pragma unroll
-      for (int i = 0; i < kWI; i++) sb[i] = sw[off[i >> 2] + 16 * kScPitch * i];
+        for (int h = 0; h < 2; h++) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int t = 0; t < 4; t++) v |= (uint32_t)sw[off[h] + 16 * kScPitch * (4 * h + t)] << (8 * t);
+          sb[h] = v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kWI; i++) sb[i] = sw[off[i >> 2] + 16 * kScPitch * i];
+      }
     };
-    uint32_t sb_cur[kWI], sb_next[kWI];
-    auto step = [&](int q, auto xs, auto ws) {
+    auto step = [&](int q, auto xs, auto ws, auto ex, auto& sb_cur, auto& sb_next) __attribute__((always_inline)) {
+      constexpr bool EX = decltype(ex)::value;
       constexpr int R = decltype(xs)::value, WS = decltype(ws)::value;
       const uint8_t* xc = R == 0 ? X0 : X1;
       const uint8_t* wc = R == 0 ? W0 : W1;
@@ -435,16 +527,23 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
         for (int m = 0; m < kScDma; m++) dma_sc((q >> 1) + 1, m, s_other);
       }
       if (q + 1 < nq) {
-        dma_x(q + 1, R == 0 ? X1 : X0);
+        dma_x(q + 1, R == 0 ? X1 : X0, R == 0 ? XE1 : XE0);
         dma_w(q + 1, R == 0 ? W1 : W0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
       if (live) {
         // chunk q + 1 is in this window (q even) or the next one (q odd)
         if (q + 1 < nq) read_sb(q + 1, R == 0 ? s_this : s_other, sb_next);
-        mma_chunk(xc, wc, sb_cur);
+        if constexpr (EX) {
+          uint32_t sb[kWI];
 #pragma unroll
-        for (int i = 0; i < kWI; i++) sb_cur[i] = sb_next[i];
+          for (int i = 0; i < kWI; i++) sb[i] = (sb_cur[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          mma_chunk(ex, xc, wc, R == 0 ? XE0 : XE1, sb);
+        } else {
+          mma_chunk(ex, xc, wc, nullptr, sb_cur);
+        }
+#pragma unroll
+        for (int h = 0; h < (EX ? 2 : kWI); h++) sb_cur[h] = sb_next[h];
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's requests have landed
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
@@ -452,7 +551,7 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    dma_x(0, X0);
+    dma_x(0, X0, XE0);
     dma_w(0, W0, 0);
 #pragma unroll
     for (int m = 0; m < kScDma; m++) dma_sc(0, m, Sc0);
@@ -462,17 +561,31 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __builtin_amdgcn_s_barrier();
-    if (live) read_sb(0, Sc0, sb_cur);
-    int q = 0;
-    for (; q + 3 < nq; q += 4) {
-      step(q, C0{}, C0{});
-      step(q + 1, C1{}, C0{});
-      step(q + 2, C0{}, C1{});
-      step(q + 3, C1{}, C1{});
+    // the chunk loop, with or without the merged pairs' MFMAs (two copies of
+    // the loop, not a test per chunk: one copy's registers then never meet the other's)
+    auto run = [&](auto ex) __attribute__((always_inline)) {
+      constexpr bool EX = decltype(ex)::value;
+      uint32_t sb_cur[EX ? 2 : kWI], sb_next[EX ? 2 : kWI];
+      if (live) read_sb(0, Sc0, sb_cur);
+      int q = 0;
+      for (; q + 3 < nq; q += 4) {
+        step(q, C0{}, C0{}, ex, sb_cur, sb_next);
+        step(q + 1, C1{}, C0{}, ex, sb_cur, sb_next);
+        step(q + 2, C0{}, C1{}, ex, sb_cur, sb_next);
+        step(q + 3, C1{}, C1{}, ex, sb_cur, sb_next);
+      }
+      if (q < nq) step(q, C0{}, C0{}, ex, sb_cur, sb_next);
+      if (q + 1 < nq) step(q + 1, C1{}, C0{}, ex, sb_cur, sb_next);
+      if (q + 2 < nq) step(q + 2, C0{}, C1{}, ex, sb_cur, sb_next);
+    };
+    if constexpr (kMerge) {
+      if (extra)
+        run(std::true_type{});
+      else
+        run(std::false_type{});
+    } else {
+      run(std::false_type{});
     }
-    if (q < nq) step(q, C0{}, C0{});
-    if (q + 1 < nq) step(q + 1, C1{}, C0{});
-    if (q + 2 < nq) step(q + 2, C0{}, C1{});
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may land in LDS after the workgroup ends
   if (shifted) {
@@ -480,6 +593,8 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     for (int i = 0; i < kWI; i++)
 #pragma unroll
       for (int j = 0; j < kWJ; j++) acc[i][j] *= 8.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) accx[i] *= 8.0f;
   }
 
   // lane (lr, lc) of MFMA tile (i, j): pair 64 wm + 16 j + lr, rows 4 lc .. 4 lc + 3 of fragment i
@@ -513,8 +628,18 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
       float* row = part + (int64_t)(tl.row0 + p) * O;
 #pragma unroll
       for (int i = 0; i < kWI; i++) {
-        const int r = NW * nt + PT * wn + 16 * i + 4 * lc;  // O % 4 == 0: all four or none
+        // iteration i's fragment (i + fo) & 7
+        const int r = NW * nt + PT * wn + 16 * (i < 4 ? i + fo : i - fo) + 4 * lc;  // O % 4 == 0: all four or none
         if (r < O) *reinterpret_cast<v4f*>(row + r) = acc[i][j];
+      }
+    }
+    if (extra && MT + lr < mtot) {
+      // merged pair MT + lr: fragments 4 wm .. 4 wm + 3 of this wave's column
+      float* row = part + (int64_t)(tl.row0 + MT + lr) * O;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = NW * nt + PT * wn + 16 * (i + fo) + 4 * lc;
+        if (r < O) *reinterpret_cast<v4f*>(row + r) = accx[i];
       }
     }
   }
