@@ -22,9 +22,10 @@
 // 4 h + s holding for lane l dword s of fragments 4 h .. 4 h + 3; and the
 // slots' scale bytes, four fragments to a dword per lane).
 //
-// Work: the M-tiles of the bucketing (<= 128 pairs of one expert) x N-tiles
-// of 512 weight rows (modes below: the routed linear, and the two stages of
-// the SwiGLU expert block). Eight waves per workgroup, 2 (pairs) x 4 (rows): wave
+// Work: the M-tiles of the bucketing (<= 128 pairs of one expert; on
+// canonical weights a full tile also takes the partial tile of at most 16
+// pairs that follows it, see kMergeMax) x N-tiles of 512 weight rows (modes
+// below: the routed linear, and the two stages of the SwiGLU expert block). Eight waves per workgroup, 2 (pairs) x 4 (rows): wave
 // (wm, wn) owns pairs 64 wm .. +63 and the 128 rows of prepared tile
 // 4 nt + wn, 8 x 4 MFMA tiles of 16 x 16. Inputs go in chunks of 128 (4
 // groups). Per chunk the workgroup brings into LDS, by DMA (buffer loads that
