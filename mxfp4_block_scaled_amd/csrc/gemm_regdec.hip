@@ -12,9 +12,6 @@
 // bytes, into one 1 KB block per 16-row fragment and chunk, and the scale
 // bytes come into LDS in windows of 8 groups (each row's bytes read as whole
 // dwords from the dword boundary below them).
-// The weights and activations then use two-slot rings, one chunk ahead,
-// with a full wait per chunk, as the scale windows leave no room for a third
-// weight slot.
 // Prepared: the weights come in the prepared layout of prepare_mx_kernel (a load-time
 // byte permutation: per expert, 128-row tile and chunk of 4 groups, the group
 // slots of the 8 16-row fragments in MFMA lane order - slot l of fragment f =
@@ -22,20 +19,22 @@
 // 4 h + s holding for lane l dword s of fragments 4 h .. 4 h + 3; and the
 // slots' scale bytes, four fragments to a dword per lane).
 //
-// Work: the M-tiles of the bucketing (<= 128 pairs of one expert; on
-// canonical weights a full tile also takes the partial tile of at most 16
-// pairs that follows it, see kMergeMax) x N-tiles of 512 weight rows (modes
-// below: the routed linear, and the two stages of the SwiGLU expert block). Eight waves per workgroup, 2 (pairs) x 4 (rows): wave
+// Work: the M-tiles of the bucketing (<= 128 pairs of one expert; a full
+// tile also takes the partial tile of at most 16 pairs that follows it, see
+// kMergeMax) x N-tiles of 512 weight rows (modes below: the routed linear,
+// and the two stages of the SwiGLU expert block). Eight waves per workgroup,
+// 2 (pairs) x 4 (rows): wave
 // (wm, wn) owns pairs 64 wm .. +63 and the 128 rows of prepared tile
 // 4 nt + wn, 8 x 4 MFMA tiles of 16 x 16. Inputs go in chunks of 128 (4
 // groups). Per chunk the workgroup brings into LDS, by DMA (buffer loads that
 // write LDS directly, no registers): the 128 gathered activation rows (row =
 // perm / K; 32 KB; two-slot ring, one chunk ahead - they come from L2,
 // shared by the N-tiles of the M-tile) and the 32 fragment blocks of its
-// weights (32 KB; three-slot ring, two chunks ahead - they come from HBM).
+// weights (32 KB; two-slot ring, one chunk ahead - they come from HBM), and
+// the scale bytes: canonical, windows of 8 groups of the workgroup's rows,
+// two slots; prepared, two dwords per wave and chunk straight to registers.
 // Each weight byte is fetched once per workgroup; each activation row once
-// per 512 weight rows. The scale dwords go straight to registers (two per
-// wave and chunk, a three-slot ring).
+// per 512 weight rows. One full wait and one barrier per chunk.
 //
 // Operand A = weights: for MFMA k-step s (0..3) lane (r, c) reads, with two
 // conflict-free 16-byte LDS reads, dword s of its slot of all 8 fragments and
@@ -47,10 +46,7 @@
 // weight lane (r, c) of that k-step, so every product pairs x_i with w_i. The
 // 16-byte pieces of activation row m sit at position piece ^ (m & 15) of its
 // LDS row: the 16 lanes that LDS serves together (16 bytes each across its 64
-// banks) read 16 rows at 16 distinct positions. Every chunk issues the
-// same number of requests, so one counted wait (this wave's activation DMA
-// of the next chunk, which also covers the older weight DMA) and a bare
-// barrier per chunk replace a full fence. Rows past the tile, inputs past I
+// banks) read 16 rows at 16 distinct positions. Rows past the tile, inputs past I
 // and prepared tiles past O read through an offset beyond their buffer
 // resource: zeros, no memory traffic.
 //
@@ -97,8 +93,8 @@ constexpr int kScWords = kScPitch / 4;
 constexpr int kScWin = NW * kScPitch;
 constexpr int kScDma = kScWin / (256 * kWaves);
 constexpr int kScZero = 16 * kScPitch * kWI;  // zero bytes after a window slot
-// canonical weights: an expert's partial M-tile of at most kMergeMax pairs that
-// follows its last full tile is multiplied by the full tile's workgroup
+// an expert's partial M-tile of at most kMergeMax pairs that follows its last
+// full tile is multiplied by the full tile's workgroup
 constexpr int kMergeMax = 16;
 constexpr int kXEBytes = kMergeMax * ROWB;  // activation slot of the merged pairs (4 KB)
 static_assert(kScDma * 256 * kWaves == kScWin, "scale window DMA");
@@ -144,13 +140,13 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   const int n_t = n_tiles[0];
   if (ti >= n_t) return;
   const GemmTile tl = tiles[ti];
-  // Merged remainders (canonical weights; not the SwiGLU gate/up stage, whose
+  // Merged remainders (not the SwiGLU gate/up stage, whose
   // epilogue needs a gate and an up fragment in one wave): a tile of at most
   // kMergeMax pairs that continues the rows of its expert's full tile right
   // before it in the list is multiplied by that tile's workgroup, which then
   // reads the expert's weights once for both; both workgroups test the same
   // two list entries, so every pair is multiplied exactly once.
-  constexpr bool kMerge = CANON && MODE != kSwiGLU;
+  constexpr bool kMerge = MODE != kSwiGLU;
   int mtot = tl.mlen;  // pairs this workgroup multiplies: the tile's and a merged remainder's
   if constexpr (kMerge) {
     // the neighbours are read together with the tile (not after testing it)
@@ -172,15 +168,14 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   __shared__ __attribute__((aligned(16))) uint8_t X1[kXBytes];
   __shared__ __attribute__((aligned(16))) uint8_t W0[kWBytes];
   __shared__ __attribute__((aligned(16))) uint8_t W1[kWBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t W2[CANON ? 16 : kWBytes];  // canonical: two weight slots
   // canonical: scale-byte windows of 8 groups, two slots, each followed by
   // zero bytes (separate arrays, and every read indexes one of them, so that
   // a read of one is never taken to wait for a DMA into the other)
   __shared__ __attribute__((aligned(16))) uint8_t Sc0[CANON ? kScWin + kScZero : 16];
   __shared__ __attribute__((aligned(16))) uint8_t Sc1[CANON ? kScWin + kScZero : 16];
   // the merged pairs' activation rows, two slots
-  __shared__ __attribute__((aligned(16))) uint8_t XE0[CANON && MODE != kSwiGLU ? kXEBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t XE1[CANON && MODE != kSwiGLU ? kXEBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t XE0[MODE != kSwiGLU ? kXEBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t XE1[MODE != kSwiGLU ? kXEBytes : 16];
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lc = lane >> 4;
@@ -286,8 +281,8 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     }
   }
 
-  // prepared: two scale dwords per chunk (four fragments each), a three-slot ring
-  uint32_t wsp[3][kScLoads];
+  // prepared: two scale dwords per chunk (four fragments each), a two-slot ring
+  uint32_t wsp[2][kScLoads];
   auto dma_x = [&](int q, uint8_t* dst, uint8_t* xe_dst) {
 #pragma unroll
     for (int j = 0; j < kXDma; j++) {
@@ -329,13 +324,6 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(dst + (kScDma * w + m) * 256), 4,
                                              (int)(sw_off[m] + 8u * C), 0, 0, 0);
   };
-  // wait until this wave's activation DMA of the next chunk has landed: it
-  // was followed by one chunk's weight and scale requests
-  auto wait_next_x = [&]() {
-    constexpr int n = kWDma + kScLoads;
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
-  };
-
   // whether this wave multiplies anything: pairs left in the tile, rows left in O
   const bool live = 64 * wm < tl.mlen && (MODE == kSwiGLU ? 64 * pt < F : NW * nt + PT * wn < O);
 
@@ -360,6 +348,8 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   const int wpos = 4 * lr + ((lc + (lr >> 2)) & 3);  // canonical: this lane's slot in a weight block
   // canonical: this lane's dword 0 of iteration i's weight block is at wlo + 1024 i (i < 4), whi + 1024 (i - 4)
   const int wlo = (8 * wn + fo) * 1024 + 16 * wpos, whi = (8 * wn + 4 - fo) * 1024 + 16 * wpos;
+  // prepared: iterations 0..3 read blocks plo + s (dword s of fragments fo .. fo + 3), 4..7 blocks phi + s
+  const int plo = wn * kWI + fo, phi = wn * kWI + 4 - fo;
   auto mma_chunk = [&](auto ex, const uint8_t* xc, const uint8_t* wc, const uint8_t* xe,
                        const uint32_t(&sb_in)[kWI]) __attribute__((always_inline)) {
     constexpr bool EX = decltype(ex)::value;
@@ -415,8 +405,8 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
           raw[i] = *reinterpret_cast<const uint32_t*>(&wc[(i < 4 ? wlo + 1024 * i : whi + 1024 * (i - 4)) + 4 * sd]);
       } else {
         // dword s of this lane's slot of each fragment (8 codes each): blocks s and 4 + s of tile wn
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + s) * 1024 + 16 * lane]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(&wc[(wn * kWI + 4 + s) * 1024 + 16 * lane]);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&wc[(plo + s) * 1024 + 16 * lane]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&wc[(phi + s) * 1024 + 16 * lane]);
 #pragma unroll
         for (int t = 0; t < 4; t++) raw[t] = lo[t], raw[4 + t] = hi[t];
       }
@@ -434,54 +424,53 @@ __global__ void __launch_bounds__(512, 1) gemm_regdec_kernel(const uint16_t* __r
   };
 
   if constexpr (!CANON) {
-    // One chunk q, activation slot q mod 2 and weight slot q mod 3 (both
-    // compile-time): request the activations of chunk q + 1 (into the slot read
-    // last during chunk q - 1) and the weights of chunk q + 2 (likewise),
-    // multiply chunk q, wait for this wave's activation DMA of chunk q + 1,
-    // barrier. Past the last chunk the requests repeat the last chunk into
-    // slots nobody reads again, so the number of requests per chunk - and every
-    // wait count - is fixed.
-    auto step = [&](int q, auto xs, auto ws) {
-      constexpr int RX = decltype(xs)::value, RW = decltype(ws)::value, RWN = (RW + 2) % 3;
-      const uint8_t* xc = RX == 0 ? X0 : X1;
-      uint8_t* xn = RX == 0 ? X1 : X0;
-      const uint8_t* wc = RW == 0 ? W0 : (RW == 1 ? W1 : W2);
-      uint8_t* wnx = RWN == 0 ? W0 : (RWN == 1 ? W1 : W2);
-      dma_x(min(q + 1, nq - 1), xn, nullptr);
-      dma_w(min(q + 2, nq - 1), wnx, RWN);
+    // One chunk q, activation and weight slots q mod 2 (compile-time): request
+    // the activations, weights and scale dwords of chunk q + 1 (into the slots
+    // read last during chunk q - 1), multiply chunk q, wait for all of this
+    // wave's requests, barrier.
+    auto step = [&](int q, auto xs, auto ex) __attribute__((always_inline)) {
+      constexpr int R = decltype(xs)::value;
+      const uint8_t* xc = R == 0 ? X0 : X1;
+      const uint8_t* wc = R == 0 ? W0 : W1;
+      if (q + 1 < nq) {
+        dma_x(q + 1, R == 0 ? X1 : X0, R == 0 ? XE1 : XE0);
+        dma_w(q + 1, R == 0 ? W1 : W0, R ^ 1);
+      }
       __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
       if (live) {
+        // iteration i takes fragment (i + fo) & 7: the scale dwords swap with the fragment halves
+        const uint32_t s0 = fo ? wsp[R][1] : wsp[R][0], s1 = fo ? wsp[R][0] : wsp[R][1];
         uint32_t sb[kWI];
 #pragma unroll
-        for (int i = 0; i < kWI; i++) sb[i] = (wsp[RW][i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        mma_chunk(std::false_type{}, xc, wc, nullptr, sb);
+        for (int i = 0; i < kWI; i++) sb[i] = ((i < 4 ? s0 : s1) >> (8 * (i & 3))) & 0xFFu;
+        mma_chunk(ex, xc, wc, R == 0 ? XE0 : XE1, sb);
       }
-      wait_next_x();
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's requests have landed
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
       __builtin_amdgcn_s_barrier();
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    using C2 = std::integral_constant<int, 2>;
-    dma_x(0, X0, nullptr);
+    dma_x(0, X0, XE0);
     dma_w(0, W0, 0);
-    dma_w(min(1, nq - 1), W1, 1);
-    wait_next_x();  // chunk 0's activations and weights: followed by chunk 1's weight requests
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __builtin_amdgcn_s_barrier();
-    int q = 0;
-    for (; q + 5 < nq; q += 6) {  // activation slots cycle by 2, weight slots by 3
-      step(q, C0{}, C0{});
-      step(q + 1, C1{}, C1{});
-      step(q + 2, C0{}, C2{});
-      step(q + 3, C1{}, C0{});
-      step(q + 4, C0{}, C1{});
-      step(q + 5, C1{}, C2{});
+    auto run = [&](auto ex) __attribute__((always_inline)) {
+      int q = 0;
+      for (; q + 1 < nq; q += 2) {
+        step(q, C0{}, ex);
+        step(q + 1, C1{}, ex);
+      }
+      if (q < nq) step(q, C0{}, ex);
+    };
+    if constexpr (kMerge) {
+      if (extra)
+        run(std::true_type{});
+      else
+        run(std::false_type{});
+    } else {
+      run(std::false_type{});
     }
-    if (q < nq) step(q, C0{}, C0{});
-    if (q + 1 < nq) step(q + 1, C1{}, C1{});
-    if (q + 2 < nq) step(q + 2, C0{}, C2{});
-    if (q + 3 < nq) step(q + 3, C1{}, C0{});
-    if (q + 4 < nq) step(q + 4, C0{}, C1{});
   } else {
     // One chunk q, activation and weight slots q mod 2 and scale window slot
     // (q >> 1) mod 2 (all compile-time): at a window's first chunk request

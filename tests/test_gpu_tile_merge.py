@@ -1,5 +1,5 @@
-"""GPU parity of the prefill-shaped grouped GEMM on canonical weights around
-the M-tile boundary: experts whose pair count just passes a multiple of the
+"""GPU parity of the prefill-shaped grouped GEMM (canonical and prepared
+weights) around the M-tile boundary: experts whose pair count just passes a multiple of the
 128-pair tile (129, 144, 145, 261 pairs, ...), where the few pairs left over
 form a partial tile of their own in the bucketing's tile list.
 
@@ -106,10 +106,14 @@ def linear_case(seed, counts, K, G, O, xscale=1.0, scale_lo=118, scale_hi=130, b
     return x, packed, scales, sel, p, shared
 
 
-def run_linear(x, packed, scales, sel, p, shared):
+def run_linear(x, packed, scales, sel, p, shared, layout="canonical"):
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)  # noqa: E731
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
-    y = mx.moe_linear(bf(x), dv(packed), dv(scales), dv(sel), dv(p), bf(shared), flags=_abi.FLAG_FORCE_GEMM)
+    if layout == "canonical":
+        y = mx.moe_linear(bf(x), dv(packed), dv(scales), dv(sel), dv(p), bf(shared), flags=_abi.FLAG_FORCE_GEMM)
+    else:
+        prep = mx.prepare_bf16(dv(packed), dv(scales))
+        y = mx.moe_linear_prepared(bf(x), prep, dv(sel), dv(p), bf(shared))
     torch.cuda.synchronize()
     return y
 
@@ -121,33 +125,40 @@ LINEAR_CASES = [  # seed, counts per expert, K, G, O
 ]
 
 
+LAYOUTS = ["canonical", "prepared"]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("c", LINEAR_CASES, ids=lambda c: "K{}G{}O{}".format(*c[2:]))
-def test_partial_tiles_linear(c):
+def test_partial_tiles_linear(c, layout):
     seed, counts, K, G, O = c
-    say(f"tile boundary linear {c}")
+    say(f"tile boundary linear {c} {layout}")
     host = linear_case(seed, counts, K, G, O)
-    y = run_linear(*host)
-    assert_bf16_close(host64(y), oracle.expert_linear(*host), f"linear {c}")
+    y = run_linear(*host, layout=layout)
+    assert_bf16_close(host64(y), oracle.expert_linear(*host), f"linear {c} {layout}")
     toks = leftover_tokens(host[3], counts)
     assert toks.size > 0
     x, packed, scales, sel, p, shared = host
-    y_own = run_linear(x[toks], packed, scales, sel[toks], p[toks], shared[toks])
+    y_own = run_linear(x[toks], packed, scales, sel[toks], p[toks], shared[toks], layout=layout)
     assert torch.equal(y[torch.from_numpy(toks).to(DEV)], y_own), "left-over pairs differ when run on their own"
 
 
-def test_partial_tiles_largest_scales():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_partial_tiles_largest_scales(layout):
     # expert 1 (144 pairs: 16 left over) with scale bytes 244..254, activations scaled by 2^-100
     counts = [145, 144, 129, 30]
+    say(f"tile boundary largest scales {layout}")
     host = linear_case(9, counts, 2, 6, 260, xscale=2.0 ** -100, big_expert=1)
-    y = run_linear(*host)
-    assert_bf16_close(host64(y), oracle.expert_linear(*host), "largest scales")
+    y = run_linear(*host, layout=layout)
+    assert_bf16_close(host64(y), oracle.expert_linear(*host), f"largest scales {layout}")
     toks = leftover_tokens(host[3], counts)
     x, packed, scales, sel, p, shared = host
-    y_own = run_linear(x[toks], packed, scales, sel[toks], p[toks], shared[toks])
+    y_own = run_linear(x[toks], packed, scales, sel[toks], p[toks], shared[toks], layout=layout)
     assert torch.equal(y[torch.from_numpy(toks).to(DEV)], y_own)
 
 
-def test_partial_tiles_swiglu():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_partial_tiles_swiglu(layout):
     # the SwiGLU block: the down projection runs over the sorted rows with the same tile list
     counts = [145, 144, 129, 261, 16, 128, 90, 1]
     K, G, F, O = 2, 5, 160, 520
@@ -162,11 +173,17 @@ def test_partial_tiles_swiglu():
     dn_s = rng.integers(118, 127, (E, O, F // 32), dtype=np.uint8)
     p = rng.random((T, K)).astype(np.float32)
 
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)  # noqa: E731
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    prep = mx.prepare_swiglu(dv(gu_p), dv(gu_s), dv(dn_p), dv(dn_s)) if layout == "prepared" else None
+    say(f"tile boundary swiglu {layout}")
+
     def run(rows):
-        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)  # noqa: E731
-        dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
-        y = mx.moe_swiglu(bf(x[rows]), dv(gu_p), dv(gu_s), dv(dn_p), dv(dn_s), dv(sel[rows]), dv(p[rows]),
-                          bf(shared[rows]))
+        if prep is None:
+            y = mx.moe_swiglu(bf(x[rows]), dv(gu_p), dv(gu_s), dv(dn_p), dv(dn_s), dv(sel[rows]), dv(p[rows]),
+                              bf(shared[rows]))
+        else:
+            y = mx.moe_swiglu_prepared(bf(x[rows]), prep, dv(sel[rows]), dv(p[rows]), bf(shared[rows]))
         torch.cuda.synchronize()
         return y
 
@@ -182,4 +199,4 @@ def test_partial_tiles_swiglu():
         h = np.abs(oracle.swiglu_hidden(x64[ts], gu_p[e], gu_s[e]))
         D = np.abs(oracle.decode_expert(dn_p[e], dn_s[e]))
         np.add.at(reach, ts, p[ts, ks].astype(np.float64)[:, None] * (h @ D.T))
-    assert_bf16_close(host64(y), ref, "swiglu", extra=2.0 ** -8 * reach)
+    assert_bf16_close(host64(y), ref, f"swiglu {layout}", extra=2.0 ** -8 * reach)
