@@ -36,14 +36,16 @@
 // Each weight byte is fetched once per workgroup; each activation row once
 // per 512 weight rows. One full wait and one barrier per chunk.
 //
-// Operand A = weights: for MFMA k-step s (0..3) lane (r, c) reads, with two
-// conflict-free 16-byte LDS reads, dword s of its slot of all 8 fragments and
-// turns each dword's 8 codes into
-// 8 bf16 with gfx950's scaled FP4 convert, scale applied (exact: E2M1 times
-// a power of two is a bf16 value, or +-inf where it overflows). No decoded
-// weight is stored anywhere. Operand B = activations: lane (p, c) of k-step s
-// takes the 8 bf16 inputs 128q + 32c + 8s .. +7 of pair p - the inputs of the
-// weight lane (r, c) of that k-step, so every product pairs x_i with w_i. The
+// Operand A = weights: for MFMA k-step s (0..3) lane (r, c) reads dword d of
+// its slot of all 8 fragments (prepared: d = s, two conflict-free 16-byte LDS
+// reads of the interleaved blocks; canonical: d = (s + c) mod 4, eight 4-byte
+// reads that the slot positions spread over 64 banks) and turns each dword's
+// 8 codes into 8 bf16 with gfx950's scaled FP4 convert, scale applied (exact:
+// E2M1 times a power of two is a bf16 value, or +-inf where it overflows). No
+// decoded weight is stored anywhere. Operand B = activations: lane (p, c) of
+// k-step s takes the 8 bf16 inputs 128q + 32c + 8d .. +7 of pair p - the
+// inputs of the weight lane (r, c) of that k-step, so every product pairs x_i
+// with w_i. The
 // 16-byte pieces of activation row m sit at position piece ^ (m & 15) of its
 // LDS row: the 16 lanes that LDS serves together (16 bytes each across its 64
 // banks) read 16 rows at 16 distinct positions. Rows past the tile, inputs past I
