@@ -122,7 +122,9 @@ __global__ void __launch_bounds__(kWaves * 64, MXFP4_DECODE1_MIN_WAVES) gemv_one
       const uint32_t out = row_out | ((uint32_t)(G - 1 - g) >> 31);
       const uint32_t off = (uint32_t)(row * G + g) | (out * kOobGroup);
       wq[pos][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(off * 16u), 0, kCodeLoadPolicy));
-      sq[pos][j] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)off, 0, 0);
+      // the scale bytes non-temporal too: decode 9.44-9.51 -> 9.35-9.39 us (the
+      // row-contiguous kernel's decode8 measured slower with them: 112.8 -> 119.7 us)
+      sq[pos][j] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)off, 0, kCodeLoadPolicy);
     }
     // the shared output of the row, with the row set's last slot (a wave-uniform test)
     const uint32_t last = (live && i_k == K - 1) ? 0u : 1u;
